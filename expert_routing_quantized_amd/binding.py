@@ -1,0 +1,166 @@
+"""ctypes binding of libmoe (include/moe.h): argument marshalling only.
+
+Every step of the layer runs in the HIP kernels behind the C ABI; this
+module turns torch tensors into device pointers and the current HIP stream
+into a ``hipStream_t``.  If ``libmoe.so`` has not been built the import
+fails loudly -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16, MOE_Q4B32 = 0, 1, 2
+MOE_ROUTER_HE, MOE_ROUTER_EH = 0, 1
+MOE_LAYER_FORCE_EXACT_REFINE = 1
+MOE_ROUTE_INTERNAL, MOE_ROUTE_GIVEN = 0, 1
+
+STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE",
+          -4: "MOE_E_ALIGN", -5: "MOE_E_WORKSPACE", -6: "MOE_E_RANGE", -7: "MOE_E_HIP",
+          -8: "MOE_E_DEVICE_FLAG"}
+
+EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
+           "moe_expert_decode", "moe_grouped_forward", "moe_device_error",
+           "moe_status_string", "moe_last_error_message", "moe_abi_version"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("inter", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32), ("expert_dtype", ctypes.c_int32),
+        ("router_layout", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe.so and declare its prototypes (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() "
+                          "(python expert_routing_quantized_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    lib.moe_layer_create.argtypes = [ctypes.POINTER(LayerDesc), vp, ctypes.POINTER(vp)]
+    lib.moe_layer_destroy.argtypes = [vp]
+    lib.moe_workspace_bytes.argtypes = [vp, i32, ctypes.POINTER(sz)]
+    lib.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
+    lib.moe_expert_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_grouped_forward.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp, sz, vp]
+    lib.moe_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error_message.argtypes = []
+    lib.moe_last_error_message.restype = ctypes.c_char_p
+    lib.moe_abi_version.argtypes = []
+    for name in ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
+                 "moe_expert_decode", "moe_grouped_forward", "moe_device_error", "moe_abi_version"]:
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        detail = load_library().moe_last_error_message().decode()
+        raise MoeError(st, where, detail)
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Layer:
+    """One MoE layer over caller-owned device tensors.
+
+    The tensors passed here must stay alive and unchanged for the layer's
+    lifetime (the object keeps references to them).
+    """
+
+    def __init__(self, *, hidden, n_experts, top_k, inter, max_tokens, act_dtype, expert_dtype,
+                 router_w, w_gate, w_up, w_down, router_bias=None, s_gate=None, s_up=None,
+                 s_down=None, router_layout=MOE_ROUTER_EH, flags=0, stream=None):
+        self.lib = load_library()
+        self._keep = (router_w, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
+        self.desc = LayerDesc(hidden, n_experts, top_k, inter, max_tokens, act_dtype,
+                              expert_dtype, router_layout, flags, _ptr(router_w),
+                              _ptr(router_bias), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                              _ptr(s_gate), _ptr(s_up), _ptr(s_down))
+        self.H, self.E, self.k, self.I = hidden, n_experts, top_k, inter
+        self.max_tokens = max_tokens
+        h = ctypes.c_void_p()
+        _check(self.lib.moe_layer_create(ctypes.byref(self.desc), _stream(stream), ctypes.byref(h)),
+               "moe_layer_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self.lib.moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_bytes(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        _check(self.lib.moe_workspace_bytes(self.handle, T, ctypes.byref(n)), "moe_workspace_bytes")
+        return n.value
+
+    def workspace(self, T: int, device="cuda"):
+        import torch
+        return torch.empty(max(1, self.workspace_bytes(T)), dtype=torch.uint8, device=device)
+
+    def route(self, x, T, idx, gates, ws, stream=None):
+        _check(self.lib.moe_route(self.handle, _ptr(x), T, _ptr(idx), _ptr(gates), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)), "moe_route")
+
+    def expert_decode(self, x, idx, gates, out, ws, stream=None):
+        _check(self.lib.moe_expert_decode(self.handle, _ptr(x), _ptr(idx), _ptr(gates), _ptr(out),
+                                          _ptr(ws), ws.numel() if ws is not None else 0,
+                                          _stream(stream)), "moe_expert_decode")
+
+    def grouped_forward(self, x, T, idx, gates, flags, out, ws, stream=None):
+        _check(self.lib.moe_grouped_forward(self.handle, _ptr(x), T, _ptr(idx), _ptr(gates), flags,
+                                            _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
+                                            _stream(stream)), "moe_grouped_forward")
+
+    def device_error(self, stream=None) -> int:
+        code = ctypes.c_int32()
+        st = self.lib.moe_device_error(self.handle, _stream(stream), ctypes.byref(code))
+        if st not in (0, -8):
+            _check(st, "moe_device_error")
+        return code.value

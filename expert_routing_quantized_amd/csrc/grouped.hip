@@ -1,0 +1,405 @@
+// Grouped expert path for T > 1 tokens (verify windows and prefill chunks:
+// pyshine source tour, "Guess, then check" and "Prompts are read in batched
+// pieces").  The T*k token-expert pairs are sorted by expert so that each
+// active expert's weights are streamed once for all of its tokens:
+//
+//   counts[e]  = #pairs routed to e            (integer atomics)
+//   offsets    = exclusive scan of counts; active = experts with counts > 0
+//   pos[p]     = offsets[e_p] + rank of p inside e's segment
+//   ptok[pos]  = token of the pair stored at that segment position
+//   Hm[pos][:] = silu(G_e x_t) * (U_e x_t)       (fp32)
+//   Y[pos][:]  = D_e Hm[pos]                      (fp32)
+//   out[t]     = sum_j g[t][j] Y[pos[t k + j]]    (j in order: deterministic)
+//
+// The order of pairs inside a segment comes from atomics, but no result
+// depends on it: every row of Hm and Y is computed from its own token only.
+// The vector-ALU kernels below keep one weight row slice in registers and
+// loop over the segment's tokens, which suits the small groups of verify
+// windows (about 1.1 tokens per active expert at T = 5).
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ float silu_g(float a) { return a / (1.0f + expf(-a)); }
+
+__device__ __forceinline__ float q4_dot32(const uint4 w, const float* xv) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = ws[q] & 0x0f0f0f0fu;
+    const uint32_t hi = (ws[q] >> 4) & 0x0f0f0f0fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      acc = fmaf((float)((lo >> (8 * b)) & 0xffu), xv[8 * q + 2 * b], acc);
+      acc = fmaf((float)((hi >> (8 * b)) & 0xffu), xv[8 * q + 2 * b + 1], acc);
+    }
+  }
+  return acc;
+}
+
+struct GroupArgs {
+  const void* x;            // [T][H]
+  const int32_t* idx;       // [T][k]
+  const float* gates;       // [T][k]
+  const void *wg, *wu, *wd;
+  const uint16_t *sg, *su, *sd;
+  int T, H, I, E, k, P;
+  int* counts;              // [E]
+  int* offsets;             // [E+1]
+  int* slot;                // [P]
+  int* pos;                 // [P]
+  int* ptok;                // [P]
+  int* active;              // [E+1]: [0] = number of active experts
+  float* hm;                // [P][I]
+  float* y;                 // [P][H]
+  float* out;               // [T][H]
+  int* dev_flag;
+};
+
+__global__ void fill_i32_kernel(int* p, int v, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+__global__ void hist_kernel(GroupArgs a) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= a.P) return;
+  const int e = a.idx[p];
+  if (e < 0 || e >= a.E) {
+    atomicOr(a.dev_flag, kDevBadIndex);
+    a.slot[p] = -1;
+    return;
+  }
+  const int t = p / a.k, j = p - t * a.k;
+  for (int jj = 0; jj < j; ++jj)
+    if (a.idx[t * a.k + jj] == e) atomicOr(a.dev_flag, kDevDupIndex);
+  a.slot[p] = atomicAdd(&a.counts[e], 1);
+}
+
+// Single-workgroup exclusive scan of counts and compaction of active experts.
+__global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
+  __shared__ int s_sum[1024];
+  __shared__ int s_act[1024];
+  __shared__ int carry, acarry;
+  if (threadIdx.x == 0) {
+    carry = 0;
+    acarry = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < a.E; base += 1024) {
+    const int e = base + threadIdx.x;
+    const int c = (e < a.E) ? a.counts[e] : 0;
+    s_sum[threadIdx.x] = c;
+    s_act[threadIdx.x] = (c > 0);
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {   // Hillis-Steele inclusive scans
+      const int v = (threadIdx.x >= off) ? s_sum[threadIdx.x - off] : 0;
+      const int w = (threadIdx.x >= off) ? s_act[threadIdx.x - off] : 0;
+      __syncthreads();
+      s_sum[threadIdx.x] += v;
+      s_act[threadIdx.x] += w;
+      __syncthreads();
+    }
+    if (e < a.E) {
+      a.offsets[e] = carry + s_sum[threadIdx.x] - c;
+      if (c > 0) a.active[1 + acarry + s_act[threadIdx.x] - 1] = e;
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) {
+      carry += s_sum[1023];
+      acarry += s_act[1023];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    a.offsets[a.E] = carry;
+    a.active[0] = acarry;
+  }
+}
+
+__global__ void scatter_kernel(GroupArgs a) {
+  const int p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= a.P) return;
+  const int s = a.slot[p];
+  if (s < 0) {
+    a.pos[p] = -1;
+    return;
+  }
+  const int q = a.offsets[a.idx[p]] + s;
+  a.pos[p] = q;
+  a.ptok[q] = p / a.k;
+}
+
+// --------------------------------------------------------------- gate/up
+// One wave per pair of intermediate rows of one active expert; the weights
+// stay in registers while the wave walks the expert's tokens.
+template <int ACT, int WD, int SL>
+__global__ __launch_bounds__(256) void grouped_gateup_kernel(GroupArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nact = a.active[0];
+  constexpr int kRows = 2;
+  const int i0 = (blockIdx.x * 4 + wave) * kRows;
+  // slot layout: q4 -> SL quant blocks of 32 per lane; dense -> SL chunks of 8 per lane
+  constexpr int kElems = (WD == MOE_Q4B32) ? 32 : 8;
+  const int nsl = a.H / kElems;
+  for (int ai = blockIdx.y; ai < nact; ai += gridDim.y) {
+    const int e = a.active[1 + ai];
+    const int n = a.counts[e];
+    const int seg = a.offsets[e];
+    uint4 wq[2][kRows][SL];
+    float dq[2][kRows][SL];
+    Chunk<WD == MOE_Q4B32 ? MOE_BF16 : WD> wdn[2][kRows][(WD == MOE_Q4B32) ? 1 : SL];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int i = i0 + r;
+      const size_t row = size_t(e) * a.I + i;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const int c = s * 64 + lane;
+        const bool ok = (i < a.I) && (c < nsl);
+        if constexpr (WD == MOE_Q4B32) {
+          if (ok) {
+            wq[0][r][s] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * (a.H / 2) + c * 16);
+            wq[1][r][s] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * (a.H / 2) + c * 16);
+            dq[0][r][s] = f16_to_f32(a.sg[row * nsl + c]);
+            dq[1][r][s] = f16_to_f32(a.su[row * nsl + c]);
+          } else {
+            wq[0][r][s] = wq[1][r][s] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+            dq[0][r][s] = dq[1][r][s] = 0.f;
+          }
+        } else {
+          if (ok) {
+            wdn[0][r][s].load(a.wg, row * a.H + c * 8);
+            wdn[1][r][s].load(a.wu, row * a.H + c * 8);
+          } else {
+            if constexpr (WD == MOE_BF16) { wdn[0][r][s].v = wdn[1][r][s].v = make_uint4(0, 0, 0, 0); }
+            else { wdn[0][r][s].a = wdn[0][r][s].b = wdn[1][r][s].a = wdn[1][r][s].b = make_float4(0, 0, 0, 0); }
+          }
+        }
+      }
+    }
+    for (int q = 0; q < n; ++q) {
+      const int t = a.ptok[seg + q];
+      float pa[kRows] = {}, pu[kRows] = {};
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const int c = s * 64 + lane;
+        if (c >= nsl) continue;
+        float xv[kElems];
+#pragma unroll
+        for (int cc = 0; cc < kElems / 8; ++cc) {
+          Chunk<ACT> ch;
+          ch.load(a.x, size_t(t) * a.H + c * kElems + cc * 8);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xv[cc * 8 + i] = ch.get(i);
+        }
+        if constexpr (WD == MOE_Q4B32) {
+          float xs = 0.f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) xs += xv[i];
+#pragma unroll
+          for (int r = 0; r < kRows; ++r) {
+            pa[r] = fmaf(dq[0][r][s], q4_dot32(wq[0][r][s], xv) - 8.f * xs, pa[r]);
+            pu[r] = fmaf(dq[1][r][s], q4_dot32(wq[1][r][s], xv) - 8.f * xs, pu[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < kRows; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              pa[r] = fmaf(wdn[0][r][s].get(i), xv[i], pa[r]);
+              pu[r] = fmaf(wdn[1][r][s].get(i), xv[i], pu[r]);
+            }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const float av = wave_sum(pa[r]), uv = wave_sum(pu[r]);
+        const int i = i0 + r;
+        if (lane == 0 && i < a.I) a.hm[size_t(seg + q) * a.I + i] = silu_g(av) * uv;
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------- down
+// 8 lanes per output row; 8 rows per wave; weights in registers, tokens looped.
+template <int WD, int SL>
+__global__ __launch_bounds__(256) void grouped_down_kernel(GroupArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane & 7, grp = lane >> 3;
+  const int nact = a.active[0];
+  const int o = (blockIdx.x * 4 + wave) * 8 + grp;
+  constexpr int kElems = (WD == MOE_Q4B32) ? 32 : 8;
+  const int nsl = a.I / kElems;
+  for (int ai = blockIdx.y; ai < nact; ai += gridDim.y) {
+    const int e = a.active[1 + ai];
+    const int n = a.counts[e];
+    const int seg = a.offsets[e];
+    const size_t row = size_t(e) * a.H + o;
+    uint4 wq[SL];
+    float dq[SL];
+    Chunk<WD == MOE_Q4B32 ? MOE_BF16 : WD> wdn[(WD == MOE_Q4B32) ? 1 : SL];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) {
+      const int c = s * 8 + g;
+      const bool ok = (o < a.H) && (c < nsl);
+      if constexpr (WD == MOE_Q4B32) {
+        if (ok) {
+          wq[s] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (a.I / 2) + c * 16);
+          dq[s] = f16_to_f32(a.sd[row * nsl + c]);
+        } else {
+          wq[s] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+          dq[s] = 0.f;
+        }
+      } else {
+        if (ok) {
+          wdn[s].load(a.wd, row * a.I + c * 8);
+        } else {
+          if constexpr (WD == MOE_BF16) wdn[s].v = make_uint4(0, 0, 0, 0);
+          else { wdn[s].a = wdn[s].b = make_float4(0, 0, 0, 0); }
+        }
+      }
+    }
+    for (int q = 0; q < n; ++q) {
+      const float* hr = a.hm + size_t(seg + q) * a.I;
+      float p = 0.f;
+#pragma unroll
+      for (int s = 0; s < SL; ++s) {
+        const int c = s * 8 + g;
+        if (c >= nsl) continue;
+        float hv[kElems];
+#pragma unroll
+        for (int i = 0; i < kElems; i += 4) {
+          const float4 v4 = *reinterpret_cast<const float4*>(hr + c * kElems + i);
+          hv[i] = v4.x; hv[i + 1] = v4.y; hv[i + 2] = v4.z; hv[i + 3] = v4.w;
+        }
+        if constexpr (WD == MOE_Q4B32) {
+          float hs = 0.f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) hs += hv[i];
+          p = fmaf(dq[s], q4_dot32(wq[s], hv) - 8.f * hs, p);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p = fmaf(wdn[s].get(i), hv[i], p);
+        }
+      }
+      p = group_sum(p, 8);
+      if (g == 0 && o < a.H) a.y[size_t(seg + q) * a.H + o] = p;
+    }
+  }
+}
+
+// --------------------------------------------------------------- combine
+__global__ __launch_bounds__(256) void combine_kernel(GroupArgs a) {
+  const int t = blockIdx.y;
+  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  if (o >= a.H) return;
+  bool bad = false;
+  float acc = 0.f;
+  for (int j = 0; j < a.k; ++j) {
+    const int p = t * a.k + j;
+    const int q = a.pos[p];
+    if (q < 0) {
+      bad = true;
+      continue;
+    }
+    for (int jj = 0; jj < j; ++jj) bad |= (a.idx[t * a.k + jj] == a.idx[p]);
+    acc = fmaf(a.gates[p], a.y[size_t(q) * a.H + o], acc);
+  }
+  a.out[size_t(t) * a.H + o] = bad ? NAN : acc;
+}
+
+hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const int32_t* idx,
+                                  const float* gates, float* out, char* ws, const Workspace& W,
+                                  hipStream_t s) {
+  GroupArgs a;
+  a.x = x;
+  a.idx = idx;
+  a.gates = gates;
+  a.wg = L.d.w_gate;
+  a.wu = L.d.w_up;
+  a.wd = L.d.w_down;
+  a.sg = L.d.s_gate;
+  a.su = L.d.s_up;
+  a.sd = L.d.s_down;
+  a.T = T;
+  a.H = L.d.hidden;
+  a.I = L.d.inter;
+  a.E = L.d.n_experts;
+  a.k = L.d.top_k;
+  a.P = T * a.k;
+  a.counts = reinterpret_cast<int*>(ws + W.counts);
+  a.offsets = reinterpret_cast<int*>(ws + W.offsets);
+  a.slot = reinterpret_cast<int*>(ws + W.slot);
+  a.pos = reinterpret_cast<int*>(ws + W.pos);
+  a.ptok = reinterpret_cast<int*>(ws + W.ptok);
+  a.active = reinterpret_cast<int*>(ws + W.active);
+  a.hm = reinterpret_cast<float*>(ws + W.hm);
+  a.y = reinterpret_cast<float*>(ws + W.y);
+  a.out = out;
+  a.dev_flag = L.dev_flag;
+
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(min(1024, (a.E + 255) / 256)), dim3(256), 0, s, a.counts, 0, a.E);
+  hipLaunchKernelGGL(hist_kernel, dim3((a.P + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3((a.P + 255) / 256), dim3(256), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  const int maxact = min(a.P, a.E);
+  const int gy = min(maxact, 4096);
+  const int act = L.d.act_dtype, wd = L.d.expert_dtype;
+  dim3 g1((a.I + 7) / 8, gy);
+  if (wd == MOE_Q4B32) {
+    const int sl = (a.H / 32 + 63) / 64;
+#define MOE_GG_Q4(S)                                                                           \
+  if (sl <= S) {                                                                               \
+    if (act == MOE_BF16)                                                                       \
+      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_BF16, MOE_Q4B32, S>), g1, dim3(256), 0, s, a); \
+    else                                                                                       \
+      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_Q4B32, S>), g1, dim3(256), 0, s, a);  \
+  } else
+    MOE_GG_Q4(1) MOE_GG_Q4(2) MOE_GG_Q4(4) return hipErrorInvalidValue;
+#undef MOE_GG_Q4
+  } else {
+    const int sl = (a.H / 8 + 63) / 64;
+#define MOE_GG_D(S)                                                                                 \
+  if (sl <= S) {                                                                                    \
+    if (act == MOE_BF16 && wd == MOE_BF16)                                                          \
+      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_BF16, MOE_BF16, S>), g1, dim3(256), 0, s, a);   \
+    else if (act == MOE_F32 && wd == MOE_BF16)                                                      \
+      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_BF16, S>), g1, dim3(256), 0, s, a);    \
+    else                                                                                            \
+      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_F32, S>), g1, dim3(256), 0, s, a);     \
+  } else
+    MOE_GG_D(1) MOE_GG_D(2) MOE_GG_D(4) MOE_GG_D(8) MOE_GG_D(16) return hipErrorInvalidValue;
+#undef MOE_GG_D
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+
+  dim3 g2((a.H + 31) / 32, gy);
+  if (wd == MOE_Q4B32) {
+    const int sl = (a.I / 32 + 7) / 8;
+#define MOE_GD_Q4(S) \
+  if (sl <= S) hipLaunchKernelGGL((grouped_down_kernel<MOE_Q4B32, S>), g2, dim3(256), 0, s, a); else
+    MOE_GD_Q4(1) MOE_GD_Q4(2) MOE_GD_Q4(4) MOE_GD_Q4(8) MOE_GD_Q4(16) return hipErrorInvalidValue;
+#undef MOE_GD_Q4
+  } else {
+    const int sl = (a.I / 8 + 7) / 8;
+#define MOE_GD_D(S)                                                                      \
+  if (sl <= S) {                                                                         \
+    if (wd == MOE_BF16) hipLaunchKernelGGL((grouped_down_kernel<MOE_BF16, S>), g2, dim3(256), 0, s, a); \
+    else hipLaunchKernelGGL((grouped_down_kernel<MOE_F32, S>), g2, dim3(256), 0, s, a);  \
+  } else
+    MOE_GD_D(1) MOE_GD_D(2) MOE_GD_D(4) MOE_GD_D(8) MOE_GD_D(16) MOE_GD_D(32) MOE_GD_D(64) return hipErrorInvalidValue;
+#undef MOE_GD_D
+  }
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(combine_kernel, dim3((a.H + 255) / 256, T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,124 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Indices bit-exact (ordered), gates within 1e-6, outputs within a relative
+L2 error of 1e-3 per token.  Small layers span several router blocks and
+ragged tails; the full-size workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "C0": synth.CONFIGS["C0"],
+    "tiny_bf16": synth.small_spec(H=256, E=200, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_BF16,
+                                  bias_alpha=0.37, weight_seed=21, token_seed=22, name="tiny_bf16"),
+    "tiny_q4": synth.small_spec(H=256, E=200, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                                bias_alpha=0.37, weight_seed=23, token_seed=24, name="tiny_q4"),
+    "wide_q4": synth.small_spec(H=2048, E=130, k=10, I=256, act=synth.DT_BF16, expert=synth.DT_Q4,
+                                bias_alpha=0.37, weight_seed=25, token_seed=26, name="wide_q4"),
+    "odd_q4": synth.small_spec(H=96, E=70, k=3, I=32, act=synth.DT_BF16, expert=synth.DT_Q4,
+                               bias_alpha=None, weight_seed=27, token_seed=28, name="odd_q4"),
+    "f32_bf16x": synth.small_spec(H=136, E=65, k=5, I=40, act=synth.DT_F32, expert=synth.DT_BF16,
+                                  bias_alpha=0.37, weight_seed=29, token_seed=30, name="f32_bf16x"),
+}
+
+_cache = {}
+
+
+def setup(name):
+    if name not in _cache:
+        import synth.device as SD
+        spec = SMALL[name]
+        dl = SD.device_layer(spec)
+        _cache[name] = (spec, dl, G.host_oracle(spec))
+    return _cache[name]
+
+
+def test_device_generator_matches_host():
+    """Device fill == host generator, bit for bit (every format)."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    for name in ["C0", "tiny_bf16", "tiny_q4", "odd_q4"]:
+        G.note("generator", name)
+        spec, dl, _ = setup(name)
+        assert np.array_equal(SD.to_numpy_bits(dl.router_eh), synth.router_eh(spec))
+        for e in [0, 1, spec.E - 1]:
+            for which, t, s in [("gate", dl.w_gate, dl.s_gate), ("up", dl.w_up, dl.s_up),
+                                ("down", dl.w_down, dl.s_down)]:
+                kind, payload = synth.expert_stored(spec, e, which)
+                if kind == "q4":
+                    assert np.array_equal(SD.to_numpy_bits(t[e]), payload[0]), (name, e, which)
+                    assert np.array_equal(SD.to_numpy_bits(s[e]), payload[1]), (name, e, which)
+                else:
+                    assert np.array_equal(SD.to_numpy_bits(t[e]), payload), (name, e, which)
+        x = SD.device_tokens(spec, 3, 5)
+        assert np.array_equal(SD.to_numpy_bits(x), synth.tokens(spec, 3, 5))
+    torch.cuda.synchronize()
+
+
+def test_device_generator_fullsize_rows():
+    """Rows of the full-size pools, generated on device by counter offset."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec = synth.CONFIGS["C2"]
+    for e in [0, 7777, spec.E - 1]:
+        for which, tag, rows, K in [("gate", synth.TAG_GATE, spec.I, spec.H),
+                                    ("down", synth.TAG_DOWN, spec.H, spec.I)]:
+            G.note("fullsize rows", e, which)
+            codes = torch.empty((rows, K // 2), dtype=torch.uint8, device="cuda")
+            sc = torch.empty((rows, K // 32), dtype=torch.int16, device="cuda")
+            SD.fill_q4(codes, sc, synth.stream_key(spec.weight_seed, tag), e * rows, K, spec.sigma_w)
+            kind, (hq, hs) = synth.expert_stored(spec, e, which)
+            assert np.array_equal(SD.to_numpy_bits(codes), hq)
+            assert np.array_equal(SD.to_numpy_bits(sc), hs)
+            dense = torch.empty((rows, K), dtype=torch.bfloat16, device="cuda")
+            SD.fill_values(dense, synth.stream_key(spec.weight_seed, tag), e * rows * K, spec.sigma_w)
+            assert np.array_equal(SD.to_numpy_bits(dense), synth.expert_dense(spec, e, which))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("layout", ["EH", "HE"])
+def test_decode_parity_small(name, layout):
+    import synth.device as SD
+    spec, dl, L = setup(name)
+    G.note("decode", name, layout)
+    layer = SD.make_layer(dl, max_tokens=48, router_layout=layout)
+    x = SD.device_tokens(spec, 0, 48)
+    idx, gates, out = G.run_route_decode(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, 48)
+    r = G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/{layout}")
+    print(f"{name}/{layout}: rel L2 max {r.max():.2e} median {np.median(r):.2e}")
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("name", ["C0", "tiny_q4", "wide_q4", "f32_bf16x"])
+def test_forced_exact_refinement(name):
+    """The integer-accumulator refinement gives the same routing."""
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_FORCE_EXACT_REFINE
+    spec, dl, L = setup(name)
+    G.note("forced exact", name)
+    layer = SD.make_layer(dl, max_tokens=16, flags=MOE_LAYER_FORCE_EXACT_REFINE)
+    x = SD.device_tokens(spec, 100, 16)
+    idx, gates, out = G.run_route_decode(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 100, 16)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, name)
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("name", ["C0", "tiny_bf16", "tiny_q4", "wide_q4", "odd_q4", "f32_bf16x"])
+@pytest.mark.parametrize("T", [2, 5, 37])
+def test_grouped_parity_small(name, T):
+    import synth.device as SD
+    spec, dl, L = setup(name)
+    G.note("grouped", name, T)
+    layer = SD.make_layer(dl, max_tokens=T)
+    x = SD.device_tokens(spec, 200, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 200, T)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/T={T}")
+    assert layer.device_error() == 0
