@@ -1,0 +1,242 @@
+"""Benchmark of the MoE layer on one MI355X.
+
+Default workload: batch-1 decode through the 4-bit layer (H=2048, E=24,576,
+top-10, I=256, 4-bit experts in 32-element blocks with fp16 scales, bf16
+router and hidden states, Zipf-shaped router bias), sequential tokens.  One
+"step" is one token through the whole path: router GEMV, exact top-k with
+softmax gates, expert gate/up GEMV, down GEMV with the weighted combine.
+
+* Inputs are synthetic and seeded, generated straight into HBM before the
+  timed region.
+* The K timed steps (and the W warm-up steps) are captured into HIP graphs
+  and replayed; time = HIP events around the replay on the capture stream.
+* Cold router (default): the router is held in 3 bitwise-identical copies
+  (302 MB, more than the 256 MB Infinity Cache) and token t reads copy t % 3,
+  so each token's router read comes from HBM, as it would with the other
+  layers of a model running in between.  ``--mode warm`` uses one copy.
+* Roofline of the dominant kernel (the router GEMV, 92% of the bytes): the
+  same kernel is launched alone (moe_router_logits) K times in a graph and
+  timed with HIP events on its stream.
+* CPU baseline: the float64 oracle, timed on a bounded sample of tokens on
+  the host's cores; its results also check the GPU outputs of those tokens.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--config", default="C2", choices=["C1", "C2"])
+    p.add_argument("--mode", default="cold", choices=["cold", "warm"])
+    p.add_argument("--cpu-sample", type=int, default=12, help="tokens the oracle is timed on (0: skip)")
+    return p.parse_args()
+
+
+def step_bytes(spec) -> dict:
+    """Algorithmic bytes of one decode token (what the method must move)."""
+    H, E, k, I = spec.H, spec.E, spec.k, spec.I
+    act = 2 if spec.act == 1 else 4
+    router = E * H * act + E * 4 + H * act            # weights + bias + x
+    if spec.expert == 2:
+        per_expert = 3 * I * H // 2 + 3 * I * (H // 32) * 2
+    else:
+        per_expert = 3 * I * H * (2 if spec.expert == 1 else 4)
+    experts = k * per_expert
+    out = H * 4 + k * 8
+    return {"router": router, "experts": experts, "total": router + experts + out}
+
+
+def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out):
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp:
+        threads = min(threads, int(omp))
+    log(f"oracle: building float64 router ({spec.E}x{spec.H})")
+    L0 = oracle.layer_from_spec(spec)
+    X = oracle.tokens_f64(spec, first, count)
+    stored = {}
+
+    def fetch(e, which):
+        key = (e, which)
+        if key not in stored:
+            stored[key] = synth.expert_stored(spec, e, which)
+        return stored[key]
+    # untimed pass: generates the experts' stored bytes (data preparation)
+    Lp = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
+    Lp._absR = L0.absR()
+    oracle.moe_tokens(X[:count], Lp)
+    # timed pass: a fresh oracle over the same stored bytes
+    Lt = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
+    Lt._absR = L0.absR()
+    t0 = time.perf_counter()
+    o_idx, o_g, _, o_out = oracle.moe_tokens(X, Lt)
+    dt = time.perf_counter() - t0
+    rel = np.linalg.norm(gpu_out.astype(np.float64) - o_out, axis=1) / np.linalg.norm(o_out, axis=1)
+    parity = {"tokens": count, "idx_exact": bool(np.array_equal(gpu_idx, o_idx)),
+              "gate_max_abs_err": float(np.abs(gpu_gates - o_g).max()),
+              "out_rel_l2_max": float(rel.max()), "out_rel_l2_median": float(np.median(rel))}
+    base = {"value": count / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{count} tokens (tokens {first}..{first + count - 1} of the timed stream), "
+                      f"float64 numpy, {dt:.1f} s; expert bytes pre-generated"}
+    return base, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
+                                   "(the multi-GPU sharding is a design, see DESIGN.md)"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.device as SD
+
+    spec = synth.CONFIGS[args.config]
+    K, W = args.steps, args.warmup
+    n_rep = 3 if args.mode == "cold" else 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    dl = SD.device_layer(spec)
+    routers = [dl.router_eh] + [SD.device_router(spec) for _ in range(n_rep - 1)]
+    layers = [SD.make_layer(dl, max_tokens=1, router=r) for r in routers]
+    X = SD.device_tokens(spec, 0, W + K)
+    torch.cuda.synchronize()
+    log(f"layer ready in {time.time() - t0:.1f}s: pool {dl.nbytes_pool() / 1e9:.2f} GB, "
+        f"{n_rep} router copies")
+
+    ws = layers[0].workspace(1)
+    idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((W + K, spec.k), dtype=torch.float32, device=dev)
+    out = torch.zeros((W + K, spec.H), dtype=torch.float32, device=dev)
+    zbuf = torch.empty((spec.E,), dtype=torch.float32, device=dev)
+
+    def token(t):
+        L = layers[t % n_rep]
+        L.route(X[t], 1, idx[t], gates[t], ws)
+        L.expert_decode(X[t], idx[t], gates[t], out[t], ws)
+
+    # eager pass over the warm-up tokens (also loads the kernels)
+    for t in range(W):
+        token(t)
+    torch.cuda.synchronize()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g_warm, g_main, g_router = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g_warm, stream=s):
+            for t in range(W):
+                token(t)
+        with torch.cuda.graph(g_main, stream=s):
+            for t in range(W, W + K):
+                token(t)
+        with torch.cuda.graph(g_router, stream=s):
+            for t in range(W, W + K):
+                layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
+    torch.cuda.synchronize()
+
+    with torch.cuda.stream(s):
+        g_warm.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g_main.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        # the dominant kernel alone, same launch configuration
+        g_router.replay()
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(s)
+        g_router.replay()
+        r1.record(s)
+        torch.cuda.synchronize()
+        ms_router = r0.elapsed_time(r1)
+    errs = [L.device_error() for L in layers]
+
+    per_tok_s = ms / 1e3 / K
+    tok_s = K / (ms / 1e3)
+    by = step_bytes(spec)
+    router_s = ms_router / 1e3 / K
+    router_gbs = by["router"] / router_s / 1e9
+    res = {
+        "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, 4-bit experts)"
+                  if args.config == "C2" else "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, bf16 experts)",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{args.config} batch-1 decode: H={spec.H}, E={spec.E}, top-{spec.k}, I={spec.I}, "
+                         + ("4-bit experts (32-blocks, fp16 scales)" if spec.expert == 2 else "bf16 experts")
+                         + f", bf16 router and hidden states, {K} sequential tokens, "
+                         + f"{args.mode} router ({n_rep} cop{'ies' if n_rep > 1 else 'y'})"),
+            "operands": "x bf16, router bf16, experts " + ("q4b32" if spec.expert == 2 else "bf16")
+                        + ", fp32 accumulation, f64 near-tie refinement",
+            "bytes_per_token": by["total"],
+            "hbm_gbs": by["total"] / per_tok_s / 1e9,
+            "us_per_token": per_tok_s * 1e6,
+            "device_errors": errs,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "router GEMV (moe::router_kernel<bf16, CPL=4, NT=1>)",
+            "achieved": router_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": router_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "avg_launch_us": router_s * 1e6,
+            "bytes_per_launch": by["router"],
+        },
+    }
+    if args.cpu_sample > 0:
+        n = min(args.cpu_sample, K)
+        gi = idx[W:W + n].cpu().numpy()
+        gg = gates[W:W + n].cpu().numpy()
+        go = out[W:W + n].cpu().numpy()
+        base, parity = cpu_baseline(spec, W, n, gi, gg, go)
+        res["cpu_baseline"] = base
+        res["config"]["parity_sample"] = parity
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE"
           -8: "MOE_E_DEVICE_FLAG"}
 
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
-           "moe_expert_decode", "moe_grouped_forward", "moe_device_error",
+           "moe_expert_decode", "moe_grouped_forward", "moe_device_error", "moe_router_logits",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_workspace_bytes.argtypes = [vp, i32, ctypes.POINTER(sz)]
     lib.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
     lib.moe_expert_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_router_logits.argtypes = [vp, vp, i32, vp, vp, sz, vp]
     lib.moe_grouped_forward.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp, sz, vp]
     lib.moe_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.moe_status_string.argtypes = [i32]
@@ -71,7 +72,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_last_error_message.restype = ctypes.c_char_p
     lib.moe_abi_version.argtypes = []
     for name in ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
-                 "moe_expert_decode", "moe_grouped_forward", "moe_device_error", "moe_abi_version"]:
+                 "moe_expert_decode", "moe_grouped_forward", "moe_device_error", "moe_router_logits", "moe_abi_version"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -147,6 +148,11 @@ class Layer:
     def route(self, x, T, idx, gates, ws, stream=None):
         _check(self.lib.moe_route(self.handle, _ptr(x), T, _ptr(idx), _ptr(gates), _ptr(ws),
                                   ws.numel() if ws is not None else 0, _stream(stream)), "moe_route")
+
+    def router_logits(self, x, T, z, ws, stream=None):
+        _check(self.lib.moe_router_logits(self.handle, _ptr(x), T, _ptr(z), _ptr(ws),
+                                          ws.numel() if ws is not None else 0, _stream(stream)),
+               "moe_router_logits")
 
     def expert_decode(self, x, idx, gates, out, ws, stream=None):
         _check(self.lib.moe_expert_decode(self.handle, _ptr(x), _ptr(idx), _ptr(gates), _ptr(out),

@@ -67,18 +67,13 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(DecodeArgs a) {
   for (int m = 0; m < MB; ++m) {
     const int b = m * 64 + lane;
     xs[m] = 0.f;
+    Chunk<ACT> ch[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      Chunk<ACT> ch;
-      if (b < nblk) {
-        ch.load(a.x, b * 32 + c * 8);
+    for (int c = 0; c < 4; ++c) ch[c].load(a.x, min(b, nblk - 1) * 32 + c * 8);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = ch.get(i);
-      } else {
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = 0.f;
-      }
-    }
+      for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = (b < nblk) ? ch[c].get(i) : 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) xs[m] += xv[m][i];
   }
@@ -87,24 +82,26 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(DecodeArgs a) {
   const size_t rowb = size_t(a.H) / 2;
   uint4 wg[kRowsPerWave][MB], wu[kRowsPerWave][MB];
   float dg[kRowsPerWave][MB], du[kRowsPerWave][MB];
+  // clamped indices: every load issues unconditionally; out-of-range lanes
+  // get scale 0 below (their codes are then irrelevant)
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = i0 + r;
+    const int i = min(i0 + r, a.I - 1);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      const int b = m * 64 + lane;
-      if (valid && i < a.I && b < nblk) {
-        const size_t row = size_t(e) * a.I + i;
-        wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * rowb + b * 16);
-        wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * rowb + b * 16);
-        dg[r][m] = f16_to_f32(a.sg[row * nblk + b]);
-        du[r][m] = f16_to_f32(a.su[row * nblk + b]);
-      } else {
-        wg[r][m] = wu[r][m] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        dg[r][m] = du[r][m] = 0.f;
-      }
+      const int b = min(m * 64 + lane, nblk - 1);
+      const size_t row = size_t(valid ? e : 0) * a.I + i;
+      wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * rowb + b * 16);
+      wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * rowb + b * 16);
+      dg[r][m] = f16_to_f32(a.sg[row * nblk + b]);
+      du[r][m] = f16_to_f32(a.su[row * nblk + b]);
     }
   }
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      if (!(i0 + r < a.I && m * 64 + lane < nblk)) dg[r][m] = du[r][m] = 0.f;
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     float pa = 0.f, pu = 0.f;
@@ -128,38 +125,36 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(DecodeArgs a) {
   const bool valid = (e >= 0 && e < a.E);
   const int nch = a.H >> 3;
   float xv[CPL][8];
+  {
+    Chunk<ACT> ch[CPL];
 #pragma unroll
-  for (int s = 0; s < CPL; ++s) {
-    const int c = s * 64 + lane;
-    Chunk<ACT> ch;
-    if (c < nch) {
-      ch.load(a.x, c * 8);
+    for (int s = 0; s < CPL; ++s) ch[s].load(a.x, min(s * 64 + lane, nch - 1) * 8);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[s][i] = ch.get(i);
-    } else {
+    for (int s = 0; s < CPL; ++s)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xv[s][i] = 0.f;
-    }
+      for (int i = 0; i < 8; ++i) xv[s][i] = (s * 64 + lane < nch) ? ch[s].get(i) : 0.f;
   }
   constexpr int kRowsPerWave = 2;
   const int i0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
   Chunk<WD> wg[kRowsPerWave][CPL], wu[kRowsPerWave][CPL];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = i0 + r;
+    const size_t row = size_t(valid ? e : 0) * a.I + min(i0 + r, a.I - 1);
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
-      const int c = s * 64 + lane;
-      if (valid && i < a.I && c < nch) {
-        const size_t row = size_t(e) * a.I + i;
-        wg[r][s].load(a.wg, row * a.H + c * 8);
-        wu[r][s].load(a.wu, row * a.H + c * 8);
-      } else {
-        if constexpr (WD == MOE_BF16) { wg[r][s].v = wu[r][s].v = make_uint4(0, 0, 0, 0); }
-        else { wg[r][s].a = wg[r][s].b = wu[r][s].a = wu[r][s].b = make_float4(0, 0, 0, 0); }
-      }
+      const int c = min(s * 64 + lane, nch - 1);
+      wg[r][s].load(a.wg, row * a.H + c * 8);
+      wu[r][s].load(a.wu, row * a.H + c * 8);
     }
   }
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+    for (int s = 0; s < CPL; ++s)
+      if (!(i0 + r < a.I && s * 64 + lane < nch)) {
+        wg[r][s].zero();
+        wu[r][s].zero();
+      }
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
     float pa = 0.f, pu = 0.f;
@@ -178,73 +173,78 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------ down + combine
 
+// One block per 8 output rows; wave w of the block handles the selected
+// experts j = w, w + W, ... (W = min(k, 16) waves), 8 lanes per output row,
+// lane g of a row covering quant blocks (or 8-element chunks) g, g + 8, ...
+// of I.  The expert's h slice comes straight from L2 into registers, so the
+// weights, the scales and h are all in flight together.  Each wave's
+// g_j-weighted partials go through LDS and are summed over the waves in a
+// fixed order (deterministic, no float atomics).
 template <int WD>
-__global__ __launch_bounds__(256) void down_combine_kernel(DecodeArgs a) {
-  extern __shared__ float sh[];          // [k][hpad(I)] then hsum [k][I/32]
+__global__ __launch_bounds__(1024) void down_combine_kernel(DecodeArgs a) {
+  __shared__ float part[kMaxK][8];
+  __shared__ int s_bad;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int g = lane & 7, grp = lane >> 3;
   const int I = a.I, k = a.k;
-  const int ipad = hpad(I);
+  const int o = blockIdx.x * 8 + grp;
+  const int oc = min(o, a.H - 1);
+  constexpr int kElems = (WD == MOE_Q4B32) ? 32 : 8;
+  const int nsl = I / kElems;
   const int nblk = I >> 5;
-  float* hs = sh + k * ipad;
-  __shared__ int s_bad;
-  if (threadIdx.x == 0) {
-    int bad = 0;
-    for (int j = 0; j < k; ++j) {
-      const int e = a.idx[j];
-      if (e < 0 || e >= a.E) bad |= kDevBadIndex;
-      for (int jj = 0; jj < j; ++jj)
-        if (a.idx[jj] == e) bad |= kDevDupIndex;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  if (threadIdx.x < k) {        // one thread per selected expert checks its index
+    const int j = threadIdx.x, e = a.idx[j];
+    int bad = (e < 0 || e >= a.E) ? kDevBadIndex : 0;
+    for (int jj = 0; jj < j; ++jj)
+      if (a.idx[jj] == e) bad |= kDevDupIndex;
+    if (bad) {
+      atomicOr(&s_bad, bad);
+      if (blockIdx.x == 0) atomicOr(a.dev_flag, bad);
     }
-    s_bad = bad;
-    if (bad && blockIdx.x == 0) atomicOr(a.dev_flag, bad);
   }
-  for (int q = threadIdx.x; q < k * I; q += blockDim.x) {
-    const int j = q / I, i = q - j * I;
-    sh[j * ipad + hpad(i)] = a.h[q];
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < k * nblk; q += blockDim.x) {
-    const int j = q / nblk, b = q - j * nblk;
-    float s = 0.f;
-    for (int i = 0; i < 32; ++i) s += sh[j * ipad + hpad(b * 32 + i)];
-    hs[q] = s;
-  }
-  __syncthreads();
 
-  const int o = (blockIdx.x * 4 + wave) * 8 + grp;
   float acc = 0.f;
-  if (o < a.H && !s_bad) {
-    for (int j = 0; j < k; ++j) {
-      const int e = a.idx[j];
-      const float gj = a.gates[j];
-      const size_t row = size_t(e) * a.H + o;
-      const float* hj = sh + j * ipad;
-      float p = 0.f;
-      if constexpr (WD == MOE_Q4B32) {
-        for (int b = g; b < nblk; b += 8) {
-          const uint4 w = *reinterpret_cast<const uint4*>(
-              reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + b * 16);
-          const float d = f16_to_f32(a.sd[row * nblk + b]);
-          float hv[32];
+  for (int j = wave; j < k; j += nw) {
+    int e = a.idx[j];
+    e = (e >= 0 && e < a.E) ? e : 0;                   // addresses stay in range
+    const float gj = a.gates[j];
+    const size_t row = size_t(e) * a.H + oc;
+    const float* hj = a.h + size_t(j) * I;
+    for (int sl = g; sl < nsl; sl += 8) {
+      float hv[kElems];
 #pragma unroll
-          for (int i = 0; i < 32; ++i) hv[i] = hj[hpad(b * 32) + i];
-          p = fmaf(d, q4_block_dot(w, hv) - 8.f * hs[j * nblk + b], p);
-        }
-      } else {
-        for (int c = g; c < (I >> 3); c += 8) {
-          Chunk<WD> w;
-          w.load(a.wd, row * I + c * 8);
-          const float* hv = hj + hpad(c * 8);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) p = fmaf(w.get(i), hv[i], p);
-        }
+      for (int i = 0; i < kElems; i += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(hj + sl * kElems + i);
+        hv[i] = v4.x; hv[i + 1] = v4.y; hv[i + 2] = v4.z; hv[i + 3] = v4.w;
       }
-      acc = fmaf(gj, p, acc);
+      if constexpr (WD == MOE_Q4B32) {
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + sl * 16);
+        const float d = f16_to_f32(a.sd[row * nblk + sl]);
+        float hs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) hs += hv[i];
+        acc = fmaf(gj, d * (q4_block_dot(w, hv) - 8.f * hs), acc);
+      } else {
+        Chunk<WD> w;
+        w.load(a.wd, row * I + sl * 8);
+        float p = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p = fmaf(w.get(i), hv[i], p);
+        acc = fmaf(gj, p, acc);
+      }
     }
   }
-  acc = group_sum(acc, 8);
-  if (g == 0 && o < a.H) a.out[o] = s_bad ? NAN : acc;
+  acc = group8_sum(acc);
+  if (g == 0) part[wave][grp] = acc;
+  __syncthreads();
+  if (threadIdx.x < 8 && blockIdx.x * 8 + (int)threadIdx.x < a.H) {
+    float s = 0.f;
+    for (int w = 0; w < nw; ++w) s += part[w][threadIdx.x];
+    a.out[blockIdx.x * 8 + threadIdx.x] = s_bad ? NAN : s;
+  }
 }
 
 hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* idx,
@@ -295,14 +295,14 @@ hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* i
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t lds = sizeof(float) * (size_t(a.k) * hpad(a.I) + size_t(a.k) * (a.I / 32 + 1));
-  dim3 g2((a.H + 31) / 32);
+  const int nw = a.k < 16 ? a.k : 16;
+  dim3 g2((a.H + 7) / 8);
   if (wd == MOE_Q4B32)
-    hipLaunchKernelGGL(down_combine_kernel<MOE_Q4B32>, g2, dim3(256), lds, s, a);
+    hipLaunchKernelGGL(down_combine_kernel<MOE_Q4B32>, g2, dim3(64 * nw), 0, s, a);
   else if (wd == MOE_BF16)
-    hipLaunchKernelGGL(down_combine_kernel<MOE_BF16>, g2, dim3(256), lds, s, a);
+    hipLaunchKernelGGL(down_combine_kernel<MOE_BF16>, g2, dim3(64 * nw), 0, s, a);
   else
-    hipLaunchKernelGGL(down_combine_kernel<MOE_F32>, g2, dim3(256), lds, s, a);
+    hipLaunchKernelGGL(down_combine_kernel<MOE_F32>, g2, dim3(64 * nw), 0, s, a);
   return hipGetLastError();
 }
 

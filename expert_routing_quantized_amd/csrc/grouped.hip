@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupArgs a) {
           for (int i = 0; i < 8; ++i) p = fmaf(wdn[s].get(i), hv[i], p);
         }
       }
-      p = group_sum(p, 8);
+      p = group8_sum(p);
       if (g == 0 && o < a.H) a.y[size_t(seg + q) * a.H + o] = p;
     }
   }

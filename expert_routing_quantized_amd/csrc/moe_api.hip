@@ -100,21 +100,14 @@ moe_status check_ws(const Layer& L, int T, const void* ws, size_t ws_bytes, Work
   return MOE_OK;
 }
 
-double gamma_f32(int n) {
-  const double u = 0x1p-23;   // twice the fp32 unit roundoff: also bounds truncation
-  return n * u / (1.0 - n * u);
-}
-
 moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float* gates,
                       char* ws, const Workspace& W, hipStream_t s) {
-  float* z = reinterpret_cast<float*>(ws + W.z);
-  float* tau = reinterpret_cast<float*>(ws + W.tau);
-  hipError_t e = moe::launch_router(L, x, T, z, tau, s);
+  double* z = reinterpret_cast<double*>(ws + W.z);
+  float* gmax = reinterpret_cast<float*>(ws + W.gmax);
+  double* xnorm = reinterpret_cast<double*>(ws + W.xnorm);
+  hipError_t e = moe::launch_router(L, x, T, z, gmax, xnorm, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  const int depth = moe::router_depth(L, T);
-  const double bt_unit = gamma_f32(depth) * 1.01 * L.norm_max;
-  const double bt_abs = depth * 0x1p-125;
-  e = moe::launch_select_impl(L, x, T, z, tau, W.ntau, idx, gates, bt_unit, bt_abs, s);
+  e = moe::launch_select_impl(L, x, T, z, gmax, xnorm, idx, gates, moe::router_bound(L, T), s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return MOE_OK;
 }
@@ -128,15 +121,15 @@ Workspace workspace_layout(const Layer& L, int T) {
   const size_t E = L.d.n_experts, k = L.d.top_k, I = L.d.inter, H = L.d.hidden;
   const size_t Tz = T < 1 ? 1 : size_t(T);
   const size_t P = Tz * k;
-  W.ntau = router_ntau(L);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
     off = round_up(off + bytes, 256);
     return o;
   };
-  W.z = take(Tz * E * 4);
-  W.tau = take(Tz * size_t(W.ntau) * 4);
+  W.z = take(Tz * E * 8);
+  W.gmax = take(Tz * ((E + 3) / 4) * 4);
+  W.xnorm = take(Tz * 8);
   W.idx = take(P * 4);
   W.gates = take(P * 4);
   W.h = take(k * I * 4);
@@ -257,6 +250,25 @@ moe_status moe_route(const moe_layer* layer, const void* x, int32_t T, int32_t* 
   return ok();
 }
 
+moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, double* z, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const Layer& L = layer->L;
+  if (T < 0 || T > L.d.max_tokens) return fail(MOE_E_RANGE, "T=%d outside [0, max_tokens=%d]", T, L.d.max_tokens);
+  if (T == 0) return ok();
+  if (!x || !z) return fail(MOE_E_NULL, "x and z are required");
+  if (!aligned(x, 16)) return fail(MOE_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(z, 8)) return fail(MOE_E_ALIGN, "z must be 8-byte aligned");
+  Workspace W;
+  if (moe_status st = check_ws(L, T, ws, ws_bytes, &W)) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = moe::launch_router(L, x, T, z, reinterpret_cast<float*>(w + W.gmax),
+                                    reinterpret_cast<double*>(w + W.xnorm), s);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  return ok();
+}
+
 moe_status moe_expert_decode(const moe_layer* layer, const void* x, const int32_t* idx,
                              const float* gates, float* out, void* ws, size_t ws_bytes,
                              void* stream) {
@@ -266,10 +278,6 @@ moe_status moe_expert_decode(const moe_layer* layer, const void* x, const int32_
   if (!aligned(x, 16)) return fail(MOE_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(idx, 4) || !aligned(gates, 4) || !aligned(out, 4))
     return fail(MOE_E_ALIGN, "idx/gates/out must be 4-byte aligned");
-  const size_t lds = sizeof(float) * (size_t(L.d.top_k) * moe::hpad(L.d.inter) +
-                                      size_t(L.d.top_k) * (L.d.inter / 32 + 1));
-  if (lds > 64 * 1024)
-    return fail(MOE_E_GEOMETRY, "top_k * inter too large for the single-token path (%zu B of LDS)", lds);
   Workspace W;
   if (moe_status st = check_ws(L, 1, ws, ws_bytes, &W)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -298,12 +306,6 @@ moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
     return fail(MOE_E_ALIGN, "idx/gates/out must be 4-byte aligned");
   Workspace W;
   if (moe_status st = check_ws(L, T, ws, ws_bytes, &W)) return st;
-  if (T == 1) {
-    const size_t lds = sizeof(float) * (size_t(L.d.top_k) * moe::hpad(L.d.inter) +
-                                        size_t(L.d.top_k) * (L.d.inter / 32 + 1));
-    if (lds > 64 * 1024)
-      return fail(MOE_E_GEOMETRY, "top_k * inter too large for the single-token path (%zu B of LDS)", lds);
-  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);

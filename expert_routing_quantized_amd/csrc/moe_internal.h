@@ -14,9 +14,9 @@ namespace moe {
 constexpr int kMaxK = 32;
 constexpr int kMaxH = 8192;
 constexpr int kMaxI = 4096;
-constexpr int kRouterEPB = 64;      // experts per router block (one k-th-value per block)
-constexpr int kSelectThreads = 1024;
-constexpr int kSelectMaxCand = 2048;  // candidates held in LDS at once
+constexpr int kRouterWaves = 4;      // router block = 4 waves, one expert row per wave
+constexpr int kSelectThreads = 512;
+constexpr int kSelectMaxCand = 1024;  // candidates held in LDS at once
 
 // device fault bits (moe_device_error)
 constexpr int kDevBadIndex = 1;
@@ -37,8 +37,9 @@ struct Layer {
 
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct Workspace {
-  size_t z;         // fp32 [T][E] approximate logits
-  size_t tau;       // fp32 [T][ntau] per-block k-th largest approximate logit
+  size_t z;         // f64 [T][E] approximate logits
+  size_t gmax;      // f32 [T][ceil(E/4)] maxima of 4 consecutive logits (rounded up)
+  size_t xnorm;     // f64 [T] squared norms of the hidden states
   size_t idx;       // int32 [T][k] routing (when the caller passes none)
   size_t gates;     // fp32 [T][k]
   size_t h;         // fp32 [k][I] decode intermediate
@@ -51,7 +52,6 @@ struct Workspace {
   size_t hm;        // fp32 [P][I] grouped intermediate (or bf16 hi/lo pairs)
   size_t y;         // fp32 [P][H] grouped expert outputs
   size_t total;
-  int ntau;
 };
 
 Workspace workspace_layout(const Layer& L, int T);
@@ -66,20 +66,89 @@ __device__ __forceinline__ float f16_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
-// Butterfly sum over the 64 lanes of a wave: every lane ends with the same
-// bits (each level adds the partner's value; fp addition commutes).
+// DPP lane exchanges (within 16-lane rows, plus row broadcasts).
+#define MOE_DPP_F32(v, ctrl, rmask) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), (rmask), 0xf, false))
+
+// Sum over the 64 lanes of a wave, returned to every lane.  Fixed tree for
+// every call: pairs inside quads, then quads, then 8-lane halves of a row
+// (each lane of a row then holds the row sum), then row 0 into row 1 and
+// row 2 into row 3 (row_bcast15), then rows 0-1 into rows 2-3 (row_bcast31);
+// lane 63 holds (r2 + r3) + (r0 + r1) and is broadcast.  Depth 6.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
+  v += MOE_DPP_F32(v, 0xB1, 0xf);     // quad_perm [1,0,3,2]
+  v += MOE_DPP_F32(v, 0x4E, 0xf);     // quad_perm [2,3,0,1]
+  v += MOE_DPP_F32(v, 0x141, 0xf);    // row_half_mirror
+  v += MOE_DPP_F32(v, 0x140, 0xf);    // row_mirror
+  v += MOE_DPP_F32(v, 0x142, 0xa);    // row_bcast:15 into rows 1 and 3
+  v += MOE_DPP_F32(v, 0x143, 0xc);    // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// Maximum over the 64 lanes (NaN-free inputs), returned to every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, MOE_DPP_F32(v, 0xB1, 0xf));
+  v = fmaxf(v, MOE_DPP_F32(v, 0x4E, 0xf));
+  v = fmaxf(v, MOE_DPP_F32(v, 0x141, 0xf));
+  v = fmaxf(v, MOE_DPP_F32(v, 0x140, 0xf));
+  const float b15 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v = fmaxf(v, b15);
+  const float b31 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+  v = fmaxf(v, b31);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+// Sum over aligned groups of 8 lanes; every lane of a group gets its sum.
+__device__ __forceinline__ float group8_sum(float v) {
+  v += MOE_DPP_F32(v, 0xB1, 0xf);
+  v += MOE_DPP_F32(v, 0x4E, 0xf);
+  v += MOE_DPP_F32(v, 0x141, 0xf);
   return v;
+}
+// 64-bit lane exchanges as two 32-bit DPP moves.
+// Lanes of rows outside RMASK receive `old`.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ double dpp_f64(double v, double old = 0.0) {
+  const long long b = __double_as_longlong(v), o = __double_as_longlong(old);
+  const int lo = __builtin_amdgcn_update_dpp(int(o & 0xffffffff), int(b & 0xffffffff), CTRL, RMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(int(o >> 32), int(b >> 32), CTRL, RMASK, 0xf, false);
+  return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+#define MOE_DPP_F64(v, ctrl, rmask) dpp_f64<(ctrl), (rmask)>(v)
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(int(b & 0xffffffff), lane);
+  const int hi = __builtin_amdgcn_readlane(int(b >> 32), lane);
+  return __longlong_as_double((long long)(unsigned)lo | ((long long)hi << 32));
+}
+// f64 sum over the 64 lanes with the same fixed tree as wave_sum (depth 6).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += MOE_DPP_F64(v, 0xB1, 0xf);
+  v += MOE_DPP_F64(v, 0x4E, 0xf);
+  v += MOE_DPP_F64(v, 0x141, 0xf);
+  v += MOE_DPP_F64(v, 0x140, 0xf);
+  v += MOE_DPP_F64(v, 0x142, 0xa);
+  v += MOE_DPP_F64(v, 0x143, 0xc);
+  return readlane_f64(v, 63);
+}
+// f64 maximum over each 16-lane row (every lane of a row gets its row max).
+__device__ __forceinline__ double row_max_f64(double v) {
+  v = fmax(v, MOE_DPP_F64(v, 0xB1, 0xf));
+  v = fmax(v, MOE_DPP_F64(v, 0x4E, 0xf));
+  v = fmax(v, MOE_DPP_F64(v, 0x141, 0xf));
+  v = fmax(v, MOE_DPP_F64(v, 0x140, 0xf));
+  return v;
+}
+// f64 maximum over the 64 lanes (NaN-free inputs), returned to every lane.
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = row_max_f64(v);
+  v = fmax(v, dpp_f64<0x142, 0xa>(v, -INFINITY));
+  v = fmax(v, dpp_f64<0x143, 0xc>(v, -INFINITY));
+  return readlane_f64(v, 63);
 }
 __device__ __forceinline__ double wave_sum_d(double v) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m);
-  return v;
-}
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int m = 1; m < width; m <<= 1) v += __shfl_xor(v, m);
   return v;
 }
 
@@ -102,6 +171,14 @@ __device__ __forceinline__ void two_sum(double a, double b, double& s, double& e
   e = (a - (s - bb)) + (b - bb);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed data that is read once).
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Router chunk decoding: 8 consecutive elements of an act-dtype row.
 template <int ACT>
 struct Chunk;
@@ -111,6 +188,10 @@ struct Chunk<MOE_BF16> {
   __device__ __forceinline__ void load(const void* base, size_t elem) {
     v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + elem);
   }
+  __device__ __forceinline__ void load_stream(const void* base, size_t elem) {
+    v = load_nt(reinterpret_cast<const uint16_t*>(base) + elem);
+  }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ float get(int i) const {
     uint32_t w = (i < 2) ? v.x : (i < 4) ? v.y : (i < 6) ? v.z : v.w;
     return (i & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -124,6 +205,16 @@ struct Chunk<MOE_F32> {
     a = p[0];
     b = p[1];
   }
+  __device__ __forceinline__ void load_stream(const void* base, size_t elem) {
+    const float* p = reinterpret_cast<const float*>(base) + elem;
+    const uint4 u = load_nt(p), w = load_nt(p + 4);
+    a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+    b = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+  }
+  __device__ __forceinline__ void zero() {
+    a = make_float4(0, 0, 0, 0);
+    b = a;
+  }
   __device__ __forceinline__ float get(int i) const {
     switch (i) {
       case 0: return a.x; case 1: return a.y; case 2: return a.z; case 3: return a.w;
@@ -133,18 +224,26 @@ struct Chunk<MOE_F32> {
 };
 
 // ------------------------------------------------------------------ launchers
-// router.hip: approximate fp32 logits z[t][e] for tokens [0, T) and per-block
-// k-th largest value tau[t][b]; returns the number of blocks (tau columns).
-int router_ntau(const Layer& L);
-hipError_t launch_router(const Layer& L, const void* x, int T, float* z, float* tau,
-                         hipStream_t s);
-// Rounding depth of one router logit of launch_router (see router.hip).
-int router_depth(const Layer& L, int T);
-// select.hip: exact top-k + gates per token from z/tau; bt_unit/bt_abs give
+// router.hip: approximate logits z[t][e] (binary64) for tokens [0, T), the
+// maximum of every 4 consecutive logits gmax[t][e/4] (binary32, rounded up)
+// and ||x_t||^2 (binary64).
+hipError_t launch_router(const Layer& L, const void* x, int T, double* z, float* gmax,
+                         double* xnorm, hipStream_t s);
+// Error model of one router logit:
+//   |z_hat - z| <= (gamma(d32, 2^-23) + gamma(d64, 2^-52)) ||x|| ||R_e||
+//                  + d32 2^-125 + d64 2^-1021 + 2^-52 |z_hat|,
+// gamma(n, u) = n u / (1 - n u) (the u's are twice the unit roundoffs, which
+// also covers truncating hardware).
+struct RouterBound {
+  int d32;
+  int d64;
+};
+RouterBound router_bound(const Layer& L, int T);
+// select.hip: exact top-k + gates per token from z; bt_unit/bt_abs give
 // the router's error bound Bt = bt_unit * ||x||_2 + bt_abs.
-hipError_t launch_select_impl(const Layer& L, const void* x, int T, const float* z,
-                              const float* tau, int ntau, int32_t* idx, float* gates,
-                              double bt_unit, double bt_abs, hipStream_t s);
+hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double* z,
+                              const float* gmax, const double* xnorm, int32_t* idx,
+                              float* gates, const RouterBound& rb, hipStream_t s);
 // experts.hip: single-token expert GEMVs and combine.
 hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* idx,
                                  const float* gates, float* out, float* h, hipStream_t s);

@@ -7,20 +7,28 @@
 // product runs on the vector ALUs.
 //
 // Layout: the router is read expert-major, row e = the H weights of expert
-// e (4 KB for H = 2048 in bf16).  A wave owns one row at a time: chunk c of
-// 8 elements (16 B in bf16) goes to lane c % 64, so each of the wave's loads
-// is 1 KB contiguous.  Each lane keeps the same chunks of x in registers.
+// e (4 KB for H = 2048 in bf16).  One wave owns one row: chunk c of 8
+// elements (16 B in bf16) goes to lane c % 64, so each of the wave's loads
+// is 1 KB contiguous, and all of the row's loads are issued at once
+// (non-temporal: the router is streamed once per token).  Each lane keeps
+// the same chunks of x in registers.  Blocks of 4 waves, one block per 4
+// experts: a measured sweep of launch shapes on gfx950 put this shape at
+// the streaming-read ceiling (about 6.5 TB/s), ahead of fewer, longer-lived
+// waves and of larger blocks.  Each block also writes the maximum of its 4
+// logits (per token), and block 0 writes ||x||^2, so the selection kernel
+// reads 1/4 of the logits' bytes to find its candidates.
 //
-// Rounding model (used by the selection kernel to bound |z_hat - z|): a lane
-// accumulates its 8*CPL products in a fixed order with one fp32 rounding per
-// product (fmaf on exact bf16 x bf16 products, or the bf16 dot2 instruction
-// counted as two roundings per pair), then a 6-level butterfly, then the
-// bias: depth 8*CPL + 7 for every expert, independent of e, so identical
-// rows give identical logits.
-//
-// Each block owns kRouterEPB = 64 consecutive experts and also writes the
-// k-th largest of its 64 logits per token (a lower bound on the token's
-// k-th largest logit, used to pre-filter candidates).
+// Rounding model (used by the selection kernel to bound |z_hat - z|), the
+// same for every expert, so identical rows give identical logits: each lane
+// accumulates its products in binary32 chains of 8 (one chain per 16-byte
+// chunk: fmaf on exact bf16 x bf16 products, or, for several tokens, four
+// bf16 dot2 instructions counted as two roundings each), converts each chain
+// sum to binary64 (exact), and everything after that -- the chains of the
+// lane, the 6-level DPP tree across the wave, the bias -- is binary64:
+//   |z_hat - z| <= gamma(d32, 2^-23) sum|p| + gamma(d64, 2^-52) sum|p| + ...
+// with d32 = 7 (fmaf) or 8 (dot2) and d64 = log2(CPL) + 7.  Converting once
+// per chain instead of once per product keeps the conversion (a slow
+// instruction) off the bandwidth-bound path.
 #include "moe_internal.h"
 
 namespace moe {
@@ -28,137 +36,159 @@ namespace moe {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <int ACT, int CPL, int NT>
-__global__ __launch_bounds__(512) void router_kernel(
+__global__ __launch_bounds__(kRouterWaves * 64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 8 : 1)))
+void router_kernel(
     const void* __restrict__ R, const void* __restrict__ x, const float* __restrict__ bias,
-    int H, int E, int T, int k, float* __restrict__ z, float* __restrict__ tau, int ntau) {
-  constexpr int kWaves = 8;
-  constexpr int kPerWave = kRouterEPB / kWaves;   // 8 experts per wave
-  constexpr int kUnroll = (ACT == MOE_BF16) ? 4 : 2;
-  __shared__ float zl[NT][kRouterEPB];
-
+    int H, int E, int T, double* __restrict__ z, float* __restrict__ gmax,
+    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
+  __shared__ double zl[NT][kRouterWaves];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int e = min(blockIdx.x * kRouterWaves + wave, E - 1);   // waves past E redo E-1, unused
+  const bool live = blockIdx.x * kRouterWaves + wave < E;
   const int nch = H >> 3;
   const int t0 = blockIdx.y * NT;
   const int nt = min(NT, T - t0);
+  const int G4 = (E + kRouterWaves - 1) / kRouterWaves;
 
-  // x chunks of this lane: floats for one token, packed bf16 pairs for several.
+  // The row's chunks first (longest latency), then x.  Chunk indices past
+  // the row are clamped to its last chunk and the values zeroed afterwards,
+  // so every load is issued unconditionally (no branch between loads).
+  Chunk<ACT> r[CPL];
+#pragma unroll
+  for (int s = 0; s < CPL; ++s) {
+    const int c = min(s * 64 + lane, nch - 1);
+    r[s].load_stream(R, size_t(e) * H + c * 8);
+  }
+  const float b = (bias != nullptr) ? bias[e] : 0.f;
+#pragma unroll
+  for (int s = 0; s < CPL; ++s)
+    if (s * 64 + lane >= nch) r[s].zero();
   constexpr bool kPacked = (ACT == MOE_BF16) && (NT > 1);
-  float xf[kPacked ? 1 : CPL][kPacked ? 1 : 8];
-  uint4 xp[kPacked ? NT : 1][kPacked ? CPL : 1];
   if constexpr (kPacked) {
+    uint4 xp[NT][CPL];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
-        const int c = s * 64 + lane;
-        xp[t][s] = make_uint4(0, 0, 0, 0);
-        if (c < nch && t < nt)
-          xp[t][s] = *reinterpret_cast<const uint4*>(
-              reinterpret_cast<const uint16_t*>(x) + size_t(t0 + t) * H + c * 8);
+        const int c = min(s * 64 + lane, nch - 1);
+        const int tt = min(t, nt - 1);
+        xp[t][s] = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const uint16_t*>(x) + size_t(t0 + tt) * H + c * 8);
       }
-  } else {
 #pragma unroll
-    for (int s = 0; s < CPL; ++s) {
-      const int c = s * 64 + lane;
-      Chunk<ACT> ch;
-      if (c < nch) {
-        ch.load(x, size_t(t0) * H + c * 8);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xf[s][i] = ch.get(i);
-      } else {
+      for (int s = 0; s < CPL; ++s)
+        if (s * 64 + lane >= nch || t >= nt) xp[t][s] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xf[s][i] = 0.f;
-      }
-    }
-  }
-
-  const int e_base = blockIdx.x * kRouterEPB + wave * kPerWave;
-  for (int i0 = 0; i0 < kPerWave; i0 += kUnroll) {
-    Chunk<ACT> r[kUnroll][CPL];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = e_base + i0 + u;
+    for (int t = 0; t < NT; ++t) {
+      double acc[CPL];
 #pragma unroll
       for (int s = 0; s < CPL; ++s) {
-        const int c = s * 64 + lane;
-        if (e < E && c < nch) {
-          r[u][s].load(R, size_t(e) * H + c * 8);
-        } else {
-          if constexpr (ACT == MOE_BF16) r[u][s].v = make_uint4(0, 0, 0, 0);
-          else { r[u][s].a = make_float4(0, 0, 0, 0); r[u][s].b = r[u][s].a; }
-        }
-      }
-    }
+        const uint32_t xw[4] = {xp[t][s].x, xp[t][s].y, xp[t][s].z, xp[t][s].w};
+        const uint32_t rw[4] = {r[s].v.x, r[s].v.y, r[s].v.z, r[s].v.w};
+        float c = 0.f;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int e = e_base + i0 + u;
-      const int le = wave * kPerWave + i0 + u;
-      const float b = (bias != nullptr && e < E) ? bias[e] : 0.f;
+        for (int q = 0; q < 4; ++q)
+          c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw[q]),
+                                              __builtin_bit_cast(bf16x2_t, rw[q]), c, false);
+        acc[s] = (double)c;
+      }
+#pragma unroll
+      for (int w = 1; w < CPL; w <<= 1)
+#pragma unroll
+        for (int s = 0; s + w < CPL; s += 2 * w) acc[s] += acc[s + w];
+      const double v = wave_sum_f64(acc[0]) + (double)b;
+      if (lane == t && t < nt && live) z[size_t(t0 + t) * E + e] = v;
+      if (lane == 0) zl[t][wave] = live ? v : -INFINITY;
+    }
+    if (blockIdx.x == 0) {      // ||x_t||^2 of this block's tokens (binary32 sums)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        float acc = 0.f;
-        if constexpr (kPacked) {
+        if (t % kRouterWaves != wave || t >= nt) continue;   // wave-uniform
+        float q = 0.f;
 #pragma unroll
-          for (int s = 0; s < CPL; ++s) {
-            const uint32_t xw[4] = {xp[t][s].x, xp[t][s].y, xp[t][s].z, xp[t][s].w};
-            const uint32_t rw[4] = {r[u][s].v.x, r[u][s].v.y, r[u][s].v.z, r[u][s].v.w};
+        for (int s2 = 0; s2 < CPL; ++s2) {
+          const uint32_t xw[4] = {xp[t][s2].x, xp[t][s2].y, xp[t][s2].z, xp[t][s2].w};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw[q]),
-                                                    __builtin_bit_cast(bf16x2_t, rw[q]), acc,
-                                                    false);
+          for (int i = 0; i < 8; ++i) {
+            const float xv = (i & 1) ? bf16_hi(xw[i >> 1]) : bf16_lo(xw[i >> 1]);
+            q = fmaf(xv, xv, q);
           }
-        } else {
-#pragma unroll
-          for (int s = 0; s < CPL; ++s)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc = fmaf(xf[s][i], r[u][s].get(i), acc);
         }
-        const float v = wave_sum(acc) + b;
-        if (lane == t) {
-          if (e < E && t < nt) z[size_t(t0 + t) * E + e] = v;
-          zl[t][le] = (e < E) ? v : -INFINITY;
-        }
+        q = wave_sum(q);
+        if (lane == 0) xnorm[t0 + t] = (double)q;
       }
+    }
+  } else {
+    // one token: binary32 chains of 8 exact products, then binary64
+    static_assert(NT == 1, "unpacked path handles one token per block row");
+    Chunk<ACT> xc[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) xc[s].load(x, size_t(t0) * H + min(s * 64 + lane, nch - 1) * 8);
+    auto xf_get = [](const Chunk<ACT>& c, int i, bool in) { return in ? c.get(i) : 0.f; };
+    double acc[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+      const bool in = s * 64 + lane < nch;
+      float c = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c = fmaf(in ? xc[s].get(i) : 0.f, r[s].get(i), c);
+      acc[s] = (double)c;
+    }
+#pragma unroll
+    for (int w = 1; w < CPL; w <<= 1)
+#pragma unroll
+      for (int s = 0; s + w < CPL; s += 2 * w) acc[s] += acc[s + w];
+    const double v = wave_sum_f64(acc[0]) + (double)b;
+    if (lane == 0 && live) z[size_t(t0) * E + e] = v;
+    if (lane == 0) zl[0][wave] = live ? v : -INFINITY;
+    if (blockIdx.x == 0 && wave == 0) {   // ||x||^2 (binary32 sum; the bound keeps a margin)
+      float q = 0.f;
+#pragma unroll
+      for (int s = 0; s < CPL; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xs = xf_get(xc[s], i, s * 64 + lane < nch);
+          q = fmaf(xs, xs, q);
+        }
+      q = wave_sum(q);
+      if (lane == 0) xnorm[t0] = (double)q;
     }
   }
+  // maximum of the block's logits per token, rounded up to binary32 (an
+  // upper bound: the selection scans a group whenever it might hold a
+  // candidate); NaN counts as -inf and raises the non-finite flag.
   __syncthreads();
-
-  // k-th largest of this block's logits, per token (NaN ranks lowest).
-  for (int t = 0; t < nt; ++t) {
-    if (threadIdx.x < kRouterEPB) {
-      const int j = threadIdx.x;
-      const float v = zl[t][j];
-      const uint32_t kv = f32_key(v);
-      int rank = 0;
-      for (int m = 0; m < kRouterEPB; ++m) {
-        const uint32_t km = f32_key(zl[t][m]);
-        rank += (km > kv) || (km == kv && m < j);
-      }
-      if (rank == k - 1) tau[size_t(t0 + t) * ntau + blockIdx.x] = isnan(v) ? -INFINITY : v;
+  if (threadIdx.x < nt) {
+    const int t = threadIdx.x;
+    double m = -INFINITY;
+    bool bad = false;
+    for (int w = 0; w < kRouterWaves; ++w) {
+      const double v = zl[t][w];
+      const bool lw = blockIdx.x * kRouterWaves + w < E;
+      if (lw && !isfinite(v)) bad = true;
+      if (!isnan(v)) m = fmax(m, v);
     }
-    if (k > kRouterEPB && threadIdx.x == 0) tau[size_t(t0 + t) * ntau + blockIdx.x] = -INFINITY;
+    if (bad) atomicOr(dev_flag, kDevNonFinite);
+    gmax[size_t(t0 + t) * G4 + blockIdx.x] = __double2float_ru(m);
   }
 }
 
-int router_ntau(const Layer& L) { return (L.d.n_experts + kRouterEPB - 1) / kRouterEPB; }
-
 template <int ACT, int NT>
-static hipError_t launch_cpl(const Layer& L, const void* x, int T, float* z, float* tau,
-                             hipStream_t s) {
+static hipError_t launch_cpl(const Layer& L, const void* x, int T, double* z, float* gmax,
+                             double* xnorm, hipStream_t s) {
   const int H = L.d.hidden, E = L.d.n_experts;
-  const int nch = H / 8;
-  const int cpl = (nch + 63) / 64;
-  const int nb = router_ntau(L);
-  dim3 grid(nb, (T + NT - 1) / NT);
-#define MOE_ROUTER_CASE(C)                                                                  \
-  if (cpl <= C) {                                                                           \
-    constexpr int NTX = (ACT == MOE_BF16 && NT > 1) ? ((NT * C > 32) ? 32 / C : NT) : NT; \
-    grid.y = (T + NTX - 1) / NTX;                                                           \
-    hipLaunchKernelGGL((router_kernel<ACT, C, NTX>), grid, dim3(512), 0, s, L.router_eh, x, \
-                       L.d.router_bias, H, E, T, L.d.top_k, z, tau, nb);                    \
-    return hipGetLastError();                                                               \
+  const int cpl = (H / 8 + 63) / 64;
+  dim3 grid((E + kRouterWaves - 1) / kRouterWaves, 1);
+#define MOE_ROUTER_CASE(C)                                                                    \
+  if (cpl <= C) {                                                                             \
+    constexpr int NTX = (ACT == MOE_BF16 && NT > 1) ? ((NT * C > 32) ? 32 / C : NT) : 1;    \
+    grid.y = (T + NTX - 1) / NTX;                                                             \
+    hipLaunchKernelGGL((router_kernel<ACT, C, NTX>), grid, dim3(kRouterWaves * 64), 0, s,     \
+                       L.router_eh, x, L.d.router_bias, H, E, T, z, gmax, xnorm, L.dev_flag); \
+    return hipGetLastError();                                                                 \
   }
   MOE_ROUTER_CASE(1)
   MOE_ROUTER_CASE(2)
@@ -169,18 +199,23 @@ static hipError_t launch_cpl(const Layer& L, const void* x, int T, float* z, flo
   return hipErrorInvalidValue;
 }
 
-// Rounding depth of one logit for the kernel chosen for (H, T): see header.
-int router_depth(const Layer& L, int T) {
-  (void)T;
+// Error model of the kernel chosen for (act dtype, T): see the header comment.
+RouterBound router_bound(const Layer& L, int T) {
   const int cpl = (L.d.hidden / 8 + 63) / 64;
-  return 8 * cpl + 7;
+  int lg = 0;
+  while ((1 << lg) < cpl) ++lg;
+  RouterBound b;
+  const bool dot2 = (L.d.act_dtype == MOE_BF16 && T > 1);
+  b.d32 = dot2 ? 8 : 7;
+  b.d64 = lg + 7;
+  return b;
 }
 
-hipError_t launch_router(const Layer& L, const void* x, int T, float* z, float* tau,
-                         hipStream_t s) {
-  if (L.d.act_dtype == MOE_F32) return launch_cpl<MOE_F32, 1>(L, x, T, z, tau, s);
-  if (T == 1) return launch_cpl<MOE_BF16, 1>(L, x, T, z, tau, s);
-  return launch_cpl<MOE_BF16, 8>(L, x, T, z, tau, s);
+hipError_t launch_router(const Layer& L, const void* x, int T, double* z, float* gmax,
+                         double* xnorm, hipStream_t s) {
+  if (L.d.act_dtype == MOE_F32) return launch_cpl<MOE_F32, 1>(L, x, T, z, gmax, xnorm, s);
+  if (T == 1) return launch_cpl<MOE_BF16, 1>(L, x, T, z, gmax, xnorm, s);
+  return launch_cpl<MOE_BF16, 8>(L, x, T, z, gmax, xnorm, s);
 }
 
 }  // namespace moe

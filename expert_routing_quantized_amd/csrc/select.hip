@@ -4,24 +4,37 @@
 // drafts are verified "bit-for-bit identical to greedy" ("Guess, then
 // check"); here the selected experts must equal those of the exact logits
 // (each rounded once to binary64, ties to the lower expert index).  The
-// router kernel's fp32 logits z_hat obey |z_hat - z| <= B(z_hat) with
-//   B(v) = Bt + 2^-23 |v|,   Bt = gamma'(d) ||x||_2 max_e ||R_e||_2 (1.01)
-// (Cauchy-Schwarz on the classical depth-d summation bound, gamma'(n) =
-// n 2^-23 / (1 - n 2^-23) which also covers truncating hardware, plus a
-// flush-to-zero term).  With tau the k-th largest z_hat, L = tau - B(tau) is
-// a lower bound on the k-th largest exact logit, so any expert with
-// z_hat + B(z_hat) < L has k experts strictly above it.  The remaining
-// candidates (k plus the few inside the band) are recomputed exactly:
+// router kernel's logits z_hat obey |z_hat - z| <= B(z_hat) with
+//   B(v) = Bt + 2^-52 |v|,
+//   Bt = (gamma(d32, 2^-23) + gamma(d64, 2^-52)) ||x||_2 max_e ||R_e||_2 (1.01) + tiny
+// (Cauchy-Schwarz on the classical summation bounds of the router's binary32
+// chains and binary64 tail; see router.hip).
+//
+// Fast path: from the router's maxima of every 4 consecutive logits, the
+// k-th largest of 64 maxima over disjoint sets of experts is a lower bound
+// tau0 on the k-th largest z_hat, since k distinct experts reach it.  Only
+// the groups of 4 whose maximum reaches the candidate threshold are read
+// (about a dozen of 6,144), their candidates are compacted with a wave
+// ballot and ranked by one wave, and if
+// no two of the k+1 leading intervals [z_hat - B, z_hat + B] overlap, their
+// order is the exact order: idx and the gates (from the binary64 logits) are
+// written without recomputing anything.
+//
+// Exact path (overlapping intervals: exact or near-exact ties; more than 64
+// survivors; binary32-accumulated logits): tau = k-th largest z_hat gives
+// L = tau - B(tau), a lower bound on the k-th largest exact logit; experts
+// with z_hat + B(z_hat) < L have k experts strictly above them, and the rest
+// are recomputed exactly:
 //  * double-double accumulation of the exact f64 products (TwoSum chains,
-//    Ogita-Rump-Oishi "Sum2" style); its error |s + c - z| is bounded by
-//    1.1 (n_l + 16)^2 2^-106 (sum|p| + |b|), n_l = products per lane;
-//  * if that interval does not decide the binary64 rounding of z (a value
-//    within the bound of a rounding midpoint), an exact fixed-point sum in
-//    16-bit digits (integer atomics in LDS) gives the correctly rounded value.
-// The pre-filter uses the router blocks' own k-th largest values (a lower
-// bound on tau), so the scan keeps only a few dozen survivors whose ranks
-// give tau exactly; a bisection over the fp32 keys covers the degenerate
-// case of more survivors than fit in LDS (e.g. all logits equal).
+//    Ogita-Rump-Oishi "Sum2" style), error <= 1.1 (n_l + 16)^2 2^-106
+//    (sum|p| + |b|), n_l = products per lane;
+//  * if that interval does not decide the binary64 rounding of z, an exact
+//    fixed-point sum in 16-bit digits (integer atomics in LDS) gives the
+//    correctly rounded value.
+// Every global load of a phase is issued before any is consumed: this kernel
+// is latency-bound.
+#include <float.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -34,14 +47,16 @@ struct SelectArgs {
   const void* R;          // expert-major router [E][H]
   const float* bias;
   const void* x;          // [T][H]
-  const float* z;         // [T][E]
-  const float* tau;       // [T][ntau]
-  int ntau, H, E, k;
+  const double* z;        // [T][E] router logits (binary64)
+  const float* gmax;      // [T][ceil(E/4)] maxima of 4 consecutive logits (rounded up)
+  const double* xnorm;    // [T] ||x_t||^2
+  int H, E, k;
   int32_t* idx;           // [T][k]
   float* gates;           // [T][k]
   int* dev_flag;
-  double bt_unit;         // gamma'(d) * 1.01 * max_e ||R_e||
+  double bt_unit;         // gamma(d, u) * 1.01 * max_e ||R_e||
   double bt_abs;          // absolute (flush-to-zero) term
+  double rel;             // u: relative term of the bound (final rounding)
   int force_exact;
 };
 
@@ -175,20 +190,39 @@ template <int ACT>
 __device__ double refine_logit(const SelectArgs& a, int t, int e, long long* bins, int lane) {
   const int nch = a.H >> 3;
   const double b = a.bias ? (double)a.bias[e] : 0.0;
-  double s = 0.0, c = 0.0, asum = 0.0;
-  for (int ch = lane; ch < nch; ch += 64) {
-    Chunk<ACT> xc, rc;
-    xc.load(a.x, size_t(t) * a.H + ch * 8);
-    rc.load(a.R, size_t(e) * a.H + ch * 8);
+  // Four independent TwoSum chains per lane (one per chunk slot) for
+  // instruction-level parallelism, merged error-free below.
+  double sc[4] = {0.0, 0.0, 0.0, 0.0}, cc[4] = {0.0, 0.0, 0.0, 0.0}, asum = 0.0;
+  // up to 4 chunks per lane per batch, all loads issued before the sums
+  for (int base = 0; base < nch; base += 256) {
+    Chunk<ACT> xc[4], rc[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const double p = (double)xc.get(i) * (double)rc.get(i);
-      double ss, ee;
-      two_sum(s, p, ss, ee);
-      s = ss;
-      c += ee;
-      asum += fabs(p);
+    for (int u = 0; u < 4; ++u) {
+      const int ch = min(base + u * 64 + lane, nch - 1);   // clamped: loads issue unconditionally
+      xc[u].load(a.x, size_t(t) * a.H + ch * 8);
+      rc[u].load(a.R, size_t(e) * a.H + ch * 8);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (base + u * 64 + lane >= nch) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const double p = (double)xc[u].get(i) * (double)rc[u].get(i);
+        double ss, ee;
+        two_sum(sc[u], p, ss, ee);
+        sc[u] = ss;
+        cc[u] += ee;
+        asum += fabs(p);
+      }
+    }
+  }
+  double s, c;
+  {
+    double s01, e01, s23, e23, ee;
+    two_sum(sc[0], sc[1], s01, e01);
+    two_sum(sc[2], sc[3], s23, e23);
+    two_sum(s01, s23, s, ee);
+    c = ((cc[0] + cc[1]) + e01) + ((cc[2] + cc[3]) + e23) + ee;
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -238,107 +272,197 @@ __device__ double refine_logit(const SelectArgs& a, int t, int e, long long* bin
 }
 
 // ---------------------------------------------------------------- kernel
+// Smallest value th such that every v >= th can satisfy v + Bt + u |v| >= L
+// (rounded down: the test is conservative).
+__device__ double cand_threshold(double L, double Bt, double u) {
+  if (isinf(L)) return L;
+  const double D = L - Bt;
+  double th = (D >= 0) ? D / (1.0 + u) : D / (1.0 - u);
+  return th - (1e-12 * fabs(th) + 1e-300);
+}
+
+__device__ __forceinline__ unsigned long long f64_key(double d) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(d);
+  if (isnan(d)) return 0ull;
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_f64(unsigned long long k) {
+  const unsigned long long u = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+  return __longlong_as_double((long long)u);
+}
+
 template <int ACT>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-  __shared__ float s_val[kSelectMaxCand];
+  constexpr int GPT = 12;                          // group maxima per thread (E <= 24,576 in one pass)
+  constexpr int GPASS = kSelectThreads * GPT;      // groups per pass
+  __shared__ double s_val[kSelectMaxCand];
   __shared__ int s_id[kSelectMaxCand];
   __shared__ int c_id[kSelectMaxCand];
   __shared__ double c_z[kSelectMaxCand];
+  __shared__ int s_glist[kSelectMaxCand];
+  __shared__ float s_tmax[kSelectThreads];
   __shared__ int top_e[kMaxK], new_e[kMaxK];
-  __shared__ double top_z[kMaxK], new_z[kMaxK];
+  __shared__ double top_z[kMaxK], new_z[kMaxK], s_w[kMaxK];
   __shared__ long long bins[kWavesSel][kBins];
   __shared__ double red[kWavesSel];
-  __shared__ int s_cnt, c_cnt, s_ntop, s_nonfinite;
-  __shared__ float s_tau;
+  __shared__ int s_cnt, c_cnt, s_ntop, s_done, s_ng;
+  __shared__ double s_tau, s_tau0;
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k;
-  const float* zr = a.z + size_t(t) * E;
+  const int G = (E + 3) / 4;                       // groups of 4 consecutive experts
+  const double* zr = a.z + size_t(t) * E;
+  const float* gr = a.gmax + size_t(t) * G;
+  int32_t* oi = a.idx + size_t(t) * k;
+  float* og = a.gates + size_t(t) * k;
+  const int npass = (G + GPASS - 1) / GPASS;
 
   if (tid == 0) {
     s_cnt = 0;
     c_cnt = 0;
     s_ntop = 0;
-    s_nonfinite = 0;
+    s_done = 0;
+    s_ng = 0;
     s_tau = -INFINITY;
+    s_tau0 = -INFINITY;
   }
 
-  // 1. ||x_t||_2 in f64 (squares of fp32 values are exact in f64).
-  double sq = 0.0;
-  for (int h = tid; h < a.H; h += kSelectThreads) {
-    const float v = (ACT == MOE_BF16)
-                        ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.x)[size_t(t) * a.H + h])
-                        : reinterpret_cast<const float*>(a.x)[size_t(t) * a.H + h];
-    sq += (double)v * (double)v;
-  }
-  const double xn = sqrt(block_sum_d(sq, red)) * (1.0 + 1e-12);
+  // 1. loads: the group maxima (rounded-up binary32 maxima of 4 logits) and ||x||^2.
+  float gv[GPT];
+  auto load_pass = [&](int ps) {
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) gv[i] = gr[min(ps * GPASS + i * kSelectThreads + tid, G - 1)];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i)
+      if (ps * GPASS + i * kSelectThreads + tid >= G) gv[i] = -INFINITY;
+  };
+  load_pass(0);
+  const double xn = sqrt(a.xnorm[t]) * (1.0 + 1e-3);   // ||x||^2 was summed in binary32
   const double Bt = a.bt_unit * xn + a.bt_abs;
+  const double u = a.rel;
 
-  // 2. tau0: largest per-block k-th value (a lower bound on tau).
-  float tmax = -INFINITY;
-  for (int i = tid; i < a.ntau; i += kSelectThreads) {
-    const float v = a.tau[size_t(t) * a.ntau + i];
-    if (!isnan(v)) tmax = fmaxf(tmax, v);
-  }
-  const float tau0 = block_max_f(tmax, red);
-
+  auto bound = [&](double v) -> double { return Bt + u * fabs(v); };
   auto lower = [&](double tv) -> double {   // L(tau) = tau - B(tau), rounded down
-    if (isinf(tv)) return -INFINITY;
-    const double B = Bt + 0x1p-23 * fabs(tv);
+    if (isinf(tv)) return tv < 0 ? -INFINITY : tv;
+    const double B = bound(tv);
     const double L = tv - B;
     return L - 1e-15 * (fabs(tv) + B + 1.0);
   };
-  auto is_cand = [&](float v, double L) -> bool {
-    if (!isfinite(v)) return false;
-    const double dv = (double)v;
-    return dv + (Bt + 0x1p-23 * fabs(dv)) >= L;
-  };
 
-  // 3. survivors of the pre-filter.
-  const double L0 = lower((double)tau0);
-  for (int e = tid; e < E; e += kSelectThreads) {
-    const float v = zr[e];
-    if (!isfinite(v)) s_nonfinite = 1;
-    if (is_cand(v, L0)) {
-      const int p = atomicAdd(&s_cnt, 1);
-      if (p < kSelectMaxCand) {
+  // 2. tau0, a lower bound on the k-th largest z_hat: each thread's maximum
+  //    over its groups, then in wave 0 the maximum over 8 threads per lane
+  //    (64 disjoint sets of experts), the k-th largest of those 64 by rank,
+  //    one binary32 ulp down (the maxima were rounded up): k distinct experts
+  //    lie above it.
+  float tm = -INFINITY;
+  for (int ps = 0; ps < npass; ++ps) {
+    if (ps > 0) load_pass(ps);
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) tm = fmaxf(tm, gv[i]);
+  }
+  if (npass > 1) load_pass(0);
+  s_tmax[tid] = tm;
+  __syncthreads();
+  if (wave == 0 && G >= k) {
+    float lm = -INFINITY;
+    for (int w = 0; w < kWavesSel; ++w) lm = fmaxf(lm, s_tmax[w * 64 + lane]);
+    // k-th largest of the 64 lane values: bisection on the monotone key,
+    // one ballot per bit (largest K with #{key >= K} >= k)
+    const uint32_t key = f32_key(lm);
+    uint32_t K = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = K | (1u << bit);
+      if (__popcll(__ballot(key >= cand)) >= k) K = cand;
+    }
+    if (lane == 0 && K != 0) s_tau0 = (double)nextafterf(key_f32(K), -INFINITY);
+  }
+  __syncthreads();
+
+  // 3. groups whose maximum reaches theta0, then their experts with
+  //    z_hat >= theta0, compacted with one LDS atomic per wave and step.
+  const double th0 = cand_threshold(lower(s_tau0), Bt, u);
+  for (int ps = 0; ps < npass; ++ps) {
+    if (ps > 0) load_pass(ps);
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+      const int g = ps * GPASS + i * kSelectThreads + tid;
+      const bool pred = g < G && (double)gv[i] >= th0;
+      const unsigned long long m = __ballot(pred);
+      if (m) {
+        const int leader = __ffsll((long long)m) - 1;
+        int base = 0;
+        if (lane == leader) base = atomicAdd(&s_ng, __popcll(m));
+        base = __shfl(base, leader);
+        const int p = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (pred && p < kSelectMaxCand) s_glist[p] = g;
+      }
+    }
+  }
+  __syncthreads();
+  const int ng = min(s_ng, kSelectMaxCand);
+  for (int i0 = 0; i0 < 4 * ng; i0 += kSelectThreads) {   // 4 experts per listed group
+    const int i = i0 + tid;
+    const int e = (i < 4 * ng) ? s_glist[i >> 2] * 4 + (i & 3) : E;
+    const double v = zr[min(e, E - 1)];
+    const bool pred = e < E && isfinite(v) && v >= th0;
+    const unsigned long long m = __ballot(pred);
+    if (m) {
+      const int leader = __ffsll((long long)m) - 1;
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&s_cnt, __popcll(m));
+      base = __shfl(base, leader);
+      const int p = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (pred && p < kSelectMaxCand) {
         s_val[p] = v;
         s_id[p] = e;
       }
     }
   }
   __syncthreads();
-  const int n = s_cnt;
+  const int n = (s_ng > kSelectMaxCand) ? kSelectMaxCand + 1 : s_cnt;
 
-  // 4. tau = k-th largest z_hat.
-  if (n <= kSelectMaxCand) {
-    for (int i = tid; i < n; i += kSelectThreads) {
-      const float v = s_val[i];
-      int gt = 0, ge = 0;
-      for (int j = 0; j < n; ++j) {
-        gt += s_val[j] > v;
-        ge += s_val[j] >= v;
+  // 5a. fast path: one wave ranks the survivors and certifies the order.
+  if (n <= 64 && !a.force_exact && wave == 0) {
+    const double v = (lane < n) ? s_val[lane] : -INFINITY;
+    const int e = (lane < n) ? s_id[lane] : 0x7fffffff;
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const double vj = readlane_f64(v, j);
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      rank += (vj > v) || (vj == v && ej < e);
+    }
+    if (lane < n) {
+      c_z[rank] = v;
+      c_id[rank] = e;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // ranks r and r+1 must not overlap for r < k (order of the k, and the cut)
+    const int npair = min(k, n - 1);
+    bool bad = false;
+    if (lane < npair) {
+      const double hi = c_z[lane], lo = c_z[lane + 1];
+      bad = !(hi - bound(hi) > lo + bound(lo));
+    }
+    const bool certified = (n >= k) && (__ballot(bad) == 0ull);
+    if (certified) {
+      if (lane < k) s_w[lane] = exp(c_z[lane] - c_z[0]);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < k) {
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += s_w[j];
+        oi[lane] = c_id[lane];
+        og[lane] = (float)(s_w[lane] / sum);
       }
-      if (gt < k && k <= ge) s_tau = v;
+      if (lane == 0) s_done = 1;
     }
-    __syncthreads();
-  } else {
-    // bisection on the monotone key: largest K with #{key >= K} >= k
-    uint32_t K = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = K | (1u << bit);
-      int cnt = 0;
-      for (int e = tid; e < E; e += kSelectThreads) cnt += (f32_key(zr[e]) >= cand);
-      cnt = block_sum_i(cnt, red);
-      if (cnt >= k) K = cand;
-    }
-    if (tid == 0) s_tau = (K == 0) ? -INFINITY : key_f32(K);
-    __syncthreads();
   }
-  const double L = lower((double)s_tau);
+  __syncthreads();
+  if (s_done) return;
 
-  // 5./6. candidates -> exact logits -> running top-k.
+  // 5b. exact path.
   auto process = [&](int nc) {
     for (int i = wave; i < nc; i += kWavesSel) {
       const double zz = refine_logit<ACT>(a, t, c_id[i], bins[wave], lane);
@@ -347,9 +471,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     __syncthreads();
     const int ntop = s_ntop;
     const int nu = ntop + nc;
-    for (int u = tid; u < nu; u += kSelectThreads) {
-      const int eu = (u < ntop) ? top_e[u] : c_id[u - ntop];
-      const double zu = (u < ntop) ? top_z[u] : c_z[u - ntop];
+    for (int q = tid; q < nu; q += kSelectThreads) {
+      const int eu = (q < ntop) ? top_e[q] : c_id[q - ntop];
+      const double zu = (q < ntop) ? top_z[q] : c_z[q - ntop];
       int rank = 0;
       for (int w = 0; w < nu; ++w) {
         const int ew = (w < ntop) ? top_e[w] : c_id[w - ntop];
@@ -375,65 +499,84 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
   };
 
   if (n <= kSelectMaxCand) {
+    // tau = k-th largest z_hat among the survivors, then the band around it
+    for (int i = tid; i < n; i += kSelectThreads) {
+      const double v = s_val[i];
+      int gt = 0, ge = 0;
+      for (int j = 0; j < n; ++j) {
+        gt += s_val[j] > v;
+        ge += s_val[j] >= v;
+      }
+      if (gt < k && k <= ge) s_tau = v;
+    }
+    __syncthreads();
+    const double th = cand_threshold(lower(s_tau), Bt, u);
     for (int i = tid; i < n; i += kSelectThreads)
-      if (is_cand(s_val[i], L)) c_id[atomicAdd(&c_cnt, 1)] = s_id[i];
+      if (s_val[i] >= th) c_id[atomicAdd(&c_cnt, 1)] = s_id[i];
     __syncthreads();
     process(c_cnt);
   } else {
+    // degenerate: more survivors than LDS holds.  Bisection on the monotone
+    // 64-bit key for tau, then the candidates range by range.
+    unsigned long long K = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const unsigned long long cand = K | (1ull << bit);
+      int cnt = 0;
+      for (int e = tid; e < E; e += kSelectThreads) cnt += (f64_key(zr[e]) >= cand);
+      cnt = block_sum_i(cnt, red);
+      if (cnt >= k) K = cand;
+    }
+    const double tau = (K == 0) ? -INFINITY : key_f64(K);
+    const double th = cand_threshold(lower(tau), Bt, u);
     for (int r0 = 0; r0 < E; r0 += kSelectMaxCand) {
       const int r1 = min(E, r0 + kSelectMaxCand);
-      for (int e = r0 + tid; e < r1; e += kSelectThreads)
-        if (is_cand(zr[e], L)) c_id[atomicAdd(&c_cnt, 1)] = e;
+      for (int e = r0 + tid; e < r1; e += kSelectThreads) {
+        const double v = zr[e];
+        if (isfinite(v) && v >= th) c_id[atomicAdd(&c_cnt, 1)] = e;
+      }
       __syncthreads();
       process(c_cnt);
     }
   }
 
-  // 7. outputs.
-  if (tid == 0) {
-    const int nt = s_ntop;
-    int32_t* oi = a.idx + size_t(t) * k;
-    float* og = a.gates + size_t(t) * k;
-    if (s_nonfinite || nt < k) atomicOr(a.dev_flag, kDevNonFinite);
+  // 6. outputs: gates = softmax over the k exact logits (f64), one thread per gate.
+  const int nt = s_ntop;
+  if (nt == k && tid < k) s_w[tid] = exp(top_z[tid] - top_z[0]);
+  __syncthreads();
+  if (tid < k) {
     if (nt < k) {
-      for (int j = 0; j < k; ++j) {
-        oi[j] = (j < nt) ? top_e[j] : -1;
-        og[j] = NAN;
-      }
+      oi[tid] = (tid < nt) ? top_e[tid] : -1;
+      og[tid] = NAN;
     } else {
-      const double m = top_z[0];
-      double w[kMaxK];
       double sum = 0.0;
-      for (int j = 0; j < k; ++j) {
-        w[j] = exp(top_z[j] - m);
-        sum += w[j];
-      }
-      for (int j = 0; j < k; ++j) {
-        oi[j] = top_e[j];
-        og[j] = (float)(w[j] / sum);
-      }
+      for (int j = 0; j < k; ++j) sum += s_w[j];
+      oi[tid] = top_e[tid];
+      og[tid] = (float)(s_w[tid] / sum);
     }
   }
+  if (tid == 0 && nt < k) atomicOr(a.dev_flag, kDevNonFinite);
 }
 
-hipError_t launch_select_impl(const Layer& L, const void* x, int T, const float* z,
-                              const float* tau, int ntau, int32_t* idx, float* gates,
-                              double bt_unit, double bt_abs, hipStream_t s) {
+hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double* z,
+                              const float* gmax, const double* xnorm, int32_t* idx,
+                              float* gates, const RouterBound& rb, hipStream_t s) {
   SelectArgs a;
   a.R = L.router_eh;
   a.bias = L.d.router_bias;
   a.x = x;
   a.z = z;
-  a.tau = tau;
-  a.ntau = ntau;
+  a.gmax = gmax;
+  a.xnorm = xnorm;
   a.H = L.d.hidden;
   a.E = L.d.n_experts;
   a.k = L.d.top_k;
   a.idx = idx;
   a.gates = gates;
   a.dev_flag = L.dev_flag;
-  a.bt_unit = bt_unit;
-  a.bt_abs = bt_abs;
+  auto gamma = [](int n, double u) { return n * u / (1.0 - n * u); };
+  a.bt_unit = (gamma(rb.d32, 0x1p-23) + gamma(rb.d64, 0x1p-52)) * 1.01 * L.norm_max;
+  a.bt_abs = rb.d32 * 0x1p-125 + rb.d64 * 0x1p-1021;
+  a.rel = 0x1p-52;
   a.force_exact = (L.d.flags & MOE_LAYER_FORCE_EXACT_REFINE) ? 1 : 0;
   if (L.d.act_dtype == MOE_BF16)
     hipLaunchKernelGGL(select_kernel<MOE_BF16>, dim3(T), dim3(kSelectThreads), 0, s, a);
