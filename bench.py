@@ -46,7 +46,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--config", default="C2", choices=["C1", "C2"])
+    p.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4"],
+                   help="C1/C2: batch-1 decode (the headline is C2); C3: T=5 verify steps "
+                        "through the 4-bit layer; C4: T=2048 prefill chunks through the bf16 layer")
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
     p.add_argument("--cpu-sample", type=int, default=12, help="tokens the oracle is timed on (0: skip)")
     return p.parse_args()
@@ -106,6 +108,73 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out):
     return base, parity
 
 
+def grouped_main(args, spec):
+    """C3 / C4: T tokens per call through moe_grouped_forward (one step = one call)."""
+    import torch
+
+    import synth.device as SD
+    T = spec.T
+    K, W = args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=T)
+    nseq = min(K + W, 64)                        # distinct token batches, reused cyclically
+    X = SD.device_tokens(spec, 0, nseq * T).view(nseq, T, spec.H)
+    ws = layer.workspace(T)
+    idx = torch.zeros((nseq, T, spec.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((nseq, T, spec.k), dtype=torch.float32, device=dev)
+    out = torch.zeros((nseq, T, spec.H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    log(f"layer ready in {time.time() - t0:.1f}s: pool {dl.nbytes_pool() / 1e9:.2f} GB, T={T}")
+
+    def step(i):
+        b = i % nseq
+        layer.grouped_forward(X[b], T, idx[b], gates[b], 0, out[b], ws)
+
+    for i in range(min(W, 3)):
+        step(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g_warm, stream=s):
+            for i in range(W):
+                step(i)
+        with torch.cuda.graph(g_main, stream=s):
+            for i in range(W, W + K):
+                step(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        g_warm.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        g_main.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+    err = layer.device_error()
+    import numpy as np
+    distinct = [len(np.unique(idx[b].cpu().numpy())) for b in range(min(nseq, 8))]
+    per_step = ms / 1e3 / K
+    res = {
+        "metric": f"MoE-layer grouped forward tokens/s ({spec.name}: T={T} per call)",
+        "value": T * K / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": ms / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{spec.name}: T={T} tokens per call, H={spec.H}, E={spec.E}, top-{spec.k}, "
+                               f"I={spec.I}, experts {'q4b32' if spec.expert == 2 else 'bf16'}",
+                   "us_per_step": per_step * 1e6, "distinct_experts_per_step": distinct,
+                   "device_errors": err},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,6 +188,8 @@ def main():
     import synth.device as SD
 
     spec = synth.CONFIGS[args.config]
+    if spec.T > 1:
+        return grouped_main(args, spec)
     K, W = args.steps, args.warmup
     n_rep = 3 if args.mode == "cold" else 1
     dev = torch.device("cuda:0")
@@ -137,7 +208,7 @@ def main():
     idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
     gates = torch.zeros((W + K, spec.k), dtype=torch.float32, device=dev)
     out = torch.zeros((W + K, spec.H), dtype=torch.float32, device=dev)
-    zbuf = torch.empty((spec.E,), dtype=torch.float32, device=dev)
+    zbuf = torch.empty((spec.E,), dtype=torch.float64, device=dev)
 
     def token(t):
         L = layers[t % n_rep]

@@ -38,25 +38,6 @@ __device__ __forceinline__ float q4_dot32(const uint4 w, const float* xv) {
   return acc;
 }
 
-struct GroupArgs {
-  const void* x;            // [T][H]
-  const int32_t* idx;       // [T][k]
-  const float* gates;       // [T][k]
-  const void *wg, *wu, *wd;
-  const uint16_t *sg, *su, *sd;
-  int T, H, I, E, k, P;
-  int* counts;              // [E]
-  int* offsets;             // [E+1]
-  int* slot;                // [P]
-  int* pos;                 // [P]
-  int* ptok;                // [P]
-  int* active;              // [E+1]: [0] = number of active experts
-  float* hm;                // [P][I]
-  float* y;                 // [P][H]
-  float* out;               // [T][H]
-  int* dev_flag;
-};
-
 __global__ void fill_i32_kernel(int* p, int v, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
 }
@@ -76,44 +57,55 @@ __global__ void hist_kernel(GroupArgs a) {
   a.slot[p] = atomicAdd(&a.counts[e], 1);
 }
 
-// Single-workgroup exclusive scan of counts and compaction of active experts.
+// Single-workgroup exclusive scan of counts and compaction of the active
+// experts: each thread scans a contiguous chunk sequentially, one block-wide
+// scan combines the 1024 chunk totals (Hillis-Steele over LDS), and a second
+// sequential pass writes offsets and the active list in expert order.
 __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
   __shared__ int s_sum[1024];
   __shared__ int s_act[1024];
-  __shared__ int carry, acarry;
-  if (threadIdx.x == 0) {
-    carry = 0;
-    acarry = 0;
+  __shared__ int s_til[1024];
+  const int tid = threadIdx.x;
+  const int per = (a.E + 1023) / 1024;
+  const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
+  int sum = 0, act = 0, til = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = a.counts[e];
+    sum += c;
+    act += (c > 0);
+    til += (c + kTileRows - 1) / kTileRows;
   }
+  s_sum[tid] = sum;
+  s_act[tid] = act;
+  s_til[tid] = til;
   __syncthreads();
-  for (int base = 0; base < a.E; base += 1024) {
-    const int e = base + threadIdx.x;
-    const int c = (e < a.E) ? a.counts[e] : 0;
-    s_sum[threadIdx.x] = c;
-    s_act[threadIdx.x] = (c > 0);
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = (tid >= off) ? s_sum[tid - off] : 0;
+    const int w = (tid >= off) ? s_act[tid - off] : 0;
+    const int x = (tid >= off) ? s_til[tid - off] : 0;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {   // Hillis-Steele inclusive scans
-      const int v = (threadIdx.x >= off) ? s_sum[threadIdx.x - off] : 0;
-      const int w = (threadIdx.x >= off) ? s_act[threadIdx.x - off] : 0;
-      __syncthreads();
-      s_sum[threadIdx.x] += v;
-      s_act[threadIdx.x] += w;
-      __syncthreads();
-    }
-    if (e < a.E) {
-      a.offsets[e] = carry + s_sum[threadIdx.x] - c;
-      if (c > 0) a.active[1 + acarry + s_act[threadIdx.x] - 1] = e;
-    }
-    __syncthreads();
-    if (threadIdx.x == 1023) {
-      carry += s_sum[1023];
-      acarry += s_act[1023];
-    }
+    s_sum[tid] += v;
+    s_act[tid] += w;
+    s_til[tid] += x;
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    a.offsets[a.E] = carry;
-    a.active[0] = acarry;
+  // exclusive prefixes of this chunk
+  int run = s_sum[tid] - sum, arun = s_act[tid] - act, trun = s_til[tid] - til;
+  for (int e = e0; e < e1; ++e) {
+    const int c = a.counts[e];
+    a.offsets[e] = run;
+    if (c > 0) a.active[1 + arun++] = e;
+    for (int r0 = 0; r0 < c; r0 += kTileRows) {
+      a.tiles[1 + 2 * trun] = e;
+      a.tiles[2 + 2 * trun] = r0;
+      ++trun;
+    }
+    run += c;
+  }
+  if (tid == 1023) {
+    a.offsets[a.E] = s_sum[1023];
+    a.active[0] = s_act[1023];
+    a.tiles[0] = s_til[1023];
   }
 }
 
@@ -335,6 +327,7 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
   a.pos = reinterpret_cast<int*>(ws + W.pos);
   a.ptok = reinterpret_cast<int*>(ws + W.ptok);
   a.active = reinterpret_cast<int*>(ws + W.active);
+  a.tiles = reinterpret_cast<int*>(ws + W.tiles);
   a.hm = reinterpret_cast<float*>(ws + W.hm);
   a.y = reinterpret_cast<float*>(ws + W.y);
   a.out = out;
@@ -347,6 +340,12 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
+  if (grouped_uses_mfma(L, T)) {
+    err = launch_grouped_mfma(a, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(combine_kernel, dim3((a.H + 255) / 256, T), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   const int maxact = min(a.P, a.E);
   const int gy = min(maxact, 4096);
   const int act = L.d.act_dtype, wd = L.d.expert_dtype;

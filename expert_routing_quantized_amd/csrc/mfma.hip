@@ -1,0 +1,330 @@
+// Router logits of a prefill chunk or large verify batch as a bf16 MFMA GEMM:
+// z[t][e] = sum_h x[t][h] R[e][h] + b[e] for T tokens at once.
+//
+// At batch 1 the router is a GEMV and matrix units waste their tile (the
+// hexlives dispatch's archived tensor-core experiment); with T = 2048 tokens
+// it is a dense 2048 x 2048 x 24,576 contraction (206 GFLOP), the one place
+// on the path where MFMA is the bound.  Both operands are K-contiguous (x
+// rows, router rows): each 256-thread block computes a 64-token x 128-expert
+// tile with v_mfma_f32_32x32x16_bf16 (4 waves, each 32 tokens x 64 experts),
+// staging 32-wide K slices of both operands through LDS (double-buffered,
+// next slice prefetched into registers while the current one is consumed).
+//
+// Rounding model for the certified selection: the fp32 MFMA accumulators are
+// added into binary64 accumulators after every 128 of K (8 instructions of
+// K = 16, each counted as at most 17 binary32 roundings, truncation
+// included), and the remaining sums and the bias are binary64: d32 = 136,
+// d64 = H/128 + 1.  The epilogue writes the binary64 logits, the maximum of
+// every 4 consecutive experts (rounded up to binary32) and ||x_t||^2 -- the
+// same outputs as the vector-ALU router, so the same selection kernel runs.
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 64, kBN = 128, kBK = 32, kPadK = 40;   // LDS row stride (bf16) with padding
+constexpr int kF64Every = 4;                               // K slices (of 32) per binary64 fold
+
+__global__ __launch_bounds__(256) void router_gemm_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
+    int T, int H, int E, double* __restrict__ z, float* __restrict__ gmax,
+    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kBM][kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kBN][kPadK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
+  const int wm = (wave & 1) * 32, wn = (wave >> 1) * 64;
+
+  // global -> register staging: A 64x32 (one 16-byte load per thread), B 128x32 (two)
+  const int ar = tid >> 2, ac = (tid & 3) * 8;
+  const int br0 = tid >> 2, br1 = br0 + 64;
+  const uint16_t* pa = X + size_t(min(m0 + ar, T - 1)) * H + ac;
+  const uint16_t* pb0 = R + size_t(min(n0 + br0, E - 1)) * H + ac;
+  const uint16_t* pb1 = R + size_t(min(n0 + br1, E - 1)) * H + ac;
+  uint4 ra = *reinterpret_cast<const uint4*>(pa);
+  uint4 rb0 = load_nt(pb0), rb1 = load_nt(pb1);
+
+  f32x16_t acc[2];
+  double accd[2][16];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc[n][i] = 0.f;
+      accd[n][i] = 0.0;
+    }
+
+  const int nk = H / kBK;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    *reinterpret_cast<uint4*>(&sa[buf][ar][ac]) = ra;
+    *reinterpret_cast<uint4*>(&sb[buf][br0][ac]) = rb0;
+    *reinterpret_cast<uint4*>(&sb[buf][br1][ac]) = rb1;
+    __syncthreads();
+    if (kt + 1 < nk) {                          // prefetch the next slice
+      const int ko = (kt + 1) * kBK;
+      ra = *reinterpret_cast<const uint4*>(pa + ko);
+      rb0 = load_nt(pb0 + ko);
+      rb1 = load_nt(pb1 + ko);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK; kk += 16) {
+      const int kc = kk + 8 * (lane >> 5);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sa[buf][wm + (lane & 31)][kc]);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sb[buf][wn + 32 * n + (lane & 31)][kc]);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[n], 0, 0, 0);
+      }
+    }
+    if ((kt + 1) % kF64Every == 0 || kt + 1 == nk) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          accd[n][i] += (double)acc[n][i];
+          acc[n][i] = 0.f;
+        }
+    }
+  }
+
+  // epilogue: lane holds rows 8*(i/4) + 4*(lane/32) + i%4 of column lane%32
+  bool bad = false;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int e = n0 + wn + 32 * n + (lane & 31);
+    const double b = (e < E && bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = m0 + wm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      const double v = accd[n][i] + b;
+      if (e < E && t < T) {
+        z[size_t(t) * E + e] = v;
+        if (!isfinite(v)) bad = true;
+      }
+      // maximum over the 4 consecutive experts of lanes 4q..4q+3
+      double m = (e < E && !isnan(v)) ? v : -INFINITY;
+      m = fmax(m, dpp_f64<0xB1, 0xf>(m, -INFINITY));
+      m = fmax(m, dpp_f64<0x4E, 0xf>(m, -INFINITY));
+      if ((lane & 3) == 0 && t < T && e < E) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = __double2float_ru(m);
+    }
+  }
+  if (bad) atomicOr(dev_flag, kDevNonFinite);
+
+  if (blockIdx.x == 0) {          // ||x_t||^2 for this block's tokens, 16 per wave
+    for (int r = 0; r < 16; ++r) {
+      const int t = m0 + wave * 16 + r;
+      if (t >= T) break;
+      float q = 0.f;
+      for (int c = lane; c < H / 8; c += 64) {
+        const uint4 v = *reinterpret_cast<const uint4*>(X + size_t(t) * H + c * 8);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+          q = fmaf(lo, lo, q);
+          q = fmaf(hi, hi, q);
+        }
+      }
+      q = wave_sum(q);
+      if (lane == 0) xnorm[t] = (double)q;
+    }
+  }
+}
+
+bool router_uses_mfma(const Layer& L, int T) {
+  return L.d.act_dtype == MOE_BF16 && T >= 16 && (L.d.hidden % kBK) == 0;
+}
+
+hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
+                              double* xnorm, hipStream_t s) {
+  const int H = L.d.hidden, E = L.d.n_experts;
+  dim3 grid((E + kBN - 1) / kBN, (T + kBM - 1) / kBM);
+  hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(L.router_eh),
+                     L.d.router_bias, T, H, E, z, gmax, xnorm, L.dev_flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped bf16 experts on MFMA (prefill chunks, large verify batches).  The
+// token-expert pairs are sorted by expert and cut into tiles of 32 rows of
+// one expert's segment; each tile is one MFMA M-tile.  Most experts of a
+// 2048-token chunk receive 1-3 tokens, so most tiles are nearly empty and
+// the kernels are bound by the expert-weight stream, which every tile reads
+// once; the few experts with hundreds of tokens are where MFMA throughput
+// matters.
+//
+// gate/up: block = (128 intermediate channels, tile); wave w owns channels
+//   32w..32w+31 of both G and U (two 32x32 accumulators), reads its weight
+//   rows straight from HBM into MFMA operand registers (each weight is used
+//   by this tile only), while the tile's gathered token rows are staged
+//   through LDS in 32-wide K slices.  Epilogue: h = silu(a) * u in fp32.
+// down: block = (128 output rows, tile); the tile's 32 rows of h (fp32) are
+//   split into bf16 hi + lo parts in LDS (h = hi + lo to 2^-16 relative) and
+//   multiplied by the same bf16 weights twice, so the down projection keeps
+//   fp32-level accuracy.
+constexpr int kGN = 128;            // channels / outputs per block
+
+bool grouped_uses_mfma(const Layer& L, int T) {
+  return L.d.expert_dtype == MOE_BF16 && L.d.act_dtype == MOE_BF16 && T >= 16 &&
+         (L.d.hidden % 32) == 0 && (L.d.inter % 32) == 0 && L.d.inter <= 256;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne_dev(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTileRows][kPadK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I;
+  const int ch = blockIdx.x * kGN + wave * 32 + (lane & 31);       // this lane's B column
+  const int chc = min(ch, I - 1);
+  const int ntiles = a.tiles[0];
+  const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
+  const uint16_t* WG = reinterpret_cast<const uint16_t*>(a.wg);
+  const uint16_t* WU = reinterpret_cast<const uint16_t*>(a.wu);
+  for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
+    const int e = a.tiles[1 + 2 * ti], r0 = a.tiles[2 + 2 * ti];
+    const int n = a.counts[e], seg = a.offsets[e];
+    const int nrow = min(kTileRows, n - r0);
+    // A staging: threads 0..127 each load 16 B of one gathered token row
+    const int ar = (tid >> 2) & 31, ac = (tid & 3) * 8;
+    const int tok = a.ptok[seg + r0 + min(ar, nrow - 1)];
+    const uint16_t* pa = X + size_t(tok) * H + ac;
+    const uint16_t* pg = WG + (size_t(e) * I + chc) * H + 8 * (lane >> 5);
+    const uint16_t* pu = WU + (size_t(e) * I + chc) * H + 8 * (lane >> 5);
+    uint4 ra = *reinterpret_cast<const uint4*>(pa);
+    uint4 bg[2], bu[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bg[kk] = load_nt(pg + 16 * kk);
+      bu[kk] = load_nt(pu + 16 * kk);
+    }
+    f32x16_t ag, au;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ag[i] = au[i] = 0.f;
+    const int nk = H / kBK;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (tid < 128) *reinterpret_cast<uint4*>(&sx[buf][ar][ac]) = ra;
+      __syncthreads();
+      uint4 ng[2], nu[2];
+      if (kt + 1 < nk) {
+        const int ko = (kt + 1) * kBK;
+        ra = *reinterpret_cast<const uint4*>(pa + ko);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          ng[kk] = load_nt(pg + ko + 16 * kk);
+          nu[kk] = load_nt(pu + ko + 16 * kk);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(&sx[buf][lane & 31][16 * kk + 8 * (lane >> 5)]);
+        ag = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8_t, bg[kk]), ag, 0, 0, 0);
+        au = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8_t, bu[kk]), au, 0, 0, 0);
+      }
+      if (kt + 1 < nk) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          bg[kk] = ng[kk];
+          bu[kk] = nu[kk];
+        }
+      }
+    }
+    // epilogue: rows 8*(i/4) + 4*(lane/32) + i%4 of column ch
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (r < nrow && ch < I) {
+        const float g = ag[i], u = au[i];
+        a.hm[size_t(seg + r0 + r) * I + ch] = g / (1.0f + expf(-g)) * u;
+      }
+    }
+    __syncthreads();   // LDS reuse by the next tile
+  }
+}
+
+template <int KS>   // K slices of 16 held in registers (I <= 16 KS)
+__global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t sh[];   // hi [32][I+8], lo [32][I+8]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I, ip = I + 8;
+  uint16_t* shi = sh;
+  uint16_t* slo = sh + kTileRows * ip;
+  const int o = blockIdx.x * kGN + wave * 32 + (lane & 31);
+  const int oc = min(o, H - 1);
+  const int ntiles = a.tiles[0];
+  const uint16_t* WD = reinterpret_cast<const uint16_t*>(a.wd);
+  for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
+    const int e = a.tiles[1 + 2 * ti], r0 = a.tiles[2 + 2 * ti];
+    const int n = a.counts[e], seg = a.offsets[e];
+    const int nrow = min(kTileRows, n - r0);
+    // weights of this lane's output row, all K at once (I/16 slices of 8)
+    const uint16_t* pw = WD + (size_t(e) * H + oc) * I + 8 * (lane >> 5);
+    uint4 b[KS];
+    const int nks = I / 16;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) b[q] = load_nt(pw + 16 * min(q, nks - 1));
+    // h rows of the tile -> bf16 hi/lo in LDS (rows past the segment: zeros)
+    for (int q = tid; q < kTileRows * (I / 4); q += 256) {
+      const int r = q / (I / 4), c = (q - r * (I / 4)) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < nrow) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + r) * I + c);
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint16_t hi = f32_to_bf16_rne_dev(vv[j]);
+        const float rem = vv[j] - __uint_as_float(uint32_t(hi) << 16);
+        shi[r * ip + c + j] = hi;
+        slo[r * ip + c + j] = f32_to_bf16_rne_dev(rem);
+      }
+    }
+    __syncthreads();
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      if (q >= nks) continue;          // block-uniform
+      const int kc = 16 * q + 8 * (lane >> 5);
+      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&shi[(lane & 31) * ip + kc]);
+      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&slo[(lane & 31) * ip + kc]);
+      const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b[q]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bb, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bb, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      if (r < nrow && o < H) a.y[size_t(seg + r0 + r) * H + o] = acc[i];
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s) {
+  const int gy = 2048;
+  hipLaunchKernelGGL(gateup_mfma_kernel, dim3((a.I + kGN - 1) / kGN, gy), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = sizeof(uint16_t) * 2 * kTileRows * (a.I + 8);
+  const dim3 g2((a.H + kGN - 1) / kGN, gy);
+  const int nks = a.I / 16;
+  if (nks <= 4)
+    hipLaunchKernelGGL(down_mfma_kernel<4>, g2, dim3(256), lds, s, a);
+  else if (nks <= 8)
+    hipLaunchKernelGGL(down_mfma_kernel<8>, g2, dim3(256), lds, s, a);
+  else if (nks <= 16)
+    hipLaunchKernelGGL(down_mfma_kernel<16>, g2, dim3(256), lds, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace moe

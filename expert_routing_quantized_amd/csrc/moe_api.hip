@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "moe_internal.h"
@@ -105,7 +106,8 @@ moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float*
   double* z = reinterpret_cast<double*>(ws + W.z);
   float* gmax = reinterpret_cast<float*>(ws + W.gmax);
   double* xnorm = reinterpret_cast<double*>(ws + W.xnorm);
-  hipError_t e = moe::launch_router(L, x, T, z, gmax, xnorm, s);
+  hipError_t e = moe::router_uses_mfma(L, T) ? moe::launch_router_gemm(L, x, T, z, gmax, xnorm, s)
+                                             : moe::launch_router(L, x, T, z, gmax, xnorm, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   e = moe::launch_select_impl(L, x, T, z, gmax, xnorm, idx, gates, moe::router_bound(L, T), s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
@@ -140,6 +142,7 @@ Workspace workspace_layout(const Layer& L, int T) {
     W.pos = take(P * 4);
     W.ptok = take(P * 4);
     W.active = take((E + 1) * 4);
+    W.tiles = take((1 + 2 * ((P + moe::kTileRows - 1) / moe::kTileRows + std::min(P, E))) * 4);
     W.hm = take(P * I * 4);
     W.y = take(P * H * 4);
   }
@@ -263,8 +266,10 @@ moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, d
   if (moe_status st = check_ws(L, T, ws, ws_bytes, &W)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = moe::launch_router(L, x, T, z, reinterpret_cast<float*>(w + W.gmax),
-                                    reinterpret_cast<double*>(w + W.xnorm), s);
+  float* gm = reinterpret_cast<float*>(w + W.gmax);
+  double* xn = reinterpret_cast<double*>(w + W.xnorm);
+  hipError_t e = moe::router_uses_mfma(L, T) ? moe::launch_router_gemm(L, x, T, z, gm, xn, s)
+                                             : moe::launch_router(L, x, T, z, gm, xn, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   return ok();
 }

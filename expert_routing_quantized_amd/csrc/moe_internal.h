@@ -49,7 +49,8 @@ struct Workspace {
   size_t pos;       // int32 [P] segment position of pair p
   size_t ptok;      // int32 [P] token of the pair at a segment position
   size_t active;    // int32 [E + 1] active experts (count first)
-  size_t hm;        // fp32 [P][I] grouped intermediate (or bf16 hi/lo pairs)
+  size_t tiles;     // int32 [1 + 2 * max tiles]: count, then (expert, first row) per 32-row tile
+  size_t hm;        // fp32 [P][I] grouped intermediate
   size_t y;         // fp32 [P][H] grouped expert outputs
   size_t total;
 };
@@ -223,6 +224,28 @@ struct Chunk<MOE_F32> {
   }
 };
 
+// Arguments of the grouped-path kernels (grouped.hip, mfma.hip).
+struct GroupArgs {
+  const void* x;            // [T][H]
+  const int32_t* idx;       // [T][k]
+  const float* gates;       // [T][k]
+  const void *wg, *wu, *wd;
+  const uint16_t *sg, *su, *sd;
+  int T, H, I, E, k, P;
+  int* counts;              // [E]
+  int* offsets;             // [E+1]
+  int* slot;                // [P]
+  int* pos;                 // [P]
+  int* ptok;                // [P]
+  int* active;              // [E+1]: [0] = number of active experts
+  int* tiles;               // [0] = number of 32-row tiles, then (expert, first row) pairs
+  float* hm;                // [P][I]
+  float* y;                 // [P][H]
+  float* out;               // [T][H]
+  int* dev_flag;
+};
+constexpr int kTileRows = 32;
+
 // ------------------------------------------------------------------ launchers
 // router.hip: approximate logits z[t][e] (binary64) for tokens [0, T), the
 // maximum of every 4 consecutive logits gmax[t][e/4] (binary32, rounded up)
@@ -239,6 +262,13 @@ struct RouterBound {
   int d64;
 };
 RouterBound router_bound(const Layer& L, int T);
+// mfma.hip: the router as a bf16 MFMA GEMM for T >= 16 tokens (same outputs).
+bool router_uses_mfma(const Layer& L, int T);
+hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
+                              double* xnorm, hipStream_t s);
+// mfma.hip: grouped bf16 experts on MFMA (used when grouped_uses_mfma).
+bool grouped_uses_mfma(const Layer& L, int T);
+hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s);
 // select.hip: exact top-k + gates per token from z; bt_unit/bt_abs give
 // the router's error bound Bt = bt_unit * ||x||_2 + bt_abs.
 hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double* z,

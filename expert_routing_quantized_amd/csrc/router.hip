@@ -205,6 +205,11 @@ RouterBound router_bound(const Layer& L, int T) {
   int lg = 0;
   while ((1 << lg) < cpl) ++lg;
   RouterBound b;
+  if (router_uses_mfma(L, T)) {     // see mfma.hip
+    b.d32 = 136;
+    b.d64 = (L.d.hidden + 127) / 128 + 1;
+    return b;
+  }
   const bool dot2 = (L.d.act_dtype == MOE_BF16 && T > 1);
   b.d32 = dot2 ? 8 : 7;
   b.d64 = lg + 7;

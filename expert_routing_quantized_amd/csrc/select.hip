@@ -575,7 +575,9 @@ hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double
   a.dev_flag = L.dev_flag;
   auto gamma = [](int n, double u) { return n * u / (1.0 - n * u); };
   a.bt_unit = (gamma(rb.d32, 0x1p-23) + gamma(rb.d64, 0x1p-52)) * 1.01 * L.norm_max;
-  a.bt_abs = rb.d32 * 0x1p-125 + rb.d64 * 0x1p-1021;
+  // absolute term: every binary32 operation may also lose up to 2^-126 to
+  // underflow (products flushed to zero included: one per element of x)
+  a.bt_abs = (rb.d32 + L.d.hidden) * 0x1p-125 + rb.d64 * 0x1p-1021;
   a.rel = 0x1p-52;
   a.force_exact = (L.d.flags & MOE_LAYER_FORCE_EXACT_REFINE) ? 1 : 0;
   if (L.d.act_dtype == MOE_BF16)

@@ -122,3 +122,34 @@ def test_grouped_parity_small(name, T):
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 200, T)
     G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/T={T}")
     assert layer.device_error() == 0
+
+
+# Grouped MFMA path (bf16 activations and experts, T >= 16): few experts and
+# many tokens, so segments span several 32-row tiles with a ragged last one;
+# I = 96 and H = 160 leave partial 128-wide channel / output blocks.
+MFMA_SPECS = {
+    "mfma_multi_tile": synth.small_spec(H=512, E=20, k=4, I=128, act=synth.DT_BF16, expert=synth.DT_BF16,
+                                        bias_alpha=0.37, weight_seed=71, token_seed=72, name="mfma_multi_tile"),
+    "mfma_ragged": synth.small_spec(H=160, E=37, k=3, I=96, act=synth.DT_BF16, expert=synth.DT_BF16,
+                                    bias_alpha=None, weight_seed=73, token_seed=74, name="mfma_ragged"),
+    "mfma_wide": synth.small_spec(H=2048, E=300, k=10, I=256, act=synth.DT_BF16, expert=synth.DT_BF16,
+                                  bias_alpha=0.37, weight_seed=75, token_seed=76, name="mfma_wide"),
+}
+
+
+@pytest.mark.parametrize("name,T", [("mfma_multi_tile", 300), ("mfma_ragged", 77), ("mfma_wide", 64),
+                                    ("mfma_wide", 16)])
+def test_grouped_mfma_tiles(name, T):
+    import synth.device as SD
+    spec = MFMA_SPECS[name]
+    G.note("grouped mfma", name, T)
+    dl = SD.device_layer(spec)
+    L = G.host_oracle(spec)
+    layer = SD.make_layer(dl, max_tokens=T)
+    x = SD.device_tokens(spec, 3, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 3, T)
+    r = G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/T={T}")
+    counts = np.bincount(o_idx.ravel(), minlength=spec.E)
+    print(f"{name} T={T}: max tokens per expert {counts.max()}, rel L2 max {r.max():.2e}")
+    assert layer.device_error() == 0
