@@ -46,9 +46,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--config", default="C2", choices=["C1", "C2", "C3", "C4"],
-                   help="C1/C2: batch-1 decode (the headline is C2); C3: T=5 verify steps "
-                        "through the 4-bit layer; C4: T=2048 prefill chunks through the bf16 layer")
+    p.add_argument("--config", default="decode_q4", choices=["decode_bf16", "decode_q4", "verify_q4", "prefill_bf16"],
+                   help="decode_bf16/decode_q4: batch-1 decode (the headline is decode_q4); verify_q4: T=5 verify steps "
+                        "through the 4-bit layer; prefill_bf16: T=2048 prefill chunks through the bf16 layer")
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
     p.add_argument("--cpu-sample", type=int, default=12, help="tokens the oracle is timed on (0: skip)")
     return p.parse_args()
@@ -109,7 +109,7 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out):
 
 
 def grouped_main(args, spec):
-    """C3 / C4: T tokens per call through moe_grouped_forward (one step = one call)."""
+    """verify_q4 / prefill_bf16: T tokens per call through moe_grouped_forward (one step = one call)."""
     import torch
 
     import synth.device as SD
@@ -262,7 +262,7 @@ def main():
     router_gbs = by["router"] / router_s / 1e9
     res = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, 4-bit experts)"
-                  if args.config == "C2" else "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, bf16 experts)",
+                  if args.config == "decode_q4" else "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, bf16 experts)",
         "value": tok_s,
         "unit": "tokens/s",
         "n_gpus": 1,

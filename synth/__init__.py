@@ -182,15 +182,15 @@ class LayerSpec:
 
 CONFIGS = {
     # tiny layer, fp32 everywhere, no bias, 1 token (a 1000-token sweep in tests)
-    "C0": LayerSpec("C0", 256, 64, 2, 128, DT_F32, DT_F32, None, 1, 1000, token_seed=42),
+    "tiny_f32": LayerSpec("tiny_f32", 256, 64, 2, 128, DT_F32, DT_F32, None, 1, 1000, token_seed=42),
     # batch-1 decode, bf16 experts
-    "C1": LayerSpec("C1", 2048, 24576, 10, 256, DT_BF16, DT_BF16, 0.37, 1, 1000, token_seed=43),
-    # batch-1 decode, 4-bit experts (C1's weights quantised)
-    "C2": LayerSpec("C2", 2048, 24576, 10, 256, DT_BF16, DT_Q4, 0.37, 1, 1000, token_seed=44),
-    # speculative verify: T=5 through C2's layer, 1000 steps
-    "C3": LayerSpec("C3", 2048, 24576, 10, 256, DT_BF16, DT_Q4, 0.37, 5, 1000, token_seed=45),
-    # prefill chunk: T=2048 through C1's layer
-    "C4": LayerSpec("C4", 2048, 24576, 10, 256, DT_BF16, DT_BF16, 0.37, 2048, 1, token_seed=46),
+    "decode_bf16": LayerSpec("decode_bf16", 2048, 24576, 10, 256, DT_BF16, DT_BF16, 0.37, 1, 1000, token_seed=43),
+    # batch-1 decode, 4-bit experts (decode_bf16's weights quantised)
+    "decode_q4": LayerSpec("decode_q4", 2048, 24576, 10, 256, DT_BF16, DT_Q4, 0.37, 1, 1000, token_seed=44),
+    # speculative verify: T=5 through decode_q4's layer, 1000 steps
+    "verify_q4": LayerSpec("verify_q4", 2048, 24576, 10, 256, DT_BF16, DT_Q4, 0.37, 5, 1000, token_seed=45),
+    # prefill chunk: T=2048 through decode_bf16's layer
+    "prefill_bf16": LayerSpec("prefill_bf16", 2048, 24576, 10, 256, DT_BF16, DT_BF16, 0.37, 2048, 1, token_seed=46),
 }
 
 

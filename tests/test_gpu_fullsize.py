@@ -18,9 +18,9 @@ _state = {}
 
 
 def host_router():
-    """Float64 router/bias shared by C1..C4 (same weights seed)."""
+    """Float64 router/bias shared by every full-size workload (same weights seed)."""
     if "R" not in _state:
-        spec = synth.CONFIGS["C1"]
+        spec = synth.CONFIGS["decode_bf16"]
         L = oracle.layer_from_spec(spec)
         _state["R"] = (L.R, L.b, L.absR())
     return _state["R"]
@@ -51,7 +51,7 @@ def layer_for(name, T):
     import synth.device as SD
     dl = device_for(name)
     spec = synth.CONFIGS[name]
-    # same weights as the config (C1/C4 and C2/C3 share a pool); tokens per config
+    # the bf16 workloads share one pool and the 4-bit ones another; tokens differ per workload
     return SD.make_layer(dl, max_tokens=T), spec
 
 
@@ -62,7 +62,7 @@ def test_router_logits_within_bound(T):
     the MFMA GEMM at T = 64 (checked on a sample of 1536 expert columns)."""
     import synth.device as SD
     torch = G.torch_mod()
-    layer, spec = layer_for("C2", T)
+    layer, spec = layer_for("decode_q4", T)
     G.note("router bound", T)
     x = SD.device_tokens(spec, 10, T)
     z = torch.empty((T, spec.E), dtype=torch.float64, device="cuda")
@@ -92,66 +92,66 @@ def test_router_logits_within_bound(T):
     assert ratio.max() < 1.0
 
 
-def test_c2_decode_parity():
+def test_decode_q4_decode_parity():
     import synth.device as SD
-    layer, spec = layer_for("C2", 16)
+    layer, spec = layer_for("decode_q4", 16)
     L = oracle_for(spec)
     for first in (0, 500, 984):
-        G.note("C2 decode tokens", first)
+        G.note("decode_q4 decode tokens", first)
         x = SD.device_tokens(spec, first, 16)
         idx, gates, out = G.run_route_decode(layer, x)
         o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, first, 16)
-        r = G.compare(idx, gates, out, o_idx, o_g, o_out, f"C2@{first}")
-        print(f"C2 tokens {first}..: rel L2 max {r.max():.2e} median {np.median(r):.2e}")
+        r = G.compare(idx, gates, out, o_idx, o_g, o_out, f"decode_q4@{first}")
+        print(f"decode_q4 tokens {first}..: rel L2 max {r.max():.2e} median {np.median(r):.2e}")
     assert layer.device_error() == 0
 
 
-def test_c2_grouped_single_token_path():
+def test_decode_q4_grouped_single_token_path():
     """moe_grouped_forward at T = 1 (the fused decode entry) matches too."""
     import synth.device as SD
-    layer, spec = layer_for("C2", 1)
+    layer, spec = layer_for("decode_q4", 1)
     L = oracle_for(spec)
     x = SD.device_tokens(spec, 7, 1)
     idx, gates, out = G.run_grouped(layer, x)
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 7, 1)
-    G.compare(idx, gates, out, o_idx, o_g, o_out, "C2 grouped T=1")
+    G.compare(idx, gates, out, o_idx, o_g, o_out, "decode_q4 grouped T=1")
 
 
-def test_c3_verify_steps_parity():
+def test_verify_q4_verify_steps_parity():
     import synth.device as SD
-    layer, spec = layer_for("C3", 5)
+    layer, spec = layer_for("verify_q4", 5)
     L = oracle_for(spec)
     for step in (0, 1, 999):
-        G.note("C3 step", step)
+        G.note("verify_q4 step", step)
         x = SD.device_tokens(spec, 5 * step, 5)
         idx, gates, out = G.run_grouped(layer, x)
         o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 5 * step, 5)
-        G.compare(idx, gates, out, o_idx, o_g, o_out, f"C3 step {step}")
+        G.compare(idx, gates, out, o_idx, o_g, o_out, f"verify_q4 step {step}")
     assert layer.device_error() == 0
 
 
-def test_c1_decode_parity():
+def test_decode_bf16_decode_parity():
     import synth.device as SD
-    layer, spec = layer_for("C1", 8)
+    layer, spec = layer_for("decode_bf16", 8)
     L = oracle_for(spec)
-    G.note("C1 decode")
+    G.note("decode_bf16 decode")
     x = SD.device_tokens(spec, 0, 8)
     idx, gates, out = G.run_route_decode(layer, x)
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, 8)
-    r = G.compare(idx, gates, out, o_idx, o_g, o_out, "C1")
-    print(f"C1: rel L2 max {r.max():.2e} median {np.median(r):.2e}")
+    r = G.compare(idx, gates, out, o_idx, o_g, o_out, "decode_bf16")
+    print(f"decode_bf16: rel L2 max {r.max():.2e} median {np.median(r):.2e}")
     assert layer.device_error() == 0
 
 
-def test_c4_prefill_chunk_parity():
+def test_prefill_bf16_prefill_chunk_parity():
     """T = 2048: every token's routing, and sampled tokens' outputs."""
     import synth.device as SD
-    layer, spec = layer_for("C4", 2048)
-    G.note("C4 grouped forward")
+    layer, spec = layer_for("prefill_bf16", 2048)
+    G.note("prefill_bf16 grouped forward")
     x = SD.device_tokens(spec, 0, 2048)
     idx, gates, out = G.run_grouped(layer, x)
     assert layer.device_error() == 0
-    G.note("C4 oracle routing")
+    G.note("prefill_bf16 oracle routing")
     L = oracle_for(spec)
     X = oracle.tokens_f64(spec, 0, 2048)
     Z, B = oracle.logits_with_bound(X, L)
@@ -160,9 +160,9 @@ def test_c4_prefill_chunk_parity():
     for t in range(2048):
         o_idx[t], zs = oracle.route_token(X[t], Z[t], B[t], L)
         o_g[t] = oracle.softmax_gates(zs)
-    G.compare(idx, gates, None, o_idx, o_g, None, "C4 routing")
+    G.compare(idx, gates, None, o_idx, o_g, None, "prefill_bf16 routing")
     sample = np.linspace(0, 2047, 12).astype(int)
     o_out = np.stack([oracle.moe_given(X[t], L, o_idx[t], o_g[t]) for t in sample])
     r = G.rel_l2(out[sample], o_out)
-    print(f"C4 sampled outputs: rel L2 max {r.max():.2e}; distinct experts {len(np.unique(idx))}")
+    print(f"prefill_bf16 sampled outputs: rel L2 max {r.max():.2e}; distinct experts {len(np.unique(idx))}")
     assert r.max() <= G.OUT_TOL

@@ -13,7 +13,7 @@ from tests import gpu_util as G
 pytestmark = pytest.mark.gpu
 
 SMALL = {
-    "C0": synth.CONFIGS["C0"],
+    "tiny_f32": synth.CONFIGS["tiny_f32"],
     "tiny_bf16": synth.small_spec(H=256, E=200, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_BF16,
                                   bias_alpha=0.37, weight_seed=21, token_seed=22, name="tiny_bf16"),
     "tiny_q4": synth.small_spec(H=256, E=200, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
@@ -42,7 +42,7 @@ def test_device_generator_matches_host():
     """Device fill == host generator, bit for bit (every format)."""
     torch = G.torch_mod()
     import synth.device as SD
-    for name in ["C0", "tiny_bf16", "tiny_q4", "odd_q4"]:
+    for name in ["tiny_f32", "tiny_bf16", "tiny_q4", "odd_q4"]:
         G.note("generator", name)
         spec, dl, _ = setup(name)
         assert np.array_equal(SD.to_numpy_bits(dl.router_eh), synth.router_eh(spec))
@@ -64,7 +64,7 @@ def test_device_generator_fullsize_rows():
     """Rows of the full-size pools, generated on device by counter offset."""
     torch = G.torch_mod()
     import synth.device as SD
-    spec = synth.CONFIGS["C2"]
+    spec = synth.CONFIGS["decode_q4"]
     for e in [0, 7777, spec.E - 1]:
         for which, tag, rows, K in [("gate", synth.TAG_GATE, spec.I, spec.H),
                                     ("down", synth.TAG_DOWN, spec.H, spec.I)]:
@@ -95,7 +95,7 @@ def test_decode_parity_small(name, layout):
     assert layer.device_error() == 0
 
 
-@pytest.mark.parametrize("name", ["C0", "tiny_q4", "wide_q4", "f32_bf16x"])
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_q4", "wide_q4", "f32_bf16x"])
 def test_forced_exact_refinement(name):
     """The integer-accumulator refinement gives the same routing."""
     import synth.device as SD
@@ -110,7 +110,7 @@ def test_forced_exact_refinement(name):
     assert layer.device_error() == 0
 
 
-@pytest.mark.parametrize("name", ["C0", "tiny_bf16", "tiny_q4", "wide_q4", "odd_q4", "f32_bf16x"])
+@pytest.mark.parametrize("name", ["tiny_f32", "tiny_bf16", "tiny_q4", "wide_q4", "odd_q4", "f32_bf16x"])
 @pytest.mark.parametrize("T", [2, 5, 37])
 def test_grouped_parity_small(name, T):
     import synth.device as SD

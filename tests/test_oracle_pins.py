@@ -313,7 +313,7 @@ def test_generator_moments_and_rounding():
 
 
 def test_bias_is_zipf_shaped():
-    spec = synth.CONFIGS["C1"]
+    spec = synth.CONFIGS["decode_bf16"]
     b = synth.router_bias(spec).astype(np.float64)
     r = np.sort(-b)                       # = 0.37 ln(rank), ascending
     assert r[0] == 0.0 and np.allclose(r, 0.37 * np.log(np.arange(1, spec.E + 1)), atol=1e-6)
