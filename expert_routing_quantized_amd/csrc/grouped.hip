@@ -16,6 +16,8 @@
 // The vector-ALU kernels below keep one weight row slice in registers and
 // loop over the segment's tokens, which suits the small groups of verify
 // windows (about 1.1 tokens per active expert at T = 5).
+#include <limits.h>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -106,6 +108,93 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
     a.offsets[a.E] = s_sum[1023];
     a.active[0] = s_act[1023];
     a.tiles[0] = s_til[1023];
+  }
+}
+
+// Exclusive prefix sum over a 1024-thread block (16 waves); *total gets the sum.
+__device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < 16; ++i) {
+    const int sw = s_w[i];
+    base += (i < w) ? sw : 0;
+    tot += sw;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// Grouping of at most 1024 pairs in one workgroup (verify windows and small
+// batches): the pairs are ranked by (expert, pair index) directly, so nothing
+// proportional to E is touched (no histogram clear, no scan over E).  Writes
+// the same outputs as hist + scan + scatter: pos, ptok, active list, tile
+// list, and counts / offsets of the active experts (the only entries read).
+__global__ __launch_bounds__(1024) void group_small_kernel(GroupArgs a) {
+  __shared__ int s_e[1024];
+  __shared__ int s_sorted[1024];
+  __shared__ int s_w[16];
+  const int p = threadIdx.x;
+  const int P = a.P;
+  int e = INT_MAX;                       // invalid pairs sort after every expert
+  if (p < P) {
+    const int v = a.idx[p];
+    if (v < 0 || v >= a.E) {
+      atomicOr(a.dev_flag, kDevBadIndex);
+    } else {
+      e = v;
+      const int t = p / a.k, j = p - t * a.k;
+      for (int jj = 0; jj < j; ++jj)
+        if (a.idx[t * a.k + jj] == v) atomicOr(a.dev_flag, kDevDupIndex);
+    }
+  }
+  s_e[p] = e;
+  const int nv = __syncthreads_count(p < P && e != INT_MAX);
+  int r = -1;
+  if (p < P && e != INT_MAX) {
+    r = 0;
+    for (int q = 0; q < P; ++q) {
+      const int eq = s_e[q];
+      r += (eq < e) || (eq == e && q < p);
+    }
+    a.ptok[r] = p / a.k;
+    s_sorted[r] = e;
+  }
+  if (p < P) a.pos[p] = r;
+  __syncthreads();
+  // thread r < nv looks at sorted position r; segment starts own their expert
+  const bool start = p < nv && (p == 0 || s_sorted[p - 1] != s_sorted[p]);
+  int cnt = 0;
+  if (start) {
+    const int es = s_sorted[p];
+    cnt = 1;
+    while (p + cnt < nv && s_sorted[p + cnt] == es) ++cnt;
+  }
+  const int nt = start ? (cnt + kTileRows - 1) / kTileRows : 0;
+  int nact, ntiles;
+  const int ai = block_excl_scan_1024(start ? 1 : 0, s_w, &nact);
+  const int ti = block_excl_scan_1024(nt, s_w, &ntiles);
+  if (start) {
+    const int es = s_sorted[p];
+    a.active[1 + ai] = es;
+    a.counts[es] = cnt;
+    a.offsets[es] = p;
+    for (int i = 0; i < nt; ++i) {
+      a.tiles[1 + 2 * (ti + i)] = es;
+      a.tiles[2 + 2 * (ti + i)] = i * kTileRows;
+    }
+  }
+  if (p == 0) {
+    a.active[0] = nact;
+    a.tiles[0] = ntiles;
   }
 }
 
@@ -333,10 +422,14 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
   a.out = out;
   a.dev_flag = L.dev_flag;
 
-  hipLaunchKernelGGL(fill_i32_kernel, dim3(min(1024, (a.E + 255) / 256)), dim3(256), 0, s, a.counts, 0, a.E);
-  hipLaunchKernelGGL(hist_kernel, dim3((a.P + 255) / 256), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a);
-  hipLaunchKernelGGL(scatter_kernel, dim3((a.P + 255) / 256), dim3(256), 0, s, a);
+  if (a.P <= 1024) {
+    hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(min(1024, (a.E + 255) / 256)), dim3(256), 0, s, a.counts, 0, a.E);
+    hipLaunchKernelGGL(hist_kernel, dim3((a.P + 255) / 256), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(scatter_kernel, dim3((a.P + 255) / 256), dim3(256), 0, s, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

@@ -149,6 +149,103 @@ hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, f
 }
 
 // ---------------------------------------------------------------------------
+// Router for a few tokens (2 <= T < 16: verify windows).  The contraction is
+// still a stream of the whole router, so the goal is the streaming-read
+// ceiling, not matrix throughput; MFMA only replaces the per-token wave
+// reductions that a vector-ALU GEMV needs for each (token, expert) pair.
+// Block = 16 experts x all T tokens (padded to 16) with v_mfma_f32_16x16x32_bf16;
+// the 4 waves split H into quarters and each lane issues all of its 16-byte
+// loads (16 router chunks, 16 hidden-state chunks) before the first MFMA.
+// Each MFMA's fp32 result (a sum of 32 exact products) is added into binary64
+// at once, and the 4 quarters, then the bias, are added in binary64:
+// d32 = 33, d64 = ceil(H / 128) + 4.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSkQ = 16;     // MFMAs (of K = 32) per wave per batch
+
+bool router_uses_skinny(const Layer& L, int T) {
+  return L.d.act_dtype == MOE_BF16 && T >= 2 && T < 16 && (L.d.hidden % 32) == 0;
+}
+
+__global__ __launch_bounds__(256) void router_skinny_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
+    int T, int H, int E, double* __restrict__ z, float* __restrict__ gmax,
+    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
+  __shared__ double red[4][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int nq = H / 32;
+  const int qpw = (nq + 3) / 4;
+  const int q0 = wave * qpw, q1 = min(nq, q0 + qpw);
+  const int tr = lane & 15;
+  const bool xin = tr < T;
+  // operand layout of 16x16x32: lane l holds row / column l % 16 and the 8
+  // consecutive K elements starting at 8 * (l / 16)
+  const uint16_t* pb = R + size_t(min(n0 + tr, E - 1)) * H + 8 * (lane >> 4);
+  const uint16_t* pa = X + size_t(min(tr, T - 1)) * H + 8 * (lane >> 4);
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int qb = q0; qb < q1; qb += kSkQ) {
+    uint4 b[kSkQ], xa[kSkQ];
+#pragma unroll
+    for (int i = 0; i < kSkQ; ++i) b[i] = load_nt(pb + 32 * min(qb + i, q1 - 1));
+#pragma unroll
+    for (int i = 0; i < kSkQ; ++i) xa[i] = *reinterpret_cast<const uint4*>(pa + 32 * min(qb + i, q1 - 1));
+#pragma unroll
+    for (int i = 0; i < kSkQ; ++i) {
+      if (qb + i < q1) {                                   // wave-uniform
+        const uint4 av = xin ? xa[i] : make_uint4(0u, 0u, 0u, 0u);
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                     __builtin_bit_cast(bf16x8_t, b[i]), d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
+      }
+    }
+  }
+  // D layout: lane l holds expert column l % 16, token rows 4 * (l / 16) + r
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][lane & 15] = acc[r];
+  __syncthreads();
+  const int t = tid >> 4, el = tid & 15, e = n0 + el;
+  double v = ((red[0][t][el] + red[1][t][el]) + red[2][t][el]) + red[3][t][el];
+  v += (e < E && bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
+  const bool live = e < E && t < T;
+  if (live) z[size_t(t) * E + e] = v;
+  if (live && !isfinite(v)) atomicOr(dev_flag, kDevNonFinite);
+  // maximum over 4 consecutive experts = 4 consecutive threads of one wave
+  double m = (e < E && !isnan(v)) ? v : -INFINITY;
+  m = fmax(m, dpp_f64<0xB1, 0xf>(m, -INFINITY));
+  m = fmax(m, dpp_f64<0x4E, 0xf>(m, -INFINITY));
+  if ((el & 3) == 0 && live) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = __double2float_ru(m);
+
+  if (blockIdx.x == 0) {          // ||x_t||^2, one wave per token
+    for (int tt = wave; tt < T; tt += 4) {
+      float q = 0.f;
+      for (int c = lane; c < H / 8; c += 64) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(X + size_t(tt) * H + c * 8);
+        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+          q = fmaf(lo, lo, q);
+          q = fmaf(hi, hi, q);
+        }
+      }
+      q = wave_sum(q);
+      if (lane == 0) xnorm[tt] = (double)q;
+    }
+  }
+}
+
+hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z, float* gmax,
+                                double* xnorm, hipStream_t s) {
+  const int H = L.d.hidden, E = L.d.n_experts;
+  hipLaunchKernelGGL(router_skinny_kernel, dim3((E + 15) / 16), dim3(256), 0, s,
+                     reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(L.router_eh),
+                     L.d.router_bias, T, H, E, z, gmax, xnorm, L.dev_flag);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Grouped bf16 experts on MFMA (prefill chunks, large verify batches).  The
 // token-expert pairs are sorted by expert and cut into tiles of 32 rows of
 // one expert's segment; each tile is one MFMA M-tile.  Most experts of a

@@ -266,6 +266,10 @@ RouterBound router_bound(const Layer& L, int T);
 bool router_uses_mfma(const Layer& L, int T);
 hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
                               double* xnorm, hipStream_t s);
+// mfma.hip: the router for 2 <= T < 16 bf16 tokens on 16x16x32 MFMA tiles.
+bool router_uses_skinny(const Layer& L, int T);
+hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z, float* gmax,
+                                double* xnorm, hipStream_t s);
 // mfma.hip: grouped bf16 experts on MFMA (used when grouped_uses_mfma).
 bool grouped_uses_mfma(const Layer& L, int T);
 hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s);

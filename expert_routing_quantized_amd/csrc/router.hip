@@ -210,6 +210,11 @@ RouterBound router_bound(const Layer& L, int T) {
     b.d64 = (L.d.hidden + 127) / 128 + 1;
     return b;
   }
+  if (router_uses_skinny(L, T)) {
+    b.d32 = 33;
+    b.d64 = (L.d.hidden + 127) / 128 + 4;
+    return b;
+  }
   const bool dot2 = (L.d.act_dtype == MOE_BF16 && T > 1);
   b.d32 = dot2 ? 8 : 7;
   b.d64 = lg + 7;
@@ -218,6 +223,7 @@ RouterBound router_bound(const Layer& L, int T) {
 
 hipError_t launch_router(const Layer& L, const void* x, int T, double* z, float* gmax,
                          double* xnorm, hipStream_t s) {
+  if (router_uses_skinny(L, T)) return launch_router_skinny(L, x, T, z, gmax, xnorm, s);
   if (L.d.act_dtype == MOE_F32) return launch_cpl<MOE_F32, 1>(L, x, T, z, gmax, xnorm, s);
   if (T == 1) return launch_cpl<MOE_BF16, 1>(L, x, T, z, gmax, xnorm, s);
   return launch_cpl<MOE_BF16, 8>(L, x, T, z, gmax, xnorm, s);

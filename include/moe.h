@@ -136,16 +136,19 @@ moe_status moe_route(const moe_layer* layer, const void* x, int32_t T,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* The router step alone: z[t][e] ~ sum_h x[t][h] R[h][e] + b[e] as binary64
- * [T][E], accumulated in exactly the order that moe_route uses.  For
- * T < 16 (or f32 x): binary32 chains of 8 products per 16-byte chunk (bf16
- * dot products when T > 1), then binary64 for the chain sums, the wave
- * reduction and the bias.  For T >= 16 with bf16 x and H a multiple of 32:
- * a bf16 MFMA GEMM whose binary32 accumulators are added into binary64
- * after every 128 of H.  With c = ceil(H / 512):
+ * [T][E], accumulated in exactly the order that moe_route uses.  T = 1 (and
+ * f32 x, or H not a multiple of 32): binary32 chains of 8 products per
+ * 16-byte chunk (bf16 dot products when T > 1), then binary64 for the chain
+ * sums, the wave reduction and the bias.  bf16 x with H a multiple of 32:
+ * 2 <= T < 16 runs 16x16x32 MFMA tiles whose binary32 results (32 products
+ * each) are added into binary64 one by one; T >= 16 runs a GEMM whose
+ * binary32 accumulators are added into binary64 after every 128 of H.
+ * With c = ceil(H / 512):
  *   |z - z_exact| <= (g(d32, 2^-23) + g(d64, 2^-52)) ||x_t||_2 max_e ||R_e||_2
  *                    + (d32 + H) 2^-125 + d64 2^-1021 + 2^-52 |z|,
  *   g(n, u) = n u / (1 - n u);  vector path: d32 = 7 (8 when T > 1),
- *   d64 = log2(c) + 7;  MFMA path: d32 = 136, d64 = ceil(H / 128) + 1.
+ *   d64 = log2(c) + 7;  16x16 tiles: d32 = 33, d64 = ceil(H / 128) + 4;
+ *   GEMM: d32 = 136, d64 = ceil(H / 128) + 1.
  * moe_route recomputes exactly the logits this bound leaves undecided.
  * Useful to inspect router scores and to time the step that dominates
  * batch-1 decode.

@@ -153,3 +153,19 @@ def test_grouped_mfma_tiles(name, T):
     counts = np.bincount(o_idx.ravel(), minlength=spec.E)
     print(f"{name} T={T}: max tokens per expert {counts.max()}, rel L2 max {r.max():.2e}")
     assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("name,T", [("tiny_q4", 300), ("tiny_q4", 256), ("odd_q4", 15)])
+def test_grouped_pair_sort_paths(name, T):
+    """P = T k above and at the one-workgroup limit (1024 pairs): the
+    histogram / scan / scatter sort and the one-block rank sort give the
+    same results; T = 15 is the largest batch on the 16x16 MFMA router."""
+    import synth.device as SD
+    spec, dl, L = setup(name)
+    G.note("grouped sort path", name, T)
+    layer = SD.make_layer(dl, max_tokens=T)
+    x = SD.device_tokens(spec, 500, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 500, T)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/T={T}")
+    assert layer.device_error() == 0
