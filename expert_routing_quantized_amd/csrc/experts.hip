@@ -11,12 +11,16 @@
 // only in the down/combine kernel (pyshine source tour, "The expert handoff
 // is a verified contract").
 //
+// The same kernels serve a few tokens at once (verify windows): with T
+// tokens there are P = T k token-expert pairs, and the block that holds the
+// first pair naming an expert computes every pair of that expert, so the
+// expert's weights are read once per call and no sort is needed.
+//
 // gate/up: one wave per pair of intermediate rows (gate row i and up row i
 // of the same expert), so silu(a)*u is formed in registers; for 4-bit rows
 // lane l owns quant block l (32 elements = 16 B of codes + one scale).
-// down:    8 lanes per output row; h of all k experts is staged in LDS
-// (padded every 32 floats); each lane accumulates g_j times its partial over
-// the experts in order j = 0..k-1 and the 8 lanes are summed at the end.
+// down:    8 lanes per output row, one wave per distinct expert, per-pair
+// partials in LDS, each token summed over its pairs in selection order.
 #include "moe_internal.h"
 
 namespace moe {
@@ -40,43 +44,57 @@ __device__ __forceinline__ float q4_block_dot(const uint4 w, const float* xv) {
   return acc;
 }
 
-struct DecodeArgs {
-  const void* x;
+struct PairArgs {
+  const void* x;     // [T][H]
   const int32_t* idx;
   const float* gates;
   const void *wg, *wu, *wd;
   const uint16_t *sg, *su, *sd;
-  float* h;          // [k][I]
-  float* out;        // [H]
-  int H, I, E, k;
+  float* h;          // [P][I]
+  float* out;        // [T][H]
+  int H, I, E, k, T, P;
   int* dev_flag;
 };
 
+// Expert of pair p if pair p is the first pair naming it (else -1): the
+// block that owns the first occurrence computes every pair of that expert,
+// so each selected expert's weights are read once per call.  All threads
+// of the block take part; the matching pairs (in any order: each pair's
+// result depends on its own token only) are appended to s_match.
+__device__ __forceinline__ int claim_pairs(const PairArgs& a, int p, int* s_match, int* s_n) {
+  const int e = a.idx[p];
+  const bool valid = e >= 0 && e < a.E;
+  if (threadIdx.x == 0) *s_n = 0;
+  __syncthreads();
+  bool earlier = false;
+  for (int q = threadIdx.x; q < a.P; q += blockDim.x) {
+    if (a.idx[q] == e && valid) {
+      if (q < p) earlier = true;
+      else s_match[atomicAdd(s_n, 1)] = q;
+    }
+  }
+  if (__syncthreads_or(earlier) || !valid) return -1;
+  return e;
+}
+
 // ------------------------------------------------------------ gate/up, 4-bit
 // MB = quant blocks per lane (H / 32 / 64 rounded up).
-template <int ACT, int MB>
-__global__ __launch_bounds__(256) void gateup_q4_kernel(DecodeArgs a) {
+template <int ACT, int MB, bool SINGLE>
+__global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
+  __shared__ int s_match[kMaxPairs];
+  __shared__ int s_n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = blockIdx.y;
-  const int e = a.idx[j];
-  const bool valid = (e >= 0 && e < a.E);
-  const int nblk = a.H >> 5;
-  float xv[MB][32];
-  float xs[MB];
-#pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    const int b = m * 64 + lane;
-    xs[m] = 0.f;
-    Chunk<ACT> ch[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ch[c].load(a.x, min(b, nblk - 1) * 32 + c * 8);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = (b < nblk) ? ch[c].get(i) : 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) xs[m] += xv[m][i];
+  int e;
+  bool valid = true;
+  if constexpr (SINGLE) {          // one token: every pair is its own group
+    e = a.idx[blockIdx.y];
+    valid = e >= 0 && e < a.E;
+    e = valid ? e : 0;             // addresses stay in range; h becomes NaN
+  } else {
+    e = claim_pairs(a, blockIdx.y, s_match, &s_n);
+    if (e < 0) return;
   }
+  const int nblk = a.H >> 5;
   constexpr int kRowsPerWave = 2;
   const int i0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
   const size_t rowb = size_t(a.H) / 2;
@@ -90,7 +108,7 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const int b = min(m * 64 + lane, nblk - 1);
-      const size_t row = size_t(valid ? e : 0) * a.I + i;
+      const size_t row = size_t(e) * a.I + i;
       wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * rowb + b * 16);
       wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * rowb + b * 16);
       dg[r][m] = f16_to_f32(a.sg[row * nblk + b]);
@@ -102,44 +120,71 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       if (!(i0 + r < a.I && m * 64 + lane < nblk)) dg[r][m] = du[r][m] = 0.f;
+  const int n = SINGLE ? 1 : s_n;
+  for (int mi = 0; mi < n; ++mi) {
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    float pa = 0.f, pu = 0.f;
+    for (int r = 0; r < kRowsPerWave; ++r)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        opaque_reg(wg[r][m]);
+        opaque_reg(wu[r][m]);
+      }
+    const int q = SINGLE ? (int)blockIdx.y : s_match[mi];
+    const size_t xoff = size_t(q / a.k) * a.H;
+    float xv[MB][32];
+    float xs[MB];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      pa = fmaf(dg[r][m], q4_block_dot(wg[r][m], xv[m]) - 8.f * xs[m], pa);
-      pu = fmaf(du[r][m], q4_block_dot(wu[r][m], xv[m]) - 8.f * xs[m], pu);
+      const int b = m * 64 + lane;
+      xs[m] = 0.f;
+      Chunk<ACT> ch[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ch[c].load(a.x, xoff + min(b, nblk - 1) * 32 + c * 8);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = (b < nblk) ? ch[c].get(i) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) xs[m] += xv[m][i];
     }
-    const float av = wave_sum(pa), uv = wave_sum(pu);
-    const int i = i0 + r;
-    if (lane == 0 && i < a.I) a.h[size_t(j) * a.I + i] = valid ? silu_f(av) * uv : NAN;
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      float pa = 0.f, pu = 0.f;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        pa = fmaf(dg[r][m], q4_block_dot(wg[r][m], xv[m]) - 8.f * xs[m], pa);
+        pu = fmaf(du[r][m], q4_block_dot(wu[r][m], xv[m]) - 8.f * xs[m], pu);
+      }
+      const float av = wave_sum(pa), uv = wave_sum(pu);
+      const int i = i0 + r;
+      if (lane == 0 && i < a.I) a.h[size_t(q) * a.I + i] = valid ? silu_f(av) * uv : NAN;
+    }
   }
 }
 
 // ------------------------------------------------------------ gate/up, dense
-template <int ACT, int WD, int CPL>
-__global__ __launch_bounds__(256) void gateup_dense_kernel(DecodeArgs a) {
+template <int ACT, int WD, int CPL, bool SINGLE>
+__global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
+  __shared__ int s_match[kMaxPairs];
+  __shared__ int s_n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = blockIdx.y;
-  const int e = a.idx[j];
-  const bool valid = (e >= 0 && e < a.E);
-  const int nch = a.H >> 3;
-  float xv[CPL][8];
-  {
-    Chunk<ACT> ch[CPL];
-#pragma unroll
-    for (int s = 0; s < CPL; ++s) ch[s].load(a.x, min(s * 64 + lane, nch - 1) * 8);
-#pragma unroll
-    for (int s = 0; s < CPL; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xv[s][i] = (s * 64 + lane < nch) ? ch[s].get(i) : 0.f;
+  int e;
+  bool valid = true;
+  if constexpr (SINGLE) {
+    e = a.idx[blockIdx.y];
+    valid = e >= 0 && e < a.E;
+    e = valid ? e : 0;
+  } else {
+    e = claim_pairs(a, blockIdx.y, s_match, &s_n);
+    if (e < 0) return;
   }
+  const int nch = a.H >> 3;
   constexpr int kRowsPerWave = 2;
   const int i0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
   Chunk<WD> wg[kRowsPerWave][CPL], wu[kRowsPerWave][CPL];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
-    const size_t row = size_t(valid ? e : 0) * a.I + min(i0 + r, a.I - 1);
+    const size_t row = size_t(e) * a.I + min(i0 + r, a.I - 1);
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
       const int c = min(s * 64 + lane, nch - 1);
@@ -155,33 +200,54 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(DecodeArgs a) {
         wg[r][s].zero();
         wu[r][s].zero();
       }
+  const int n = SINGLE ? 1 : s_n;
+  for (int mi = 0; mi < n; ++mi) {
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    float pa = 0.f, pu = 0.f;
+    for (int r = 0; r < kRowsPerWave; ++r)
 #pragma unroll
-    for (int s = 0; s < CPL; ++s)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        pa = fmaf(wg[r][s].get(i), xv[s][i], pa);
-        pu = fmaf(wu[r][s].get(i), xv[s][i], pu);
+      for (int s = 0; s < CPL; ++s) {
+        wg[r][s].opaque();
+        wu[r][s].opaque();
       }
-    const float av = wave_sum(pa), uv = wave_sum(pu);
-    const int i = i0 + r;
-    if (lane == 0 && i < a.I) a.h[size_t(j) * a.I + i] = valid ? silu_f(av) * uv : NAN;
+    const int q = SINGLE ? (int)blockIdx.y : s_match[mi];
+    const size_t xoff = size_t(q / a.k) * a.H;
+    float xv[CPL][8];
+    {
+      Chunk<ACT> ch[CPL];
+#pragma unroll
+      for (int s = 0; s < CPL; ++s) ch[s].load(a.x, xoff + min(s * 64 + lane, nch - 1) * 8);
+#pragma unroll
+      for (int s = 0; s < CPL; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xv[s][i] = (s * 64 + lane < nch) ? ch[s].get(i) : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      float pa = 0.f, pu = 0.f;
+#pragma unroll
+      for (int s = 0; s < CPL; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pa = fmaf(wg[r][s].get(i), xv[s][i], pa);
+          pu = fmaf(wu[r][s].get(i), xv[s][i], pu);
+        }
+      const float av = wave_sum(pa), uv = wave_sum(pu);
+      const int i = i0 + r;
+      if (lane == 0 && i < a.I) a.h[size_t(q) * a.I + i] = valid ? silu_f(av) * uv : NAN;
+    }
   }
 }
 
 // ------------------------------------------------------------ down + combine
 
-// One block per 8 output rows; wave w of the block handles the selected
-// experts j = w, w + W, ... (W = min(k, 16) waves), 8 lanes per output row,
-// lane g of a row covering quant blocks (or 8-element chunks) g, g + 8, ...
-// of I.  The expert's h slice comes straight from L2 into registers, so the
-// weights, the scales and h are all in flight together.  Each wave's
-// g_j-weighted partials go through LDS and are summed over the waves in a
-// fixed order (deterministic, no float atomics).
+// One token: one block per 8 output rows, wave w handles the selected
+// experts j = w, w + W, ... (W = min(k, 16)), 8 lanes per output row, lane g
+// covering quant blocks (or 8-element chunks) g, g + 8, ... of I.  The
+// expert's h slice comes straight from L2 into registers, so the weights,
+// the scales and h are all in flight together.  Each wave's g_j-weighted
+// partials go through LDS and are summed over the waves in a fixed order.
 template <int WD>
-__global__ __launch_bounds__(1024) void down_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   __shared__ float part[kMaxK][8];
   __shared__ int s_bad;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -205,7 +271,6 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(DecodeArgs a) {
       if (blockIdx.x == 0) atomicOr(a.dev_flag, bad);
     }
   }
-
   float acc = 0.f;
   for (int j = wave; j < k; j += nw) {
     int e = a.idx[j];
@@ -247,9 +312,146 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* idx,
-                                 const float* gates, float* out, float* h, hipStream_t s) {
-  DecodeArgs a;
+// One block per 8 output rows of all T tokens.  The block first copies h
+// of every pair into LDS (when it fits; those loads do not depend on the
+// indices, so they overlap the index loads), lists the pairs, marks tokens
+// with a bad or repeated index and gives each distinct expert to one wave
+// (8 lanes per output row, lane g of a row covering quant blocks, or
+// 8-element chunks, g, g + 8, ... of I).  A wave loads the rows of up to UG
+// of its experts before computing any, applies each expert to the h of every
+// pair naming it, and the per-pair partials meet in LDS; each token's output
+// is summed over its pairs in selection order (fixed order, no float
+// atomics).
+constexpr int kPairHLdsBytes = 64 * 1024;
+
+template <int WD, int SPL>
+__global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float sh_h[];   // [P][I] if it fits
+  __shared__ float part[kMaxPairs][8];
+  __shared__ int s_idx[kMaxPairs];
+  __shared__ int s_uniq[kMaxPairs];
+  __shared__ int s_bad[kMaxPairs];
+  __shared__ int s_next[kMaxPairs];     // next pair naming the same expert, or -1
+  __shared__ int s_nu;
+  constexpr int UG = SPL == 1 ? 4 : (SPL <= 4 ? 2 : 1);   // experts prefetched per wave
+  constexpr int kElems = (WD == MOE_Q4B32) ? 32 : 8;
+  using WChunk = Chunk<WD == MOE_Q4B32 ? MOE_BF16 : WD>;   // q4: 16 B of codes
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int g = lane & 7, grp = lane >> 3;
+  const int I = a.I, k = a.k, P = a.P;
+  const int o = blockIdx.x * 8 + grp;
+  const int oc = min(o, a.H - 1);
+  const int nsl = I / kElems;
+  const int nblk = I >> 5;
+  const bool hl = size_t(P) * I * 4 <= kPairHLdsBytes;
+  if (hl) {
+    const float4* src = reinterpret_cast<const float4*>(a.h);
+    float4* dst = reinterpret_cast<float4*>(sh_h);
+    for (int c = threadIdx.x; c < P * I / 4; c += blockDim.x) dst[c] = src[c];
+  }
+  if (threadIdx.x == 0) s_nu = 0;
+  for (int q = threadIdx.x; q < P; q += blockDim.x) s_idx[q] = a.idx[q];
+  for (int t = threadIdx.x; t < a.T; t += blockDim.x) s_bad[t] = 0;
+  __syncthreads();
+  for (int q = threadIdx.x; q < P; q += blockDim.x) {
+    const int e = s_idx[q], t = q / k;
+    const bool valid = e >= 0 && e < a.E;
+    int bad = valid ? 0 : kDevBadIndex;
+    bool first = valid;
+    for (int qq = 0; qq < q && valid; ++qq) {
+      if (s_idx[qq] == e) {
+        first = false;
+        if (qq / k == t) bad |= kDevDupIndex;
+      }
+    }
+    if (bad) {
+      atomicOr(&s_bad[t], bad);
+      if (blockIdx.x == 0) atomicOr(a.dev_flag, bad);
+    }
+    if (first) s_uniq[atomicAdd(&s_nu, 1)] = q;
+    int nx = -1;
+    for (int qq = q + 1; qq < P && valid; ++qq)
+      if (s_idx[qq] == e) {
+        nx = qq;
+        break;
+      }
+    s_next[q] = nx;
+  }
+  __syncthreads();
+  const float* hbase = hl ? sh_h : a.h;
+  const int nu = s_nu;
+  for (int u0 = wave; u0 < nu; u0 += UG * nw) {
+    WChunk w[UG][SPL];
+    float d[UG][SPL];
+    int eu[UG], qu[UG];
+#pragma unroll
+    for (int ug = 0; ug < UG; ++ug) {
+      const int u = min(u0 + ug * nw, nu - 1);            // clamped: loads stay in range
+      qu[ug] = s_uniq[u];
+      eu[ug] = s_idx[qu[ug]];
+      const size_t row = size_t(eu[ug]) * a.H + oc;
+#pragma unroll
+      for (int sp = 0; sp < SPL; ++sp) {
+        const int sl = min(g + 8 * sp, nsl - 1);
+        if constexpr (WD == MOE_Q4B32) {
+          w[ug][sp].v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + sl * 16);
+          d[ug][sp] = f16_to_f32(a.sd[row * nblk + sl]);
+        } else {
+          w[ug][sp].load(a.wd, row * I + sl * 8);
+          d[ug][sp] = 1.f;
+        }
+      }
+    }
+#pragma unroll
+    for (int ug = 0; ug < UG; ++ug) {
+      if (u0 + ug * nw >= nu) break;                      // wave-uniform
+      for (int q = qu[ug]; q >= 0; q = s_next[q]) {
+        const float* hq = hbase + size_t(q) * I;
+        float acc = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < SPL; ++sp) {
+          const int sl = g + 8 * sp;
+          if (sl >= nsl) continue;
+          float hv[kElems];
+#pragma unroll
+          for (int i = 0; i < kElems; i += 4) {
+            const float4 v4 = *reinterpret_cast<const float4*>(hq + sl * kElems + i);
+            hv[i] = v4.x; hv[i + 1] = v4.y; hv[i + 2] = v4.z; hv[i + 3] = v4.w;
+          }
+          if constexpr (WD == MOE_Q4B32) {
+            float hs = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) hs += hv[i];
+            acc = fmaf(d[ug][sp], q4_block_dot(w[ug][sp].v, hv) - 8.f * hs, acc);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc = fmaf(w[ug][sp].get(i), hv[i], acc);
+          }
+        }
+        acc = group8_sum(acc);
+        if (g == 0) part[q][grp] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < a.T * 8; c += blockDim.x) {
+    const int t = c >> 3, r = c & 7;
+    if (blockIdx.x * 8 + r >= a.H) continue;
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s = fmaf(a.gates[t * k + j], part[t * k + j][r], s);
+    a.out[size_t(t) * a.H + blockIdx.x * 8 + r] = s_bad[t] ? NAN : s;
+  }
+}
+
+template <bool SINGLE>
+static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s);
+
+bool pair_path_fits(const Layer& L, int T) { return T >= 1 && T * L.d.top_k <= kMaxPairs; }
+
+hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32_t* idx,
+                               const float* gates, float* out, float* h, hipStream_t s) {
+  PairArgs a;
   a.x = x;
   a.idx = idx;
   a.gates = gates;
@@ -265,17 +467,25 @@ hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* i
   a.I = L.d.inter;
   a.E = L.d.n_experts;
   a.k = L.d.top_k;
+  a.T = T;
+  a.P = T * a.k;
   a.dev_flag = L.dev_flag;
-  const int act = L.d.act_dtype, wd = L.d.expert_dtype;
-  dim3 g1((a.I + 7) / 8, a.k);
+  if (a.P > kMaxPairs) return hipErrorInvalidValue;
+  if (T == 1) return launch_pairs<true>(a, L.d.act_dtype, L.d.expert_dtype, s);
+  return launch_pairs<false>(a, L.d.act_dtype, L.d.expert_dtype, s);
+}
+
+template <bool SINGLE>
+static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s) {
+  dim3 g1((a.I + 7) / 8, a.P);
   if (wd == MOE_Q4B32) {
     const int mb = (a.H / 32 + 63) / 64;
 #define MOE_GU_Q4(M)                                                                    \
   if (mb <= M) {                                                                        \
     if (act == MOE_BF16)                                                                \
-      hipLaunchKernelGGL((gateup_q4_kernel<MOE_BF16, M>), g1, dim3(256), 0, s, a);      \
+      hipLaunchKernelGGL((gateup_q4_kernel<MOE_BF16, M, SINGLE>), g1, dim3(256), 0, s, a);      \
     else                                                                                \
-      hipLaunchKernelGGL((gateup_q4_kernel<MOE_F32, M>), g1, dim3(256), 0, s, a);       \
+      hipLaunchKernelGGL((gateup_q4_kernel<MOE_F32, M, SINGLE>), g1, dim3(256), 0, s, a);       \
   } else
     MOE_GU_Q4(1) MOE_GU_Q4(2) MOE_GU_Q4(4) return hipErrorInvalidValue;
 #undef MOE_GU_Q4
@@ -284,25 +494,40 @@ hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* i
 #define MOE_GU_D(C)                                                                          \
   if (cpl <= C) {                                                                            \
     if (act == MOE_BF16 && wd == MOE_BF16)                                                   \
-      hipLaunchKernelGGL((gateup_dense_kernel<MOE_BF16, MOE_BF16, C>), g1, dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((gateup_dense_kernel<MOE_BF16, MOE_BF16, C, SINGLE>), g1, dim3(256), 0, s, a); \
     else if (act == MOE_F32 && wd == MOE_BF16)                                               \
-      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_BF16, C>), g1, dim3(256), 0, s, a);  \
+      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_BF16, C, SINGLE>), g1, dim3(256), 0, s, a);  \
     else                                                                                     \
-      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_F32, C>), g1, dim3(256), 0, s, a);   \
+      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_F32, C, SINGLE>), g1, dim3(256), 0, s, a);   \
   } else
     MOE_GU_D(1) MOE_GU_D(2) MOE_GU_D(4) MOE_GU_D(8) MOE_GU_D(16) return hipErrorInvalidValue;
 #undef MOE_GU_D
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nw = a.k < 16 ? a.k : 16;
+  const int nw = a.P < 16 ? a.P : 16;
   dim3 g2((a.H + 7) / 8);
-  if (wd == MOE_Q4B32)
-    hipLaunchKernelGGL(down_combine_kernel<MOE_Q4B32>, g2, dim3(64 * nw), 0, s, a);
-  else if (wd == MOE_BF16)
-    hipLaunchKernelGGL(down_combine_kernel<MOE_BF16>, g2, dim3(64 * nw), 0, s, a);
-  else
-    hipLaunchKernelGGL(down_combine_kernel<MOE_F32>, g2, dim3(64 * nw), 0, s, a);
+  const size_t lds = (size_t(a.P) * a.I * 4 <= kPairHLdsBytes) ? size_t(a.P) * a.I * 4 : 0;
+  const int nsl = a.I / (wd == MOE_Q4B32 ? 32 : 8);
+  const int spl = (nsl + 7) / 8;
+#define MOE_DOWN_SPL(K, S) \
+  if (spl <= S) hipLaunchKernelGGL((down_combine_kernel<K, S>), g2, dim3(64 * nw), lds, s, a); else
+#define MOE_DOWN(K)                                                                                    \
+  if constexpr (SINGLE) {                                                                              \
+    hipLaunchKernelGGL(down_combine_single_kernel<K>, g2, dim3(64 * nw), 0, s, a);                     \
+  } else {                                                                                             \
+    MOE_DOWN_SPL(K, 1) MOE_DOWN_SPL(K, 2) MOE_DOWN_SPL(K, 4) MOE_DOWN_SPL(K, 8) MOE_DOWN_SPL(K, 16)    \
+    MOE_DOWN_SPL(K, 32) MOE_DOWN_SPL(K, 64) return hipErrorInvalidValue;                               \
+  }
+  if (wd == MOE_Q4B32) {
+    MOE_DOWN(MOE_Q4B32)
+  } else if (wd == MOE_BF16) {
+    MOE_DOWN(MOE_BF16)
+  } else {
+    MOE_DOWN(MOE_F32)
+  }
+#undef MOE_DOWN
+#undef MOE_DOWN_SPL
   return hipGetLastError();
 }
 

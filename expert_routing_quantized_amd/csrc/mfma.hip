@@ -154,13 +154,21 @@ hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, f
 // ceiling, not matrix throughput; MFMA only replaces the per-token wave
 // reductions that a vector-ALU GEMV needs for each (token, expert) pair.
 // Block = 16 experts x all T tokens (padded to 16) with v_mfma_f32_16x16x32_bf16;
-// the 4 waves split H into quarters and each lane issues all of its 16-byte
-// loads (16 router chunks, 16 hidden-state chunks) before the first MFMA.
+// the 4 waves split H into quarters.  The MFMA operand layout wants 16
+// different expert rows in every load instruction (64 B per row), which
+// streams poorly; for the common hidden sizes the kernel instead loads each
+// row quarter with 512-byte-contiguous instructions (all of them issued up
+// front) and transposes it through a per-wave LDS buffer in two phases, the
+// second phase's data arriving while the first is multiplied.
 // Each MFMA's fp32 result (a sum of 32 exact products) is added into binary64
 // at once, and the 4 quarters, then the bias, are added in binary64:
 // d32 = 33, d64 = ceil(H / 128) + 4.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kSkQ = 16;     // MFMAs (of K = 32) per wave per batch
+
+__device__ __forceinline__ void skinny_epilogue(double (*red)[16][17], const uint16_t* X,
+                                                const float* bias, int T, int H, int E, int n0,
+                                                double* z, float* gmax, double* xnorm, int* dev_flag);
 
 bool router_uses_skinny(const Layer& L, int T) {
   return L.d.act_dtype == MOE_BF16 && T >= 2 && T < 16 && (L.d.hidden % 32) == 0;
@@ -205,19 +213,27 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][lane & 15] = acc[r];
   __syncthreads();
+  skinny_epilogue(red, X, bias, T, H, E, n0, z, gmax, xnorm, dev_flag);
+}
+
+// The shared epilogue of both few-token kernels: sum the 4 quarters in
+// order, add the bias, write logits and 4-expert maxima, flag non-finite
+// logits; block 0 also writes ||x_t||^2.
+__device__ __forceinline__ void skinny_epilogue(double (*red)[16][17], const uint16_t* X,
+                                                const float* bias, int T, int H, int E, int n0,
+                                                double* z, float* gmax, double* xnorm, int* dev_flag) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = tid >> 4, el = tid & 15, e = n0 + el;
   double v = ((red[0][t][el] + red[1][t][el]) + red[2][t][el]) + red[3][t][el];
   v += (e < E && bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
   const bool live = e < E && t < T;
   if (live) z[size_t(t) * E + e] = v;
   if (live && !isfinite(v)) atomicOr(dev_flag, kDevNonFinite);
-  // maximum over 4 consecutive experts = 4 consecutive threads of one wave
   double m = (e < E && !isnan(v)) ? v : -INFINITY;
   m = fmax(m, dpp_f64<0xB1, 0xf>(m, -INFINITY));
   m = fmax(m, dpp_f64<0x4E, 0xf>(m, -INFINITY));
   if ((el & 3) == 0 && live) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = __double2float_ru(m);
-
-  if (blockIdx.x == 0) {          // ||x_t||^2, one wave per token
+  if (blockIdx.x == 0) {
     for (int tt = wave; tt < T; tt += 4) {
       float q = 0.f;
       for (int c = lane; c < H / 8; c += 64) {
@@ -236,12 +252,79 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
   }
 }
 
+template <int HH>
+__global__ __launch_bounds__(256) void router_skinny_lds_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
+    int T, int E, double* __restrict__ z, float* __restrict__ gmax,
+    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
+  constexpr int NP = 2;                     // phases per row quarter
+  constexpr int PE = (HH / 4) / NP;         // elements per row per phase
+  constexpr int LPR = PE / 8;               // lanes per row in one load instruction
+  constexpr int RPI = 64 / LPR;             // rows per load instruction
+  constexpr int NI = 16 / RPI;              // load instructions per phase
+  constexpr int QP = PE / 32;               // MFMAs per phase
+  static_assert(LPR <= 64 && 64 % LPR == 0 && QP >= 1, "unsupported hidden size");
+  __shared__ __attribute__((aligned(16))) uint16_t sr[4][16][PE + 8];
+  __shared__ double red[4][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int tr = lane & 15, g = lane >> 4;
+  const bool xin = tr < T;
+  const int kw = wave * (HH / 4);
+  uint4 b[NP][NI];
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      b[p][i] = load_nt(R + size_t(min(n0 + i * RPI + lane / LPR, E - 1)) * HH + kw + p * PE + 8 * (lane % LPR));
+  const uint16_t* pa = X + size_t(min(tr, T - 1)) * HH + kw;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint4 xa[QP];
+#pragma unroll
+    for (int q = 0; q < QP; ++q)
+      xa[q] = xin ? *reinterpret_cast<const uint4*>(pa + p * PE + 32 * q + 8 * g) : make_uint4(0u, 0u, 0u, 0u);
+    // the wave's LDS buffer is reused by the next phase: a wave's LDS
+    // accesses complete in program order, so no barrier is needed
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      *reinterpret_cast<uint4*>(&sr[wave][i * RPI + lane / LPR][8 * (lane % LPR)]) = b[p][i];
+#pragma unroll
+    for (int q = 0; q < QP; ++q) {
+      const uint4 bv = *reinterpret_cast<const uint4*>(&sr[wave][tr][32 * q + 8 * g]);
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[q]),
+                                                   __builtin_bit_cast(bf16x8_t, bv), d, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][4 * g + r][tr] = acc[r];
+  __syncthreads();
+  skinny_epilogue(red, X, bias, T, HH, E, n0, z, gmax, xnorm, dev_flag);
+}
+
 hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z, float* gmax,
                                 double* xnorm, hipStream_t s) {
   const int H = L.d.hidden, E = L.d.n_experts;
-  hipLaunchKernelGGL(router_skinny_kernel, dim3((E + 15) / 16), dim3(256), 0, s,
-                     reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(L.router_eh),
-                     L.d.router_bias, T, H, E, z, gmax, xnorm, L.dev_flag);
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  const uint16_t* rb = reinterpret_cast<const uint16_t*>(L.router_eh);
+  const dim3 grid((E + 15) / 16);
+#define MOE_SKINNY_LDS(HV)                                                                        \
+  if (H == HV) {                                                                                  \
+    hipLaunchKernelGGL(router_skinny_lds_kernel<HV>, grid, dim3(256), 0, s, xb, rb, L.d.router_bias, \
+                       T, E, z, gmax, xnorm, L.dev_flag);                                         \
+    return hipGetLastError();                                                                     \
+  }
+  MOE_SKINNY_LDS(512)
+  MOE_SKINNY_LDS(1024)
+  MOE_SKINNY_LDS(2048)
+  MOE_SKINNY_LDS(4096)
+#undef MOE_SKINNY_LDS
+  hipLaunchKernelGGL(router_skinny_kernel, grid, dim3(256), 0, s, xb, rb, L.d.router_bias, T, H, E, z,
+                     gmax, xnorm, L.dev_flag);
   return hipGetLastError();
 }
 

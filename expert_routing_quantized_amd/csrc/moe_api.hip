@@ -287,7 +287,7 @@ moe_status moe_expert_decode(const moe_layer* layer, const void* x, const int32_
   if (moe_status st = check_ws(L, 1, ws, ws_bytes, &W)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* h = reinterpret_cast<float*>(static_cast<char*>(ws) + W.h);
-  hipError_t e = moe::launch_decode_experts(L, x, idx, gates, out, h, s);
+  hipError_t e = moe::launch_pair_experts(L, x, 1, idx, gates, out, h, s);
   if (e != hipSuccess) return hip_fail(e, "expert decode launch");
   return ok();
 }
@@ -320,7 +320,9 @@ moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
   }
   hipError_t e;
   if (T == 1)
-    e = moe::launch_decode_experts(L, x, ri, rg, out, reinterpret_cast<float*>(w + W.h), s);
+    e = moe::launch_pair_experts(L, x, 1, ri, rg, out, reinterpret_cast<float*>(w + W.h), s);
+  else if (!moe::grouped_uses_mfma(L, T) && moe::pair_path_fits(L, T))
+    e = moe::launch_pair_experts(L, x, T, ri, rg, out, reinterpret_cast<float*>(w + W.hm), s);
   else
     e = moe::launch_grouped_experts(L, x, T, ri, rg, out, w, W, s);
   if (e != hipSuccess) return hip_fail(e, "expert launch");

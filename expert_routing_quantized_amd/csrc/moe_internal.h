@@ -12,6 +12,7 @@ namespace moe {
 
 // ------------------------------------------------------------------ limits
 constexpr int kMaxK = 32;
+constexpr int kMaxPairs = 256;  // token-expert pairs of the few-token expert path
 constexpr int kMaxH = 8192;
 constexpr int kMaxI = 4096;
 constexpr int kRouterWaves = 4;      // router block = 4 waves, one expert row per wave
@@ -181,6 +182,16 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
 }
 
 // Router chunk decoding: 8 consecutive elements of an act-dtype row.
+// Register barrier: tells the compiler the value may change here, so work
+// derived from loop-invariant weights (e.g. expanding 4-bit codes to floats)
+// stays inside the loop instead of being hoisted into extra registers.
+__device__ __forceinline__ void opaque_reg(uint4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+__device__ __forceinline__ void opaque_reg(float4& v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 template <int ACT>
 struct Chunk;
 template <>
@@ -193,6 +204,7 @@ struct Chunk<MOE_BF16> {
     v = load_nt(reinterpret_cast<const uint16_t*>(base) + elem);
   }
   __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void opaque() { opaque_reg(v); }
   __device__ __forceinline__ float get(int i) const {
     uint32_t w = (i < 2) ? v.x : (i < 4) ? v.y : (i < 6) ? v.z : v.w;
     return (i & 1) ? bf16_hi(w) : bf16_lo(w);
@@ -211,6 +223,10 @@ struct Chunk<MOE_F32> {
     const uint4 u = load_nt(p), w = load_nt(p + 4);
     a = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
     b = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
+  }
+  __device__ __forceinline__ void opaque() {
+    opaque_reg(a);
+    opaque_reg(b);
   }
   __device__ __forceinline__ void zero() {
     a = make_float4(0, 0, 0, 0);
@@ -279,8 +295,11 @@ hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double
                               const float* gmax, const double* xnorm, int32_t* idx,
                               float* gates, const RouterBound& rb, hipStream_t s);
 // experts.hip: single-token expert GEMVs and combine.
-hipError_t launch_decode_experts(const Layer& L, const void* x, const int32_t* idx,
-                                 const float* gates, float* out, float* h, hipStream_t s);
+// experts.hip: expert GEMVs + combine for T tokens with T k <= kMaxPairs
+// (batch-1 decode and verify windows); h is [T k][I] fp32 workspace.
+bool pair_path_fits(const Layer& L, int T);
+hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32_t* idx,
+                               const float* gates, float* out, float* h, hipStream_t s);
 // grouped.hip: index sort, grouped experts, weighted un-permute.
 hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const int32_t* idx,
                                   const float* gates, float* out, char* ws,

@@ -155,11 +155,14 @@ def test_grouped_mfma_tiles(name, T):
     assert layer.device_error() == 0
 
 
-@pytest.mark.parametrize("name,T", [("tiny_q4", 300), ("tiny_q4", 256), ("odd_q4", 15)])
+@pytest.mark.parametrize("name,T", [("tiny_q4", 300), ("tiny_q4", 256), ("odd_q4", 15), ("wide_q4", 10),
+                                    ("wide_q4", 25)])
 def test_grouped_pair_sort_paths(name, T):
-    """P = T k above and at the one-workgroup limit (1024 pairs): the
-    histogram / scan / scatter sort and the one-block rank sort give the
-    same results; T = 15 is the largest batch on the 16x16 MFMA router."""
+    """P = T k above and at the one-workgroup sort limit (1024 pairs): the
+    histogram / scan / scatter sort and the one-block rank sort; at most 256
+    pairs go to the deduplicating pair kernels, with h staged in LDS (odd_q4)
+    or read from global memory (wide_q4, 100 and 250 pairs over 130 experts,
+    so experts repeat across tokens)."""
     import synth.device as SD
     spec, dl, L = setup(name)
     G.note("grouped sort path", name, T)
@@ -168,4 +171,24 @@ def test_grouped_pair_sort_paths(name, T):
     idx, gates, out = G.run_grouped(layer, x)
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 500, T)
     G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/T={T}")
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("name,T", [("mfma_multi_tile", 7), ("mfma_ragged", 9), ("mfma_wide", 2)])
+def test_few_token_router_shapes(name, T):
+    """The 16x16 MFMA router at 2 <= T < 16: H = 512 and H = 2048 (row
+    quarters transposed through LDS) and H = 160 (generic operand loads),
+    with E not a multiple of the 16-expert tile."""
+    import synth.device as SD
+    spec = MFMA_SPECS[name]
+    G.note("few-token router", name, T)
+    dl = SD.device_layer(spec)
+    L = G.host_oracle(spec)
+    layer = SD.make_layer(dl, max_tokens=T)
+    x = SD.device_tokens(spec, 40, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 40, T)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name}/T={T}")
+    idx2, gates2, out2 = G.run_route_decode(layer, x)
+    G.compare(idx2, gates2, out2, o_idx, o_g, o_out, f"{name}/T={T} route+decode")
     assert layer.device_error() == 0
