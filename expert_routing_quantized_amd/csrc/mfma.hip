@@ -335,18 +335,23 @@ hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z,
 // 2048-token chunk receive 1-3 tokens, so most tiles are nearly empty and
 // the kernels are bound by the expert-weight stream, which every tile reads
 // once; the few experts with hundreds of tokens are where MFMA throughput
-// matters.
+// matters.  So the weights are streamed the way that reads HBM best: each
+// wave loads its own 32 weight rows in 128-byte row pieces (8 lanes per
+// row), two K slices ahead of the slice being multiplied, and transposes
+// them into the MFMA operand layout through LDS.
 //
-// gate/up: block = (128 intermediate channels, tile); wave w owns channels
-//   32w..32w+31 of both G and U (two 32x32 accumulators), reads its weight
-//   rows straight from HBM into MFMA operand registers (each weight is used
-//   by this tile only), while the tile's gathered token rows are staged
-//   through LDS in 32-wide K slices.  Epilogue: h = silu(a) * u in fp32.
+// gate/up: block = (64 intermediate channels, tile); waves 0-1 own 32 gate
+//   channels each, waves 2-3 the matching up channels; the tile's gathered
+//   token rows are staged through LDS (rows past the segment are zeros);
+//   epilogue h = silu(a) * u in fp32, the up results passing through LDS.
 // down: block = (128 output rows, tile); the tile's 32 rows of h (fp32) are
 //   split into bf16 hi + lo parts in LDS (h = hi + lo to 2^-16 relative) and
 //   multiplied by the same bf16 weights twice, so the down projection keeps
 //   fp32-level accuracy.
-constexpr int kGN = 128;            // channels / outputs per block
+constexpr int kGC = 64;              // gate (and up) channels per gate/up block
+constexpr int kDR = 128;             // output rows per down block
+constexpr int kKS = 64;              // K elements per slice
+constexpr int kKP = kKS + 8;         // LDS row pitch (elements) of a slice
 
 bool grouped_uses_mfma(const Layer& L, int T) {
   return L.d.expert_dtype == MOE_BF16 && L.d.act_dtype == MOE_BF16 && T >= 16 &&
@@ -358,111 +363,129 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne_dev(float f) {
   return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
+// 16 bytes at row + k (k a multiple of 8); zeros where k >= K (the address
+// is clamped so the load stays inside the row).
+__device__ __forceinline__ uint4 load_row_chunk(const uint16_t* row, int k, int K, bool live) {
+  const uint4 v = load_nt(row + min(k, K - 8));
+  return (live && k < K) ? v : make_uint4(0u, 0u, 0u, 0u);
+}
+
 __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTileRows][kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[2][2 * kGC][kKP];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTileRows][kKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I;
-  const int ch = blockIdx.x * kGN + wave * 32 + (lane & 31);       // this lane's B column
-  const int chc = min(ch, I - 1);
-  const int ntiles = a.tiles[0];
+  const int ch0 = blockIdx.x * kGC;
+  const int wc = ch0 + 32 * (wave & 1);                  // first channel of this wave
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(wave < 2 ? a.wg : a.wu);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
-  const uint16_t* WG = reinterpret_cast<const uint16_t*>(a.wg);
-  const uint16_t* WU = reinterpret_cast<const uint16_t*>(a.wu);
+  const int lr = lane >> 3, lc = lane & 7;               // weight loads: row lr + 8 i, chunk lc
+  const int xr = tid >> 3, xc = tid & 7;                 // x loads: tile row xr, chunk xc
+  const int nks = (H + kKS - 1) / kKS;
+  const int ntiles = a.tiles[0];
   for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
     const int e = a.tiles[1 + 2 * ti], r0 = a.tiles[2 + 2 * ti];
     const int n = a.counts[e], seg = a.offsets[e];
     const int nrow = min(kTileRows, n - r0);
-    // A staging: threads 0..127 each load 16 B of one gathered token row
-    const int ar = (tid >> 2) & 31, ac = (tid & 3) * 8;
-    const int tok = a.ptok[seg + r0 + min(ar, nrow - 1)];
-    const uint16_t* pa = X + size_t(tok) * H + ac;
-    const uint16_t* pg = WG + (size_t(e) * I + chc) * H + 8 * (lane >> 5);
-    const uint16_t* pu = WU + (size_t(e) * I + chc) * H + 8 * (lane >> 5);
-    uint4 ra = *reinterpret_cast<const uint4*>(pa);
-    uint4 bg[2], bu[2];
+    const bool xlive = xr < nrow;
+    const uint16_t* px = X + size_t(a.ptok[seg + r0 + min(xr, nrow - 1)]) * H;
+    const uint16_t* pw[4];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bg[kk] = load_nt(pg + 16 * kk);
-      bu[kk] = load_nt(pu + 16 * kk);
+    for (int i = 0; i < 4; ++i) pw[i] = W + (size_t(e) * I + min(wc + lr + 8 * i, I - 1)) * H;
+    uint4 wA[4], wB[4], xA, xB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wA[i] = load_row_chunk(pw[i], 8 * lc, H, true);
+    xA = load_row_chunk(px, 8 * xc, H, xlive);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wB[i] = load_row_chunk(pw[i], kKS + 8 * lc, H, true);
+    xB = load_row_chunk(px, kKS + 8 * xc, H, xlive);
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    // one K slice: stage it, refill its registers two slices ahead, multiply
+#define MOE_GU_SLICE(KT, WR, XR, BUF)                                                          \
+    {                                                                                          \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                            \
+        *reinterpret_cast<uint4*>(&sw[BUF][32 * wave + lr + 8 * i][8 * lc]) = WR[i];           \
+      *reinterpret_cast<uint4*>(&sx[BUF][xr][8 * xc]) = XR;                                    \
+      __syncthreads();                                                                         \
+      const int kn = ((KT) + 2) * kKS;                                                         \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i) WR[i] = load_row_chunk(pw[i], kn + 8 * lc, H, true); \
+      XR = load_row_chunk(px, kn + 8 * xc, H, xlive);                                          \
+      _Pragma("unroll") for (int q = 0; q < kKS / 16; ++q) {                                   \
+        const int kk = 16 * q + 8 * (lane >> 5);                                               \
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&sx[BUF][lane & 31][kk]);       \
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&sw[BUF][32 * wave + (lane & 31)][kk]); \
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);                   \
+      }                                                                                        \
     }
-    f32x16_t ag, au;
+    for (int kt = 0; kt < nks; kt += 2) {
+      MOE_GU_SLICE(kt, wA, xA, 0)
+      if (kt + 1 < nks) MOE_GU_SLICE(kt + 1, wB, xB, 1)
+    }
+#undef MOE_GU_SLICE
+    // epilogue: D rows 8 (i / 4) + 4 (lane / 32) + i % 4 (tokens), column lane % 32 (channel)
+    __syncthreads();
+    float* su = reinterpret_cast<float*>(&sw[0][0][0]);   // [32][kGC + 1] up results
+    if (wave >= 2) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ag[i] = au[i] = 0.f;
-    const int nk = H / kBK;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (tid < 128) *reinterpret_cast<uint4*>(&sx[buf][ar][ac]) = ra;
-      __syncthreads();
-      uint4 ng[2], nu[2];
-      if (kt + 1 < nk) {
-        const int ko = (kt + 1) * kBK;
-        ra = *reinterpret_cast<const uint4*>(pa + ko);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          ng[kk] = load_nt(pg + ko + 16 * kk);
-          nu[kk] = load_nt(pu + ko + 16 * kk);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(&sx[buf][lane & 31][16 * kk + 8 * (lane >> 5)]);
-        ag = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8_t, bg[kk]), ag, 0, 0, 0);
-        au = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa, __builtin_bit_cast(bf16x8_t, bu[kk]), au, 0, 0, 0);
-      }
-      if (kt + 1 < nk) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          bg[kk] = ng[kk];
-          bu[kk] = nu[kk];
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        su[r * (kGC + 1) + 32 * (wave - 2) + (lane & 31)] = acc[i];
       }
     }
-    // epilogue: rows 8*(i/4) + 4*(lane/32) + i%4 of column ch
+    __syncthreads();
+    if (wave < 2) {
+      const int ch = wc + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (r < nrow && ch < I) {
-        const float g = ag[i], u = au[i];
-        a.hm[size_t(seg + r0 + r) * I + ch] = g / (1.0f + expf(-g)) * u;
+      for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (r < nrow && ch < I) {
+          const float g = acc[i], u = su[r * (kGC + 1) + 32 * wave + (lane & 31)];
+          a.hm[size_t(seg + r0 + r) * I + ch] = g / (1.0f + expf(-g)) * u;
+        }
       }
     }
     __syncthreads();   // LDS reuse by the next tile
   }
 }
 
-template <int KS>   // K slices of 16 held in registers (I <= 16 KS)
+template <int NS>   // K slices of 64 (I <= 64 NS)
 __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t sh[];   // hi [32][I+8], lo [32][I+8]
+  constexpr int KP = NS * kKS + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t shi[kTileRows][KP];
+  __shared__ __attribute__((aligned(16))) uint16_t slo[kTileRows][KP];
+  __shared__ __attribute__((aligned(16))) uint16_t sw[4][32][kKP];   // wave-private slices
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, I = a.I, ip = I + 8;
-  uint16_t* shi = sh;
-  uint16_t* slo = sh + kTileRows * ip;
-  const int o = blockIdx.x * kGN + wave * 32 + (lane & 31);
-  const int oc = min(o, H - 1);
-  const int ntiles = a.tiles[0];
+  const int H = a.H, I = a.I;
+  const int ow = blockIdx.x * kDR + 32 * wave;           // first output row of this wave
+  const int lr = lane >> 3, lc = lane & 7;
   const uint16_t* WD = reinterpret_cast<const uint16_t*>(a.wd);
+  const int ntiles = a.tiles[0];
   for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
     const int e = a.tiles[1 + 2 * ti], r0 = a.tiles[2 + 2 * ti];
     const int n = a.counts[e], seg = a.offsets[e];
     const int nrow = min(kTileRows, n - r0);
-    // weights of this lane's output row, all K at once (I/16 slices of 8)
-    const uint16_t* pw = WD + (size_t(e) * H + oc) * I + 8 * (lane >> 5);
-    uint4 b[KS];
-    const int nks = I / 16;
+    // the wave's 32 weight rows, all of K, in flight at once
+    uint4 w[NS][4];
 #pragma unroll
-    for (int q = 0; q < KS; ++q) b[q] = load_nt(pw + 16 * min(q, nks - 1));
-    // h rows of the tile -> bf16 hi/lo in LDS (rows past the segment: zeros)
-    for (int q = tid; q < kTileRows * (I / 4); q += 256) {
-      const int r = q / (I / 4), c = (q - r * (I / 4)) * 4;
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t* row = WD + (size_t(e) * H + min(ow + lr + 8 * i, H - 1)) * I;
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) w[sl][i] = load_row_chunk(row, sl * kKS + 8 * lc, I, true);
+    }
+    // h rows of the tile -> bf16 hi/lo (rows past the segment and columns past I: zeros)
+    for (int q = tid; q < kTileRows * (NS * kKS / 4); q += 256) {
+      const int r = q / (NS * kKS / 4), c = (q - r * (NS * kKS / 4)) * 4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < nrow) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + r) * I + c);
+      if (r < nrow && c < I) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + r) * I + c);
       const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint16_t hi = f32_to_bf16_rne_dev(vv[j]);
         const float rem = vv[j] - __uint_as_float(uint32_t(hi) << 16);
-        shi[r * ip + c + j] = hi;
-        slo[r * ip + c + j] = f32_to_bf16_rne_dev(rem);
+        shi[r][c + j] = hi;
+        slo[r][c + j] = f32_to_bf16_rne_dev(rem);
       }
     }
     __syncthreads();
@@ -470,38 +493,44 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      if (q >= nks) continue;          // block-uniform
-      const int kc = 16 * q + 8 * (lane >> 5);
-      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&shi[(lane & 31) * ip + kc]);
-      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&slo[(lane & 31) * ip + kc]);
-      const bf16x8_t bb = __builtin_bit_cast(bf16x8_t, b[q]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bb, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bb, acc, 0, 0, 0);
+    for (int sl = 0; sl < NS; ++sl) {
+      // the wave's private slice buffer: its LDS accesses complete in
+      // program order, so reusing it for the next slice needs no barrier
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sw[wave][lr + 8 * i][8 * lc]) = w[sl][i];
+#pragma unroll
+      for (int q = 0; q < kKS / 16; ++q) {
+        const int kk = 16 * q + 8 * (lane >> 5);
+        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&shi[lane & 31][sl * kKS + kk]);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&slo[lane & 31][sl * kKS + kk]);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&sw[wave][lane & 31][kk]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
+      }
     }
+    const int o = ow + (lane & 31);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
       if (r < nrow && o < H) a.y[size_t(seg + r0 + r) * H + o] = acc[i];
     }
-    __syncthreads();
+    __syncthreads();   // h staging reuse by the next tile
   }
 }
 
 hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s) {
   const int gy = 2048;
-  hipLaunchKernelGGL(gateup_mfma_kernel, dim3((a.I + kGN - 1) / kGN, gy), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(gateup_mfma_kernel, dim3((a.I + kGC - 1) / kGC, gy), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = sizeof(uint16_t) * 2 * kTileRows * (a.I + 8);
-  const dim3 g2((a.H + kGN - 1) / kGN, gy);
-  const int nks = a.I / 16;
-  if (nks <= 4)
-    hipLaunchKernelGGL(down_mfma_kernel<4>, g2, dim3(256), lds, s, a);
-  else if (nks <= 8)
-    hipLaunchKernelGGL(down_mfma_kernel<8>, g2, dim3(256), lds, s, a);
-  else if (nks <= 16)
-    hipLaunchKernelGGL(down_mfma_kernel<16>, g2, dim3(256), lds, s, a);
+  const dim3 g2((a.H + kDR - 1) / kDR, gy);
+  const int ns = (a.I + kKS - 1) / kKS;
+  if (ns == 1)
+    hipLaunchKernelGGL(down_mfma_kernel<1>, g2, dim3(256), 0, s, a);
+  else if (ns == 2)
+    hipLaunchKernelGGL(down_mfma_kernel<2>, g2, dim3(256), 0, s, a);
+  else if (ns <= 4)
+    hipLaunchKernelGGL(down_mfma_kernel<4>, g2, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
