@@ -5,10 +5,14 @@
 // hexlives dispatch's archived tensor-core experiment); with T = 2048 tokens
 // it is a dense 2048 x 2048 x 24,576 contraction (206 GFLOP), the one place
 // on the path where MFMA is the bound.  Both operands are K-contiguous (x
-// rows, router rows): each 256-thread block computes a 64-token x 128-expert
-// tile with v_mfma_f32_32x32x16_bf16 (4 waves, each 32 tokens x 64 experts),
-// staging 32-wide K slices of both operands through LDS (double-buffered,
-// next slice prefetched into registers while the current one is consumed).
+// rows, router rows).  Each 512-thread block computes a 128-token x
+// 128-expert tile with v_mfma_f32_32x32x16_bf16 (8 waves of 32 x 64),
+// staging 64-wide K slices of both operands through LDS with 128-byte row
+// pieces, two slices prefetched into registers ahead of the one being
+// multiplied.  Tiles are ordered for the 8 XCDs: blocks are dealt to XCDs
+// round-robin, so XCD j gets a contiguous range of expert tiles and walks
+// all token tiles of one expert tile before the next, which keeps that
+// router tile in its own L2 while every token tile reuses it.
 //
 // Rounding model for the certified selection: the fp32 MFMA accumulators are
 // added into binary64 accumulators after every 128 of K (8 instructions of
@@ -24,28 +28,54 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64, kBN = 128, kBK = 32, kPadK = 40;   // LDS row stride (bf16) with padding
-constexpr int kF64Every = 4;                               // K slices (of 32) per binary64 fold
+constexpr int kBK = 32;                    // K granularity the MFMA paths require
+constexpr int kRM = 128, kRN = 128;        // router GEMM block tile (tokens x experts)
+constexpr int kRK = 64, kRKP = kRK + 8;    // K slice and its LDS row pitch (elements)
+constexpr int kRThreads = 512;
+constexpr int kRChunks = (kRM + kRN) * (kRK / 8) / kRThreads;   // 16-byte loads per thread per slice
 
-__global__ __launch_bounds__(256) void router_gemm_kernel(
+__global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
-    int T, int H, int E, double* __restrict__ z, float* __restrict__ gmax,
+    int T, int H, int E, int nm, int nn, int nper, double* __restrict__ z, float* __restrict__ gmax,
     double* __restrict__ xnorm, int* __restrict__ dev_flag) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kBM][kPadK];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kBN][kPadK];
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kRM][kRKP];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kRN][kRKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
-  const int wm = (wave & 1) * 32, wn = (wave >> 1) * 64;
+  const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const int nb = xcd * nper + loc / nm, mb = loc % nm;
+  if (nb >= nn) return;                                  // whole block
+  const int m0 = mb * kRM, n0 = nb * kRN;
+  const int wm = (wave & 3) * 32, wn = (wave >> 2) * 64;
 
-  // global -> register staging: A 64x32 (one 16-byte load per thread), B 128x32 (two)
-  const int ar = tid >> 2, ac = (tid & 3) * 8;
-  const int br0 = tid >> 2, br1 = br0 + 64;
-  const uint16_t* pa = X + size_t(min(m0 + ar, T - 1)) * H + ac;
-  const uint16_t* pb0 = R + size_t(min(n0 + br0, E - 1)) * H + ac;
-  const uint16_t* pb1 = R + size_t(min(n0 + br1, E - 1)) * H + ac;
-  uint4 ra = *reinterpret_cast<const uint4*>(pa);
-  uint4 rb0 = load_nt(pb0), rb1 = load_nt(pb1);
-
+  // chunk c = tid + 512 i: staging row c / 8 (x rows, then router rows), 16-byte piece c % 8
+  const uint16_t* src[kRChunks];
+  int drow[kRChunks], dcol[kRChunks];
+  bool isb[kRChunks];
+#pragma unroll
+  for (int i = 0; i < kRChunks; ++i) {
+    const int c = tid + i * kRThreads;
+    const int r = c >> 3;
+    dcol[i] = (c & 7) * 8;
+    isb[i] = r >= kRM;
+    drow[i] = isb[i] ? r - kRM : r;
+    src[i] = isb[i] ? R + size_t(min(n0 + drow[i], E - 1)) * H : X + size_t(min(m0 + drow[i], T - 1)) * H;
+  }
+  const int nk = (H + kRK - 1) / kRK;
+  auto load = [&](int kt, uint4 (&v)[kRChunks]) {
+#pragma unroll
+    for (int i = 0; i < kRChunks; ++i) {
+      const int k = kt * kRK + dcol[i];
+      const uint4 w = *reinterpret_cast<const uint4*>(src[i] + min(k, H - 8));
+      v[i] = (k < H) ? w : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto stage = [&](int buf, const uint4 (&v)[kRChunks]) {
+#pragma unroll
+    for (int i = 0; i < kRChunks; ++i) {
+      uint16_t* d = isb[i] ? &sb[buf][drow[i]][dcol[i]] : &sa[buf][drow[i]][dcol[i]];
+      *reinterpret_cast<uint4*>(d) = v[i];
+    }
+  };
   f32x16_t acc[2];
   double accd[2][16];
 #pragma unroll
@@ -55,31 +85,18 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
       acc[n][i] = 0.f;
       accd[n][i] = 0.0;
     }
-
-  const int nk = H / kBK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    *reinterpret_cast<uint4*>(&sa[buf][ar][ac]) = ra;
-    *reinterpret_cast<uint4*>(&sb[buf][br0][ac]) = rb0;
-    *reinterpret_cast<uint4*>(&sb[buf][br1][ac]) = rb1;
-    __syncthreads();
-    if (kt + 1 < nk) {                          // prefetch the next slice
-      const int ko = (kt + 1) * kBK;
-      ra = *reinterpret_cast<const uint4*>(pa + ko);
-      rb0 = load_nt(pb0 + ko);
-      rb1 = load_nt(pb1 + ko);
-    }
+  auto compute = [&](int kt, int buf) {
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
+    for (int kk = 0; kk < kRK; kk += 16) {
       const int kc = kk + 8 * (lane >> 5);
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sa[buf][wm + (lane & 31)][kc]);
+      const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&sa[buf][wm + (lane & 31)][kc]);
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&sb[buf][wn + 32 * n + (lane & 31)][kc]);
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[n], 0, 0, 0);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&sb[buf][wn + 32 * n + (lane & 31)][kc]);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[n], 0, 0, 0);
       }
     }
-    if ((kt + 1) % kF64Every == 0 || kt + 1 == nk) {
+    if ((kt & 1) == 1 || kt + 1 == nk) {                 // every 128 of K
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -87,6 +104,21 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
           accd[n][i] += (double)acc[n][i];
           acc[n][i] = 0.f;
         }
+    }
+  };
+  uint4 v0[kRChunks], v1[kRChunks];
+  load(0, v0);
+  load(1, v1);
+  for (int kt = 0; kt < nk; kt += 2) {
+    stage(0, v0);
+    __syncthreads();
+    load(min(kt + 2, nk - 1), v0);
+    compute(kt, 0);
+    if (kt + 1 < nk) {
+      stage(1, v1);
+      __syncthreads();
+      load(min(kt + 3, nk - 1), v1);
+      compute(kt + 1, 1);
     }
   }
 
@@ -113,9 +145,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(
   }
   if (bad) atomicOr(dev_flag, kDevNonFinite);
 
-  if (blockIdx.x == 0) {          // ||x_t||^2 for this block's tokens, 16 per wave
-    for (int r = 0; r < 16; ++r) {
-      const int t = m0 + wave * 16 + r;
+  if (nb == 0) {          // ||x_t||^2 for this block's tokens, 16 per wave
+    for (int r = 0; r < kRM / 8; ++r) {
+      const int t = m0 + wave * (kRM / 8) + r;
       if (t >= T) break;
       float q = 0.f;
       for (int c = lane; c < H / 8; c += 64) {
@@ -141,10 +173,11 @@ bool router_uses_mfma(const Layer& L, int T) {
 hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
                               double* xnorm, hipStream_t s) {
   const int H = L.d.hidden, E = L.d.n_experts;
-  dim3 grid((E + kBN - 1) / kBN, (T + kBM - 1) / kBM);
-  hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, s,
+  const int nm = (T + kRM - 1) / kRM, nn = (E + kRN - 1) / kRN;
+  const int nper = (nn + 7) / 8;                         // expert tiles per XCD
+  hipLaunchKernelGGL(router_gemm_kernel, dim3(8 * nper * nm), dim3(kRThreads), 0, s,
                      reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(L.router_eh),
-                     L.d.router_bias, T, H, E, z, gmax, xnorm, L.dev_flag);
+                     L.d.router_bias, T, H, E, nm, nn, nper, z, gmax, xnorm, L.dev_flag);
   return hipGetLastError();
 }
 
