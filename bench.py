@@ -51,7 +51,78 @@ def parse():
                         "through the 4-bit layer; prefill_bf16: T=2048 prefill chunks through the bf16 layer")
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
     p.add_argument("--cpu-sample", type=int, default=12, help="tokens the oracle is timed on (0: skip)")
+    p.add_argument("--counters", action="store_true",
+                   help="hardware-counter run: launch eagerly (no graphs), run the router alone, then "
+                        "a plain copy of known size that calibrates the byte counters; prints a summary")
     return p.parse_args()
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "router_gemv_decode_q4_traffic.md")
+TRAFFIC_SOURCES = ["expert_routing_quantized_amd/csrc/router.hip", "expert_routing_quantized_amd/csrc/moe_internal.h"]
+COPY_CALIBRATION_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the router GEMV is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per router launch from the committed counter summary, or
+    None when the summary is missing or the kernel sources changed since."""
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].split(": ", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("source_sha256") != kernel_source_hash():
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def counters_main(args, spec):
+    """Eager launches for rocprofv3 --pmc runs (counter collection does not
+    need graphs): K tokens, K router-only launches, 3 calibration copies."""
+    import torch
+
+    import synth.device as SD
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n_rep = 3 if args.mode == "cold" else 1
+    dl = SD.device_layer(spec)
+    routers = [dl.router_eh] + [SD.device_router(spec) for _ in range(n_rep - 1)]
+    layers = [SD.make_layer(dl, max_tokens=1, router=r) for r in routers]
+    K, W = args.steps, args.warmup
+    X = SD.device_tokens(spec, 0, W + K)
+    ws = layers[0].workspace(1)
+    idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((W + K, spec.k), dtype=torch.float32, device=dev)
+    out = torch.zeros((W + K, spec.H), dtype=torch.float32, device=dev)
+    zbuf = torch.empty((spec.E,), dtype=torch.float64, device=dev)
+    for t in range(W + K):
+        L = layers[t % n_rep]
+        L.route(X[t], 1, idx[t], gates[t], ws)
+        L.expert_decode(X[t], idx[t], gates[t], out[t], ws)
+    for t in range(W, W + K):
+        layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
+    src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": True, "tokens": W + K, "router_launches": K,
+                      "copy_bytes": COPY_CALIBRATION_BYTES, "copies": 3,
+                      "router_bytes_per_launch": step_bytes(spec)["router"],
+                      "source_sha256": kernel_source_hash()}), flush=True)
 
 
 def step_bytes(spec) -> dict:
@@ -129,37 +200,82 @@ def grouped_main(args, spec):
     torch.cuda.synchronize()
     log(f"layer ready in {time.time() - t0:.1f}s: pool {dl.nbytes_pool() / 1e9:.2f} GB, T={T}")
 
+    from expert_routing_quantized_amd import MOE_ROUTE_GIVEN
+    zbuf = torch.empty((T, spec.E), dtype=torch.float64, device=dev)
+
     def step(i):
         b = i % nseq
         layer.grouped_forward(X[b], T, idx[b], gates[b], 0, out[b], ws)
 
-    for i in range(min(W, 3)):
+    def router_only(i):
+        layer.router_logits(X[i % nseq], T, zbuf, ws)
+
+    def experts_only(i):
+        b = i % nseq
+        layer.grouped_forward(X[b], T, idx[b], gates[b], MOE_ROUTE_GIVEN, out[b], ws)
+
+    for i in range(max(min(W, 3), min(nseq, W + K))):
         step(i)
     torch.cuda.synchronize()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
-    g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    graphs = {n: torch.cuda.CUDAGraph() for n in ("warm", "main", "router", "experts")}
     with torch.cuda.stream(s):
-        with torch.cuda.graph(g_warm, stream=s):
+        with torch.cuda.graph(graphs["warm"], stream=s):
             for i in range(W):
                 step(i)
-        with torch.cuda.graph(g_main, stream=s):
+        with torch.cuda.graph(graphs["main"], stream=s):
             for i in range(W, W + K):
                 step(i)
+        with torch.cuda.graph(graphs["router"], stream=s):
+            for i in range(W, W + K):
+                router_only(i)
+        with torch.cuda.graph(graphs["experts"], stream=s):
+            for i in range(W, W + K):
+                experts_only(i)
     torch.cuda.synchronize()
-    with torch.cuda.stream(s):
-        g_warm.replay()
-        torch.cuda.synchronize()
+
+    def timed(name):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
-        g_main.replay()
+        graphs[name].replay()
         e1.record(s)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        return e0.elapsed_time(e1)
+
+    with torch.cuda.stream(s):
+        graphs["warm"].replay()
+        torch.cuda.synchronize()
+        ms = timed("main")
+        graphs["router"].replay()
+        torch.cuda.synchronize()
+        ms_router = timed("router")
+        ms_experts = timed("experts")
     err = layer.device_error()
     import numpy as np
     distinct = [len(np.unique(idx[b].cpu().numpy())) for b in range(min(nseq, 8))]
     per_step = ms / 1e3 / K
+    router_s = ms_router / 1e3 / K
+    experts_s = ms_experts / 1e3 / K
+    act = 2 if spec.act == 1 else 4
+    if spec.expert == 2:
+        per_expert = 3 * spec.I * spec.H // 2 + 3 * spec.I * (spec.H // 32) * 2
+    else:
+        per_expert = 3 * spec.I * spec.H * (2 if spec.expert == 1 else 4)
+    d_mean = float(np.mean(distinct))
+    router_bytes = spec.E * spec.H * act + spec.E * 4 + T * spec.H * act
+    router_flops = 2.0 * T * spec.H * spec.E
+    if router_flops / router_bytes > 312.5:      # above the ridge: MFMA-bound
+        roof = {"bound": "mfma", "kernel": "router GEMM (moe::router_gemm_kernel, bf16 MFMA)",
+                "achieved": router_flops / router_s / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
+                "frac": router_flops / router_s / 1e12 / 2500.0, "traffic": None,
+                "avg_launch_us": router_s * 1e6, "flops_per_launch": router_flops}
+    else:
+        roof = {"bound": "hbm", "kernel": "router (moe::router_skinny_lds_kernel, 16x16x32 MFMA tiles)",
+                "achieved": router_bytes / router_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": router_bytes / router_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                "avg_launch_us": router_s * 1e6, "bytes_per_launch": router_bytes}
+    experts_bytes = d_mean * per_expert
     res = {
         "metric": f"MoE-layer grouped forward tokens/s ({spec.name}: T={T} per call)",
         "value": T * K / (ms / 1e3),
@@ -171,6 +287,10 @@ def grouped_main(args, spec):
                                f"I={spec.I}, experts {'q4b32' if spec.expert == 2 else 'bf16'}",
                    "us_per_step": per_step * 1e6, "distinct_experts_per_step": distinct,
                    "device_errors": err},
+        "roofline": roof,
+        "experts_stage": {"us_per_call": experts_s * 1e6, "weight_bytes_per_call": experts_bytes,
+                          "weight_gbs": experts_bytes / experts_s / 1e9,
+                          "note": "moe_grouped_forward with caller indices: pair grouping, gate/up, down, combine"},
     }
     print(json.dumps(res), flush=True)
 
@@ -188,6 +308,8 @@ def main():
     import synth.device as SD
 
     spec = synth.CONFIGS[args.config]
+    if args.counters:
+        return counters_main(args, spec)
     if spec.T > 1:
         return grouped_main(args, spec)
     K, W = args.steps, args.warmup
@@ -293,7 +415,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": router_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic() if args.mode == "cold" and args.config == "decode_q4" else None,
             "avg_launch_us": router_s * 1e6,
             "bytes_per_launch": by["router"],
         },
