@@ -266,7 +266,8 @@ def grouped_main(args, spec):
     router_bytes = spec.E * spec.H * act + spec.E * 4 + T * spec.H * act
     router_flops = 2.0 * T * spec.H * spec.E
     if router_flops / router_bytes > 312.5:      # above the ridge: MFMA-bound
-        roof = {"bound": "mfma", "kernel": "router GEMM (moe::router_gemm_kernel, bf16 MFMA)",
+        kname = ("moe::router_gemm_big_kernel, 256x256 tiles" if T >= 512 else "moe::router_gemm_kernel, 128x128 tiles")
+        roof = {"bound": "mfma", "kernel": f"router GEMM ({kname}, bf16 MFMA)",
                 "achieved": router_flops / router_s / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
                 "frac": router_flops / router_s / 1e12 / 2500.0, "traffic": None,
                 "avg_launch_us": router_s * 1e6, "flops_per_launch": router_flops}

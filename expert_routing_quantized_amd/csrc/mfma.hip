@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
   };
   uint4 v0[kRChunks], v1[kRChunks];
   load(0, v0);
-  load(1, v1);
+  load(min(1, nk - 1), v1);
   for (int kt = 0; kt < nk; kt += 2) {
     stage(0, v0);
     __syncthreads();
@@ -136,11 +136,15 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
         z[size_t(t) * E + e] = v;
         if (!isfinite(v)) bad = true;
       }
-      // maximum over the 4 consecutive experts of lanes 4q..4q+3
-      double m = (e < E && !isnan(v)) ? v : -INFINITY;
-      m = fmax(m, dpp_f64<0xB1, 0xf>(m, -INFINITY));
-      m = fmax(m, dpp_f64<0x4E, 0xf>(m, -INFINITY));
-      if ((lane & 3) == 0 && t < T && e < E) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = __double2float_ru(m);
+      // maximum over the 4 consecutive experts of lanes 4q..4q+3, taken on
+      // the values rounded up to binary32 (rounding up is monotone, so this
+      // is the rounded-up maximum)
+      float m = (e < E && !isnan(v)) ? f64_to_f32_up(v) : -INFINITY;
+      m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                       __builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, m), 0xB1, 0xf, 0xf, false)));
+      m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                       __builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, m), 0x4E, 0xf, 0xf, false)));
+      if ((lane & 3) == 0 && t < T && e < E) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = m;
     }
   }
   if (bad) atomicOr(dev_flag, kDevNonFinite);
@@ -166,17 +170,184 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large batches (T >= 512): 256-token x 256-expert tiles, 16 waves of
+// 64 x 64, 32-wide K slices, two slices of register prefetch, the same XCD
+// tile order.  The block reads 1 KB of LDS per MFMA instead of 1.5 KB, which
+// is what bounds the smaller tile, but its 64 accumulators per lane leave no
+// room for binary64 partial sums: each logit is accumulated in the MFMA's
+// fp32 accumulator over all of H and converted once.  Rounding model: H/16
+// instructions of K = 16, each counted as at most 17 binary32 roundings
+// (d32 = 17 H / 16), then the binary64 bias addition (d64 = 1).  The wider
+// bound only moves more near-ties into the selection's exact refinement.
+constexpr int kGM = 256, kGN = 256, kGK = 32, kGKP = kGK + 8;
+constexpr int kGThreads = 1024;
+constexpr int kGChunks = (kGM + kGN) * (kGK / 8) / kGThreads;
+constexpr int kBigT = 512;                // smallest batch that takes the big tiles
+
+__global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
+    int T, int H, int E, int nm, int nn, int nper, double* __restrict__ z, float* __restrict__ gmax,
+    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kGM][kGKP];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kGN][kGKP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const int nb = xcd * nper + loc / nm, mb = loc % nm;
+  if (nb >= nn) return;                                  // whole block
+  const int m0 = mb * kGM, n0 = nb * kGN;
+  const int wm = (wave & 3) * 64, wn = (wave >> 2) * 64;
+  // thread tid stages 16 bytes of token row tid / 4 and of router row tid / 4
+  // (piece tid % 4 of the 64-byte K slice) into the same LDS position
+  static_assert(kGChunks == 2 && kGM == kGN && kGM * (kGK / 8) == kGThreads, "one row piece of each operand");
+  const int lr = tid >> 2, lcol = (tid & 3) * 8;
+  const uint16_t* pa = X + size_t(min(m0 + lr, T - 1)) * H + lcol;
+  const uint16_t* pb = R + size_t(min(n0 + lr, E - 1)) * H + lcol;
+  const int nk = H / kGK;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < kGK; kk += 16) {
+      const int kc = kk + 8 * (lane >> 5);
+      bf16x8_t av[2], bv[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) av[a] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][wm + 32 * a + (lane & 31)][kc]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) bv[b] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][wn + 32 * b + (lane & 31)][kc]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  uint4 a0 = *reinterpret_cast<const uint4*>(pa), b0 = *reinterpret_cast<const uint4*>(pb);
+  const int k1 = min(1, nk - 1) * kGK;
+  uint4 a1 = *reinterpret_cast<const uint4*>(pa + k1), b1 = *reinterpret_cast<const uint4*>(pb + k1);
+  for (int kt = 0; kt < nk; kt += 2) {
+    *reinterpret_cast<uint4*>(&sa[0][lr][lcol]) = a0;
+    *reinterpret_cast<uint4*>(&sb[0][lr][lcol]) = b0;
+    __syncthreads();
+    const int k2 = min(kt + 2, nk - 1) * kGK;
+    a0 = *reinterpret_cast<const uint4*>(pa + k2);
+    b0 = *reinterpret_cast<const uint4*>(pb + k2);
+    compute(0);
+    if (kt + 1 < nk) {
+      *reinterpret_cast<uint4*>(&sa[1][lr][lcol]) = a1;
+      *reinterpret_cast<uint4*>(&sb[1][lr][lcol]) = b1;
+      __syncthreads();
+      const int k3 = min(kt + 3, nk - 1) * kGK;
+      a1 = *reinterpret_cast<const uint4*>(pa + k3);
+      b1 = *reinterpret_cast<const uint4*>(pb + k3);
+      compute(1);
+    }
+  }
+  // epilogue: lane holds rows 8*(i/4) + 4*(lane/32) + i%4 of column lane%32 of
+  // each 32x32 accumulator; interior tiles skip every bounds check
+  const bool full = m0 + kGM <= T && n0 + kGN <= E;       // block-uniform
+  const size_t G4 = size_t(E + 3) / 4;
+  bool bad = false;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int e = n0 + wn + 32 * b + (lane & 31);
+    const double bs = (bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int tb = m0 + wm + 32 * a + 4 * (lane >> 5);
+      double v[16];
+      float f[16], d[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[i] = (double)acc[a][b][i] + bs;
+        f[i] = isnan(v[i]) ? -INFINITY : f64_to_f32_up(v[i]);
+      }
+      // maximum over the 4 consecutive experts of lanes 4q..4q+3 (rounded up
+      // values: rounding up is monotone, so this is the rounded-up maximum)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        d[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f[i]), 0xB1, 0xf, 0xf, false));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f[i] = d[i] > f[i] ? d[i] : f[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        d[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f[i]), 0x4E, 0xf, 0xf, false));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) f[i] = d[i] > f[i] ? d[i] : f[i];
+      double* zb = z + size_t(tb) * E + min(e, E - 1);
+      float* gb = gmax + size_t(tb) * G4 + (min(e, E - 1) >> 2);
+      if (full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + (i & 3);
+          zb[size_t(r) * E] = v[i];
+          bad |= !isfinite(v[i]);
+        }
+        if ((lane & 3) == 0) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) gb[size_t(8 * (i >> 2) + (i & 3)) * G4] = f[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + (i & 3);
+          if (e < E && tb + r < T) {
+            zb[size_t(r) * E] = v[i];
+            bad |= !isfinite(v[i]);
+            if ((lane & 3) == 0) gb[size_t(r) * G4] = f[i];
+          }
+        }
+      }
+    }
+  }
+  if (bad) atomicOr(dev_flag, kDevNonFinite);
+  // ||x_t||^2 of this token tile: 16 groups of 16 tokens (one per wave), dealt
+  // to the tile's first expert tiles (all groups to tile 0 when nn = 1)
+  for (int g = nb; g < kGM / 16; g += nn) {
+    {
+      const int t = m0 + g * 16 + wave;
+      if (t >= T) break;
+      float q = 0.f;
+      for (int c = lane; c < H / 8; c += 64) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(X + size_t(t) * H + c * 8);
+        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+          q = fmaf(lo, lo, q);
+          q = fmaf(hi, hi, q);
+        }
+      }
+      q = wave_sum(q);
+      if (lane == 0) xnorm[t] = (double)q;
+    }
+  }
+}
+
 bool router_uses_mfma(const Layer& L, int T) {
   return L.d.act_dtype == MOE_BF16 && T >= 16 && (L.d.hidden % kBK) == 0;
 }
 
+bool router_uses_big_tiles(const Layer& L, int T) { return router_uses_mfma(L, T) && T >= kBigT; }
+
 hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
                               double* xnorm, hipStream_t s) {
   const int H = L.d.hidden, E = L.d.n_experts;
+  const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+  const uint16_t* rb = reinterpret_cast<const uint16_t*>(L.router_eh);
+  if (router_uses_big_tiles(L, T)) {
+    const int nm = (T + kGM - 1) / kGM, nn = (E + kGN - 1) / kGN, nper = (nn + 7) / 8;
+    hipLaunchKernelGGL(router_gemm_big_kernel, dim3(8 * nper * nm), dim3(kGThreads), 0, s, xb, rb,
+                       L.d.router_bias, T, H, E, nm, nn, nper, z, gmax, xnorm, L.dev_flag);
+    return hipGetLastError();
+  }
   const int nm = (T + kRM - 1) / kRM, nn = (E + kRN - 1) / kRN;
   const int nper = (nn + 7) / 8;                         // expert tiles per XCD
-  hipLaunchKernelGGL(router_gemm_kernel, dim3(8 * nper * nm), dim3(kRThreads), 0, s,
-                     reinterpret_cast<const uint16_t*>(x), reinterpret_cast<const uint16_t*>(L.router_eh),
+  hipLaunchKernelGGL(router_gemm_kernel, dim3(8 * nper * nm), dim3(kRThreads), 0, s, xb, rb,
                      L.d.router_bias, T, H, E, nm, nn, nper, z, gmax, xnorm, L.dev_flag);
   return hipGetLastError();
 }
@@ -265,7 +436,7 @@ __device__ __forceinline__ void skinny_epilogue(double (*red)[16][17], const uin
   double m = (e < E && !isnan(v)) ? v : -INFINITY;
   m = fmax(m, dpp_f64<0xB1, 0xf>(m, -INFINITY));
   m = fmax(m, dpp_f64<0x4E, 0xf>(m, -INFINITY));
-  if ((el & 3) == 0 && live) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = __double2float_ru(m);
+  if ((el & 3) == 0 && live) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = f64_to_f32_up(m);
   if (blockIdx.x == 0) {
     for (int tt = wave; tt < T; tt += 4) {
       float q = 0.f;

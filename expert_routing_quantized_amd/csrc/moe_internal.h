@@ -182,6 +182,18 @@ __device__ __forceinline__ uint4 load_nt(const void* p) {
 }
 
 // Router chunk decoding: 8 consecutive elements of an act-dtype row.
+// Upper bound of a binary64 value in binary32, without branches: the nearest
+// binary32 value, moved one ulp up when it fell below v (a value below the
+// binary32 normal range that rounded to zero gets FLT_MIN, an upper bound
+// even where denormal results are flushed).  Not for NaN inputs.
+__device__ __forceinline__ float f64_to_f32_up(double v) {
+  const float f = (float)v;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t up = (u & 0x80000000u) ? (u == 0x80000000u ? 0x00800000u : u - 1u)
+                                        : (u == 0u ? 0x00800000u : u + 1u);
+  return ((double)f < v) ? __uint_as_float(up) : f;
+}
+
 // Register barrier: tells the compiler the value may change here, so work
 // derived from loop-invariant weights (e.g. expanding 4-bit codes to floats)
 // stays inside the loop instead of being hoisted into extra registers.
@@ -280,6 +292,7 @@ struct RouterBound {
 RouterBound router_bound(const Layer& L, int T);
 // mfma.hip: the router as a bf16 MFMA GEMM for T >= 16 tokens (same outputs).
 bool router_uses_mfma(const Layer& L, int T);
+bool router_uses_big_tiles(const Layer& L, int T);   // fp32 accumulation over all of H
 hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
                               double* xnorm, hipStream_t s);
 // mfma.hip: the router for 2 <= T < 16 bf16 tokens on 16x16x32 MFMA tiles.

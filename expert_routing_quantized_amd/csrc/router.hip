@@ -172,7 +172,7 @@ void router_kernel(
       if (!isnan(v)) m = fmax(m, v);
     }
     if (bad) atomicOr(dev_flag, kDevNonFinite);
-    gmax[size_t(t0 + t) * G4 + blockIdx.x] = __double2float_ru(m);
+    gmax[size_t(t0 + t) * G4 + blockIdx.x] = isnan(m) ? -INFINITY : f64_to_f32_up(m);
   }
 }
 
@@ -205,7 +205,12 @@ RouterBound router_bound(const Layer& L, int T) {
   int lg = 0;
   while ((1 << lg) < cpl) ++lg;
   RouterBound b;
-  if (router_uses_mfma(L, T)) {     // see mfma.hip
+  if (router_uses_big_tiles(L, T)) {   // see mfma.hip
+    b.d32 = 17 * (L.d.hidden / 16);
+    b.d64 = 1;
+    return b;
+  }
+  if (router_uses_mfma(L, T)) {
     b.d32 = 136;
     b.d64 = (L.d.hidden + 127) / 128 + 1;
     return b;
