@@ -59,58 +59,6 @@ __global__ void hist_kernel(GroupArgs a) {
   a.slot[p] = atomicAdd(&a.counts[e], 1);
 }
 
-// Single-workgroup exclusive scan of counts and compaction of the active
-// experts: each thread scans a contiguous chunk sequentially, one block-wide
-// scan combines the 1024 chunk totals (Hillis-Steele over LDS), and a second
-// sequential pass writes offsets and the active list in expert order.
-__global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
-  __shared__ int s_sum[1024];
-  __shared__ int s_act[1024];
-  __shared__ int s_til[1024];
-  const int tid = threadIdx.x;
-  const int per = (a.E + 1023) / 1024;
-  const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
-  int sum = 0, act = 0, til = 0;
-  for (int e = e0; e < e1; ++e) {
-    const int c = a.counts[e];
-    sum += c;
-    act += (c > 0);
-    til += (c + kTileRows - 1) / kTileRows;
-  }
-  s_sum[tid] = sum;
-  s_act[tid] = act;
-  s_til[tid] = til;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = (tid >= off) ? s_sum[tid - off] : 0;
-    const int w = (tid >= off) ? s_act[tid - off] : 0;
-    const int x = (tid >= off) ? s_til[tid - off] : 0;
-    __syncthreads();
-    s_sum[tid] += v;
-    s_act[tid] += w;
-    s_til[tid] += x;
-    __syncthreads();
-  }
-  // exclusive prefixes of this chunk
-  int run = s_sum[tid] - sum, arun = s_act[tid] - act, trun = s_til[tid] - til;
-  for (int e = e0; e < e1; ++e) {
-    const int c = a.counts[e];
-    a.offsets[e] = run;
-    if (c > 0) a.active[1 + arun++] = e;
-    for (int r0 = 0; r0 < c; r0 += kTileRows) {
-      a.tiles[1 + 2 * trun] = e;
-      a.tiles[2 + 2 * trun] = r0;
-      ++trun;
-    }
-    run += c;
-  }
-  if (tid == 1023) {
-    a.offsets[a.E] = s_sum[1023];
-    a.active[0] = s_act[1023];
-    a.tiles[0] = s_til[1023];
-  }
-}
-
 // Exclusive prefix sum over a 1024-thread block (16 waves); *total gets the sum.
 __device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -131,6 +79,65 @@ __device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
   __syncthreads();
   *total = tot;
   return base + x - v;
+}
+
+// Single-workgroup exclusive scan of counts and compaction of the active
+// experts: thread i owns experts [i C, i C + C) with C = ceil(E / 1024),
+// loads their counts once, and three block-wide prefix sums (pairs, active
+// experts, 32-row tiles) give every thread its starting offsets; the
+// offsets, the active list and the tile list are then written from
+// registers in expert order.
+constexpr int kScanMaxPer = 32;           // E <= 32768 in registers, larger E loops
+__global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
+  __shared__ int s_w[16];
+  const int tid = threadIdx.x;
+  const int per = (a.E + 1023) / 1024;
+  const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
+  int c[kScanMaxPer];
+  int sum = 0, act = 0, til = 0;
+  if (per <= kScanMaxPer) {
+#pragma unroll
+    for (int i = 0; i < kScanMaxPer; ++i) c[i] = (e0 + i < e1) ? a.counts[e0 + i] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanMaxPer; ++i) {
+      sum += c[i];
+      act += (c[i] > 0);
+      til += (c[i] + kTileRows - 1) / kTileRows;
+    }
+  } else {
+    for (int e = e0; e < e1; ++e) {
+      const int ce = a.counts[e];
+      sum += ce;
+      act += (ce > 0);
+      til += (ce + kTileRows - 1) / kTileRows;
+    }
+  }
+  int tot_sum, tot_act, tot_til;
+  int run = block_excl_scan_1024(sum, s_w, &tot_sum);
+  int arun = block_excl_scan_1024(act, s_w, &tot_act);
+  int trun = block_excl_scan_1024(til, s_w, &tot_til);
+  auto emit = [&](int e, int ce) {
+    a.offsets[e] = run;
+    if (ce > 0) a.active[1 + arun++] = e;
+    for (int r0 = 0; r0 < ce; r0 += kTileRows) {
+      a.tiles[1 + 2 * trun] = e;
+      a.tiles[2 + 2 * trun] = r0;
+      ++trun;
+    }
+    run += ce;
+  };
+  if (per <= kScanMaxPer) {
+#pragma unroll
+    for (int i = 0; i < kScanMaxPer; ++i)
+      if (e0 + i < e1) emit(e0 + i, c[i]);
+  } else {
+    for (int e = e0; e < e1; ++e) emit(e, a.counts[e]);
+  }
+  if (tid == 0) {
+    a.offsets[a.E] = tot_sum;
+    a.active[0] = tot_act;
+    a.tiles[0] = tot_til;
+  }
 }
 
 // Grouping of at most 1024 pairs in one workgroup (verify windows and small
@@ -372,23 +379,33 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupArgs a) {
 }
 
 // --------------------------------------------------------------- combine
+// One block per (256 outputs, token): the token's k positions and gates go
+// to LDS once (with the bad / repeated index check), then each thread sums
+// its output over the pairs in selection order.
 __global__ __launch_bounds__(256) void combine_kernel(GroupArgs a) {
+  __shared__ int s_pos[kMaxK];
+  __shared__ float s_g[kMaxK];
+  __shared__ int s_bad;
   const int t = blockIdx.y;
+  const int k = a.k;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  if (threadIdx.x < k) {
+    const int j = threadIdx.x, p = t * k + j;
+    const int q = a.pos[p];
+    bool bad = q < 0;
+    const int e = a.idx[p];
+    for (int jj = 0; jj < j; ++jj) bad |= (a.idx[t * k + jj] == e);
+    s_pos[j] = q < 0 ? 0 : q;
+    s_g[j] = a.gates[p];
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
   const int o = blockIdx.x * blockDim.x + threadIdx.x;
   if (o >= a.H) return;
-  bool bad = false;
   float acc = 0.f;
-  for (int j = 0; j < a.k; ++j) {
-    const int p = t * a.k + j;
-    const int q = a.pos[p];
-    if (q < 0) {
-      bad = true;
-      continue;
-    }
-    for (int jj = 0; jj < j; ++jj) bad |= (a.idx[t * a.k + jj] == a.idx[p]);
-    acc = fmaf(a.gates[p], a.y[size_t(q) * a.H + o], acc);
-  }
-  a.out[size_t(t) * a.H + o] = bad ? NAN : acc;
+  for (int j = 0; j < k; ++j) acc = fmaf(s_g[j], a.y[size_t(s_pos[j]) * a.H + o], acc);
+  a.out[size_t(t) * a.H + o] = s_bad ? NAN : acc;
 }
 
 hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const int32_t* idx,

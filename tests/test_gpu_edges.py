@@ -84,3 +84,20 @@ def test_nan_hidden_state_sets_the_flag():
     L = oracle.layer_from_spec(spec)
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, 3)
     G.compare(idx[[0, 2]], gates[[0, 2]], out[[0, 2]], o_idx[[0, 2]], o_g[[0, 2]], o_out[[0, 2]], "nan/others")
+
+
+def test_large_pool_sorted_grouping():
+    """E = 40,000 with 1200 pairs: the sorted grouping path (histogram, scan
+    over more experts than the scan keeps in registers, scatter)."""
+    spec = synth.small_spec(H=256, E=40000, k=10, I=32, act=synth.DT_BF16, expert=synth.DT_Q4,
+                            bias_alpha=0.37, weight_seed=65, token_seed=66, name="E40k_sorted")
+    import synth.device as SD
+    dl = SD.device_layer(spec)
+    T = 120
+    layer = SD.make_layer(dl, max_tokens=T)
+    x = SD.device_tokens(spec, 0, T)
+    L = oracle.layer_from_spec(spec)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, "E40k/sorted")
+    assert layer.device_error() == 0
