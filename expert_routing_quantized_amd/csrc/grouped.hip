@@ -101,15 +101,15 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
 #pragma unroll
     for (int i = 0; i < kScanMaxPer; ++i) {
       sum += c[i];
-      act += (c[i] > 0);
-      til += (c[i] + kTileRows - 1) / kTileRows;
+      act += (c[i] > 0 && c[i] <= a.small_max);
+      til += (c[i] > a.small_max) ? (c[i] + kTileRows - 1) / kTileRows : 0;
     }
   } else {
     for (int e = e0; e < e1; ++e) {
       const int ce = a.counts[e];
       sum += ce;
-      act += (ce > 0);
-      til += (ce + kTileRows - 1) / kTileRows;
+      act += (ce > 0 && ce <= a.small_max);
+      til += (ce > a.small_max) ? (ce + kTileRows - 1) / kTileRows : 0;
     }
   }
   int tot_sum, tot_act, tot_til;
@@ -118,8 +118,8 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
   int trun = block_excl_scan_1024(til, s_w, &tot_til);
   auto emit = [&](int e, int ce) {
     a.offsets[e] = run;
-    if (ce > 0) a.active[1 + arun++] = e;
-    for (int r0 = 0; r0 < ce; r0 += kTileRows) {
+    if (ce > 0 && ce <= a.small_max) a.active[1 + arun++] = e;
+    for (int r0 = 0; ce > a.small_max && r0 < ce; r0 += kTileRows) {
       a.tiles[1 + 2 * trun] = e;
       a.tiles[2 + 2 * trun] = r0;
       ++trun;
@@ -185,13 +185,14 @@ __global__ __launch_bounds__(1024) void group_small_kernel(GroupArgs a) {
     cnt = 1;
     while (p + cnt < nv && s_sorted[p + cnt] == es) ++cnt;
   }
-  const int nt = start ? (cnt + kTileRows - 1) / kTileRows : 0;
+  const bool listed = start && cnt <= a.small_max;
+  const int nt = (start && !listed) ? (cnt + kTileRows - 1) / kTileRows : 0;
   int nact, ntiles;
-  const int ai = block_excl_scan_1024(start ? 1 : 0, s_w, &nact);
+  const int ai = block_excl_scan_1024(listed ? 1 : 0, s_w, &nact);
   const int ti = block_excl_scan_1024(nt, s_w, &ntiles);
   if (start) {
     const int es = s_sorted[p];
-    a.active[1 + ai] = es;
+    if (listed) a.active[1 + ai] = es;
     a.counts[es] = cnt;
     a.offsets[es] = p;
     for (int i = 0; i < nt; ++i) {
@@ -438,6 +439,10 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
   a.y = reinterpret_cast<float*>(ws + W.y);
   a.out = out;
   a.dev_flag = L.dev_flag;
+  // bf16 batches on MFMA: experts with few pairs still go to the vector-ALU
+  // kernels, whose row-contiguous weight loads stream faster than the
+  // tiles' transposed ones; the others get 32-row MFMA tiles
+  a.small_max = grouped_uses_mfma(L, T) ? kMfmaSmallMax : INT_MAX;
 
   if (a.P <= 1024) {
     hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(1024), 0, s, a);
@@ -450,63 +455,64 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
-  if (grouped_uses_mfma(L, T)) {
+  const bool mfma = grouped_uses_mfma(L, T);
+  if (!mfma || a.small_max > 0) {      // experts on the vector-ALU list
+    const int maxact = min(a.P, a.E);
+    const int gy = min(maxact, 4096);
+    const int act = L.d.act_dtype, wd = L.d.expert_dtype;
+    dim3 g1((a.I + 7) / 8, gy);
+    if (wd == MOE_Q4B32) {
+      const int sl = (a.H / 32 + 63) / 64;
+#define MOE_GG_Q4(S)                                                                           \
+    if (sl <= S) {                                                                               \
+      if (act == MOE_BF16)                                                                       \
+        hipLaunchKernelGGL((grouped_gateup_kernel<MOE_BF16, MOE_Q4B32, S>), g1, dim3(256), 0, s, a); \
+      else                                                                                       \
+        hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_Q4B32, S>), g1, dim3(256), 0, s, a);  \
+    } else
+      MOE_GG_Q4(1) MOE_GG_Q4(2) MOE_GG_Q4(4) return hipErrorInvalidValue;
+#undef MOE_GG_Q4
+    } else {
+      const int sl = (a.H / 8 + 63) / 64;
+#define MOE_GG_D(S)                                                                                 \
+    if (sl <= S) {                                                                                    \
+      if (act == MOE_BF16 && wd == MOE_BF16)                                                          \
+        hipLaunchKernelGGL((grouped_gateup_kernel<MOE_BF16, MOE_BF16, S>), g1, dim3(256), 0, s, a);   \
+      else if (act == MOE_F32 && wd == MOE_BF16)                                                      \
+        hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_BF16, S>), g1, dim3(256), 0, s, a);    \
+      else                                                                                            \
+        hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_F32, S>), g1, dim3(256), 0, s, a);     \
+    } else
+      MOE_GG_D(1) MOE_GG_D(2) MOE_GG_D(4) MOE_GG_D(8) MOE_GG_D(16) return hipErrorInvalidValue;
+#undef MOE_GG_D
+    }
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    dim3 g2((a.H + 31) / 32, gy);
+    if (wd == MOE_Q4B32) {
+      const int sl = (a.I / 32 + 7) / 8;
+#define MOE_GD_Q4(S) \
+    if (sl <= S) hipLaunchKernelGGL((grouped_down_kernel<MOE_Q4B32, S>), g2, dim3(256), 0, s, a); else
+      MOE_GD_Q4(1) MOE_GD_Q4(2) MOE_GD_Q4(4) MOE_GD_Q4(8) MOE_GD_Q4(16) return hipErrorInvalidValue;
+#undef MOE_GD_Q4
+    } else {
+      const int sl = (a.I / 8 + 7) / 8;
+#define MOE_GD_D(S)                                                                      \
+    if (sl <= S) {                                                                         \
+      if (wd == MOE_BF16) hipLaunchKernelGGL((grouped_down_kernel<MOE_BF16, S>), g2, dim3(256), 0, s, a); \
+      else hipLaunchKernelGGL((grouped_down_kernel<MOE_F32, S>), g2, dim3(256), 0, s, a);  \
+    } else
+      MOE_GD_D(1) MOE_GD_D(2) MOE_GD_D(4) MOE_GD_D(8) MOE_GD_D(16) MOE_GD_D(32) MOE_GD_D(64) return hipErrorInvalidValue;
+#undef MOE_GD_D
+    }
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (mfma) {
     err = launch_grouped_mfma(a, s);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(combine_kernel, dim3((a.H + 255) / 256, T), dim3(256), 0, s, a);
-    return hipGetLastError();
   }
-  const int maxact = min(a.P, a.E);
-  const int gy = min(maxact, 4096);
-  const int act = L.d.act_dtype, wd = L.d.expert_dtype;
-  dim3 g1((a.I + 7) / 8, gy);
-  if (wd == MOE_Q4B32) {
-    const int sl = (a.H / 32 + 63) / 64;
-#define MOE_GG_Q4(S)                                                                           \
-  if (sl <= S) {                                                                               \
-    if (act == MOE_BF16)                                                                       \
-      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_BF16, MOE_Q4B32, S>), g1, dim3(256), 0, s, a); \
-    else                                                                                       \
-      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_Q4B32, S>), g1, dim3(256), 0, s, a);  \
-  } else
-    MOE_GG_Q4(1) MOE_GG_Q4(2) MOE_GG_Q4(4) return hipErrorInvalidValue;
-#undef MOE_GG_Q4
-  } else {
-    const int sl = (a.H / 8 + 63) / 64;
-#define MOE_GG_D(S)                                                                                 \
-  if (sl <= S) {                                                                                    \
-    if (act == MOE_BF16 && wd == MOE_BF16)                                                          \
-      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_BF16, MOE_BF16, S>), g1, dim3(256), 0, s, a);   \
-    else if (act == MOE_F32 && wd == MOE_BF16)                                                      \
-      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_BF16, S>), g1, dim3(256), 0, s, a);    \
-    else                                                                                            \
-      hipLaunchKernelGGL((grouped_gateup_kernel<MOE_F32, MOE_F32, S>), g1, dim3(256), 0, s, a);     \
-  } else
-    MOE_GG_D(1) MOE_GG_D(2) MOE_GG_D(4) MOE_GG_D(8) MOE_GG_D(16) return hipErrorInvalidValue;
-#undef MOE_GG_D
-  }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  dim3 g2((a.H + 31) / 32, gy);
-  if (wd == MOE_Q4B32) {
-    const int sl = (a.I / 32 + 7) / 8;
-#define MOE_GD_Q4(S) \
-  if (sl <= S) hipLaunchKernelGGL((grouped_down_kernel<MOE_Q4B32, S>), g2, dim3(256), 0, s, a); else
-    MOE_GD_Q4(1) MOE_GD_Q4(2) MOE_GD_Q4(4) MOE_GD_Q4(8) MOE_GD_Q4(16) return hipErrorInvalidValue;
-#undef MOE_GD_Q4
-  } else {
-    const int sl = (a.I / 8 + 7) / 8;
-#define MOE_GD_D(S)                                                                      \
-  if (sl <= S) {                                                                         \
-    if (wd == MOE_BF16) hipLaunchKernelGGL((grouped_down_kernel<MOE_BF16, S>), g2, dim3(256), 0, s, a); \
-    else hipLaunchKernelGGL((grouped_down_kernel<MOE_F32, S>), g2, dim3(256), 0, s, a);  \
-  } else
-    MOE_GD_D(1) MOE_GD_D(2) MOE_GD_D(4) MOE_GD_D(8) MOE_GD_D(16) MOE_GD_D(32) MOE_GD_D(64) return hipErrorInvalidValue;
-#undef MOE_GD_D
-  }
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
   hipLaunchKernelGGL(combine_kernel, dim3((a.H + 255) / 256, T), dim3(256), 0, s, a);
   return hipGetLastError();
 }

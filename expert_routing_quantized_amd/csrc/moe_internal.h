@@ -265,14 +265,16 @@ struct GroupArgs {
   int* slot;                // [P]
   int* pos;                 // [P]
   int* ptok;                // [P]
-  int* active;              // [E+1]: [0] = number of active experts
-  int* tiles;               // [0] = number of 32-row tiles, then (expert, first row) pairs
+  int small_max;            // experts with 1..small_max pairs: vector-ALU list, more: MFMA tiles
+  int* active;              // [E+1]: [0] = number of listed experts (those with 1..small_max pairs)
+  int* tiles;               // [0] = number of 32-row tiles of the other experts, then (expert, first row)
   float* hm;                // [P][I]
   float* y;                 // [P][H]
   float* out;               // [T][H]
   int* dev_flag;
 };
 constexpr int kTileRows = 32;
+constexpr int kMfmaSmallMax = 0;   // bf16 MFMA path: experts with at most this many pairs run on the vector ALUs
 
 // ------------------------------------------------------------------ launchers
 // router.hip: approximate logits z[t][e] (binary64) for tokens [0, T), the
