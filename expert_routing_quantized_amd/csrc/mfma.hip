@@ -489,11 +489,12 @@ __global__ __launch_bounds__(256) void router_skinny_lds_kernel(
 #pragma unroll
     for (int q = 0; q < QP; ++q)
       xa[q] = xin ? *reinterpret_cast<const uint4*>(pa + p * PE + 32 * q + 8 * g) : make_uint4(0u, 0u, 0u, 0u);
-    // the wave's LDS buffer is reused by the next phase: a wave's LDS
-    // accesses complete in program order, so no barrier is needed
+    // the wave's LDS buffer is reused by the next phase (wave-level syncs
+    // order the lanes' accesses; no workgroup barrier is needed)
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       *reinterpret_cast<uint4*>(&sr[wave][i * RPI + lane / LPR][8 * (lane % LPR)]) = b[p][i];
+    wave_lds_sync();                                      // other lanes' writes before the reads
 #pragma unroll
     for (int q = 0; q < QP; ++q) {
       const uint4 bv = *reinterpret_cast<const uint4*>(&sr[wave][tr][32 * q + 8 * g]);
@@ -503,6 +504,7 @@ __global__ __launch_bounds__(256) void router_skinny_lds_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
     }
+    wave_lds_sync();                                      // all reads before the next phase's writes
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * g + r][tr] = acc[r];
@@ -698,10 +700,11 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl) {
-      // the wave's private slice buffer: its LDS accesses complete in
-      // program order, so reusing it for the next slice needs no barrier
+      // the wave's private slice buffer, reused by every slice (wave-level
+      // syncs order the lanes' accesses; no workgroup barrier is needed)
 #pragma unroll
       for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sw[wave][lr + 8 * i][8 * lc]) = w[sl][i];
+      wave_lds_sync();                                    // other lanes' writes before the reads
 #pragma unroll
       for (int q = 0; q < kKS / 16; ++q) {
         const int kk = 16 * q + 8 * (lane >> 5);
@@ -711,6 +714,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
       }
+      wave_lds_sync();                                    // all reads before the next slice's writes
     }
     const int o = ow + (lane & 31);
 #pragma unroll

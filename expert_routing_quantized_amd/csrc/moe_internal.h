@@ -194,6 +194,16 @@ __device__ __forceinline__ float f64_to_f32_up(double v) {
   return ((double)f < v) ? __uint_as_float(up) : f;
 }
 
+// Orders LDS writes and reads of different lanes of one wave: a wave-wide
+// barrier between release and acquire fences, so the compiler keeps every
+// LDS access on its side of it (cross-lane data exchange through LDS is a
+// race in the language model without one).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Register barrier: tells the compiler the value may change here, so work
 // derived from loop-invariant weights (e.g. expanding 4-bit codes to floats)
 // stays inside the loop instead of being hoisted into extra registers.
