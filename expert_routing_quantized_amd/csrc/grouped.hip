@@ -94,35 +94,40 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
   const int per = (a.E + 1023) / 1024;
   const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
   int c[kScanMaxPer];
-  int sum = 0, act = 0, til = 0;
+  int sum = 0, act = 0, til = 0, big = 0;
+  auto count = [&](int ce) {
+    sum += ce;
+    act += (ce > 0 && ce <= a.small_max);
+    til += (ce > a.small_max && ce <= kTileRows) ? 1 : 0;
+    big += (ce > a.small_max && ce > kTileRows) ? (ce + kBigTileRows - 1) / kBigTileRows : 0;
+  };
   if (per <= kScanMaxPer) {
 #pragma unroll
     for (int i = 0; i < kScanMaxPer; ++i) c[i] = (e0 + i < e1) ? a.counts[e0 + i] : 0;
 #pragma unroll
-    for (int i = 0; i < kScanMaxPer; ++i) {
-      sum += c[i];
-      act += (c[i] > 0 && c[i] <= a.small_max);
-      til += (c[i] > a.small_max) ? (c[i] + kTileRows - 1) / kTileRows : 0;
-    }
+    for (int i = 0; i < kScanMaxPer; ++i) count(c[i]);
   } else {
-    for (int e = e0; e < e1; ++e) {
-      const int ce = a.counts[e];
-      sum += ce;
-      act += (ce > 0 && ce <= a.small_max);
-      til += (ce > a.small_max) ? (ce + kTileRows - 1) / kTileRows : 0;
-    }
+    for (int e = e0; e < e1; ++e) count(a.counts[e]);
   }
-  int tot_sum, tot_act, tot_til;
+  int tot_sum, tot_act, tot_til, tot_big;
   int run = block_excl_scan_1024(sum, s_w, &tot_sum);
   int arun = block_excl_scan_1024(act, s_w, &tot_act);
   int trun = block_excl_scan_1024(til, s_w, &tot_til);
+  int brun = block_excl_scan_1024(big, s_w, &tot_big);
   auto emit = [&](int e, int ce) {
     a.offsets[e] = run;
-    if (ce > 0 && ce <= a.small_max) a.active[1 + arun++] = e;
-    for (int r0 = 0; ce > a.small_max && r0 < ce; r0 += kTileRows) {
+    if (ce > 0 && ce <= a.small_max) {
+      a.active[1 + arun++] = e;
+    } else if (ce > a.small_max && ce <= kTileRows) {
       a.tiles[1 + 2 * trun] = e;
-      a.tiles[2 + 2 * trun] = r0;
+      a.tiles[2 + 2 * trun] = 0;
       ++trun;
+    } else if (ce > a.small_max) {
+      for (int r0 = 0; r0 < ce; r0 += kBigTileRows) {
+        a.tiles_big[1 + 2 * brun] = e;
+        a.tiles_big[2 + 2 * brun] = r0;
+        ++brun;
+      }
     }
     run += ce;
   };
@@ -137,6 +142,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
     a.offsets[a.E] = tot_sum;
     a.active[0] = tot_act;
     a.tiles[0] = tot_til;
+    a.tiles_big[0] = tot_big;
   }
 }
 
@@ -186,23 +192,30 @@ __global__ __launch_bounds__(1024) void group_small_kernel(GroupArgs a) {
     while (p + cnt < nv && s_sorted[p + cnt] == es) ++cnt;
   }
   const bool listed = start && cnt <= a.small_max;
-  const int nt = (start && !listed) ? (cnt + kTileRows - 1) / kTileRows : 0;
-  int nact, ntiles;
+  const int nt = (start && !listed && cnt <= kTileRows) ? 1 : 0;
+  const int nb = (start && !listed && cnt > kTileRows) ? (cnt + kBigTileRows - 1) / kBigTileRows : 0;
+  int nact, ntiles, nbig;
   const int ai = block_excl_scan_1024(listed ? 1 : 0, s_w, &nact);
   const int ti = block_excl_scan_1024(nt, s_w, &ntiles);
+  const int bi = block_excl_scan_1024(nb, s_w, &nbig);
   if (start) {
     const int es = s_sorted[p];
     if (listed) a.active[1 + ai] = es;
     a.counts[es] = cnt;
     a.offsets[es] = p;
-    for (int i = 0; i < nt; ++i) {
-      a.tiles[1 + 2 * (ti + i)] = es;
-      a.tiles[2 + 2 * (ti + i)] = i * kTileRows;
+    if (nt) {
+      a.tiles[1 + 2 * ti] = es;
+      a.tiles[2 + 2 * ti] = 0;
+    }
+    for (int i = 0; i < nb; ++i) {
+      a.tiles_big[1 + 2 * (bi + i)] = es;
+      a.tiles_big[2 + 2 * (bi + i)] = i * kBigTileRows;
     }
   }
   if (p == 0) {
     a.active[0] = nact;
     a.tiles[0] = ntiles;
+    a.tiles_big[0] = nbig;
   }
 }
 
@@ -435,6 +448,7 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
   a.ptok = reinterpret_cast<int*>(ws + W.ptok);
   a.active = reinterpret_cast<int*>(ws + W.active);
   a.tiles = reinterpret_cast<int*>(ws + W.tiles);
+  a.tiles_big = reinterpret_cast<int*>(ws + W.tiles_big);
   a.hm = reinterpret_cast<float*>(ws + W.hm);
   a.y = reinterpret_cast<float*>(ws + W.y);
   a.out = out;

@@ -576,9 +576,15 @@ __device__ __forceinline__ uint4 load_row_chunk(const uint16_t* row, int k, int 
   return (live && k < K) ? v : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// MT = 32-row sub-tiles per tile: 1 for the 32-row list, 2 for the 64-row
+// list of experts with more than 32 tokens (their weights then stream once
+// per 64 tokens instead of once per 32).
+template <int MT>
 __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
+  constexpr int TR = kTileRows * MT;                     // tile rows
+  constexpr int XC = TR * (kKS / 8) / 256;               // x chunks per thread per slice
   __shared__ __attribute__((aligned(16))) uint16_t sw[2][2 * kGC][kKP];
-  __shared__ __attribute__((aligned(16))) uint16_t sx[2][kTileRows][kKP];
+  __shared__ __attribute__((aligned(16))) uint16_t sx[2][TR][kKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I;
   const int ch0 = blockIdx.x * kGC;
@@ -586,43 +592,60 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
   const uint16_t* W = reinterpret_cast<const uint16_t*>(wave < 2 ? a.wg : a.wu);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
   const int lr = lane >> 3, lc = lane & 7;               // weight loads: row lr + 8 i, chunk lc
-  const int xr = tid >> 3, xc = tid & 7;                 // x loads: tile row xr, chunk xc
+  const int xc = tid & 7;                                // x loads: tile rows (tid >> 3) + 32 j, chunk xc
   const int nks = (H + kKS - 1) / kKS;
-  const int ntiles = a.tiles[0];
+  const int* tl = (MT == 1) ? a.tiles : a.tiles_big;   // MT > 1: the big-tile list
+  const int ntiles = tl[0];
   for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
-    const int e = a.tiles[1 + 2 * ti], r0 = a.tiles[2 + 2 * ti];
+    const int e = tl[1 + 2 * ti], r0 = tl[2 + 2 * ti];
     const int n = a.counts[e], seg = a.offsets[e];
-    const int nrow = min(kTileRows, n - r0);
-    const bool xlive = xr < nrow;
-    const uint16_t* px = X + size_t(a.ptok[seg + r0 + min(xr, nrow - 1)]) * H;
+    const int nrow = min(TR, n - r0);
+    const uint16_t* px[XC];
+    bool xlive[XC];
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int xr = (tid >> 3) + 32 * j;
+      xlive[j] = xr < nrow;
+      px[j] = X + size_t(a.ptok[seg + r0 + min(xr, nrow - 1)]) * H;
+    }
     const uint16_t* pw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) pw[i] = W + (size_t(e) * I + min(wc + lr + 8 * i, I - 1)) * H;
-    uint4 wA[4], wB[4], xA, xB;
+    uint4 wA[4], wB[4], xA[XC], xB[XC];
 #pragma unroll
     for (int i = 0; i < 4; ++i) wA[i] = load_row_chunk(pw[i], 8 * lc, H, true);
-    xA = load_row_chunk(px, 8 * xc, H, xlive);
+#pragma unroll
+    for (int j = 0; j < XC; ++j) xA[j] = load_row_chunk(px[j], 8 * xc, H, xlive[j]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) wB[i] = load_row_chunk(pw[i], kKS + 8 * lc, H, true);
-    xB = load_row_chunk(px, kKS + 8 * xc, H, xlive);
-    f32x16_t acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    for (int j = 0; j < XC; ++j) xB[j] = load_row_chunk(px[j], kKS + 8 * xc, H, xlive[j]);
+    f32x16_t acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
     // one K slice: stage it, refill its registers two slices ahead, multiply
+    // (sub-tiles past the segment are skipped: a block-uniform test)
 #define MOE_GU_SLICE(KT, WR, XR, BUF)                                                          \
     {                                                                                          \
       _Pragma("unroll") for (int i = 0; i < 4; ++i)                                            \
         *reinterpret_cast<uint4*>(&sw[BUF][32 * wave + lr + 8 * i][8 * lc]) = WR[i];           \
-      *reinterpret_cast<uint4*>(&sx[BUF][xr][8 * xc]) = XR;                                    \
+      _Pragma("unroll") for (int j = 0; j < XC; ++j)                                           \
+        *reinterpret_cast<uint4*>(&sx[BUF][(tid >> 3) + 32 * j][8 * xc]) = XR[j];              \
       __syncthreads();                                                                         \
       const int kn = ((KT) + 2) * kKS;                                                         \
       _Pragma("unroll") for (int i = 0; i < 4; ++i) WR[i] = load_row_chunk(pw[i], kn + 8 * lc, H, true); \
-      XR = load_row_chunk(px, kn + 8 * xc, H, xlive);                                          \
+      _Pragma("unroll") for (int j = 0; j < XC; ++j) XR[j] = load_row_chunk(px[j], kn + 8 * xc, H, xlive[j]); \
       _Pragma("unroll") for (int q = 0; q < kKS / 16; ++q) {                                   \
         const int kk = 16 * q + 8 * (lane >> 5);                                               \
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&sx[BUF][lane & 31][kk]);       \
         const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&sw[BUF][32 * wave + (lane & 31)][kk]); \
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);                   \
+        _Pragma("unroll") for (int m = 0; m < MT; ++m) {                                       \
+          if (m == 0 || 32 * m < nrow) {                                                       \
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&sx[BUF][32 * m + (lane & 31)][kk]); \
+            acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[m], 0, 0, 0);         \
+          }                                                                                    \
+        }                                                                                      \
       }                                                                                        \
     }
     for (int kt = 0; kt < nks; kt += 2) {
@@ -631,24 +654,28 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
     }
 #undef MOE_GU_SLICE
     // epilogue: D rows 8 (i / 4) + 4 (lane / 32) + i % 4 (tokens), column lane % 32 (channel)
-    __syncthreads();
-    float* su = reinterpret_cast<float*>(&sw[0][0][0]);   // [32][kGC + 1] up results
-    if (wave >= 2) {
+    float* su = reinterpret_cast<float*>(&sw[0][0][0]);   // [32][kGC + 1] up results of one sub-tile
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        su[r * (kGC + 1) + 32 * (wave - 2) + (lane & 31)] = acc[i];
+    for (int m = 0; m < MT; ++m) {
+      if (m > 0 && 32 * m >= nrow) break;                 // block-uniform
+      __syncthreads();
+      if (wave >= 2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          su[r * (kGC + 1) + 32 * (wave - 2) + (lane & 31)] = acc[m][i];
+        }
       }
-    }
-    __syncthreads();
-    if (wave < 2) {
-      const int ch = wc + (lane & 31);
+      __syncthreads();
+      if (wave < 2) {
+        const int ch = wc + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (r < nrow && ch < I) {
-          const float g = acc[i], u = su[r * (kGC + 1) + 32 * wave + (lane & 31)];
-          a.hm[size_t(seg + r0 + r) * I + ch] = g / (1.0f + expf(-g)) * u;
+        for (int i = 0; i < 16; ++i) {
+          const int r = 32 * m + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (r < nrow && ch < I) {
+            const float g = acc[m][i], u = su[(r - 32 * m) * (kGC + 1) + 32 * wave + (lane & 31)];
+            a.hm[size_t(seg + r0 + r) * I + ch] = g / (1.0f + expf(-g)) * u;
+          }
         }
       }
     }
@@ -656,7 +683,7 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
   }
 }
 
-template <int NS>   // K slices of 64 (I <= 64 NS)
+template <int NS, int MT>   // K slices of 64 (I <= 64 NS); 32-row sub-tiles per tile
 __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
   constexpr int KP = NS * kKS + 8;
   __shared__ __attribute__((aligned(16))) uint16_t shi[kTileRows][KP];
@@ -667,12 +694,13 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
   const int ow = blockIdx.x * kDR + 32 * wave;           // first output row of this wave
   const int lr = lane >> 3, lc = lane & 7;
   const uint16_t* WD = reinterpret_cast<const uint16_t*>(a.wd);
-  const int ntiles = a.tiles[0];
+  const int* tl = (MT == 1) ? a.tiles : a.tiles_big;   // MT > 1: the big-tile list
+  const int ntiles = tl[0];
   for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
-    const int e = a.tiles[1 + 2 * ti], r0 = a.tiles[2 + 2 * ti];
+    const int e = tl[1 + 2 * ti], r0 = tl[2 + 2 * ti];
     const int n = a.counts[e], seg = a.offsets[e];
-    const int nrow = min(kTileRows, n - r0);
-    // the wave's 32 weight rows, all of K, in flight at once
+    const int nrow = min(kTileRows * MT, n - r0);
+    // the wave's 32 weight rows, all of K, in flight at once (read once per tile)
     uint4 w[NS][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -680,67 +708,77 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) w[sl][i] = load_row_chunk(row, sl * kKS + 8 * lc, I, true);
     }
-    // h rows of the tile -> bf16 hi/lo (rows past the segment and columns past I: zeros)
-    for (int q = tid; q < kTileRows * (NS * kKS / 4); q += 256) {
-      const int r = q / (NS * kKS / 4), c = (q - r * (NS * kKS / 4)) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (r < nrow && c < I) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + r) * I + c);
-      const float vv[4] = {v.x, v.y, v.z, v.w};
+    for (int m = 0; m < MT; ++m) {
+      const int mr = 32 * m;                             // first row of this sub-tile
+      if (m > 0 && mr >= nrow) break;                    // block-uniform
+      if (m > 0) __syncthreads();                        // previous sub-tile's h reads are done
+      // h rows of the sub-tile -> bf16 hi/lo (rows past the segment and columns past I: zeros)
+      for (int q = tid; q < kTileRows * (NS * kKS / 4); q += 256) {
+        const int r = q / (NS * kKS / 4), c = (q - r * (NS * kKS / 4)) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (mr + r < nrow && c < I) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + mr + r) * I + c);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint16_t hi = f32_to_bf16_rne_dev(vv[j]);
-        const float rem = vv[j] - __uint_as_float(uint32_t(hi) << 16);
-        shi[r][c + j] = hi;
-        slo[r][c + j] = f32_to_bf16_rne_dev(rem);
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t hi = f32_to_bf16_rne_dev(vv[j]);
+          const float rem = vv[j] - __uint_as_float(uint32_t(hi) << 16);
+          shi[r][c + j] = hi;
+          slo[r][c + j] = f32_to_bf16_rne_dev(rem);
+        }
       }
-    }
-    __syncthreads();
-    f32x16_t acc;
+      __syncthreads();
+      f32x16_t acc;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-      // the wave's private slice buffer, reused by every slice (wave-level
-      // syncs order the lanes' accesses; no workgroup barrier is needed)
+      for (int sl = 0; sl < NS; ++sl) {
+        // the wave's private slice buffer, reused by every slice (wave-level
+        // syncs order the lanes' accesses; no workgroup barrier is needed)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sw[wave][lr + 8 * i][8 * lc]) = w[sl][i];
-      wave_lds_sync();                                    // other lanes' writes before the reads
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sw[wave][lr + 8 * i][8 * lc]) = w[sl][i];
+        wave_lds_sync();                                  // other lanes' writes before the reads
 #pragma unroll
-      for (int q = 0; q < kKS / 16; ++q) {
-        const int kk = 16 * q + 8 * (lane >> 5);
-        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&shi[lane & 31][sl * kKS + kk]);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&slo[lane & 31][sl * kKS + kk]);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&sw[wave][lane & 31][kk]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
+        for (int q = 0; q < kKS / 16; ++q) {
+          const int kk = 16 * q + 8 * (lane >> 5);
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&shi[lane & 31][sl * kKS + kk]);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&slo[lane & 31][sl * kKS + kk]);
+          const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(&sw[wave][lane & 31][kk]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bv, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bv, acc, 0, 0, 0);
+        }
+        wave_lds_sync();                                  // all reads before the next slice's writes
       }
-      wave_lds_sync();                                    // all reads before the next slice's writes
-    }
-    const int o = ow + (lane & 31);
+      const int o = ow + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (r < nrow && o < H) a.y[size_t(seg + r0 + r) * H + o] = acc[i];
+      for (int i = 0; i < 16; ++i) {
+        const int r = mr + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (r < nrow && o < H) a.y[size_t(seg + r0 + r) * H + o] = acc[i];
+      }
     }
     __syncthreads();   // h staging reuse by the next tile
   }
 }
 
+// The 32-row tiles first (most experts: bound by the weight stream), then
+// the 64-row tiles of the hot experts.
 hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s) {
-  const int gy = 2048;
-  hipLaunchKernelGGL(gateup_mfma_kernel, dim3((a.I + kGC - 1) / kGC, gy), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 g2((a.H + kDR - 1) / kDR, gy);
+  constexpr int MB = kBigTileRows / kTileRows;
+  const int gy = 2048, gyb = 256;
   const int ns = (a.I + kKS - 1) / kKS;
-  if (ns == 1)
-    hipLaunchKernelGGL(down_mfma_kernel<1>, g2, dim3(256), 0, s, a);
-  else if (ns == 2)
-    hipLaunchKernelGGL(down_mfma_kernel<2>, g2, dim3(256), 0, s, a);
-  else if (ns <= 4)
-    hipLaunchKernelGGL(down_mfma_kernel<4>, g2, dim3(256), 0, s, a);
-  else
-    return hipErrorInvalidValue;
+  if (ns > 4) return hipErrorInvalidValue;
+  const dim3 g1((a.I + kGC - 1) / kGC, gy), g1b((a.I + kGC - 1) / kGC, gyb);
+  const dim3 g2((a.H + kDR - 1) / kDR, gy), g2b((a.H + kDR - 1) / kDR, gyb);
+  hipLaunchKernelGGL(gateup_mfma_kernel<1>, g1, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(gateup_mfma_kernel<MB>, g1b, dim3(256), 0, s, a);
+#define MOE_DOWN_NS(N)                                                    \
+  {                                                                       \
+    hipLaunchKernelGGL((down_mfma_kernel<N, 1>), g2, dim3(256), 0, s, a); \
+    hipLaunchKernelGGL((down_mfma_kernel<N, MB>), g2b, dim3(256), 0, s, a); \
+  }
+  if (ns == 1) MOE_DOWN_NS(1)
+  else if (ns == 2) MOE_DOWN_NS(2)
+  else MOE_DOWN_NS(4)
+#undef MOE_DOWN_NS
   return hipGetLastError();
 }
 

@@ -143,6 +143,7 @@ Workspace workspace_layout(const Layer& L, int T) {
     W.ptok = take(P * 4);
     W.active = take((E + 1) * 4);
     W.tiles = take((1 + 2 * ((P + moe::kTileRows - 1) / moe::kTileRows + std::min(P, E))) * 4);
+    W.tiles_big = take((1 + 2 * ((P + moe::kBigTileRows - 1) / moe::kBigTileRows + std::min(P, E))) * 4);
     W.hm = take(P * I * 4);
     W.y = take(P * H * 4);
   }
@@ -173,6 +174,13 @@ const char* moe_status_string(moe_status s) {
 
 const char* moe_last_error_message(void) { return g_last_error.c_str(); }
 
+// Frees what a layer owns (fields still null are skipped).
+static void release_layer(Layer& L) {
+  if (L.router_copy) (void)hipFree(L.router_copy);
+  if (L.norms) (void)hipFree(L.norms);
+  if (L.dev_flag) (void)hipFree(L.dev_flag);
+}
+
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out) {
   if (!out) return fail(MOE_E_NULL, "out is NULL");
   *out = nullptr;
@@ -185,9 +193,7 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
   hipError_t e = hipGetDevice(&L.device);
   const size_t E = desc->n_experts, H = desc->hidden;
   auto cleanup = [&](moe_status code) {
-    if (L.router_copy) (void)hipFree(L.router_copy);
-    if (L.norms) (void)hipFree(L.norms);
-    if (L.dev_flag) (void)hipFree(L.dev_flag);
+    release_layer(L);
     delete l;
     return code;
   };
@@ -220,10 +226,7 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
 
 moe_status moe_layer_destroy(moe_layer* layer) {
   if (!layer) return ok();
-  Layer& L = layer->L;
-  if (L.router_copy) (void)hipFree(L.router_copy);
-  if (L.norms) (void)hipFree(L.norms);
-  if (L.dev_flag) (void)hipFree(L.dev_flag);
+  release_layer(layer->L);
   delete layer;
   return ok();
 }

@@ -51,6 +51,7 @@ struct Workspace {
   size_t ptok;      // int32 [P] token of the pair at a segment position
   size_t active;    // int32 [E + 1] active experts (count first)
   size_t tiles;     // int32 [1 + 2 * max tiles]: count, then (expert, first row) per 32-row tile
+  size_t tiles_big; // int32, same layout: kBigTileRows-row tiles of experts with more than 32 pairs
   size_t hm;        // fp32 [P][I] grouped intermediate
   size_t y;         // fp32 [P][H] grouped expert outputs
   size_t total;
@@ -277,13 +278,15 @@ struct GroupArgs {
   int* ptok;                // [P]
   int small_max;            // experts with 1..small_max pairs: vector-ALU list, more: MFMA tiles
   int* active;              // [E+1]: [0] = number of listed experts (those with 1..small_max pairs)
-  int* tiles;               // [0] = number of 32-row tiles of the other experts, then (expert, first row)
+  int* tiles;               // [0] = number of 32-row tiles (experts with small_max < n <= 32), then (expert, first row)
+  int* tiles_big;           // same for kBigTileRows-row tiles of experts with n > 32
   float* hm;                // [P][I]
   float* y;                 // [P][H]
   float* out;               // [T][H]
   int* dev_flag;
 };
 constexpr int kTileRows = 32;
+constexpr int kBigTileRows = 64;
 constexpr int kMfmaSmallMax = 0;   // bf16 MFMA path: experts with at most this many pairs run on the vector ALUs
 
 // ------------------------------------------------------------------ launchers
