@@ -12,9 +12,10 @@
 // is a verified contract").
 //
 // The same kernels serve a few tokens at once (verify windows): with T
-// tokens there are P = T k token-expert pairs, and the block that holds the
-// first pair naming an expert computes every pair of that expert, so the
-// expert's weights are read once per call and no sort is needed.
+// tokens there are P = T k token-expert pairs.  Short windows compute every
+// pair on its own (INDEP); longer ones let the block that holds the first
+// pair naming an expert compute every pair of that expert, so the expert's
+// weights are read once per call and no sort is needed.
 //
 // gate/up: one wave per pair of intermediate rows (gate row i and up row i
 // of the same expert), so silu(a)*u is formed in registers; for 4-bit rows
@@ -79,14 +80,14 @@ __device__ __forceinline__ int claim_pairs(const PairArgs& a, int p, int* s_matc
 
 // ------------------------------------------------------------ gate/up, 4-bit
 // MB = quant blocks per lane (H / 32 / 64 rounded up).
-template <int ACT, int MB, bool SINGLE>
+template <int ACT, int MB, bool INDEP>
 __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
   __shared__ int s_match[kMaxPairs];
   __shared__ int s_n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e;
   bool valid = true;
-  if constexpr (SINGLE) {          // one token: every pair is its own group
+  if constexpr (INDEP) {           // independent pairs: every pair is its own group
     e = a.idx[blockIdx.y];
     valid = e >= 0 && e < a.E;
     e = valid ? e : 0;             // addresses stay in range; h becomes NaN
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       if (!(i0 + r < a.I && m * 64 + lane < nblk)) dg[r][m] = du[r][m] = 0.f;
-  const int n = SINGLE ? 1 : s_n;
+  const int n = INDEP ? 1 : s_n;
   for (int mi = 0; mi < n; ++mi) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
         opaque_reg(wg[r][m]);
         opaque_reg(wu[r][m]);
       }
-    const int q = SINGLE ? (int)blockIdx.y : s_match[mi];
+    const int q = INDEP ? (int)blockIdx.y : s_match[mi];
     const size_t xoff = size_t(q / a.k) * a.H;
     float xv[MB][32];
     float xs[MB];
@@ -163,14 +164,14 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
 }
 
 // ------------------------------------------------------------ gate/up, dense
-template <int ACT, int WD, int CPL, bool SINGLE>
+template <int ACT, int WD, int CPL, bool INDEP>
 __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
   __shared__ int s_match[kMaxPairs];
   __shared__ int s_n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e;
   bool valid = true;
-  if constexpr (SINGLE) {
+  if constexpr (INDEP) {
     e = a.idx[blockIdx.y];
     valid = e >= 0 && e < a.E;
     e = valid ? e : 0;
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
         wg[r][s].zero();
         wu[r][s].zero();
       }
-  const int n = SINGLE ? 1 : s_n;
+  const int n = INDEP ? 1 : s_n;
   for (int mi = 0; mi < n; ++mi) {
 #pragma unroll
     for (int r = 0; r < kRowsPerWave; ++r)
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
         wg[r][s].opaque();
         wu[r][s].opaque();
       }
-    const int q = SINGLE ? (int)blockIdx.y : s_match[mi];
+    const int q = INDEP ? (int)blockIdx.y : s_match[mi];
     const size_t xoff = size_t(q / a.k) * a.H;
     float xv[CPL][8];
     {
@@ -240,12 +241,13 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
 
 // ------------------------------------------------------------ down + combine
 
-// One token: one block per 8 output rows, wave w handles the selected
-// experts j = w, w + W, ... (W = min(k, 16)), 8 lanes per output row, lane g
-// covering quant blocks (or 8-element chunks) g, g + 8, ... of I.  The
-// expert's h slice comes straight from L2 into registers, so the weights,
-// the scales and h are all in flight together.  Each wave's g_j-weighted
-// partials go through LDS and are summed over the waves in a fixed order.
+// Independent pairs: block (x, t) computes 8 output rows of token t; wave w
+// handles the token's selected experts j = w, w + W, ... (W = min(k, 16)),
+// 8 lanes per output row, lane g covering quant blocks (or 8-element chunks)
+// g, g + 8, ... of I.  The expert's h slice comes straight from L2 into
+// registers, so the weights, the scales and h are all in flight together.
+// Each wave's g_j-weighted partials go through LDS and are summed over the
+// waves in a fixed order.
 template <int WD>
 __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   __shared__ float part[kMaxK][8];
@@ -253,31 +255,33 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const int g = lane & 7, grp = lane >> 3;
-  const int I = a.I, k = a.k;
+  const int I = a.I, k = a.k, t = blockIdx.y;
   const int o = blockIdx.x * 8 + grp;
   const int oc = min(o, a.H - 1);
   constexpr int kElems = (WD == MOE_Q4B32) ? 32 : 8;
   const int nsl = I / kElems;
   const int nblk = I >> 5;
+  const int32_t* ti = a.idx + size_t(t) * k;
   if (threadIdx.x == 0) s_bad = 0;
+  // every wave holds the token's k indices, one per lane (k <= 32), and
+  // checks its own experts with a ballot (no dependent loads before the
+  // weight loads)
+  const int vi = (lane < k) ? ti[lane] : -1;
   __syncthreads();
-  if (threadIdx.x < k) {        // one thread per selected expert checks its index
-    const int j = threadIdx.x, e = a.idx[j];
-    int bad = (e < 0 || e >= a.E) ? kDevBadIndex : 0;
-    for (int jj = 0; jj < j; ++jj)
-      if (a.idx[jj] == e) bad |= kDevDupIndex;
-    if (bad) {
+  float acc = 0.f;
+  for (int j = wave; j < k; j += nw) {
+    int e = __shfl(vi, j);
+    const bool inval = e < 0 || e >= a.E;
+    const bool dup = __ballot(lane < j && vi == e) != 0ull;
+    if (lane == 0 && (inval || dup)) {
+      const int bad = inval ? kDevBadIndex : kDevDupIndex;
       atomicOr(&s_bad, bad);
       if (blockIdx.x == 0) atomicOr(a.dev_flag, bad);
     }
-  }
-  float acc = 0.f;
-  for (int j = wave; j < k; j += nw) {
-    int e = a.idx[j];
-    e = (e >= 0 && e < a.E) ? e : 0;                   // addresses stay in range
-    const float gj = a.gates[j];
+    e = inval ? 0 : e;                                 // addresses stay in range
+    const float gj = a.gates[size_t(t) * k + j];
     const size_t row = size_t(e) * a.H + oc;
-    const float* hj = a.h + size_t(j) * I;
+    const float* hj = a.h + (size_t(t) * k + j) * I;
     for (int sl = g; sl < nsl; sl += 8) {
       float hv[kElems];
 #pragma unroll
@@ -308,7 +312,116 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   if (threadIdx.x < 8 && blockIdx.x * 8 + (int)threadIdx.x < a.H) {
     float s = 0.f;
     for (int w = 0; w < nw; ++w) s += part[w][threadIdx.x];
-    a.out[blockIdx.x * 8 + threadIdx.x] = s_bad ? NAN : s;
+    a.out[size_t(t) * a.H + blockIdx.x * 8 + threadIdx.x] = s_bad ? NAN : s;
+  }
+}
+
+// Short windows (2 <= T <= 8 tokens, P = T k pairs): one block per 8 output
+// rows handles every pair of the window, so each block pays one chain of
+// dependent loads instead of one per token.  h of all pairs is staged in
+// LDS (every load issued before any is stored), wave w takes pairs w,
+// w + 16, ... and issues the weight loads of all of them before computing
+// any; per-pair partials meet in LDS and each token's output is summed over
+// its pairs in selection order.  Needs P <= 128, P I floats of LDS and
+// I <= 256 (one quant block per lane of an 8-lane row group).
+constexpr int kWindowWaves = 16;
+constexpr int kPairHLdsBytes = 64 * 1024;
+
+bool down_window_fits(const PairArgs& a) {
+  return a.T >= 2 && a.P <= kWindowWaves * 8 && size_t(a.P) * a.I * 4 <= kPairHLdsBytes &&
+         a.I <= 8 * 32 && a.P * a.I / 4 <= 4 * 64 * kWindowWaves;
+}
+
+template <int UG>
+__global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kernel(PairArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float sh_h[];   // [P][I]
+  __shared__ float part[kMaxPairs][8];
+  __shared__ int s_bad[kMaxPairs];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane & 7, grp = lane >> 3;
+  const int I = a.I, k = a.k, P = a.P;
+  const int o = blockIdx.x * 8 + grp;
+  const int oc = min(o, a.H - 1);
+  const int nsl = I >> 5, nblk = I >> 5;
+  // 1. h of every pair: all loads in flight
+  const int n4 = P * I / 4;
+  float4 hv4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + i * 64 * kWindowWaves;
+    hv4[i] = (c < n4) ? reinterpret_cast<const float4*>(a.h)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // 2. this wave's pairs: index, then code bytes and scale of its rows
+  int vi[UG];
+#pragma unroll
+  for (int u = 0; u < UG; ++u) {
+    const int p = min(wave + kWindowWaves * u, P - 1);
+    const int t = p / k;
+    vi[u] = (lane < k) ? a.idx[size_t(t) * k + lane] : -1;   // the token's k indices
+  }
+  uint4 w[UG];
+  float d[UG];
+  int badu[UG];
+#pragma unroll
+  for (int u = 0; u < UG; ++u) {
+    const int p = min(wave + kWindowWaves * u, P - 1);
+    const int j = p % k;
+    int e = __shfl(vi[u], j);
+    const bool inval = e < 0 || e >= a.E;
+    const bool dup = __ballot(lane < j && vi[u] == e) != 0ull;
+    badu[u] = inval ? kDevBadIndex : (dup ? kDevDupIndex : 0);
+    e = inval ? 0 : e;                                 // addresses stay in range
+    const size_t row = size_t(e) * a.H + oc;
+    const int sl = min(g, nsl - 1);
+    w[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + sl * 16);
+    d[u] = f16_to_f32(a.sd[row * nblk + sl]);
+  }
+  // 3. h into LDS, flags cleared
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + i * 64 * kWindowWaves;
+    if (c < n4) reinterpret_cast<float4*>(sh_h)[c] = hv4[i];
+  }
+  if (tid < a.T) s_bad[tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < UG; ++u) {
+    const int p = wave + kWindowWaves * u;
+    if (p < P && lane == 0 && badu[u]) {
+      atomicOr(&s_bad[p / k], badu[u]);
+      if (blockIdx.x == 0) atomicOr(a.dev_flag, badu[u]);
+    }
+  }
+  // 4. per-pair partials
+#pragma unroll
+  for (int u = 0; u < UG; ++u) {
+    const int p = wave + kWindowWaves * u;
+    if (p >= P) break;                                 // wave-uniform
+    float acc = 0.f;
+    if (g < nsl) {
+      const float* hq = sh_h + size_t(p) * I + g * 32;
+      float hv[32];
+#pragma unroll
+      for (int i = 0; i < 32; i += 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(hq + i);
+        hv[i] = v4.x; hv[i + 1] = v4.y; hv[i + 2] = v4.z; hv[i + 3] = v4.w;
+      }
+      float hs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) hs += hv[i];
+      acc = d[u] * (q4_block_dot(w[u], hv) - 8.f * hs);
+    }
+    acc = group8_sum(acc);
+    if (g == 0) part[p][grp] = acc;
+  }
+  __syncthreads();
+  // 5. each token: its pairs in selection order, weighted by the gates
+  for (int c = tid; c < a.T * 8; c += 64 * kWindowWaves) {
+    const int t = c >> 3, r = c & 7;
+    if (blockIdx.x * 8 + r >= a.H) continue;
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s = fmaf(a.gates[t * k + j], part[t * k + j][r], s);
+    a.out[size_t(t) * a.H + blockIdx.x * 8 + r] = s_bad[t] ? NAN : s;
   }
 }
 
@@ -322,8 +435,6 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
 // pair naming it, and the per-pair partials meet in LDS; each token's output
 // is summed over its pairs in selection order (fixed order, no float
 // atomics).
-constexpr int kPairHLdsBytes = 64 * 1024;
-
 template <int WD, int SPL>
 __global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sh_h[];   // [P][I] if it fits
@@ -444,10 +555,18 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
   }
 }
 
-template <bool SINGLE>
+template <bool INDEP>
 static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s);
 
 bool pair_path_fits(const Layer& L, int T) { return T >= 1 && T * L.d.top_k <= kMaxPairs; }
+
+// Up to this many tokens every (token, expert) pair is computed on its own
+// (an expert named by two tokens is read twice, mostly from cache): in short
+// windows nearly all pairs name distinct experts, and skipping the
+// per-block deduplication takes it off the path from the indices to the
+// weight loads.  Longer windows deduplicate so that shared experts are read
+// once per call.
+constexpr int kIndependentMaxT = 8;
 
 hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32_t* idx,
                                const float* gates, float* out, float* h, hipStream_t s) {
@@ -471,11 +590,11 @@ hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32
   a.P = T * a.k;
   a.dev_flag = L.dev_flag;
   if (a.P > kMaxPairs) return hipErrorInvalidValue;
-  if (T == 1) return launch_pairs<true>(a, L.d.act_dtype, L.d.expert_dtype, s);
+  if (T <= kIndependentMaxT) return launch_pairs<true>(a, L.d.act_dtype, L.d.expert_dtype, s);
   return launch_pairs<false>(a, L.d.act_dtype, L.d.expert_dtype, s);
 }
 
-template <bool SINGLE>
+template <bool INDEP>
 static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s) {
   dim3 g1((a.I + 7) / 8, a.P);
   if (wd == MOE_Q4B32) {
@@ -483,9 +602,9 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
 #define MOE_GU_Q4(M)                                                                    \
   if (mb <= M) {                                                                        \
     if (act == MOE_BF16)                                                                \
-      hipLaunchKernelGGL((gateup_q4_kernel<MOE_BF16, M, SINGLE>), g1, dim3(256), 0, s, a);      \
+      hipLaunchKernelGGL((gateup_q4_kernel<MOE_BF16, M, INDEP>), g1, dim3(256), 0, s, a);      \
     else                                                                                \
-      hipLaunchKernelGGL((gateup_q4_kernel<MOE_F32, M, SINGLE>), g1, dim3(256), 0, s, a);       \
+      hipLaunchKernelGGL((gateup_q4_kernel<MOE_F32, M, INDEP>), g1, dim3(256), 0, s, a);       \
   } else
     MOE_GU_Q4(1) MOE_GU_Q4(2) MOE_GU_Q4(4) return hipErrorInvalidValue;
 #undef MOE_GU_Q4
@@ -494,11 +613,11 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
 #define MOE_GU_D(C)                                                                          \
   if (cpl <= C) {                                                                            \
     if (act == MOE_BF16 && wd == MOE_BF16)                                                   \
-      hipLaunchKernelGGL((gateup_dense_kernel<MOE_BF16, MOE_BF16, C, SINGLE>), g1, dim3(256), 0, s, a); \
+      hipLaunchKernelGGL((gateup_dense_kernel<MOE_BF16, MOE_BF16, C, INDEP>), g1, dim3(256), 0, s, a); \
     else if (act == MOE_F32 && wd == MOE_BF16)                                               \
-      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_BF16, C, SINGLE>), g1, dim3(256), 0, s, a);  \
+      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_BF16, C, INDEP>), g1, dim3(256), 0, s, a);  \
     else                                                                                     \
-      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_F32, C, SINGLE>), g1, dim3(256), 0, s, a);   \
+      hipLaunchKernelGGL((gateup_dense_kernel<MOE_F32, MOE_F32, C, INDEP>), g1, dim3(256), 0, s, a);   \
   } else
     MOE_GU_D(1) MOE_GU_D(2) MOE_GU_D(4) MOE_GU_D(8) MOE_GU_D(16) return hipErrorInvalidValue;
 #undef MOE_GU_D
@@ -513,8 +632,18 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
 #define MOE_DOWN_SPL(K, S) \
   if (spl <= S) hipLaunchKernelGGL((down_combine_kernel<K, S>), g2, dim3(64 * nw), lds, s, a); else
 #define MOE_DOWN(K)                                                                                    \
-  if constexpr (SINGLE) {                                                                              \
-    hipLaunchKernelGGL(down_combine_single_kernel<K>, g2, dim3(64 * nw), 0, s, a);                     \
+  if constexpr (INDEP) {                                                                              \
+    if (K == MOE_Q4B32 && down_window_fits(a)) {                                                       \
+      const int ug = (a.P + kWindowWaves - 1) / kWindowWaves;                                          \
+      const dim3 gw(g2.x), bw(64 * kWindowWaves);                                                      \
+      const size_t lh = size_t(a.P) * a.I * 4;                                                         \
+      if (ug <= 1) hipLaunchKernelGGL(down_combine_window_q4_kernel<1>, gw, bw, lh, s, a);             \
+      else if (ug <= 2) hipLaunchKernelGGL(down_combine_window_q4_kernel<2>, gw, bw, lh, s, a);        \
+      else if (ug <= 4) hipLaunchKernelGGL(down_combine_window_q4_kernel<4>, gw, bw, lh, s, a);        \
+      else hipLaunchKernelGGL(down_combine_window_q4_kernel<8>, gw, bw, lh, s, a);                     \
+    } else {                                                                                           \
+      hipLaunchKernelGGL(down_combine_single_kernel<K>, dim3(g2.x, a.T), dim3(64 * nw), 0, s, a);     \
+    }                                                                                                  \
   } else {                                                                                             \
     MOE_DOWN_SPL(K, 1) MOE_DOWN_SPL(K, 2) MOE_DOWN_SPL(K, 4) MOE_DOWN_SPL(K, 8) MOE_DOWN_SPL(K, 16)    \
     MOE_DOWN_SPL(K, 32) MOE_DOWN_SPL(K, 64) return hipErrorInvalidValue;                               \
