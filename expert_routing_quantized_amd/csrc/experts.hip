@@ -80,7 +80,7 @@ __device__ __forceinline__ int claim_pairs(const PairArgs& a, int p, int* s_matc
 
 // ------------------------------------------------------------ gate/up, 4-bit
 // MB = quant blocks per lane (H / 32 / 64 rounded up).
-template <int ACT, int MB, bool INDEP>
+template <int ACT, int MB, bool INDEP, int RPW = 2>   // RPW: intermediate rows per wave
 __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
   __shared__ int s_match[kMaxPairs];
   __shared__ int s_n;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
     if (e < 0) return;
   }
   const int nblk = a.H >> 5;
-  constexpr int kRowsPerWave = 2;
+  constexpr int kRowsPerWave = RPW;
   const int i0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
   const size_t rowb = size_t(a.H) / 2;
   uint4 wg[kRowsPerWave][MB], wu[kRowsPerWave][MB];
@@ -599,9 +599,18 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
   dim3 g1((a.I + 7) / 8, a.P);
   if (wd == MOE_Q4B32) {
     const int mb = (a.H / 32 + 63) / 64;
+    // batch 1: one row of gate and up per wave (more waves in flight for
+    // the latency-bound loads); measured slower for windows of several
+    // tokens, which keep two rows per wave
+    const bool rows1 = INDEP && a.T == 1;
+    const dim3 g4((a.I + 3) / 4, a.P);
 #define MOE_GU_Q4(M)                                                                    \
   if (mb <= M) {                                                                        \
-    if (act == MOE_BF16)                                                                \
+    if (rows1 && act == MOE_BF16)                                                       \
+      hipLaunchKernelGGL((gateup_q4_kernel<MOE_BF16, M, INDEP, 1>), g4, dim3(256), 0, s, a);   \
+    else if (rows1)                                                                     \
+      hipLaunchKernelGGL((gateup_q4_kernel<MOE_F32, M, INDEP, 1>), g4, dim3(256), 0, s, a);    \
+    else if (act == MOE_BF16)                                                           \
       hipLaunchKernelGGL((gateup_q4_kernel<MOE_BF16, M, INDEP>), g1, dim3(256), 0, s, a);      \
     else                                                                                \
       hipLaunchKernelGGL((gateup_q4_kernel<MOE_F32, M, INDEP>), g1, dim3(256), 0, s, a);       \

@@ -185,9 +185,10 @@ __device__ double bins_round(const long long* bins) {
 }
 
 // Exact logit of expert e for token t, computed by one wave (all lanes
-// return the same value).
+// return the same value).  Inlined, so the kernel's argument block is never
+// copied to private memory and its pointers keep their global address space.
 template <int ACT>
-__device__ double refine_logit(const SelectArgs& a, int t, int e, long long* bins, int lane) {
+__device__ __forceinline__ double refine_logit(const SelectArgs& a, int t, int e, long long* bins, int lane) {
   const int nch = a.H >> 3;
   const double b = a.bias ? (double)a.bias[e] : 0.0;
   // Four independent TwoSum chains per lane (one per chunk slot) for
