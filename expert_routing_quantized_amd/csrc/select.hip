@@ -306,7 +306,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
   __shared__ double top_z[kMaxK], new_z[kMaxK], s_w[kMaxK];
   __shared__ long long bins[kWavesSel][kBins];
   __shared__ double red[kWavesSel];
-  __shared__ int s_cnt, c_cnt, s_ntop, s_done, s_ng;
+  __shared__ int s_cnt, c_cnt, s_ntop, s_done, s_ng, s_nref;
+  __shared__ int s_ref[64];                        // ranks refined by the cluster pass
+  __shared__ double x_z[64];                       // their exact logits, by rank
   __shared__ double s_tau, s_tau0;
 
   const int t = blockIdx.x;
@@ -325,6 +327,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     s_ntop = 0;
     s_done = 0;
     s_ng = 0;
+    s_nref = 0;
     s_tau = -INFINITY;
     s_tau0 = -INFINITY;
   }
@@ -446,7 +449,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
       const double hi = c_z[lane], lo = c_z[lane + 1];
       bad = !(hi - bound(hi) > lo + bound(lo));
     }
-    const bool certified = (n >= k) && (__ballot(bad) == 0ull);
+    const unsigned long long bm = __ballot(bad);
+    const bool certified = (n >= k) && (bm == 0ull);
     if (certified) {
       if (lane < k) s_w[lane] = exp(c_z[lane] - c_z[0]);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -458,10 +462,74 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
         og[lane] = (float)(s_w[lane] / sum);
       }
       if (lane == 0) s_done = 1;
+    } else if (n >= k) {
+      // cluster pass: the ranks of every overlapping pair, and, when the
+      // cut (k-1, k) overlaps, every later rank whose interval reaches the
+      // lower end of rank k's, are refined to their exact logits
+      bool mark = lane < n && ((((bm >> lane) & 1ull) != 0) || (lane > 0 && ((bm >> (lane - 1)) & 1ull) != 0));
+      if (((bm >> (k - 1)) & 1ull) != 0 && lane > k && lane < n) {
+        const double zk = c_z[k];
+        if (c_z[lane] + bound(c_z[lane]) >= zk - bound(zk)) mark = true;
+      }
+      const unsigned long long mm = __ballot(mark);
+      if (mark) s_ref[__popcll(mm & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) s_nref = (__popcll(mm) <= 2 * kWavesSel) ? __popcll(mm) : 0;
     }
   }
   __syncthreads();
   if (s_done) return;
+  if (s_nref > 0) {
+    for (int i = wave; i < s_nref; i += kWavesSel) {
+      const double zz = refine_logit<ACT>(a, t, c_id[s_ref[i]], bins[wave], lane);
+      if (lane == 0) x_z[s_ref[i]] = zz;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // re-rank with the exact logits where known (interval of width 0)
+      bool ex = false;
+      for (int i = 0; i < s_nref; ++i) ex = ex || (s_ref[i] == lane);
+      const double v = (lane < n) ? (ex ? x_z[lane] : c_z[lane]) : -INFINITY;
+      const double bw = (lane < n && !ex) ? bound(c_z[lane]) : 0.0;
+      const int e = (lane < n) ? c_id[lane] : 0x7fffffff;
+      int rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const double vj = readlane_f64(v, j);
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        rank += (vj > v) || (vj == v && ej < e);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < n) {          // reuse the first slots of the candidate lists
+        s_val[rank] = v;
+        x_z[rank] = bw;
+        s_id[rank] = e;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // adjacent ranks r < k: disjoint intervals, or both exact (their
+      // order is then the exact order, ties by index)
+      const int npair = min(k, n - 1);
+      bool bad = false;
+      if (lane < npair) {
+        const double hv = s_val[lane], hb = x_z[lane], lv = s_val[lane + 1], lb = x_z[lane + 1];
+        bad = !((hv - hb > lv + lb) || (hb == 0.0 && lb == 0.0));
+      }
+      if (__ballot(bad) == 0ull) {
+        if (lane < k) s_w[lane] = exp(s_val[lane] - s_val[0]);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (lane < k) {
+          double sum = 0.0;
+          for (int j = 0; j < k; ++j) sum += s_w[j];
+          oi[lane] = s_id[lane];
+          og[lane] = (float)(s_w[lane] / sum);
+        }
+        if (lane == 0) s_done = 1;
+      }
+    }
+    __syncthreads();
+    if (s_done) return;
+  }
 
   // 5b. exact path.
   auto process = [&](int nc) {

@@ -186,3 +186,40 @@ def test_host_refusals_with_a_live_layer():
     assert e.value.status == -1
     layer.route(x, 0, idx, gates, ws)        # T = 0 is a no-op
     assert layer.workspace_bytes(0) > 0
+
+
+@pytest.mark.parametrize("rank,shift,T", [(3, 9, 1), (3, -9, 1), (1, 5, 1), (3, 9, 5), (0, -3, 5)])
+def test_ties_at_the_cut_and_inside_the_top(rank, shift, T):
+    """A copy of the expert at `rank` of token 0 placed `shift` indices away
+    (an exact tie: the lower index ranks first; at rank k-1 the tie decides
+    which of the two is selected), plus a row one bf16 ulp away from the
+    expert at rank 0 (a near tie decided by the exact logits).  T = 1 routes
+    with the batch-1 GEMV bound; T = 5 with the few-token MFMA bound."""
+    torch = G.torch_mod()
+    import oracle
+    import synth.device as SD
+    spec = SPEC_BF
+    dl = dev(spec)
+    R = dl.router_eh.clone()
+    x = SD.device_tokens(spec, 0, T)
+    layer = SD.make_layer(dl, max_tokens=8)
+    idx0, _, _ = G.run_grouped(layer, x)
+    top = [int(v) for v in idx0[0]]
+    src = top[rank]
+    dst = (src + shift) % spec.E
+    while dst in top:
+        dst = (dst + (1 if shift > 0 else -1)) % spec.E
+    R[dst] = R[src]
+    near = (top[0] + 2 * shift + 1) % spec.E
+    while near in top or near == dst:
+        near = (near + 1) % spec.E
+    R[near] = R[top[0]]
+    bits = R[near].view(torch.int16)
+    bits[37] += 1
+    dl2 = SD.DeviceLayer(spec, R, dl.bias, dl.w_gate, dl.w_up, dl.w_down)
+    layer2 = SD.make_layer(dl2, max_tokens=8)
+    idx, gates, out = G.run_grouped(layer2, x)
+    Rh = oracle.decode_bf16(SD.to_numpy_bits(R)).T
+    L = oracle.OracleLayer(Rh, np.zeros(spec.E), spec.k, lambda e, w: synth.expert_stored(spec, e, w))
+    o_idx, o_g, _, o_out = oracle.moe_tokens(oracle.tokens_f64(spec, 0, T), L)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"ties rank {rank} shift {shift} T {T}")
