@@ -50,7 +50,8 @@ def parse():
                    help="decode_bf16/decode_q4: batch-1 decode (the headline is decode_q4); verify_q4: T=5 verify steps "
                         "through the 4-bit layer; prefill_bf16: T=2048 prefill chunks through the bf16 layer")
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
-    p.add_argument("--cpu-sample", type=int, default=12, help="tokens the oracle is timed on (0: skip)")
+    p.add_argument("--cpu-sample", type=int, default=800,
+                   help="tokens the oracle is timed on (about 10 s of host work; 0: skip)")
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter run: launch eagerly (no graphs), run the router alone, then "
                         "a plain copy of known size that calibrates the byte counters; prints a summary")
@@ -139,7 +140,11 @@ def step_bytes(spec) -> dict:
     return {"router": router, "experts": experts, "total": router + experts + out}
 
 
-def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out):
+def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out, dl=None):
+    """The oracle timed on `count` tokens of the timed stream.  The experts'
+    stored bytes come from the seeded input generator: its device copy in
+    `dl` when given (bitwise equal to the host generator, and fast to copy),
+    else the host generator."""
     import numpy as np
 
     import oracle
@@ -154,15 +159,27 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out):
     X = oracle.tokens_f64(spec, first, count)
     stored = {}
 
+    def from_device(e, which):
+        w = {"gate": dl.w_gate, "up": dl.w_up, "down": dl.w_down}[which][e]
+        if spec.expert == synth.DT_Q4:
+            sc = {"gate": dl.s_gate, "up": dl.s_up, "down": dl.s_down}[which][e]
+            return ("q4", (w.cpu().numpy(), sc.cpu().numpy().view(np.uint16)))
+        if spec.expert == synth.DT_BF16:
+            import torch
+            return ("bf16", w.view(torch.int16).cpu().numpy().view(np.uint16))
+        return ("f32", w.cpu().numpy())
+
     def fetch(e, which):
         key = (e, which)
         if key not in stored:
-            stored[key] = synth.expert_stored(spec, e, which)
+            stored[key] = from_device(e, which) if dl is not None else synth.expert_stored(spec, e, which)
         return stored[key]
-    # untimed pass: generates the experts' stored bytes (data preparation)
-    Lp = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
-    Lp._absR = L0.absR()
-    oracle.moe_tokens(X[:count], Lp)
+    # untimed: the stored bytes of the experts the sample selects (data
+    # preparation; any other expert the oracle asks for is fetched on demand)
+    for e in np.unique(gpu_idx):
+        if 0 <= e < spec.E:
+            for which in ("gate", "up", "down"):
+                fetch(int(e), which)
     # timed pass: a fresh oracle over the same stored bytes
     Lt = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
     Lt._absR = L0.absR()
@@ -175,7 +192,7 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out):
               "out_rel_l2_max": float(rel.max()), "out_rel_l2_median": float(np.median(rel))}
     base = {"value": count / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{count} tokens (tokens {first}..{first + count - 1} of the timed stream), "
-                      f"float64 numpy, {dt:.1f} s; expert bytes pre-generated"}
+                      f"float64 numpy, {dt:.1f} s; expert bytes pre-generated from the seeded generator"}
     return base, parity
 
 
@@ -426,7 +443,7 @@ def main():
         gi = idx[W:W + n].cpu().numpy()
         gg = gates[W:W + n].cpu().numpy()
         go = out[W:W + n].cpu().numpy()
-        base, parity = cpu_baseline(spec, W, n, gi, gg, go)
+        base, parity = cpu_baseline(spec, W, n, gi, gg, go, dl)
         res["cpu_baseline"] = base
         res["config"]["parity_sample"] = parity
     print(json.dumps(res), flush=True)
