@@ -80,10 +80,21 @@ __device__ __forceinline__ int claim_pairs(const PairArgs& a, int p, int* s_matc
 
 // ------------------------------------------------------------ gate/up, 4-bit
 // MB = quant blocks per lane (H / 32 / 64 rounded up).
+// Independent pairs stage the token's x once per block in LDS (each quant
+// block's 16-byte chunks padded by one chunk, so a wave's reads of one
+// chunk column hit distinct banks), instead of every wave reading the whole
+// row from L2: at batch 1 the x reads were more bytes than the weights.
+template <int ACT>
+struct XStage {
+  static constexpr int kChunks = (ACT == MOE_BF16) ? 4 : 8;   // 16-byte chunks per quant block
+  static constexpr int kPitch = kChunks + 1;
+};
+
 template <int ACT, int MB, bool INDEP, int RPW = 2>   // RPW: intermediate rows per wave
 __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
   __shared__ int s_match[kMaxPairs];
   __shared__ int s_n;
+  __shared__ uint4 sx[INDEP ? (kMaxH / 32) * XStage<ACT>::kPitch : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int e;
   bool valid = true;
@@ -121,6 +132,25 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       if (!(i0 + r < a.I && m * 64 + lane < nblk)) dg[r][m] = du[r][m] = 0.f;
+  if constexpr (INDEP) {           // x of the pair's token into LDS, while the weights load
+    constexpr int CK = XStage<ACT>::kChunks, PK = XStage<ACT>::kPitch;
+    const int nc = nblk * CK;
+    const uint4* xs = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.x) +
+                                                     size_t(blockIdx.y / a.k) * a.H * (ACT == MOE_BF16 ? 2 : 4));
+    constexpr int NU = (64 * MB * CK + 255) / 256;   // chunks per thread (nblk <= 64 MB)
+    uint4 xr[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      xr[u] = xs[min(c, nc - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      if (c < nc) sx[(c / CK) * PK + c % CK] = xr[u];
+    }
+    __syncthreads();
+  }
   const int n = INDEP ? 1 : s_n;
   for (int mi = 0; mi < n; ++mi) {
 #pragma unroll
@@ -139,8 +169,23 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
       const int b = m * 64 + lane;
       xs[m] = 0.f;
       Chunk<ACT> ch[4];
+      if constexpr (INDEP) {
+        constexpr int PK = XStage<ACT>::kPitch;
+        const uint4* sb = sx + min(b, nblk - 1) * PK;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ch[c].load(a.x, xoff + min(b, nblk - 1) * 32 + c * 8);
+        for (int c = 0; c < 4; ++c) {
+          if constexpr (ACT == MOE_BF16) {
+            ch[c].v = sb[c];
+          } else {
+            const uint4 p0 = sb[2 * c], p1 = sb[2 * c + 1];
+            ch[c].a = make_float4(__uint_as_float(p0.x), __uint_as_float(p0.y), __uint_as_float(p0.z), __uint_as_float(p0.w));
+            ch[c].b = make_float4(__uint_as_float(p1.x), __uint_as_float(p1.y), __uint_as_float(p1.z), __uint_as_float(p1.w));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ch[c].load(a.x, xoff + min(b, nblk - 1) * 32 + c * 8);
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
