@@ -87,12 +87,29 @@ __device__ int block_excl_scan_1024(int v, int* s_w, int* total) {
 // experts, 32-row tiles) give every thread its starting offsets; the
 // offsets, the active list and the tile list are then written from
 // registers in expert order.
+// Up to kScanLdsPer experts per thread (E <= 24,576) the counts pass
+// through LDS with coalesced global reads and writes: each thread's range
+// sits at an odd pitch, so the threads of a wave reading the same position
+// of their ranges hit distinct banks.
 constexpr int kScanMaxPer = 32;           // E <= 32768 in registers, larger E loops
+constexpr int kScanLdsPer = 24;
 __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
   __shared__ int s_w[16];
+  __shared__ int s_c[1024 * (kScanLdsPer + 1)];
   const int tid = threadIdx.x;
   const int per = (a.E + 1023) / 1024;
   const int e0 = min(tid * per, a.E), e1 = min(e0 + per, a.E);
+  const bool lds = per <= kScanLdsPer;
+  const int pitch = per | 1;
+  const unsigned long long magic = ((1ull << 32) + per - 1) / per;   // j / per = (j magic) >> 32 for j < 2^20
+  auto spos = [&](int j) {
+    const int q = int((unsigned long long)j * magic >> 32);
+    return q * pitch + (j - q * per);
+  };
+  if (lds) {
+    for (int j = tid; j < a.E; j += 1024) s_c[spos(j)] = a.counts[j];
+    __syncthreads();
+  }
   int c[kScanMaxPer];
   int sum = 0, act = 0, til = 0, big = 0;
   auto count = [&](int ce) {
@@ -101,7 +118,12 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
     til += (ce > a.small_max && ce <= kTileRows) ? 1 : 0;
     big += (ce > a.small_max && ce > kTileRows) ? (ce + kBigTileRows - 1) / kBigTileRows : 0;
   };
-  if (per <= kScanMaxPer) {
+  if (lds) {
+#pragma unroll
+    for (int i = 0; i < kScanLdsPer; ++i) c[i] = (e0 + i < e1) ? s_c[tid * pitch + i] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanLdsPer; ++i) count(c[i]);
+  } else if (per <= kScanMaxPer) {
 #pragma unroll
     for (int i = 0; i < kScanMaxPer; ++i) c[i] = (e0 + i < e1) ? a.counts[e0 + i] : 0;
 #pragma unroll
@@ -115,7 +137,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
   int trun = block_excl_scan_1024(til, s_w, &tot_til);
   int brun = block_excl_scan_1024(big, s_w, &tot_big);
   auto emit = [&](int e, int ce) {
-    a.offsets[e] = run;
+    if (lds)
+      s_c[tid * pitch + (e - e0)] = run;          // written back below, coalesced
+    else
+      a.offsets[e] = run;
     if (ce > 0 && ce <= a.small_max) {
       a.active[1 + arun++] = e;
     } else if (ce > a.small_max && ce <= kTileRows) {
@@ -131,7 +156,13 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
     }
     run += ce;
   };
-  if (per <= kScanMaxPer) {
+  if (lds) {
+#pragma unroll
+    for (int i = 0; i < kScanLdsPer; ++i)
+      if (e0 + i < e1) emit(e0 + i, c[i]);
+    __syncthreads();
+    for (int j = tid; j < a.E; j += 1024) a.offsets[j] = s_c[spos(j)];
+  } else if (per <= kScanMaxPer) {
 #pragma unroll
     for (int i = 0; i < kScanMaxPer; ++i)
       if (e0 + i < e1) emit(e0 + i, c[i]);
