@@ -432,24 +432,38 @@ __global__ __launch_bounds__(256) void combine_kernel(GroupArgs a) {
   __shared__ float s_g[kMaxK];
   __shared__ int s_bad;
   const int t = blockIdx.y;
-  const int k = a.k;
-  if (threadIdx.x == 0) s_bad = 0;
-  __syncthreads();
-  if (threadIdx.x < k) {
-    const int j = threadIdx.x, p = t * k + j;
-    const int q = a.pos[p];
-    bool bad = q < 0;
-    const int e = a.idx[p];
-    for (int jj = 0; jj < j; ++jj) bad |= (a.idx[t * k + jj] == e);
-    s_pos[j] = q < 0 ? 0 : q;
-    s_g[j] = a.gates[p];
-    if (bad) atomicOr(&s_bad, 1);
+  const int k = a.k, lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {          // wave 0: the token's k pairs, one per lane (k <= 32)
+    const bool live = lane < k;
+    const int p = t * k + lane;
+    const int e = live ? a.idx[p] : -1;
+    const int q = live ? a.pos[p] : 0;
+    const float g = live ? a.gates[p] : 0.f;
+    bool bad = live && q < 0;
+    for (int jj = 0; jj < k; ++jj) {   // a repeated index of the token (shuffles, no loads)
+      const int ej = __shfl(e, jj);
+      bad |= live && jj < lane && ej == e;
+    }
+    if (live) {
+      s_pos[lane] = q < 0 ? 0 : q;
+      s_g[lane] = g;
+    }
+    const bool any_bad = __ballot(bad) != 0ull;
+    if (lane == 0) s_bad = any_bad ? 1 : 0;
   }
   __syncthreads();
   const int o = blockIdx.x * blockDim.x + threadIdx.x;
   if (o >= a.H) return;
+  // the k rows' values in flight together (groups of 8), summed in j order
   float acc = 0.f;
-  for (int j = 0; j < k; ++j) acc = fmaf(s_g[j], a.y[size_t(s_pos[j]) * a.H + o], acc);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (j0 + u < k) ? a.y[size_t(s_pos[j0 + u]) * a.H + o] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k) acc = fmaf(s_g[j0 + u], v[u], acc);
+  }
   a.out[size_t(t) * a.H + o] = s_bad ? NAN : acc;
 }
 
