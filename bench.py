@@ -46,9 +46,15 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=1000)
     p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--config", default="decode_q4", choices=["decode_bf16", "decode_q4", "verify_q4", "prefill_bf16"],
+    p.add_argument("--config", default="decode_q4",
+                   choices=["decode_bf16", "decode_q4", "verify_q4", "prefill_bf16", "prefill_bf16_hot"],
                    help="decode_bf16/decode_q4: batch-1 decode (the headline is decode_q4); verify_q4: T=5 verify steps "
-                        "through the 4-bit layer; prefill_bf16: T=2048 prefill chunks through the bf16 layer")
+                        "through the 4-bit layer; prefill_bf16: T=2048 prefill chunks through the bf16 layer; "
+                        "prefill_bf16_hot (supplementary): the same chunk routed to 64 hot experts, so the grouped "
+                        "expert kernels are matrix-bound")
+    p.add_argument("--sweep", action="store_true",
+                   help="cost table of moe_grouped_forward over T: 1-8 tokens through the 4-bit layer, "
+                        "16-8192 through the bf16 layer (one JSON line)")
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
     p.add_argument("--cpu-sample", type=int, default=800,
                    help="tokens the oracle is timed on (about 10 s of host work; 0: skip)")
@@ -294,6 +300,8 @@ def grouped_main(args, spec):
                 "frac": router_bytes / router_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
                 "avg_launch_us": router_s * 1e6, "bytes_per_launch": router_bytes}
     experts_bytes = d_mean * per_expert
+    # executed expert matrix work: gate, up and down, 2 H I flops each per pair
+    experts_flops = 6.0 * T * spec.k * spec.H * spec.I
     res = {
         "metric": f"MoE-layer grouped forward tokens/s ({spec.name}: T={T} per call)",
         "value": T * K / (ms / 1e3),
@@ -308,9 +316,69 @@ def grouped_main(args, spec):
         "roofline": roof,
         "experts_stage": {"us_per_call": experts_s * 1e6, "weight_bytes_per_call": experts_bytes,
                           "weight_gbs": experts_bytes / experts_s / 1e9,
+                          "flops_per_call": experts_flops,
+                          "tflops": experts_flops / experts_s / 1e12,
+                          "mfma_frac": experts_flops / experts_s / 1e12 / 2500.0,
                           "note": "moe_grouped_forward with caller indices: pair grouping, gate/up, down, combine"},
     }
     print(json.dumps(res), flush=True)
+
+
+def sweep_main(args):
+    """Cost of one moe_grouped_forward call over T (graph-captured calls on
+    distinct token batches): the table a draft or chunking policy reads."""
+    import torch
+
+    import synth
+    import synth.device as SD
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rows = []
+    for name, Ts in (("verify_q4", [1, 2, 3, 4, 5, 6, 8]),
+                     ("prefill_bf16", [16, 64, 256, 512, 1024, 2048, 4096, 8192])):
+        spec = synth.CONFIGS[name]
+        dl = SD.device_layer(spec)
+        layer = SD.make_layer(dl, max_tokens=max(Ts))
+        for T in Ts:
+            reps = max(3, min(200, 200 * 16 // T))
+            nb = min(reps, max(1, 16384 // T))             # distinct batches, reused cyclically
+            X = SD.device_tokens(spec, 0, nb * T).view(nb, T, spec.H)
+            ws = layer.workspace(T)
+            idx = torch.empty((T, spec.k), dtype=torch.int32, device=dev)
+            gates = torch.empty((T, spec.k), dtype=torch.float32, device=dev)
+            out = torch.empty((T, spec.H), dtype=torch.float32, device=dev)
+            for i in range(2):
+                layer.grouped_forward(X[i % nb], T, idx, gates, 0, out, ws)
+            torch.cuda.synchronize()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s):
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(reps):
+                        layer.grouped_forward(X[i % nb], T, idx, gates, 0, out, ws)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(s):
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                g.replay()
+                e1.record(s)
+                torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rows.append({"layer": name.split("_")[1], "T": T, "us_per_call": us,
+                         "us_per_token": us / T, "tokens_per_s": T / us * 1e6,
+                         "device_errors": layer.device_error()})
+            log(f"sweep {name} T={T}: {us:.1f} us per call, {T / us * 1e6:.0f} tokens/s")
+            del g, X, ws, idx, gates, out
+        del layer, dl
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "moe_grouped_forward cost per call over T (cost table)",
+                      "unit": "us per call", "n_gpus": 1, "data": "synthetic",
+                      "config": {"workload": "T = 1-8 through the 4-bit decode layer, T = 16-8192 through the "
+                                             "bf16 layer (H=2048, E=24576, top-10, I=256)"},
+                      "sweep": rows}), flush=True)
 
 
 def main():
@@ -325,6 +393,8 @@ def main():
     import synth
     import synth.device as SD
 
+    if args.sweep:
+        return sweep_main(args)
     spec = synth.CONFIGS[args.config]
     if args.counters:
         return counters_main(args, spec)

@@ -759,26 +759,149 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Down projection of the big tiles (experts with more than 32 tokens) as a
+// small GEMM: block = (128 output rows, tile of TM tokens); per K slice of
+// 32 the tile's h (fp32) is split into bf16 hi + lo in LDS and both parts
+// meet the same bf16 weight slice, staged once in LDS for all waves (the
+// 32-row kernel gives each wave its own weight rows and repeats them per
+// 32-row sub-tile).  Both operands are K-contiguous; LDS rows hold 32 K
+// elements (64 B) with 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 3),
+// so the staging writes and the operand reads of a wave hit distinct banks.
+// The accumulation order (K ascending in steps of 16, hi then lo, fp32) is
+// the one of the 32-row kernel.
+constexpr int kHotBK = 32;
+
+__device__ __forceinline__ int hot_pos(int row, int chunk) {
+  return row * kHotBK + ((chunk ^ ((row >> 1) & 3)) << 3);
+}
+
+template <int TM>   // tokens per tile: waves (token half, output half) hold TM/2 x 64
+__global__ __launch_bounds__(256, 2) void down_tile_kernel(GroupArgs a) {
+  constexpr int MB = TM / 64;                      // 32-row blocks per wave
+  constexpr int HR = TM / 64;                      // h rows per staging thread
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(2 * TM + 128) * kHotBK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, I = a.I;
+  const int* tl = a.tiles_big;
+  const int o0 = blockIdx.x * 128;
+  const uint16_t* WD = reinterpret_cast<const uint16_t*>(a.wd);
+  const int sr = tid >> 2, sc = tid & 3;           // staging: chunk sc of rows sr + 64 i
+  const int wm = (wave & 1) * (TM / 2), wn = (wave >> 1) * 64;
+  const int rl = lane & 31, hk = lane >> 5;
+  const int nk = I / kHotBK;
+  const int ntiles = tl[0];
+  for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
+    const int e = tl[1 + 2 * ti], r0 = tl[2 + 2 * ti];
+    const int n = a.counts[e], seg = a.offsets[e];
+    const int nrow = min(TM, n - r0);
+    const float* hsrc[HR];
+    const uint16_t* wsrc[2];
+#pragma unroll
+    for (int i = 0; i < HR; ++i)              // rows past the tile repeat its last row
+      hsrc[i] = a.hm + size_t(seg + r0 + min(sr + 64 * i, nrow - 1)) * I + sc * 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wsrc[i] = WD + (size_t(e) * H + min(o0 + sr + 64 * i, H - 1)) * I + sc * 8;
+    f32x16_t acc[MB][2];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[m][b][i] = 0.f;
+    float4 hf[HR][2];
+    uint4 wv[2];
+    auto gload = [&](int kt) {
+      const int ko = kt * kHotBK;
+#pragma unroll
+      for (int i = 0; i < HR; ++i) {
+        hf[i][0] = *reinterpret_cast<const float4*>(hsrc[i] + ko);
+        hf[i][1] = *reinterpret_cast<const float4*>(hsrc[i] + ko + 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wv[i] = load_nt(wsrc[i] + ko);
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < HR; ++i) {
+        const float v[8] = {hf[i][0].x, hf[i][0].y, hf[i][0].z, hf[i][0].w,
+                            hf[i][1].x, hf[i][1].y, hf[i][1].z, hf[i][1].w};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint16_t h0 = f32_to_bf16_rne_dev(v[2 * j]), h1 = f32_to_bf16_rne_dev(v[2 * j + 1]);
+          const uint16_t l0 = f32_to_bf16_rne_dev(v[2 * j] - __uint_as_float(uint32_t(h0) << 16));
+          const uint16_t l1 = f32_to_bf16_rne_dev(v[2 * j + 1] - __uint_as_float(uint32_t(h1) << 16));
+          hi[j] = uint32_t(h0) | (uint32_t(h1) << 16);
+          lo[j] = uint32_t(l0) | (uint32_t(l1) << 16);
+        }
+        const int r = sr + 64 * i;
+        *reinterpret_cast<uint4*>(&lds[buf][hot_pos(r, sc)]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(&lds[buf][hot_pos(TM + r, sc)]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(&lds[buf][hot_pos(2 * TM + sr + 64 * i, sc)]) = wv[i];
+    };
+    __syncthreads();                               // LDS reuse by the previous tile
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      gload(min(kt + 1, nk - 1));
+#pragma unroll
+      for (int q = 0; q < kHotBK / 16; ++q) {
+        const int ck = 2 * q + hk;
+        bf16x8_t ah[MB], al[MB], bv[2];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          ah[m] = *reinterpret_cast<const bf16x8_t*>(&lds[buf][hot_pos(wm + 32 * m + rl, ck)]);
+          al[m] = *reinterpret_cast<const bf16x8_t*>(&lds[buf][hot_pos(TM + wm + 32 * m + rl, ck)]);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) bv[b] = *reinterpret_cast<const bf16x8_t*>(&lds[buf][hot_pos(2 * TM + wn + 32 * b + rl, ck)]);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            acc[m][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[m], bv[b], acc[m][b], 0, 0, 0);
+            acc[m][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[m], bv[b], acc[m][b], 0, 0, 0);
+          }
+      }
+      if (kt + 1 < nk) lstore(buf ^ 1);
+      __syncthreads();
+    }
+    // D rows 8 (i / 4) + 4 (lane / 32) + i % 4 (tokens), column lane % 32 (output row)
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int o = o0 + wn + 32 * b + rl;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm + 32 * m + 8 * (i >> 2) + 4 * hk + (i & 3);
+          if (r < nrow && o < H) a.y[size_t(seg + r0 + r) * H + o] = acc[m][b][i];
+        }
+      }
+  }
+}
+
 // The 32-row tiles first (most experts: bound by the weight stream), then
-// the 64-row tiles of the hot experts.
+// the 64-row tiles of the hot experts (gate/up as 2 sub-tiles, down as a
+// small GEMM).
 hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s) {
   constexpr int MB = kBigTileRows / kTileRows;
   const int gy = 2048, gyb = 256;
   const int ns = (a.I + kKS - 1) / kKS;
   if (ns > 4) return hipErrorInvalidValue;
   const dim3 g1((a.I + kGC - 1) / kGC, gy), g1b((a.I + kGC - 1) / kGC, gyb);
-  const dim3 g2((a.H + kDR - 1) / kDR, gy), g2b((a.H + kDR - 1) / kDR, gyb);
+  const dim3 g2((a.H + kDR - 1) / kDR, gy);
   hipLaunchKernelGGL(gateup_mfma_kernel<1>, g1, dim3(256), 0, s, a);
   hipLaunchKernelGGL(gateup_mfma_kernel<MB>, g1b, dim3(256), 0, s, a);
-#define MOE_DOWN_NS(N)                                                    \
-  {                                                                       \
-    hipLaunchKernelGGL((down_mfma_kernel<N, 1>), g2, dim3(256), 0, s, a); \
-    hipLaunchKernelGGL((down_mfma_kernel<N, MB>), g2b, dim3(256), 0, s, a); \
-  }
-  if (ns == 1) MOE_DOWN_NS(1)
-  else if (ns == 2) MOE_DOWN_NS(2)
-  else MOE_DOWN_NS(4)
-#undef MOE_DOWN_NS
+  if (ns == 1) hipLaunchKernelGGL((down_mfma_kernel<1, 1>), g2, dim3(256), 0, s, a);
+  else if (ns == 2) hipLaunchKernelGGL((down_mfma_kernel<2, 1>), g2, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((down_mfma_kernel<4, 1>), g2, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(down_tile_kernel<kBigTileRows>, dim3((a.H + 127) / 128, gyb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

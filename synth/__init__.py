@@ -174,6 +174,7 @@ class LayerSpec:
     token_seed: int = 42
     sigma_w: float = 0.02
     sigma_x: float = 1.0
+    hot: int = 0        # > 0: only the `hot` experts of lowest rank get bias 0, all others -20
 
     @property
     def router(self) -> int:
@@ -191,6 +192,11 @@ CONFIGS = {
     "verify_q4": LayerSpec("verify_q4", 2048, 24576, 10, 256, DT_BF16, DT_Q4, 0.37, 5, 1000, token_seed=45),
     # prefill chunk: T=2048 through decode_bf16's layer
     "prefill_bf16": LayerSpec("prefill_bf16", 2048, 24576, 10, 256, DT_BF16, DT_BF16, 0.37, 2048, 1, token_seed=46),
+    # supplementary (not one of the five workloads): prefill_bf16's weights with the bias
+    # concentrated on 64 experts, so each gets about 320 of the 20,480 pairs and the
+    # grouped expert kernels become matrix-bound
+    "prefill_bf16_hot": LayerSpec("prefill_bf16_hot", 2048, 24576, 10, 256, DT_BF16, DT_BF16, 0.37, 2048, 1,
+                                  token_seed=47, hot=64),
 }
 
 
@@ -219,13 +225,16 @@ def router_eh(spec: LayerSpec) -> np.ndarray:
 
 
 def router_bias(spec: LayerSpec) -> np.ndarray:
-    """fp32 [E] logit bias: -alpha * ln(rank), rank = 1 + seeded permutation."""
+    """fp32 [E] logit bias: -alpha * ln(rank), rank = 1 + seeded permutation
+    (with ``hot`` > 0: 0 for ranks 1..hot, -20 for the rest)."""
     if spec.bias_alpha is None:
         return np.zeros(spec.E, dtype=np.float32)
     key = stream_key(spec.weight_seed, TAG_BIAS)
     perm = np.argsort(raw64(key, np.arange(spec.E, dtype=np.uint64)), kind="stable")
     rank = np.empty(spec.E, dtype=np.float64)
     rank[perm] = np.arange(1, spec.E + 1, dtype=np.float64)
+    if spec.hot > 0:
+        return np.where(rank <= spec.hot, 0.0, -20.0).astype(np.float32)
     return (-spec.bias_alpha * np.log(rank)).astype(np.float32)
 
 

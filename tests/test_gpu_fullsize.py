@@ -173,3 +173,82 @@ def test_prefill_bf16_prefill_chunk_parity():
     r = G.rel_l2(out[sample], o_out)
     print(f"prefill_bf16 sampled outputs: rel L2 max {r.max():.2e}; distinct experts {len(np.unique(idx))}")
     assert r.max() <= G.OUT_TOL
+
+
+@pytest.mark.parametrize("T", [2, 3, 4, 6, 8])
+def test_verify_window_sizes_parity(T):
+    """Verify windows of other sizes through the 4-bit layer (the drafters'
+    depths: up to 3 + 1 and 5 + 1 tokens, and the largest independent-pair
+    window)."""
+    import synth.device as SD
+    layer, spec = layer_for("verify_q4", 8)
+    L = oracle_for(spec)
+    first = 5 * 321 + T
+    G.note("verify window T", T)
+    x = SD.device_tokens(spec, first, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, first, T)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"verify window T={T}")
+    assert layer.device_error() == 0
+
+
+def _route_sample(spec, L, X, rows):
+    Z, B = oracle.logits_with_bound(X[rows], L)
+    o_idx = np.empty((len(rows), spec.k), np.int64)
+    o_g = np.empty((len(rows), spec.k))
+    for i, t in enumerate(rows):
+        o_idx[i], zs = oracle.route_token(X[t], Z[i], B[i], L)
+        o_g[i] = oracle.softmax_gates(zs)
+    return o_idx, o_g
+
+
+def test_prefill_chunk_8192_sampled_parity():
+    """The largest prefill chunk (8,192 tokens): routing on 192 sampled
+    tokens, outputs on 8 of them."""
+    import synth.device as SD
+    layer, spec = layer_for("prefill_bf16", 8192)
+    G.note("prefill T=8192 grouped forward")
+    x = SD.device_tokens(spec, 0, 8192)
+    idx, gates, out = G.run_grouped(layer, x)
+    assert layer.device_error() == 0
+    L = oracle_for(spec)
+    X = oracle.tokens_f64(spec, 0, 8192)
+    rows = np.unique(np.concatenate([np.arange(0, 8192, 43), [8191]]))
+    o_idx, o_g = _route_sample(spec, L, X, rows)
+    G.compare(idx[rows], gates[rows], None, o_idx, o_g, None, "prefill T=8192 routing")
+    sel = np.linspace(0, len(rows) - 1, 8).astype(int)
+    o_out = np.stack([oracle.moe_given(X[rows[i]], L, o_idx[i], o_g[i]) for i in sel])
+    r = G.rel_l2(out[rows[sel]], o_out)
+    print(f"prefill T=8192 sampled outputs: rel L2 max {r.max():.2e}")
+    assert r.max() <= G.OUT_TOL
+
+
+def test_prefill_hot_experts_parity():
+    """Supplementary: the bias concentrated on 64 experts, so each gets about
+    320 pairs and the 64-row MFMA tiles carry nearly all the work."""
+    import torch
+    import synth.device as SD
+    spec = synth.CONFIGS["prefill_bf16_hot"]
+    dl0 = device_for("prefill_bf16")
+    hot_bias = torch.from_numpy(synth.router_bias(spec)).to(dl0.router_eh.device)
+    dl = SD.DeviceLayer(spec, dl0.router_eh, hot_bias, dl0.w_gate, dl0.w_up, dl0.w_down)
+    layer = SD.make_layer(dl, max_tokens=2048)
+    G.note("prefill hot grouped forward")
+    x = SD.device_tokens(spec, 0, 2048)
+    idx, gates, out = G.run_grouped(layer, x)
+    assert layer.device_error() == 0
+    counts = np.bincount(idx.ravel(), minlength=spec.E)
+    assert np.count_nonzero(counts) <= 64 and counts.max() > 200
+    R, _, absR = host_router()
+    L = oracle.OracleLayer(R, synth.router_bias(spec).astype(np.float64), spec.k,
+                           lambda e, w: synth.expert_stored(spec, e, w), cache_size=128)
+    L._absR = absR
+    X = oracle.tokens_f64(spec, 0, 2048)
+    rows = np.arange(0, 2048, 7)
+    o_idx, o_g = _route_sample(spec, L, X, rows)
+    G.compare(idx[rows], gates[rows], None, o_idx, o_g, None, "prefill hot routing")
+    sel = np.linspace(0, len(rows) - 1, 10).astype(int)
+    o_out = np.stack([oracle.moe_given(X[rows[i]], L, o_idx[i], o_g[i]) for i in sel])
+    r = G.rel_l2(out[rows[sel]], o_out)
+    print(f"prefill hot sampled outputs: rel L2 max {r.max():.2e}; experts used {np.count_nonzero(counts)}")
+    assert r.max() <= G.OUT_TOL
