@@ -587,8 +587,6 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sx[2][TR][kKP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, I = a.I;
-  const int ch0 = blockIdx.x * kGC;
-  const int wc = ch0 + 32 * (wave & 1);                  // first channel of this wave
   const uint16_t* W = reinterpret_cast<const uint16_t*>(wave < 2 ? a.wg : a.wu);
   const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
   const int lr = lane >> 3, lc = lane & 7;               // weight loads: row lr + 8 i, chunk lc
@@ -596,7 +594,20 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
   const int nks = (H + kKS - 1) / kKS;
   const int* tl = (MT == 1) ? a.tiles : a.tiles_big;   // MT > 1: the big-tile list
   const int ntiles = tl[0];
-  for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
+  // work item w = (tile, channel block), tile-major.  32-row list: the grid's
+  // y walks the tiles.  Big tiles: blocks are dealt to the 8 XCDs round-robin,
+  // so XCD j takes a contiguous run of work items: a tile's channel blocks
+  // (same token rows) and an expert's consecutive tiles (same weights) then
+  // meet in one L2.
+  const int nwork = ntiles * gridDim.x;
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y, nblk = gridDim.x * gridDim.y;
+  const int per_xcd = (nwork + 7) / 8;
+  for (int it = (MT == 1 ? lin : lin / 8); it < (MT == 1 ? nwork : per_xcd); it += (MT == 1 ? nblk : nblk / 8)) {
+    const int w = (MT == 1) ? it : (lin & 7) * per_xcd + it;
+    if (w >= nwork) break;                               // block-uniform
+    const int ti = w / gridDim.x;
+    const int ch0 = (w - ti * gridDim.x) * kGC;
+    const int wc = ch0 + 32 * (wave & 1);                // first channel of this wave
     const int e = tl[1 + 2 * ti], r0 = tl[2 + 2 * ti];
     const int n = a.counts[e], seg = a.offsets[e];
     const int nrow = min(TR, n - r0);
