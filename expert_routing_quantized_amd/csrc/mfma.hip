@@ -594,16 +594,15 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
   const int nks = (H + kKS - 1) / kKS;
   const int* tl = (MT == 1) ? a.tiles : a.tiles_big;   // MT > 1: the big-tile list
   const int ntiles = tl[0];
-  // work item w = (tile, channel block), tile-major.  32-row list: the grid's
-  // y walks the tiles.  Big tiles: blocks are dealt to the 8 XCDs round-robin,
-  // so XCD j takes a contiguous run of work items: a tile's channel blocks
-  // (same token rows) and an expert's consecutive tiles (same weights) then
-  // meet in one L2.
+  // work item w = (tile, channel block), tile-major.  Blocks are dealt to the
+  // 8 XCDs round-robin, so XCD j takes a contiguous run of work items: a
+  // tile's channel blocks (same token rows) and an expert's consecutive tiles
+  // (same weights) then meet in one L2.
   const int nwork = ntiles * gridDim.x;
   const int lin = blockIdx.x + gridDim.x * blockIdx.y, nblk = gridDim.x * gridDim.y;
   const int per_xcd = (nwork + 7) / 8;
-  for (int it = (MT == 1 ? lin : lin / 8); it < (MT == 1 ? nwork : per_xcd); it += (MT == 1 ? nblk : nblk / 8)) {
-    const int w = (MT == 1) ? it : (lin & 7) * per_xcd + it;
+  for (int it = lin / 8; it < per_xcd; it += nblk / 8) {
+    const int w = (lin & 7) * per_xcd + it;
     if (w >= nwork) break;                               // block-uniform
     const int ti = w / gridDim.x;
     const int ch0 = (w - ti * gridDim.x) * kGC;
