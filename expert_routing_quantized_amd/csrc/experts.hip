@@ -367,14 +367,16 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
 // LDS (every load issued before any is stored), wave w takes pairs w,
 // w + 16, ... and issues the weight loads of all of them before computing
 // any; per-pair partials meet in LDS and each token's output is summed over
-// its pairs in selection order.  Needs P <= 128, P I floats of LDS and
-// I <= 256 (one quant block per lane of an 8-lane row group).
+// its pairs in selection order.  Needs P <= 128 and I <= 256 (one quant
+// block per lane of an 8-lane row group), so h takes at most 128 KB of LDS
+// and UG float4 per thread stage it (P I / 4 <= 64 kWindowWaves UG).
 constexpr int kWindowWaves = 16;
 constexpr int kPairHLdsBytes = 64 * 1024;
+constexpr int kWindowHLdsBytes = 128 * 1024;
 
 bool down_window_fits(const PairArgs& a) {
-  return a.T >= 2 && a.P <= kWindowWaves * 8 && size_t(a.P) * a.I * 4 <= kPairHLdsBytes &&
-         a.I <= 8 * 32 && a.P * a.I / 4 <= 4 * 64 * kWindowWaves;
+  return a.T >= 2 && a.P <= kWindowWaves * 8 && a.I <= 8 * 32 && a.I % 32 == 0 &&
+         size_t(a.P) * a.I * 4 <= kWindowHLdsBytes;
 }
 
 template <int UG>
@@ -388,11 +390,11 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
   const int o = blockIdx.x * 8 + grp;
   const int oc = min(o, a.H - 1);
   const int nsl = I >> 5, nblk = I >> 5;
-  // 1. h of every pair: all loads in flight
+  // 1. h of every pair: all loads in flight (P I / 4 <= 64 kWindowWaves UG)
   const int n4 = P * I / 4;
-  float4 hv4[4];
+  float4 hv4[UG];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < UG; ++i) {
     const int c = tid + i * 64 * kWindowWaves;
     hv4[i] = (c < n4) ? reinterpret_cast<const float4*>(a.h)[c] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
   }
   // 3. h into LDS, flags cleared
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < UG; ++i) {
     const int c = tid + i * 64 * kWindowWaves;
     if (c < n4) reinterpret_cast<float4*>(sh_h)[c] = hv4[i];
   }
@@ -468,6 +470,24 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
     for (int j = 0; j < k; ++j) s = fmaf(a.gates[t * k + j], part[t * k + j][r], s);
     a.out[size_t(t) * a.H + blockIdx.x * 8 + r] = s_bad[t] ? NAN : s;
   }
+}
+
+// The window kernels take up to kWindowHLdsBytes of dynamic LDS; allow it
+// once per process (the attribute belongs to the function, on every device).
+hipError_t window_lds_attributes() {
+  static const hipError_t err = [] {
+    const void* fns[] = {reinterpret_cast<const void*>(&down_combine_window_q4_kernel<1>),
+                         reinterpret_cast<const void*>(&down_combine_window_q4_kernel<2>),
+                         reinterpret_cast<const void*>(&down_combine_window_q4_kernel<4>),
+                         reinterpret_cast<const void*>(&down_combine_window_q4_kernel<8>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               kWindowHLdsBytes);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
+  return err;
 }
 
 // One block per 8 output rows of all T tokens.  The block first copies h
@@ -691,6 +711,7 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
       const int ug = (a.P + kWindowWaves - 1) / kWindowWaves;                                          \
       const dim3 gw(g2.x), bw(64 * kWindowWaves);                                                      \
       const size_t lh = size_t(a.P) * a.I * 4;                                                         \
+      if (hipError_t ea = window_lds_attributes(); ea != hipSuccess) return ea;                        \
       if (ug <= 1) hipLaunchKernelGGL(down_combine_window_q4_kernel<1>, gw, bw, lh, s, a);             \
       else if (ug <= 2) hipLaunchKernelGGL(down_combine_window_q4_kernel<2>, gw, bw, lh, s, a);        \
       else if (ug <= 4) hipLaunchKernelGGL(down_combine_window_q4_kernel<4>, gw, bw, lh, s, a);        \
