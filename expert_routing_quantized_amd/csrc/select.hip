@@ -10,9 +10,11 @@
 // (Cauchy-Schwarz on the classical summation bounds of the router's binary32
 // chains and binary64 tail; see router.hip).
 //
-// Fast path: from the router's maxima of every 4 consecutive logits, the
-// k-th largest of 64 maxima over disjoint sets of experts is a lower bound
-// tau0 on the k-th largest z_hat, since k distinct experts reach it.  Only
+// Fast path: from the router's maxima of every 4 consecutive logits, any
+// value that k of 64 maxima over disjoint sets of experts reach is a lower
+// bound tau0 on the k-th largest z_hat, since k distinct experts reach it;
+// a 12-step bisection in value space finds one within 2^-12 of the range of
+// the 64 maxima (the k-th largest itself is not needed).  Only
 // the groups of 4 whose maximum reaches the candidate threshold are read
 // (about a dozen of 6,144), their candidates are compacted with a wave
 // ballot and ranked by one wave, and if
@@ -273,6 +275,12 @@ __device__ __forceinline__ double refine_logit(const SelectArgs& a, int t, int e
 }
 
 // ---------------------------------------------------------------- kernel
+constexpr int kTauSteps = 12;   // bisection steps for tau0
+
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
 // Smallest value th such that every v >= th can satisfy v + Bt + u |v| >= L
 // (rounded down: the test is conservative).
 __device__ double cand_threshold(double L, double Bt, double u) {
@@ -309,7 +317,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
   __shared__ int s_cnt, c_cnt, s_ntop, s_done, s_ng, s_nref;
   __shared__ int s_ref[64];                        // ranks refined by the cluster pass
   __shared__ double x_z[64];                       // their exact logits, by rank
-  __shared__ double s_tau, s_tau0;
+  __shared__ double s_tau, s_th0;
+  __shared__ float s_thf;                          // s_th0 in binary32, rounded down
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -329,7 +338,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
     s_ng = 0;
     s_nref = 0;
     s_tau = -INFINITY;
-    s_tau0 = -INFINITY;
+    s_th0 = -INFINITY;
+    s_thf = -INFINITY;
   }
 
   // 1. loads: the group maxima (rounded-up binary32 maxima of 4 logits) and ||x||^2.
@@ -356,9 +366,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
 
   // 2. tau0, a lower bound on the k-th largest z_hat: each thread's maximum
   //    over its groups, then in wave 0 the maximum over 8 threads per lane
-  //    (64 disjoint sets of experts), the k-th largest of those 64 by rank,
+  //    (64 disjoint sets of experts), a value lo that k of those 64 reach,
   //    one binary32 ulp down (the maxima were rounded up): k distinct experts
-  //    lie above it.
+  //    lie above it.  Wave 0 also turns it into the candidate threshold.
   float tm = -INFINITY;
   for (int ps = 0; ps < npass; ++ps) {
     if (ps > 0) load_pass(ps);
@@ -370,36 +380,67 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
   __syncthreads();
   if (wave == 0 && G >= k) {
     float lm = -INFINITY;
-    for (int w = 0; w < kWavesSel; ++w) lm = fmaxf(lm, s_tmax[w * 64 + lane]);
-    // k-th largest of the 64 lane values: bisection on the monotone key,
-    // one ballot per bit (largest K with #{key >= K} >= k)
-    const uint32_t key = f32_key(lm);
-    uint32_t K = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = K | (1u << bit);
-      if (__popcll(__ballot(key >= cand)) >= k) K = cand;
+    for (int w = 0; w < kWavesSel; ++w) lm = fmaxf(lm, s_tmax[w * 64 + lane]);   // never NaN
+    double tau0 = -INFINITY;
+    const bool fin = lm > -INFINITY && lm < INFINITY;
+    if (__popcll(__ballot(fin)) >= k && __ballot(lm == INFINITY) == 0ull) {
+      // bisection in value space; invariant: at least k lane values >= lo
+      float hi = wave_max(fin ? lm : -INFINITY);
+      float lo = -wave_max(fin ? -lm : -INFINITY);
+#pragma unroll
+      for (int it = 0; it < kTauSteps; ++it) {
+        const float mid = lo + 0.5f * (hi - lo);
+        if (__popcll(__ballot(lm >= mid)) >= k) lo = mid;
+        else hi = mid;
+      }
+      tau0 = (double)nextafterf(lo, -INFINITY);
+    } else {
+      // infinite maxima or fewer than k finite ones: the k-th largest by a
+      // bisection on the monotone key (largest K with #{key >= K} >= k)
+      const uint32_t key = f32_key(lm);
+      uint32_t K = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = K | (1u << bit);
+        if (__popcll(__ballot(key >= cand)) >= k) K = cand;
+      }
+      if (K != 0) tau0 = (double)nextafterf(key_f32(K), -INFINITY);
     }
-    if (lane == 0 && K != 0) s_tau0 = (double)nextafterf(key_f32(K), -INFINITY);
+    const double th = cand_threshold(lower(tau0), Bt, u);
+    float thf = (float)th;
+    if ((double)thf > th) thf = nextafterf(thf, -INFINITY);
+    if (lane == 0) {
+      s_th0 = th;
+      s_thf = thf;
+    }
   }
   __syncthreads();
 
-  // 3. groups whose maximum reaches theta0, then their experts with
-  //    z_hat >= theta0, compacted with one LDS atomic per wave and step.
-  const double th0 = cand_threshold(lower(s_tau0), Bt, u);
+  // 3. groups whose maximum reaches the threshold (compared in binary32
+  //    against th0 rounded down: a superset), listed with one LDS atomic per
+  //    wave; then their experts with z_hat >= th0, compacted the same way.
+  const double th0 = s_th0;
+  const float thf = s_thf;
   for (int ps = 0; ps < npass; ++ps) {
     if (ps > 0) load_pass(ps);
+    unsigned long long msk[GPT];
+    int tot = 0;
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
       const int g = ps * GPASS + i * kSelectThreads + tid;
-      const bool pred = g < G && (double)gv[i] >= th0;
-      const unsigned long long m = __ballot(pred);
-      if (m) {
-        const int leader = __ffsll((long long)m) - 1;
-        int base = 0;
-        if (lane == leader) base = atomicAdd(&s_ng, __popcll(m));
-        base = __shfl(base, leader);
-        const int p = base + __popcll(m & ((1ull << lane) - 1ull));
-        if (pred && p < kSelectMaxCand) s_glist[p] = g;
+      msk[i] = __ballot(g < G && gv[i] >= thf);
+      tot += __popcll(msk[i]);
+    }
+    if (tot != 0) {                                    // wave-uniform
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_ng, tot);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int i = 0; i < GPT; ++i) {
+        if ((msk[i] >> lane) & 1ull) {
+          const int p = base + lanes_below(msk[i]);
+          if (p < kSelectMaxCand) s_glist[p] = ps * GPASS + i * kSelectThreads + tid;
+        }
+        base += __popcll(msk[i]);
       }
     }
   }
