@@ -116,9 +116,7 @@ def counters_main(args, spec):
     out = torch.zeros((W + K, spec.H), dtype=torch.float32, device=dev)
     zbuf = torch.empty((spec.E,), dtype=torch.float64, device=dev)
     for t in range(W + K):
-        L = layers[t % n_rep]
-        L.route(X[t], 1, idx[t], gates[t], ws)
-        L.expert_decode(X[t], idx[t], gates[t], out[t], ws)
+        layers[t % n_rep].grouped_forward(X[t], 1, idx[t], gates[t], 0, out[t], ws)
     for t in range(W, W + K):
         layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
     src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
@@ -421,9 +419,9 @@ def main():
     zbuf = torch.empty((spec.E,), dtype=torch.float64, device=dev)
 
     def token(t):
-        L = layers[t % n_rep]
-        L.route(X[t], 1, idx[t], gates[t], ws)
-        L.expert_decode(X[t], idx[t], gates[t], out[t], ws)
+        # one moe_grouped_forward call per token (at T = 1 with 4-bit experts
+        # the selection runs fused with gate/up)
+        layers[t % n_rep].grouped_forward(X[t], 1, idx[t], gates[t], 0, out[t], ws)
 
     # eager pass over the warm-up tokens (also loads the kernels)
     for t in range(W):

@@ -23,6 +23,7 @@
 // down:    8 lanes per output row, one wave per distinct expert, per-pair
 // partials in LDS, each token summed over its pairs in selection order.
 #include "moe_internal.h"
+#include "select_block.h"
 
 namespace moe {
 
@@ -205,6 +206,113 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
       const int i = i0 + r;
       if (lane == 0 && i < a.I) a.h[size_t(q) * a.I + i] = valid ? silu_f(av) * uv : NAN;
     }
+  }
+}
+
+// ------------------------------------------------------ decode: select + gate/up
+// Batch-1 decode with 4-bit experts: the selection and the gate/up
+// projections in one launch.  Every block runs the certified selection on
+// its own (select_block: the order depends only on the logits and the
+// expert indices, so all blocks reach the same one) and then computes
+// kDecodeRowsPerBlock intermediate rows of one selected expert, with the
+// same per-row arithmetic as gateup_q4_kernel.  There is then no launch gap
+// and no dependent index load between the selection and the weight stream;
+// the redundant selections read the group maxima from L2.  Block 0
+// publishes idx and gates for the down projection.
+constexpr int kDecodeRowsPerWave = 2;
+constexpr int kDecodeRowsPerBlock = kDecodeRowsPerWave * (kSelectThreads / 64);
+
+template <int ACT, int MB>
+__global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(SelectArgs sa, PairArgs a) {
+  constexpr int RPW = kDecodeRowsPerWave;
+  constexpr int CK = XStage<ACT>::kChunks, PK = XStage<ACT>::kPitch;
+  __shared__ uint4 sx[(kMaxH / 32) * PK];
+  __shared__ int32_t s_idx[kMaxK];
+  __shared__ float s_gate[kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = a.H >> 5;
+  {   // the token's x into LDS (ordered before its reads by the selection's barriers)
+    const int nc = nblk * CK;
+    const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+    constexpr int NU = (64 * MB * CK + kSelectThreads - 1) / kSelectThreads;
+    uint4 xr[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) xr[u] = xs[min(tid + kSelectThreads * u, nc - 1)];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = tid + kSelectThreads * u;
+      if (c < nc) sx[(c / CK) * PK + c % CK] = xr[u];
+    }
+  }
+  select_block<ACT>(sa, 0, s_idx, s_gate);
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < a.k) {
+    sa.idx[tid] = s_idx[tid];
+    sa.gates[tid] = s_gate[tid];
+  }
+  const int bpp = (a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock;   // blocks per expert
+  const int j = blockIdx.x / bpp;
+  const int i0 = (blockIdx.x - j * bpp) * kDecodeRowsPerBlock + wave * RPW;
+  int e = s_idx[j];
+  const bool valid = e >= 0 && e < a.E;
+  e = valid ? e : 0;                                   // addresses stay in range; h becomes NaN
+  const size_t rowb = size_t(a.H) / 2;
+  uint4 wg[RPW][MB], wu[RPW][MB];
+  float dg[RPW][MB], du[RPW][MB];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int i = min(i0 + r, a.I - 1);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const int b = min(m * 64 + lane, nblk - 1);
+      const size_t row = size_t(e) * a.I + i;
+      wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * rowb + b * 16);
+      wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * rowb + b * 16);
+      dg[r][m] = f16_to_f32(a.sg[row * nblk + b]);
+      du[r][m] = f16_to_f32(a.su[row * nblk + b]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+      if (!(i0 + r < a.I && m * 64 + lane < nblk)) dg[r][m] = du[r][m] = 0.f;
+  float xv[MB][32];
+  float xsum[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    const int b = m * 64 + lane;
+    xsum[m] = 0.f;
+    Chunk<ACT> ch[4];
+    const uint4* sb = sx + min(b, nblk - 1) * PK;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (ACT == MOE_BF16) {
+        ch[c].v = sb[c];
+      } else {
+        const uint4 p0 = sb[2 * c], p1 = sb[2 * c + 1];
+        ch[c].a = make_float4(__uint_as_float(p0.x), __uint_as_float(p0.y), __uint_as_float(p0.z), __uint_as_float(p0.w));
+        ch[c].b = make_float4(__uint_as_float(p1.x), __uint_as_float(p1.y), __uint_as_float(p1.z), __uint_as_float(p1.w));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = (b < nblk) ? ch[c].get(i) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) xsum[m] += xv[m][i];
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    float pa = 0.f, pu = 0.f;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      pa = fmaf(dg[r][m], q4_block_dot(wg[r][m], xv[m]) - 8.f * xsum[m], pa);
+      pu = fmaf(du[r][m], q4_block_dot(wu[r][m], xv[m]) - 8.f * xsum[m], pu);
+    }
+    const float av = wave_sum(pa), uv = wave_sum(pu);
+    const int i = i0 + r;
+    if (lane == 0 && i < a.I) a.h[size_t(j) * a.I + i] = valid ? silu_f(av) * uv : NAN;
   }
 }
 
@@ -633,8 +741,8 @@ bool pair_path_fits(const Layer& L, int T) { return T >= 1 && T * L.d.top_k <= k
 // once per call.
 constexpr int kIndependentMaxT = 8;
 
-hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32_t* idx,
-                               const float* gates, float* out, float* h, hipStream_t s) {
+static PairArgs pair_args(const Layer& L, const void* x, int T, const int32_t* idx,
+                          const float* gates, float* out, float* h) {
   PairArgs a;
   a.x = x;
   a.idx = idx;
@@ -654,6 +762,12 @@ hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32
   a.T = T;
   a.P = T * a.k;
   a.dev_flag = L.dev_flag;
+  return a;
+}
+
+hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32_t* idx,
+                               const float* gates, float* out, float* h, hipStream_t s) {
+  const PairArgs a = pair_args(L, x, T, idx, gates, out, h);
   if (a.P > kMaxPairs) return hipErrorInvalidValue;
   if (T <= kIndependentMaxT) return launch_pairs<true>(a, L.d.act_dtype, L.d.expert_dtype, s);
   return launch_pairs<false>(a, L.d.act_dtype, L.d.expert_dtype, s);
@@ -732,6 +846,34 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
   }
 #undef MOE_DOWN
 #undef MOE_DOWN_SPL
+  return hipGetLastError();
+}
+
+bool decode_fused_fits(const Layer& L) {
+  return L.d.expert_dtype == MOE_Q4B32 && L.d.top_k <= kMaxK && (L.d.hidden / 32 + 63) / 64 <= 4;
+}
+
+hipError_t launch_decode_q4(const Layer& L, const void* x, const double* z, const float* gmax,
+                            const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
+                            float* out, float* h, hipStream_t s) {
+  if (!decode_fused_fits(L)) return hipErrorInvalidValue;
+  const SelectArgs sa = make_select_args(L, x, z, gmax, xnorm, idx, gates, rb);
+  const PairArgs a = pair_args(L, x, 1, idx, gates, out, h);
+  const int mb = (a.H / 32 + 63) / 64;
+  const dim3 g1(a.k * ((a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock));
+#define MOE_DEC_Q4(M)                                                                             \
+  if (mb <= M) {                                                                                  \
+    if (L.d.act_dtype == MOE_BF16)                                                                \
+      hipLaunchKernelGGL((select_gateup_q4_kernel<MOE_BF16, M>), g1, dim3(kSelectThreads), 0, s, sa, a); \
+    else                                                                                          \
+      hipLaunchKernelGGL((select_gateup_q4_kernel<MOE_F32, M>), g1, dim3(kSelectThreads), 0, s, sa, a);  \
+  } else
+  MOE_DEC_Q4(1) MOE_DEC_Q4(2) MOE_DEC_Q4(4) return hipErrorInvalidValue;
+#undef MOE_DEC_Q4
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nw = a.P < 16 ? a.P : 16;
+  hipLaunchKernelGGL(down_combine_single_kernel<MOE_Q4B32>, dim3((a.H + 7) / 8, 1), dim3(64 * nw), 0, s, a);
   return hipGetLastError();
 }
 

@@ -318,6 +318,18 @@ moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
   char* w = static_cast<char*>(ws);
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
   float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
+  if (flags == MOE_ROUTE_INTERNAL && T == 1 && !moe::router_uses_mfma(L, 1) && moe::decode_fused_fits(L)) {
+    // batch-1 4-bit decode: router, then the selection fused with gate/up
+    double* z = reinterpret_cast<double*>(w + W.z);
+    float* gmax = reinterpret_cast<float*>(w + W.gmax);
+    double* xnorm = reinterpret_cast<double*>(w + W.xnorm);
+    hipError_t e = moe::launch_router(L, x, 1, z, gmax, xnorm, s);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    e = moe::launch_decode_q4(L, x, z, gmax, xnorm, moe::router_bound(L, 1), ri, rg, out,
+                              reinterpret_cast<float*>(w + W.h), s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return ok();
+  }
   if (flags == MOE_ROUTE_INTERNAL) {
     if (moe_status st = route_impl(L, x, T, ri, rg, w, W, s)) return st;
   }

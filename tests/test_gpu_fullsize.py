@@ -114,14 +114,38 @@ def test_decode_q4_decode_parity():
 
 
 def test_decode_q4_grouped_single_token_path():
-    """moe_grouped_forward at T = 1 (the fused decode entry) matches too."""
+    """moe_grouped_forward at T = 1 (selection fused with gate/up) against
+    the oracle on 16 tokens, and bitwise against moe_route +
+    moe_expert_decode on all 1000 tokens of the stream (including the ones
+    whose order needs exact refinement)."""
+    import torch
     import synth.device as SD
     layer, spec = layer_for("decode_q4", 1)
     L = oracle_for(spec)
-    x = SD.device_tokens(spec, 7, 1)
-    idx, gates, out = G.run_grouped(layer, x)
-    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 7, 1)
+    first = 400
+    x = SD.device_tokens(spec, first, 16)
+    rows = [G.run_grouped(layer, x[t:t + 1]) for t in range(16)]
+    idx = np.concatenate([r[0] for r in rows])
+    gates = np.concatenate([r[1] for r in rows])
+    out = np.concatenate([r[2] for r in rows])
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, first, 16)
     G.compare(idx, gates, out, o_idx, o_g, o_out, "decode_q4 grouped T=1")
+    n = 1000
+    X = SD.device_tokens(spec, 0, n)
+    ws = layer.workspace(1)
+    fi = torch.empty((n, spec.k), dtype=torch.int32, device=X.device)
+    fg = torch.empty((n, spec.k), dtype=torch.float32, device=X.device)
+    fo = torch.empty((n, spec.H), dtype=torch.float32, device=X.device)
+    si, sg, so = torch.empty_like(fi), torch.empty_like(fg), torch.empty_like(fo)
+    for t in range(n):
+        layer.grouped_forward(X[t], 1, fi[t], fg[t], 0, fo[t], ws)
+        layer.route(X[t], 1, si[t], sg[t], ws)
+        layer.expert_decode(X[t], si[t], sg[t], so[t], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fi, si)
+    assert torch.equal(fg.view(torch.int32), sg.view(torch.int32))
+    assert torch.equal(fo.view(torch.int32), so.view(torch.int32))
+    assert layer.device_error() == 0
 
 
 def test_verify_q4_verify_steps_parity():

@@ -124,6 +124,51 @@ def test_grouped_parity_small(name, T):
     assert layer.device_error() == 0
 
 
+# Batch-1 4-bit decode through moe_grouped_forward: the selection runs inside
+# every gate/up block.  fp32 activations, H = 4096 (two quant blocks per lane)
+# and the odd shapes of the small layers above.
+FUSED_SPECS = {
+    "q4_f32x": synth.small_spec(H=256, E=150, k=6, I=96, act=synth.DT_F32, expert=synth.DT_Q4,
+                                bias_alpha=0.37, weight_seed=81, token_seed=82, name="q4_f32x"),
+    "q4_h4096": synth.small_spec(H=4096, E=70, k=8, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                                 bias_alpha=0.37, weight_seed=83, token_seed=84, name="q4_h4096"),
+}
+SMALL.update(FUSED_SPECS)
+
+
+@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "q4_f32x", "q4_h4096"])
+@pytest.mark.parametrize("exact", [False, True])
+def test_fused_decode_single_token(name, exact):
+    """moe_grouped_forward at T = 1 against the oracle, and bitwise against
+    moe_route + moe_expert_decode on the same tokens one at a time (with
+    exact refinement forced, every block runs the exact path)."""
+    import torch
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_FORCE_EXACT_REFINE
+    spec, dl, L = setup(name)
+    G.note("fused decode", name, "exact" if exact else "")
+    n = 8 if exact else 24
+    layer = SD.make_layer(dl, max_tokens=n, flags=MOE_LAYER_FORCE_EXACT_REFINE if exact else 0)
+    x = SD.device_tokens(spec, 300, n)
+    rows = [G.run_grouped(layer, x[t:t + 1]) for t in range(n)]
+    idx = np.concatenate([r[0] for r in rows])
+    gates = np.concatenate([r[1] for r in rows])
+    out = np.concatenate([r[2] for r in rows])
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 300, n)
+    r = G.compare(idx, gates, out, o_idx, o_g, o_out, f"fused {name}")
+    # the reference runs the same router kernel (T = 1): gates are computed
+    # from the router's logits, which differ in the last bits between kernels
+    srows = [G.run_route_decode(layer, x[t:t + 1]) for t in range(n)]
+    s_idx = np.concatenate([r[0] for r in srows])
+    s_g = np.concatenate([r[1] for r in srows])
+    s_out = np.concatenate([r[2] for r in srows])
+    assert np.array_equal(idx, s_idx)
+    assert np.array_equal(gates.view(np.uint32), s_g.view(np.uint32))
+    assert np.array_equal(out.view(np.uint32), s_out.view(np.uint32))
+    print(f"fused {name}: rel L2 max {r.max():.2e}")
+    assert layer.device_error() == 0
+
+
 # Grouped MFMA path (bf16 activations and experts, T >= 16): few experts and
 # many tokens, so segments span several 32-row tiles with a ragged last one;
 # I = 96 and H = 160 leave partial 128-wide channel / output blocks.
