@@ -69,6 +69,23 @@ TRAFFIC_SOURCES = ["expert_routing_quantized_amd/csrc/router.hip", "expert_routi
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
+def median_replay_ms(graph, stream, reps=5):
+    """Median over `reps` replays of a captured graph, each bracketed by HIP
+    events on the capture stream and a device synchronisation."""
+    import statistics
+    import torch
+    times = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return statistics.median(times)
+
+
 def kernel_source_hash() -> str:
     """sha256 over the sources the router GEMV is compiled from."""
     import hashlib
@@ -257,12 +274,7 @@ def grouped_main(args, spec):
     torch.cuda.synchronize()
 
     def timed(name):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        graphs[name].replay()
-        e1.record(s)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
+        return median_replay_ms(graphs[name], s)
 
     with torch.cuda.stream(s):
         graphs["warm"].replay()
@@ -358,13 +370,8 @@ def sweep_main(args):
             torch.cuda.synchronize()
             with torch.cuda.stream(s):
                 g.replay()
-                torch.cuda.synchronize()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(s)
-                g.replay()
-                e1.record(s)
-                torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+                ms = median_replay_ms(g, s)
+            us = ms * 1e3 / reps
             rows.append({"layer": name.split("_")[1], "T": T, "us_per_call": us,
                          "us_per_token": us / T, "tokens_per_s": T / us * 1e6,
                          "device_errors": layer.device_error()})
@@ -446,21 +453,11 @@ def main():
     with torch.cuda.stream(s):
         g_warm.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        g_main.replay()
-        e1.record(s)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        ms = median_replay_ms(g_main, s)
         # the dominant kernel alone, same launch configuration
         g_router.replay()
         torch.cuda.synchronize()
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record(s)
-        g_router.replay()
-        r1.record(s)
-        torch.cuda.synchronize()
-        ms_router = r0.elapsed_time(r1)
+        ms_router = median_replay_ms(g_router, s)
     errs = [L.device_error() for L in layers]
 
     per_tok_s = ms / 1e3 / K

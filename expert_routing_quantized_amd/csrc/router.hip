@@ -10,8 +10,9 @@
 // e (4 KB for H = 2048 in bf16).  One wave owns one row: chunk c of 8
 // elements (16 B in bf16) goes to lane c % 64, so each of the wave's loads
 // is 1 KB contiguous, and all of the row's loads are issued at once
-// (non-temporal: the router is streamed once per token).  Each lane keeps
-// the same chunks of x in registers.  Blocks of 4 waves, one block per 4
+// (non-temporal: the router is streamed once per token).  For one token x
+// is staged once per block in LDS (its loads issued before the row's) and
+// each lane takes the same chunks of it.  Blocks of 4 waves, one block per 4
 // experts: a measured sweep of launch shapes on gfx950 put this shape at
 // the streaming-read ceiling (about 6.5 TB/s), ahead of fewer, longer-lived
 // waves and of larger blocks.  Each block also writes the maximum of its 4
@@ -51,21 +52,32 @@ void router_kernel(
   const int nt = min(NT, T - t0);
   const int G4 = (E + kRouterWaves - 1) / kRouterWaves;
 
-  // The row's chunks first (longest latency), then x.  Chunk indices past
-  // the row are clamped to its last chunk and the values zeroed afterwards,
-  // so every load is issued unconditionally (no branch between loads).
+  // One token: the block's threads first load x (16 bytes each) for the
+  // block's LDS copy, so each wave reads x from LDS instead of all of it
+  // through its own loads (as many bytes as its router row); then every
+  // wave's row chunks (longest latency).  Chunk indices past the row are
+  // clamped to its last chunk and masked afterwards, so every load is
+  // issued unconditionally (no branch between loads).
+  constexpr int kXPer = (NT == 1) ? ((ACT == MOE_F32 ? 2 : 1) * CPL + 3) / 4 : 1;   // x pieces per thread
+  const int n16 = (ACT == MOE_F32 ? 2 : 1) * nch;                                       // 16-byte pieces of x
+  uint4 xq[kXPer];
+  if constexpr (NT == 1) {
+    const uint4* x16 = reinterpret_cast<const uint4*>(x) + size_t(t0) * n16;
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) xq[u] = x16[min((int)threadIdx.x + kRouterWaves * 64 * u, n16 - 1)];
+  }
   Chunk<ACT> r[CPL];
 #pragma unroll
   for (int s = 0; s < CPL; ++s) {
     const int c = min(s * 64 + lane, nch - 1);
     r[s].load_stream(R, size_t(e) * H + c * 8);
   }
-  const float b = (bias != nullptr) ? bias[e] : 0.f;
-#pragma unroll
-  for (int s = 0; s < CPL; ++s)
-    if (s * 64 + lane >= nch) r[s].zero();
   constexpr bool kPacked = (ACT == MOE_BF16) && (NT > 1);
   if constexpr (kPacked) {
+    const float b = (bias != nullptr) ? bias[e] : 0.f;
+#pragma unroll
+    for (int s = 0; s < CPL; ++s)
+      if (s * 64 + lane >= nch) r[s].zero();
     uint4 xp[NT][CPL];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -122,19 +134,57 @@ void router_kernel(
       }
     }
   } else {
-    // one token: binary32 chains of 8 exact products, then binary64
+    // one token: binary32 chains of 8 exact products, then binary64.  x
+    // (before the row) and the bias (right behind it) are loaded with no
+    // branch or wait in between (a bias load under a branch made every wave
+    // wait for its row before it even asked for x); chunks past the row end
+    // (clamped loads) are masked by selects on both operands, so they add
+    // exact zeros.
     static_assert(NT == 1, "unpacked path handles one token per block row");
+    extern __shared__ uint4 sx[];                      // x of the token, n16 pieces + a spare
+    const float* bp = (bias != nullptr) ? bias + e : reinterpret_cast<const float*>(x);
+    const float bl = *bp;                              // unconditional; unused without a bias
+    const float b = (bias != nullptr) ? bl : 0.f;
+    // unconditional stores (pieces past x go to a spare slot that is never
+    // read): a store under a branch let the compiler sink the x load behind
+    // the row loads
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) {
+      const int c = threadIdx.x + kRouterWaves * 64 * u;
+      sx[c < n16 ? c : n16] = xq[u];
+    }
+    __syncthreads();
     Chunk<ACT> xc[CPL];
 #pragma unroll
-    for (int s = 0; s < CPL; ++s) xc[s].load(x, size_t(t0) * H + min(s * 64 + lane, nch - 1) * 8);
+    for (int s = 0; s < CPL; ++s) {
+      const int c = min(s * 64 + lane, nch - 1);
+      if constexpr (ACT == MOE_F32) {
+        const uint4 p0 = sx[2 * c], p1 = sx[2 * c + 1];
+        xc[s].a = make_float4(__uint_as_float(p0.x), __uint_as_float(p0.y), __uint_as_float(p0.z), __uint_as_float(p0.w));
+        xc[s].b = make_float4(__uint_as_float(p1.x), __uint_as_float(p1.y), __uint_as_float(p1.z), __uint_as_float(p1.w));
+      } else {
+        xc[s].v = sx[c];
+      }
+    }
     auto xf_get = [](const Chunk<ACT>& c, int i, bool in) { return in ? c.get(i) : 0.f; };
+    // chunks past the row end: both operands zeroed by word selects
+    auto masked = [](Chunk<ACT> c, bool in) {
+      if constexpr (ACT == MOE_BF16) {
+        c.v = make_uint4(in ? c.v.x : 0u, in ? c.v.y : 0u, in ? c.v.z : 0u, in ? c.v.w : 0u);
+      } else {
+        c.a = make_float4(in ? c.a.x : 0.f, in ? c.a.y : 0.f, in ? c.a.z : 0.f, in ? c.a.w : 0.f);
+        c.b = make_float4(in ? c.b.x : 0.f, in ? c.b.y : 0.f, in ? c.b.z : 0.f, in ? c.b.w : 0.f);
+      }
+      return c;
+    };
     double acc[CPL];
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
       const bool in = s * 64 + lane < nch;
+      const Chunk<ACT> xm = masked(xc[s], in), rm = masked(r[s], in);
       float c = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c = fmaf(in ? xc[s].get(i) : 0.f, r[s].get(i), c);
+      for (int i = 0; i < 8; ++i) c = fmaf(xm.get(i), rm.get(i), c);
       acc[s] = (double)c;
     }
 #pragma unroll
@@ -186,7 +236,8 @@ static hipError_t launch_cpl(const Layer& L, const void* x, int T, double* z, fl
   if (cpl <= C) {                                                                             \
     constexpr int NTX = (ACT == MOE_BF16 && NT > 1) ? ((NT * C > 32) ? 32 / C : NT) : 1;    \
     grid.y = (T + NTX - 1) / NTX;                                                             \
-    hipLaunchKernelGGL((router_kernel<ACT, C, NTX>), grid, dim3(kRouterWaves * 64), 0, s,     \
+    const size_t lds = (NTX == 1) ? (size_t(H / 8) * (ACT == MOE_F32 ? 2 : 1) + 1) * 16 : 0;  \
+    hipLaunchKernelGGL((router_kernel<ACT, C, NTX>), grid, dim3(kRouterWaves * 64), lds, s,   \
                        L.router_eh, x, L.d.router_bias, H, E, T, z, gmax, xnorm, L.dev_flag); \
     return hipGetLastError();                                                                 \
   }
