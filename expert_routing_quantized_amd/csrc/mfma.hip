@@ -371,8 +371,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kSkQ = 16;     // MFMAs (of K = 32) per wave per batch
 
 __device__ __forceinline__ void skinny_epilogue(double (*red)[16][17], const uint16_t* X,
-                                                const float* bias, int T, int H, int E, int n0,
+                                                float bias_v, int T, int H, int E, int n0,
                                                 double* z, float* gmax, double* xnorm, int* dev_flag);
+// Bias of expert e (clamped: lanes past E are never stored), loaded at the
+// start of the kernel; the pointer is never null (the layer passes zeros),
+// because a load under a null-pointer test in the epilogue cost every block
+// one more memory round trip at its end.
+__device__ __forceinline__ float skinny_bias(const float* bias, int e, int E) {
+  return bias[min(e, E - 1)];
+}
 
 bool router_uses_skinny(const Layer& L, int T) {
   return L.d.act_dtype == MOE_BF16 && T >= 2 && T < 16 && (L.d.hidden % 32) == 0;
@@ -389,11 +396,11 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
   const int qpw = (nq + 3) / 4;
   const int q0 = wave * qpw, q1 = min(nq, q0 + qpw);
   const int tr = lane & 15;
-  const bool xin = tr < T;
   // operand layout of 16x16x32: lane l holds row / column l % 16 and the 8
   // consecutive K elements starting at 8 * (l / 16)
   const uint16_t* pb = R + size_t(min(n0 + tr, E - 1)) * H + 8 * (lane >> 4);
   const uint16_t* pa = X + size_t(min(tr, T - 1)) * H + 8 * (lane >> 4);
+  const float bias_v = skinny_bias(bias, n0 + (tid & 15), E);
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   for (int qb = q0; qb < q1; qb += kSkQ) {
     uint4 b[kSkQ], xa[kSkQ];
@@ -404,9 +411,8 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < kSkQ; ++i) {
       if (qb + i < q1) {                                   // wave-uniform
-        const uint4 av = xin ? xa[i] : make_uint4(0u, 0u, 0u, 0u);
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+        f32x4_t d = {0.f, 0.f, 0.f, 0.f};                   // rows past T: token T-1 again, never stored
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa[i]),
                                                      __builtin_bit_cast(bf16x8_t, b[i]), d, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[r] += (double)d[r];
@@ -417,19 +423,19 @@ __global__ __launch_bounds__(256) void router_skinny_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * (lane >> 4) + r][lane & 15] = acc[r];
   __syncthreads();
-  skinny_epilogue(red, X, bias, T, H, E, n0, z, gmax, xnorm, dev_flag);
+  skinny_epilogue(red, X, bias_v, T, H, E, n0, z, gmax, xnorm, dev_flag);
 }
 
 // The shared epilogue of both few-token kernels: sum the 4 quarters in
 // order, add the bias, write logits and 4-expert maxima, flag non-finite
 // logits; block 0 also writes ||x_t||^2.
 __device__ __forceinline__ void skinny_epilogue(double (*red)[16][17], const uint16_t* X,
-                                                const float* bias, int T, int H, int E, int n0,
+                                                float bias_v, int T, int H, int E, int n0,
                                                 double* z, float* gmax, double* xnorm, int* dev_flag) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = tid >> 4, el = tid & 15, e = n0 + el;
   double v = ((red[0][t][el] + red[1][t][el]) + red[2][t][el]) + red[3][t][el];
-  v += (e < E && bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
+  v += (double)bias_v;
   const bool live = e < E && t < T;
   if (live) z[size_t(t) * E + e] = v;
   if (live && !isfinite(v)) atomicOr(dev_flag, kDevNonFinite);
@@ -473,7 +479,6 @@ __global__ __launch_bounds__(256) void router_skinny_lds_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
   const int tr = lane & 15, g = lane >> 4;
-  const bool xin = tr < T;
   const int kw = wave * (HH / 4);
   uint4 b[NP][NI];
 #pragma unroll
@@ -481,14 +486,15 @@ __global__ __launch_bounds__(256) void router_skinny_lds_kernel(
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       b[p][i] = load_nt(R + size_t(min(n0 + i * RPI + lane / LPR, E - 1)) * HH + kw + p * PE + 8 * (lane % LPR));
+  const float bias_v = skinny_bias(bias, n0 + (tid & 15), E);
   const uint16_t* pa = X + size_t(min(tr, T - 1)) * HH + kw;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     uint4 xa[QP];
 #pragma unroll
-    for (int q = 0; q < QP; ++q)
-      xa[q] = xin ? *reinterpret_cast<const uint4*>(pa + p * PE + 32 * q + 8 * g) : make_uint4(0u, 0u, 0u, 0u);
+    for (int q = 0; q < QP; ++q)   // rows past T repeat token T-1; their outputs are never stored
+      xa[q] = *reinterpret_cast<const uint4*>(pa + p * PE + 32 * q + 8 * g);
     // the wave's LDS buffer is reused by the next phase (wave-level syncs
     // order the lanes' accesses; no workgroup barrier is needed)
 #pragma unroll
@@ -509,7 +515,7 @@ __global__ __launch_bounds__(256) void router_skinny_lds_kernel(
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * g + r][tr] = acc[r];
   __syncthreads();
-  skinny_epilogue(red, X, bias, T, HH, E, n0, z, gmax, xnorm, dev_flag);
+  skinny_epilogue(red, X, bias_v, T, HH, E, n0, z, gmax, xnorm, dev_flag);
 }
 
 hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z, float* gmax,
@@ -520,7 +526,7 @@ hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z,
   const dim3 grid((E + 15) / 16);
 #define MOE_SKINNY_LDS(HV)                                                                        \
   if (H == HV) {                                                                                  \
-    hipLaunchKernelGGL(router_skinny_lds_kernel<HV>, grid, dim3(256), 0, s, xb, rb, L.d.router_bias, \
+    hipLaunchKernelGGL(router_skinny_lds_kernel<HV>, grid, dim3(256), 0, s, xb, rb, router_bias_or_zero(L), \
                        T, E, z, gmax, xnorm, L.dev_flag);                                         \
     return hipGetLastError();                                                                     \
   }
@@ -529,7 +535,7 @@ hipError_t launch_router_skinny(const Layer& L, const void* x, int T, double* z,
   MOE_SKINNY_LDS(2048)
   MOE_SKINNY_LDS(4096)
 #undef MOE_SKINNY_LDS
-  hipLaunchKernelGGL(router_skinny_kernel, grid, dim3(256), 0, s, xb, rb, L.d.router_bias, T, H, E, z,
+  hipLaunchKernelGGL(router_skinny_kernel, grid, dim3(256), 0, s, xb, rb, router_bias_or_zero(L), T, H, E, z,
                      gmax, xnorm, L.dev_flag);
   return hipGetLastError();
 }

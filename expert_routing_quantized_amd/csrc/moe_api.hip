@@ -179,6 +179,7 @@ static void release_layer(Layer& L) {
   if (L.router_copy) (void)hipFree(L.router_copy);
   if (L.norms) (void)hipFree(L.norms);
   if (L.dev_flag) (void)hipFree(L.dev_flag);
+  if (L.zero_bias) (void)hipFree(L.zero_bias);
 }
 
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out) {
@@ -204,6 +205,12 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
     return cleanup(hip_fail(e, "hipMalloc(flag)"));
   if ((e = hipMemsetAsync(L.dev_flag, 0, sizeof(int), s)) != hipSuccess)
     return cleanup(hip_fail(e, "hipMemsetAsync(flag)"));
+  if (!desc->router_bias) {
+    if ((e = hipMalloc(&L.zero_bias, E * sizeof(float))) != hipSuccess)
+      return cleanup(hip_fail(e, "hipMalloc(zero bias)"));
+    if ((e = hipMemsetAsync(L.zero_bias, 0, E * sizeof(float), s)) != hipSuccess)
+      return cleanup(hip_fail(e, "hipMemsetAsync(zero bias)"));
+  }
   if (desc->router_layout == MOE_ROUTER_HE) {
     if ((e = hipMalloc(&L.router_copy, E * H * act_bytes(desc->act_dtype))) != hipSuccess)
       return cleanup(hip_fail(e, "hipMalloc(router copy)"));

@@ -32,9 +32,16 @@ struct Layer {
   void* router_copy;        // owned copy when the caller's layout is [H][E]
   float* norms;             // owned: [E] router row 2-norms (rounded up), then [1] max
   int* dev_flag;            // owned: sticky device fault word
+  float* zero_bias;         // owned: [E] zeros when the caller gives no bias, else null
   double norm_max;          // host copy of max_e ||R_e||_2 (rounded up)
   int device;
 };
+
+// The router bias as the GEMV and few-token router kernels read it: never
+// null (zeros when the caller gives none), so their loads need no branch.
+inline const float* router_bias_or_zero(const Layer& L) {
+  return L.d.router_bias != nullptr ? L.d.router_bias : L.zero_bias;
+}
 
 // Byte offsets of the per-call scratch regions inside the caller's workspace.
 struct Workspace {

@@ -136,15 +136,13 @@ void router_kernel(
   } else {
     // one token: binary32 chains of 8 exact products, then binary64.  x
     // (before the row) and the bias (right behind it) are loaded with no
-    // branch or wait in between (a bias load under a branch made every wave
-    // wait for its row before it even asked for x); chunks past the row end
-    // (clamped loads) are masked by selects on both operands, so they add
-    // exact zeros.
+    // branch or wait in between (a bias load under a null-pointer branch
+    // made every wave wait for its row before it even asked for x, so the
+    // layer passes zeros instead of null); chunks past the row end (clamped
+    // loads) are masked by selects on both operands, so they add exact zeros.
     static_assert(NT == 1, "unpacked path handles one token per block row");
     extern __shared__ uint4 sx[];                      // x of the token, n16 pieces + a spare
-    const float* bp = (bias != nullptr) ? bias + e : reinterpret_cast<const float*>(x);
-    const float bl = *bp;                              // unconditional; unused without a bias
-    const float b = (bias != nullptr) ? bl : 0.f;
+    const float b = bias[e];                           // never null on this path (zeros without a bias)
     // unconditional stores (pieces past x go to a spare slot that is never
     // read): a store under a branch let the compiler sink the x load behind
     // the row loads
@@ -238,7 +236,7 @@ static hipError_t launch_cpl(const Layer& L, const void* x, int T, double* z, fl
     grid.y = (T + NTX - 1) / NTX;                                                             \
     const size_t lds = (NTX == 1) ? (size_t(H / 8) * (ACT == MOE_F32 ? 2 : 1) + 1) * 16 : 0;  \
     hipLaunchKernelGGL((router_kernel<ACT, C, NTX>), grid, dim3(kRouterWaves * 64), lds, s,   \
-                       L.router_eh, x, L.d.router_bias, H, E, T, z, gmax, xnorm, L.dev_flag); \
+                       L.router_eh, x, router_bias_or_zero(L), H, E, T, z, gmax, xnorm, L.dev_flag); \
     return hipGetLastError();                                                                 \
   }
   MOE_ROUTER_CASE(1)
