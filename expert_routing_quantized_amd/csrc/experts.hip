@@ -210,15 +210,17 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
 }
 
 // ------------------------------------------------------ decode: select + gate/up
-// Batch-1 decode with 4-bit experts: the selection and the gate/up
-// projections in one launch.  Every block runs the certified selection on
-// its own (select_block: the order depends only on the logits and the
-// expert indices, so all blocks reach the same one) and then computes
-// kDecodeRowsPerBlock intermediate rows of one selected expert, with the
-// same per-row arithmetic as gateup_q4_kernel.  There is then no launch gap
-// and no dependent index load between the selection and the weight stream;
-// the redundant selections read the group maxima from L2.  Block 0
-// publishes idx and gates for the down projection.
+// Decode and short verify windows (T <= 8 tokens) with 4-bit experts: the
+// selection and the gate/up projections in one launch.  Block b serves pair
+// p = b / bpp (token t = p / k, rank j = p % k): it runs the certified
+// selection of token t on its own (select_block: the order depends only on
+// the logits and the expert indices, so every block of the token reaches
+// the same one) and then computes kDecodeRowsPerBlock intermediate rows of
+// the token's rank-j expert, with the same per-row arithmetic as
+// gateup_q4_kernel.  There is then no launch gap and no dependent index
+// load between the selection and the weight stream; the redundant
+// selections read the group maxima from L2.  The first block of each token
+// publishes its idx and gates for the down projection.
 constexpr int kDecodeRowsPerWave = 2;
 constexpr int kDecodeRowsPerBlock = kDecodeRowsPerWave * (kSelectThreads / 64);
 
@@ -231,9 +233,11 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(Select
   __shared__ float s_gate[kMaxK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = a.H >> 5;
+  const int bpp = (a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock;   // blocks per pair
+  const int p = blockIdx.x / bpp, t = p / a.k, j = p - t * a.k;
   {   // the token's x into LDS (ordered before its reads by the selection's barriers)
     const int nc = nblk * CK;
-    const uint4* xs = reinterpret_cast<const uint4*>(a.x);
+    const uint4* xs = reinterpret_cast<const uint4*>(a.x) + size_t(t) * nc;
     constexpr int NU = (64 * MB * CK + kSelectThreads - 1) / kSelectThreads;
     uint4 xr[NU];
 #pragma unroll
@@ -244,15 +248,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(Select
       if (c < nc) sx[(c / CK) * PK + c % CK] = xr[u];
     }
   }
-  select_block<ACT>(sa, 0, s_idx, s_gate);
+  select_block<ACT>(sa, t, s_idx, s_gate);
   __syncthreads();
-  if (blockIdx.x == 0 && tid < a.k) {
-    sa.idx[tid] = s_idx[tid];
-    sa.gates[tid] = s_gate[tid];
+  if (j == 0 && blockIdx.x == p * bpp && tid < a.k) {   // first block of the token
+    sa.idx[size_t(t) * a.k + tid] = s_idx[tid];
+    sa.gates[size_t(t) * a.k + tid] = s_gate[tid];
   }
-  const int bpp = (a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock;   // blocks per expert
-  const int j = blockIdx.x / bpp;
-  const int i0 = (blockIdx.x - j * bpp) * kDecodeRowsPerBlock + wave * RPW;
+  const int i0 = (blockIdx.x - p * bpp) * kDecodeRowsPerBlock + wave * RPW;
   int e = s_idx[j];
   const bool valid = e >= 0 && e < a.E;
   e = valid ? e : 0;                                   // addresses stay in range; h becomes NaN
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(Select
     }
     const float av = wave_sum(pa), uv = wave_sum(pu);
     const int i = i0 + r;
-    if (lane == 0 && i < a.I) a.h[size_t(j) * a.I + i] = valid ? silu_f(av) * uv : NAN;
+    if (lane == 0 && i < a.I) a.h[size_t(p) * a.I + i] = valid ? silu_f(av) * uv : NAN;
   }
 }
 
@@ -773,6 +775,28 @@ hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32
   return launch_pairs<false>(a, L.d.act_dtype, L.d.expert_dtype, s);
 }
 
+// Down + combine of independent pairs (T <= kIndependentMaxT): the window
+// kernel when h of every pair fits in LDS (4-bit experts), else one block row
+// per token.
+template <int K>
+static hipError_t launch_down_indep(const PairArgs& a, hipStream_t s) {
+  const dim3 g2((a.H + 7) / 8);
+  if (K == MOE_Q4B32 && down_window_fits(a)) {
+    const int ug = (a.P + kWindowWaves - 1) / kWindowWaves;
+    const dim3 bw(64 * kWindowWaves);
+    const size_t lh = size_t(a.P) * a.I * 4;
+    if (hipError_t ea = window_lds_attributes(); ea != hipSuccess) return ea;
+    if (ug <= 1) hipLaunchKernelGGL(down_combine_window_q4_kernel<1>, g2, bw, lh, s, a);
+    else if (ug <= 2) hipLaunchKernelGGL(down_combine_window_q4_kernel<2>, g2, bw, lh, s, a);
+    else if (ug <= 4) hipLaunchKernelGGL(down_combine_window_q4_kernel<4>, g2, bw, lh, s, a);
+    else hipLaunchKernelGGL(down_combine_window_q4_kernel<8>, g2, bw, lh, s, a);
+  } else {
+    const int nw = a.P < 16 ? a.P : 16;
+    hipLaunchKernelGGL(down_combine_single_kernel<K>, dim3(g2.x, a.T), dim3(64 * nw), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 template <bool INDEP>
 static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s) {
   dim3 g1((a.I + 7) / 8, a.P);
@@ -821,18 +845,7 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
   if (spl <= S) hipLaunchKernelGGL((down_combine_kernel<K, S>), g2, dim3(64 * nw), lds, s, a); else
 #define MOE_DOWN(K)                                                                                    \
   if constexpr (INDEP) {                                                                              \
-    if (K == MOE_Q4B32 && down_window_fits(a)) {                                                       \
-      const int ug = (a.P + kWindowWaves - 1) / kWindowWaves;                                          \
-      const dim3 gw(g2.x), bw(64 * kWindowWaves);                                                      \
-      const size_t lh = size_t(a.P) * a.I * 4;                                                         \
-      if (hipError_t ea = window_lds_attributes(); ea != hipSuccess) return ea;                        \
-      if (ug <= 1) hipLaunchKernelGGL(down_combine_window_q4_kernel<1>, gw, bw, lh, s, a);             \
-      else if (ug <= 2) hipLaunchKernelGGL(down_combine_window_q4_kernel<2>, gw, bw, lh, s, a);        \
-      else if (ug <= 4) hipLaunchKernelGGL(down_combine_window_q4_kernel<4>, gw, bw, lh, s, a);        \
-      else hipLaunchKernelGGL(down_combine_window_q4_kernel<8>, gw, bw, lh, s, a);                     \
-    } else {                                                                                           \
-      hipLaunchKernelGGL(down_combine_single_kernel<K>, dim3(g2.x, a.T), dim3(64 * nw), 0, s, a);     \
-    }                                                                                                  \
+    if (hipError_t ed = launch_down_indep<K>(a, s); ed != hipSuccess) return ed;                      \
   } else {                                                                                             \
     MOE_DOWN_SPL(K, 1) MOE_DOWN_SPL(K, 2) MOE_DOWN_SPL(K, 4) MOE_DOWN_SPL(K, 8) MOE_DOWN_SPL(K, 16)    \
     MOE_DOWN_SPL(K, 32) MOE_DOWN_SPL(K, 64) return hipErrorInvalidValue;                               \
@@ -849,18 +862,25 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
   return hipGetLastError();
 }
 
-bool decode_fused_fits(const Layer& L) {
-  return L.d.expert_dtype == MOE_Q4B32 && L.d.top_k <= kMaxK && (L.d.hidden / 32 + 63) / 64 <= 4;
+// The kernel serves windows of up to kIndependentMaxT tokens, but it is
+// dispatched at T = 1 only: at T = 5 the per-block selections (and the
+// exact refinements they run in every block of a token) cost more than the
+// launch gap they save (49.2 against 45.9 us per window).
+constexpr int kFusedMaxT = 1;
+
+bool decode_fused_fits(const Layer& L, int T) {
+  return L.d.expert_dtype == MOE_Q4B32 && L.d.top_k <= kMaxK && (L.d.hidden / 32 + 63) / 64 <= 4 &&
+         T >= 1 && T <= kFusedMaxT && T <= kIndependentMaxT && T * L.d.top_k <= kMaxPairs;
 }
 
-hipError_t launch_decode_q4(const Layer& L, const void* x, const double* z, const float* gmax,
+hipError_t launch_decode_q4(const Layer& L, const void* x, int T, const double* z, const float* gmax,
                             const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
                             float* out, float* h, hipStream_t s) {
-  if (!decode_fused_fits(L)) return hipErrorInvalidValue;
+  if (!decode_fused_fits(L, T)) return hipErrorInvalidValue;
   const SelectArgs sa = make_select_args(L, x, z, gmax, xnorm, idx, gates, rb);
-  const PairArgs a = pair_args(L, x, 1, idx, gates, out, h);
+  const PairArgs a = pair_args(L, x, T, idx, gates, out, h);
   const int mb = (a.H / 32 + 63) / 64;
-  const dim3 g1(a.k * ((a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock));
+  const dim3 g1(a.P * ((a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock));
 #define MOE_DEC_Q4(M)                                                                             \
   if (mb <= M) {                                                                                  \
     if (L.d.act_dtype == MOE_BF16)                                                                \
@@ -872,9 +892,7 @@ hipError_t launch_decode_q4(const Layer& L, const void* x, const double* z, cons
 #undef MOE_DEC_Q4
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nw = a.P < 16 ? a.P : 16;
-  hipLaunchKernelGGL(down_combine_single_kernel<MOE_Q4B32>, dim3((a.H + 7) / 8, 1), dim3(64 * nw), 0, s, a);
-  return hipGetLastError();
+  return launch_down_indep<MOE_Q4B32>(a, s);
 }
 
 }  // namespace moe

@@ -334,10 +334,11 @@ hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double
 bool pair_path_fits(const Layer& L, int T);
 hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32_t* idx,
                                const float* gates, float* out, float* h, hipStream_t s);
-// experts.hip: one routed 4-bit decode token after the router: selection
-// fused with gate/up (idx, gates written), then down + combine.
-bool decode_fused_fits(const Layer& L);
-hipError_t launch_decode_q4(const Layer& L, const void* x, const double* z, const float* gmax,
+// experts.hip: T <= 8 routed tokens with 4-bit experts after the router:
+// selection fused with gate/up (idx, gates written), then down + combine;
+// h is [T k][I] fp32 workspace.
+bool decode_fused_fits(const Layer& L, int T);
+hipError_t launch_decode_q4(const Layer& L, const void* x, int T, const double* z, const float* gmax,
                             const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
                             float* out, float* h, hipStream_t s);
 // grouped.hip: index sort, grouped experts, weighted un-permute.

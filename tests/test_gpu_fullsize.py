@@ -216,6 +216,33 @@ def test_verify_window_sizes_parity(T):
     assert layer.device_error() == 0
 
 
+@pytest.mark.parametrize("T", [2, 5, 8])
+def test_verify_internal_routing_matches_given_routing(T):
+    """Over 200 windows of the verify stream, moe_grouped_forward with
+    internal routing gives the same idx, gates and outputs, bit for bit, as
+    moe_route followed by moe_grouped_forward with the given routing."""
+    import torch
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_ROUTE_GIVEN
+    layer, spec = layer_for("verify_q4", 8)
+    n = 200
+    X = SD.device_tokens(spec, 0, n * T).view(n, T, spec.H)
+    ws = layer.workspace(T)
+    fi = torch.empty((n, T, spec.k), dtype=torch.int32, device=X.device)
+    fg = torch.empty((n, T, spec.k), dtype=torch.float32, device=X.device)
+    fo = torch.empty((n, T, spec.H), dtype=torch.float32, device=X.device)
+    si, sg, so = torch.empty_like(fi), torch.empty_like(fg), torch.empty_like(fo)
+    for w in range(n):
+        layer.grouped_forward(X[w], T, fi[w], fg[w], 0, fo[w], ws)
+        layer.route(X[w], T, si[w], sg[w], ws)
+        layer.grouped_forward(X[w], T, si[w], sg[w], MOE_ROUTE_GIVEN, so[w], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fi, si)
+    assert torch.equal(fg.view(torch.int32), sg.view(torch.int32))
+    assert torch.equal(fo.view(torch.int32), so.view(torch.int32))
+    assert layer.device_error() == 0
+
+
 def _route_sample(spec, L, X, rows):
     Z, B = oracle.logits_with_bound(X[rows], L)
     o_idx = np.empty((len(rows), spec.k), np.int64)

@@ -169,6 +169,32 @@ def test_fused_decode_single_token(name, exact):
     assert layer.device_error() == 0
 
 
+@pytest.mark.parametrize("name", ["tiny_q4", "odd_q4", "q4_f32x", "q4_h4096"])
+@pytest.mark.parametrize("T", [2, 3, 8])
+def test_window_internal_routing_matches_given_routing(name, T):
+    """Windows of T tokens against the oracle, and bitwise against
+    moe_route + moe_grouped_forward with the given routing."""
+    import torch
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_ROUTE_GIVEN
+    spec, dl, L = setup(name)
+    G.note("window routing", name, T)
+    layer = SD.make_layer(dl, max_tokens=T)
+    x = SD.device_tokens(spec, 500, T)
+    idx, gates, out = G.run_grouped(layer, x)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 500, T)
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"window {name} T={T}")
+    ws = layer.workspace(T)
+    si = torch.empty((T, spec.k), dtype=torch.int32, device=x.device)
+    sg = torch.empty((T, spec.k), dtype=torch.float32, device=x.device)
+    layer.route(x, T, si, sg, ws)
+    s_idx, s_g, s_out = G.run_grouped(layer, x, flags=MOE_ROUTE_GIVEN, idx=si, gates=sg)
+    assert np.array_equal(idx, s_idx)
+    assert np.array_equal(gates.view(np.uint32), s_g.view(np.uint32))
+    assert np.array_equal(out.view(np.uint32), s_out.view(np.uint32))
+    assert layer.device_error() == 0
+
+
 # Grouped MFMA path (bf16 activations and experts, T >= 16): few experts and
 # many tokens, so segments span several 32-row tiles with a ragged last one;
 # I = 96 and H = 160 leave partial 128-wide channel / output blocks.
