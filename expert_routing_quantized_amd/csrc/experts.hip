@@ -877,7 +877,7 @@ hipError_t launch_decode_q4(const Layer& L, const void* x, int T, const double* 
                             const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
                             float* out, float* h, hipStream_t s) {
   if (!decode_fused_fits(L, T)) return hipErrorInvalidValue;
-  const SelectArgs sa = make_select_args(L, x, z, gmax, xnorm, idx, gates, rb);
+  const SelectArgs sa = make_select_args(L, x, z, false, gmax, xnorm, idx, gates, rb);
   const PairArgs a = pair_args(L, x, T, idx, gates, out, h);
   const int mb = (a.H / 32 + 63) / 64;
   const dim3 g1(a.P * ((a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock));

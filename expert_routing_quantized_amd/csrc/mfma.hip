@@ -109,6 +109,9 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
   uint4 v0[kRChunks], v1[kRChunks];
   load(0, v0);
   load(min(1, nk - 1), v1);
+  float bpre[2];                                         // bias, loaded before the K loop (never null)
+#pragma unroll
+  for (int n = 0; n < 2; ++n) bpre[n] = bias[min(n0 + wn + 32 * n + (lane & 31), E - 1)];
   for (int kt = 0; kt < nk; kt += 2) {
     stage(0, v0);
     __syncthreads();
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int e = n0 + wn + 32 * n + (lane & 31);
-    const double b = (e < E && bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
+    const double b = (e < E) ? (double)bpre[n] : 0.0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int t = m0 + wm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
@@ -185,9 +188,10 @@ constexpr int kGThreads = 1024;
 constexpr int kGChunks = (kGM + kGN) * (kGK / 8) / kGThreads;
 constexpr int kBigT = 512;                // smallest batch that takes the big tiles
 
+template <typename ZT>   // logits stored in binary64, or in binary32 for the selection (one more rounding)
 __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
-    int T, int H, int E, int nm, int nn, int nper, double* __restrict__ z, float* __restrict__ gmax,
+    int T, int H, int E, int nm, int nn, int nper, ZT* __restrict__ z, float* __restrict__ gmax,
     double* __restrict__ xnorm, int* __restrict__ dev_flag) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][kGM][kGKP];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][kGN][kGKP];
@@ -227,6 +231,9 @@ __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
     }
   };
   uint4 a0 = *reinterpret_cast<const uint4*>(pa), b0 = *reinterpret_cast<const uint4*>(pb);
+  float bpre[2];                                         // bias, loaded before the K loop (never null)
+#pragma unroll
+  for (int b = 0; b < 2; ++b) bpre[b] = bias[min(n0 + wn + 32 * b + (lane & 31), E - 1)];
   const int k1 = min(1, nk - 1) * kGK;
   uint4 a1 = *reinterpret_cast<const uint4*>(pa + k1), b1 = *reinterpret_cast<const uint4*>(pb + k1);
   for (int kt = 0; kt < nk; kt += 2) {
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int e = n0 + wn + 32 * b + (lane & 31);
-    const double bs = (bias != nullptr) ? (double)bias[min(e, E - 1)] : 0.0;
+    const double bs = (double)bpre[b];
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const int tb = m0 + wm + 32 * a + 4 * (lane >> 5);
@@ -278,13 +285,13 @@ __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
         d[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f[i]), 0x4E, 0xf, 0xf, false));
 #pragma unroll
       for (int i = 0; i < 16; ++i) f[i] = d[i] > f[i] ? d[i] : f[i];
-      double* zb = z + size_t(tb) * E + min(e, E - 1);
+      ZT* zb = z + size_t(tb) * E + min(e, E - 1);
       float* gb = gmax + size_t(tb) * G4 + (min(e, E - 1) >> 2);
       if (full) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 8 * (i >> 2) + (i & 3);
-          zb[size_t(r) * E] = v[i];
+          zb[size_t(r) * E] = (ZT)v[i];
           bad |= !isfinite(v[i]);
         }
         if ((lane & 3) == 0) {
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
         for (int i = 0; i < 16; ++i) {
           const int r = 8 * (i >> 2) + (i & 3);
           if (e < E && tb + r < T) {
-            zb[size_t(r) * E] = v[i];
+            zb[size_t(r) * E] = (ZT)v[i];
             bad |= !isfinite(v[i]);
             if ((lane & 3) == 0) gb[size_t(r) * G4] = f[i];
           }
@@ -334,21 +341,31 @@ bool router_uses_mfma(const Layer& L, int T) {
 
 bool router_uses_big_tiles(const Layer& L, int T) { return router_uses_mfma(L, T) && T >= kBigT; }
 
-hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
+bool router_logits_f32(const Layer& L, int T) { return router_uses_big_tiles(L, T); }
+
+hipError_t launch_router_gemm(const Layer& L, const void* x, int T, void* z, bool z32, float* gmax,
                               double* xnorm, hipStream_t s) {
   const int H = L.d.hidden, E = L.d.n_experts;
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
   const uint16_t* rb = reinterpret_cast<const uint16_t*>(L.router_eh);
   if (router_uses_big_tiles(L, T)) {
     const int nm = (T + kGM - 1) / kGM, nn = (E + kGN - 1) / kGN, nper = (nn + 7) / 8;
-    hipLaunchKernelGGL(router_gemm_big_kernel, dim3(8 * nper * nm), dim3(kGThreads), 0, s, xb, rb,
-                       L.d.router_bias, T, H, E, nm, nn, nper, z, gmax, xnorm, L.dev_flag);
+    if (z32)
+      hipLaunchKernelGGL(router_gemm_big_kernel<float>, dim3(8 * nper * nm), dim3(kGThreads), 0, s, xb, rb,
+                         router_bias_or_zero(L), T, H, E, nm, nn, nper, static_cast<float*>(z), gmax,
+                         xnorm, L.dev_flag);
+    else
+      hipLaunchKernelGGL(router_gemm_big_kernel<double>, dim3(8 * nper * nm), dim3(kGThreads), 0, s, xb, rb,
+                         router_bias_or_zero(L), T, H, E, nm, nn, nper, static_cast<double*>(z), gmax,
+                         xnorm, L.dev_flag);
     return hipGetLastError();
   }
+  if (z32) return hipErrorInvalidValue;                  // binary32 logits only from the big tiles
   const int nm = (T + kRM - 1) / kRM, nn = (E + kRN - 1) / kRN;
   const int nper = (nn + 7) / 8;                         // expert tiles per XCD
   hipLaunchKernelGGL(router_gemm_kernel, dim3(8 * nper * nm), dim3(kRThreads), 0, s, xb, rb,
-                     L.d.router_bias, T, H, E, nm, nn, nper, z, gmax, xnorm, L.dev_flag);
+                     router_bias_or_zero(L), T, H, E, nm, nn, nper, static_cast<double*>(z), gmax, xnorm,
+                     L.dev_flag);
   return hipGetLastError();
 }
 

@@ -103,13 +103,16 @@ moe_status check_ws(const Layer& L, int T, const void* ws, size_t ws_bytes, Work
 
 moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float* gates,
                       char* ws, const Workspace& W, hipStream_t s) {
-  double* z = reinterpret_cast<double*>(ws + W.z);
+  // the selection reads binary32 logits from the big-tile GEMM (half the bytes to write)
+  void* z = ws + W.z;
   float* gmax = reinterpret_cast<float*>(ws + W.gmax);
   double* xnorm = reinterpret_cast<double*>(ws + W.xnorm);
-  hipError_t e = moe::router_uses_mfma(L, T) ? moe::launch_router_gemm(L, x, T, z, gmax, xnorm, s)
-                                             : moe::launch_router(L, x, T, z, gmax, xnorm, s);
+  const bool z32 = moe::router_uses_mfma(L, T) && moe::router_logits_f32(L, T);
+  hipError_t e = moe::router_uses_mfma(L, T)
+                     ? moe::launch_router_gemm(L, x, T, z, z32, gmax, xnorm, s)
+                     : moe::launch_router(L, x, T, static_cast<double*>(z), gmax, xnorm, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
-  e = moe::launch_select_impl(L, x, T, z, gmax, xnorm, idx, gates, moe::router_bound(L, T), s);
+  e = moe::launch_select_impl(L, x, T, z, z32, gmax, xnorm, idx, gates, moe::router_bound(L, T), s);
   if (e != hipSuccess) return hip_fail(e, "select launch");
   return MOE_OK;
 }
@@ -278,7 +281,7 @@ moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, d
   char* w = static_cast<char*>(ws);
   float* gm = reinterpret_cast<float*>(w + W.gmax);
   double* xn = reinterpret_cast<double*>(w + W.xnorm);
-  hipError_t e = moe::router_uses_mfma(L, T) ? moe::launch_router_gemm(L, x, T, z, gm, xn, s)
+  hipError_t e = moe::router_uses_mfma(L, T) ? moe::launch_router_gemm(L, x, T, z, false, gm, xn, s)
                                              : moe::launch_router(L, x, T, z, gm, xn, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   return ok();

@@ -315,7 +315,10 @@ RouterBound router_bound(const Layer& L, int T);
 // mfma.hip: the router as a bf16 MFMA GEMM for T >= 16 tokens (same outputs).
 bool router_uses_mfma(const Layer& L, int T);
 bool router_uses_big_tiles(const Layer& L, int T);   // fp32 accumulation over all of H
-hipError_t launch_router_gemm(const Layer& L, const void* x, int T, double* z, float* gmax,
+// Binary32 logits (the big-tile GEMM's fp32 sums plus the bias, rounded once
+// more) when the route path calls it with z32; binary64 otherwise.
+bool router_logits_f32(const Layer& L, int T);
+hipError_t launch_router_gemm(const Layer& L, const void* x, int T, void* z, bool z32, float* gmax,
                               double* xnorm, hipStream_t s);
 // mfma.hip: the router for 2 <= T < 16 bf16 tokens on 16x16x32 MFMA tiles.
 bool router_uses_skinny(const Layer& L, int T);
@@ -326,7 +329,7 @@ bool grouped_uses_mfma(const Layer& L, int T);
 hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s);
 // select.hip: exact top-k + gates per token from z; bt_unit/bt_abs give
 // the router's error bound Bt = bt_unit * ||x||_2 + bt_abs.
-hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double* z,
+hipError_t launch_select_impl(const Layer& L, const void* x, int T, const void* z, bool z32,
                               const float* gmax, const double* xnorm, int32_t* idx,
                               float* gates, const RouterBound& rb, hipStream_t s);
 // experts.hip: expert GEMVs + combine for T tokens with T k <= kMaxPairs

@@ -12,13 +12,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
   select_block<ACT>(a, t, a.idx + size_t(t) * a.k, a.gates + size_t(t) * a.k);
 }
 
-SelectArgs make_select_args(const Layer& L, const void* x, const double* z, const float* gmax,
+SelectArgs make_select_args(const Layer& L, const void* x, const void* z, bool z32, const float* gmax,
                             const double* xnorm, int32_t* idx, float* gates, const RouterBound& rb) {
   SelectArgs a;
   a.R = L.router_eh;
   a.bias = L.d.router_bias;
   a.x = x;
   a.z = z;
+  a.z32 = z32 ? 1 : 0;
   a.gmax = gmax;
   a.xnorm = xnorm;
   a.H = L.d.hidden;
@@ -33,14 +34,20 @@ SelectArgs make_select_args(const Layer& L, const void* x, const double* z, cons
   // underflow (products flushed to zero included: one per element of x)
   a.bt_abs = (rb.d32 + L.d.hidden) * 0x1p-125 + rb.d64 * 0x1p-1021;
   a.rel = 0x1p-52;
+  if (z32) {
+    // stored in binary32: one more rounding, |fl32(v) - v| <= 2^-24 |v|
+    // (|v| <= |fl32(v)| (1 + 2^-23)), or 2^-126 where it underflows
+    a.rel = (0x1p-24 + 0x1p-52) * (1.0 + 0x1p-20);
+    a.bt_abs += 0x1p-125;
+  }
   a.force_exact = (L.d.flags & MOE_LAYER_FORCE_EXACT_REFINE) ? 1 : 0;
   return a;
 }
 
-hipError_t launch_select_impl(const Layer& L, const void* x, int T, const double* z,
+hipError_t launch_select_impl(const Layer& L, const void* x, int T, const void* z, bool z32,
                               const float* gmax, const double* xnorm, int32_t* idx,
                               float* gates, const RouterBound& rb, hipStream_t s) {
-  const SelectArgs a = make_select_args(L, x, z, gmax, xnorm, idx, gates, rb);
+  const SelectArgs a = make_select_args(L, x, z, z32, gmax, xnorm, idx, gates, rb);
   if (L.d.act_dtype == MOE_BF16)
     hipLaunchKernelGGL(select_kernel<MOE_BF16>, dim3(T), dim3(kSelectThreads), 0, s, a);
   else

@@ -51,7 +51,8 @@ struct SelectArgs {
   const void* R;          // expert-major router [E][H]
   const float* bias;
   const void* x;          // [T][H]
-  const double* z;        // [T][E] router logits (binary64)
+  const void* z;          // [T][E] router logits: binary64, or binary32 when z32
+  int z32;
   const float* gmax;      // [T][ceil(E/4)] maxima of 4 consecutive logits (rounded up)
   const double* xnorm;    // [T] ||x_t||^2
   int H, E, k;
@@ -327,7 +328,11 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k;
   const int G = (E + 3) / 4;                       // groups of 4 consecutive experts
-  const double* zr = a.z + size_t(t) * E;
+  // logit e of this token (binary64 or binary32 storage)
+  auto zr = [&](int e) -> double {
+    const size_t i = size_t(t) * E + e;
+    return a.z32 ? (double)static_cast<const float*>(a.z)[i] : static_cast<const double*>(a.z)[i];
+  };
   const float* gr = a.gmax + size_t(t) * G;
   const int npass = (G + GPASS - 1) / GPASS;
 
@@ -450,7 +455,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
   for (int i0 = 0; i0 < 4 * ng; i0 += kSelectThreads) {   // 4 experts per listed group
     const int i = i0 + tid;
     const int e = (i < 4 * ng) ? s_glist[i >> 2] * 4 + (i & 3) : E;
-    const double v = zr[min(e, E - 1)];
+    const double v = zr(min(e, E - 1));
     const bool pred = e < E && isfinite(v) && v >= th0;
     const unsigned long long m = __ballot(pred);
     if (m) {
@@ -633,7 +638,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
     for (int bit = 63; bit >= 0; --bit) {
       const unsigned long long cand = K | (1ull << bit);
       int cnt = 0;
-      for (int e = tid; e < E; e += kSelectThreads) cnt += (f64_key(zr[e]) >= cand);
+      for (int e = tid; e < E; e += kSelectThreads) cnt += (f64_key(zr(e)) >= cand);
       cnt = block_sum_i(cnt, red);
       if (cnt >= k) K = cand;
     }
@@ -642,7 +647,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
     for (int r0 = 0; r0 < E; r0 += kSelectMaxCand) {
       const int r1 = min(E, r0 + kSelectMaxCand);
       for (int e = r0 + tid; e < r1; e += kSelectThreads) {
-        const double v = zr[e];
+        const double v = zr(e);
         if (isfinite(v) && v >= th) c_id[atomicAdd(&c_cnt, 1)] = e;
       }
       __syncthreads();
@@ -669,7 +674,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
 }
 
 // SelectArgs of a layer for one call (host).
-SelectArgs make_select_args(const Layer& L, const void* x, const double* z, const float* gmax,
+SelectArgs make_select_args(const Layer& L, const void* x, const void* z, bool z32, const float* gmax,
                             const double* xnorm, int32_t* idx, float* gates, const RouterBound& rb);
 
 }  // namespace moe
