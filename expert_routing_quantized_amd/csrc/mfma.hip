@@ -716,7 +716,7 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(GroupArgs a) {
   }
 }
 
-template <int NS, int MT>   // K slices of 64 (I <= 64 NS); 32-row sub-tiles per tile
+template <int NS>   // K slices of 64 (I <= 64 NS); 32-row tiles
 __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
   constexpr int KP = NS * kKS + 8;
   __shared__ __attribute__((aligned(16))) uint16_t shi[kTileRows][KP];
@@ -727,12 +727,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
   const int ow = blockIdx.x * kDR + 32 * wave;           // first output row of this wave
   const int lr = lane >> 3, lc = lane & 7;
   const uint16_t* WD = reinterpret_cast<const uint16_t*>(a.wd);
-  const int* tl = (MT == 1) ? a.tiles : a.tiles_big;   // MT > 1: the big-tile list
+  const int* tl = a.tiles;                               // the 32-row tile list
   const int ntiles = tl[0];
   for (int ti = blockIdx.y; ti < ntiles; ti += gridDim.y) {
     const int e = tl[1 + 2 * ti], r0 = tl[2 + 2 * ti];
     const int n = a.counts[e], seg = a.offsets[e];
-    const int nrow = min(kTileRows * MT, n - r0);
+    const int nrow = min(kTileRows, n - r0);
     // the wave's 32 weight rows, all of K, in flight at once (read once per tile)
     uint4 w[NS][4];
 #pragma unroll
@@ -741,15 +741,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) w[sl][i] = load_row_chunk(row, sl * kKS + 8 * lc, I, true);
     }
-    for (int m = 0; m < MT; ++m) {
-      const int mr = 32 * m;                             // first row of this sub-tile
-      if (m > 0 && mr >= nrow) break;                    // block-uniform
-      if (m > 0) __syncthreads();                        // previous sub-tile's h reads are done
-      // h rows of the sub-tile -> bf16 hi/lo (rows past the segment and columns past I: zeros)
+    {
+      // h rows of the tile -> bf16 hi/lo (rows past the segment and columns past I: zeros)
       for (int q = tid; q < kTileRows * (NS * kKS / 4); q += 256) {
         const int r = q / (NS * kKS / 4), c = (q - r * (NS * kKS / 4)) * 4;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (mr + r < nrow && c < I) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + mr + r) * I + c);
+        if (r < nrow && c < I) v = *reinterpret_cast<const float4*>(a.hm + size_t(seg + r0 + r) * I + c);
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -784,7 +781,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
       const int o = ow + (lane & 31);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int r = mr + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        const int r = 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
         if (r < nrow && o < H) a.y[size_t(seg + r0 + r) * H + o] = acc[i];
       }
     }
@@ -797,8 +794,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(GroupArgs a) {
 // small GEMM: block = (128 output rows, tile of TM tokens); per K slice of
 // 32 the tile's h (fp32) is split into bf16 hi + lo in LDS and both parts
 // meet the same bf16 weight slice, staged once in LDS for all waves (the
-// 32-row kernel gives each wave its own weight rows and repeats them per
-// 32-row sub-tile).  Both operands are K-contiguous; LDS rows hold 32 K
+// 32-row kernel gives each wave its own weight rows, which would repeat
+// them per 32-row part of a larger tile).  Both operands are K-contiguous; LDS rows hold 32 K
 // elements (64 B) with 16-byte chunk c of row r at chunk c ^ ((r >> 1) & 3),
 // so the staging writes and the operand reads of a wave hit distinct banks.
 // The accumulation order (K ascending in steps of 16, hi then lo, fp32) is
@@ -931,9 +928,9 @@ hipError_t launch_grouped_mfma(const GroupArgs& a, hipStream_t s) {
   const dim3 g2((a.H + kDR - 1) / kDR, gy);
   hipLaunchKernelGGL(gateup_mfma_kernel<1>, g1, dim3(256), 0, s, a);
   hipLaunchKernelGGL(gateup_mfma_kernel<MB>, g1b, dim3(256), 0, s, a);
-  if (ns == 1) hipLaunchKernelGGL((down_mfma_kernel<1, 1>), g2, dim3(256), 0, s, a);
-  else if (ns == 2) hipLaunchKernelGGL((down_mfma_kernel<2, 1>), g2, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((down_mfma_kernel<4, 1>), g2, dim3(256), 0, s, a);
+  if (ns == 1) hipLaunchKernelGGL((down_mfma_kernel<1>), g2, dim3(256), 0, s, a);
+  else if (ns == 2) hipLaunchKernelGGL((down_mfma_kernel<2>), g2, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((down_mfma_kernel<4>), g2, dim3(256), 0, s, a);
   hipLaunchKernelGGL(down_tile_kernel<kBigTileRows>, dim3((a.H + 127) / 128, gyb), dim3(256), 0, s, a);
   return hipGetLastError();
 }
