@@ -141,14 +141,18 @@ moe_status moe_route(const moe_layer* layer, const void* x, int32_t T,
  * 16-byte chunk (bf16 dot products when T > 1), then binary64 for the chain
  * sums, the wave reduction and the bias.  bf16 x with H a multiple of 32:
  * 2 <= T < 16 runs 16x16x32 MFMA tiles whose binary32 results (32 products
- * each) are added into binary64 one by one; T >= 16 runs a GEMM whose
- * binary32 accumulators are added into binary64 after every 128 of H.
+ * each) are added into binary64 one by one; 16 <= T < 512 runs a GEMM whose
+ * binary32 accumulators are added into binary64 after every 128 of H;
+ * T >= 512 runs 256x256 GEMM tiles whose binary32 accumulators run over all
+ * of H before the binary64 bias addition (moe_route then keeps these logits
+ * in binary32: one more rounding, covered by a 2^-24 |z| relative term).
  * With c = ceil(H / 512):
  *   |z - z_exact| <= (g(d32, 2^-23) + g(d64, 2^-52)) ||x_t||_2 max_e ||R_e||_2
  *                    + (d32 + H) 2^-125 + d64 2^-1021 + 2^-52 |z|,
  *   g(n, u) = n u / (1 - n u);  vector path: d32 = 7 (8 when T > 1),
  *   d64 = log2(c) + 7;  16x16 tiles: d32 = 33, d64 = ceil(H / 128) + 4;
- *   GEMM: d32 = 136, d64 = ceil(H / 128) + 1.
+ *   GEMM: d32 = 136, d64 = ceil(H / 128) + 1;  256x256 GEMM: d32 = 17 H / 16,
+ *   d64 = 1.
  * moe_route recomputes exactly the logits this bound leaves undecided.
  * Useful to inspect router scores and to time the step that dominates
  * batch-1 decode.
@@ -170,8 +174,10 @@ moe_status moe_expert_decode(const moe_layer* layer, const void* x,
 /* The whole layer for T tokens: route (or take the given routing), group the
  * T*k token-expert pairs by expert, run each active expert once over its
  * tokens, and un-permute with the weighted combine.  out fp32 [T][H].
- * Row t of out equals the single-token result for x[t] within fp32
- * accumulation error; idx and gates are identical. */
+ * idx and gates are identical to those of moe_route on the same T tokens;
+ * row t of out equals moe_expert_decode of x[t] with that routing within
+ * fp32 accumulation error (bit for bit at T = 1, where the selection runs
+ * fused with the 4-bit gate/up projections). */
 moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
                                int32_t* idx, float* gates, uint32_t flags,
                                float* out, void* ws, size_t ws_bytes, void* stream);
