@@ -23,6 +23,8 @@
 // same outputs as the vector-ALU router, so the same selection kernel runs.
 #include "moe_internal.h"
 
+#include <type_traits>
+
 namespace moe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -174,98 +176,165 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Large batches (T >= 512): 256-token x 256-expert tiles, 16 waves of
-// 64 x 64, 32-wide K slices, two slices of register prefetch, the same XCD
-// tile order.  The block reads 1 KB of LDS per MFMA instead of 1.5 KB, which
-// is what bounds the smaller tile, but its 64 accumulators per lane leave no
-// room for binary64 partial sums: each logit is accumulated in the MFMA's
-// fp32 accumulator over all of H and converted once.  Rounding model: H/16
-// instructions of K = 16, each counted as at most 17 binary32 roundings
-// (d32 = 17 H / 16), then the binary64 bias addition (d64 = 1).  The wider
-// bound only moves more near-ties into the selection's exact refinement.
-constexpr int kGM = 256, kGN = 256, kGK = 32, kGKP = kGK + 8;
-constexpr int kGThreads = 1024;
-constexpr int kGChunks = (kGM + kGN) * (kGK / 8) / kGThreads;
-constexpr int kBigT = 512;                // smallest batch that takes the big tiles
+// Large batches (T >= 512, H >= 128): 256-token x 256-expert tiles, 4 waves
+// of 128 x 128 (256 fp32 accumulators per lane, one wave per SIMD), 32-wide
+// K slices.  Operands go from memory straight into LDS with the direct
+// 16-byte LDS loads (no register staging, no LDS store instructions), into a
+// ring of 4 slices (128 KB): slice k + 3 is requested while slice k is
+// multiplied.  Each wave's half-step interleaves its 16 MFMAs with the 8
+// operand reads for the next half-step and the 8 slice loads, so the LDS
+// and memory requests of the 4 waves are spread over the MFMA time instead
+// of arriving in one burst after every barrier (that burst alone cost 15 %
+// of the loop).  The LDS rows (64 bytes) hold their four 16-byte pieces in
+// an XOR order that keeps every group of 8 or 16 consecutive lanes of an
+// operand read on distinct banks.  Tiles are dealt to the 8 XCDs as in the
+// small kernel.  The 256 accumulators per lane leave no room for binary64
+// partial sums: each logit is accumulated in the MFMA's fp32 accumulator
+// over all of H and converted once.  Rounding model: H/16 instructions of
+// K = 16, each counted as at most 17 binary32 roundings (d32 = 17 H / 16),
+// then the binary64 bias addition (d64 = 1).  The wider bound only moves
+// more near-ties into the selection's exact refinement.  The group maxima
+// go through LDS so they leave as 16-byte row pieces.
+constexpr int kGM = 256, kGN = 256, kGK = 32, kGStages = 4;
+constexpr int kGThreads = 256;
+constexpr int kGOpBytes = kGM * kGK * 2;                 // one operand of one slice: 16 KB
+constexpr int kGStage = 2 * kGOpBytes;
+constexpr int kGLds = kGStages * kGStage;                // 128 KB of dynamic LDS
+constexpr int kBigT = 512;                               // smallest batch that takes the big tiles
+constexpr int kBigMinH = 4 * kGK;                        // the K loop keeps 3 slices in flight
+
+// XOR order of the four 16-byte pieces of LDS row r (bits 1..4 of r)
+__device__ __forceinline__ int gpiece(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Direct load of 16 bytes per lane from sbase + voff into LDS at m0 + 16 lane.
+// The LDS address travels in M0, which needs one wait state after it is set.
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr)
+               : "memory");
+}
 
 template <typename ZT>   // logits stored in binary64, or in binary32 for the selection (one more rounding)
-__global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
+__global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
     int T, int H, int E, int nm, int nn, int nper, ZT* __restrict__ z, float* __restrict__ gmax,
     double* __restrict__ xnorm, int* __restrict__ dev_flag) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][kGM][kGKP];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][kGN][kGKP];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
   const int nb = xcd * nper + loc / nm, mb = loc % nm;
   if (nb >= nn) return;                                  // whole block
   const int m0 = mb * kGM, n0 = nb * kGN;
-  const int wm = (wave & 3) * 64, wn = (wave >> 2) * 64;
-  // thread tid stages 16 bytes of token row tid / 4 and of router row tid / 4
-  // (piece tid % 4 of the 64-byte K slice) into the same LDS position
-  static_assert(kGChunks == 2 && kGM == kGN && kGM * (kGK / 8) == kGThreads, "one row piece of each operand");
-  const int lr = tid >> 2, lcol = (tid & 3) * 8;
-  const uint16_t* pa = X + size_t(min(m0 + lr, T - 1)) * H + lcol;
-  const uint16_t* pb = R + size_t(min(n0 + lr, E - 1)) * H + lcol;
-  const int nk = H / kGK;
-  f32x16_t acc[2][2];
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
+  // slice loads: wave w, instruction j moves rows 16 (4 w + j) .. +15 of an
+  // operand; lane l lands in LDS slot l (row l / 4, stored piece l % 4).
+  // Rows past T or E repeat the last row (never stored).
+  uint32_t voa[4], vob[4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (4 * wave + j) + (lane >> 2);
+    const int c = (lane & 3) ^ gpiece(r);
+    voa[j] = uint32_t((min(m0 + r, T - 1) - m0) * H + c * 8) * 2;
+    vob[j] = uint32_t((min(n0 + r, E - 1) - n0) * H + c * 8) * 2;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)glds;
+  const uint16_t* xa = X + size_t(m0) * H;
+  const uint16_t* xb = R + size_t(n0) * H;
+  // operand reads: row (lane & 31) of a 32-row group, logical piece 2 s + (lane >> 5)
+  const int pc = (lane >> 5) ^ gpiece(lane & 31);
+  const uint32_t lb0 = (lane & 31) * 64 + pc * 16, lb1 = (lane & 31) * 64 + (pc ^ 2) * 16;
+  float bpre[4];                                         // bias, loaded before the K loop (never null)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < 4; ++b) bpre[b] = bias[min(n0 + wn + 32 * b + (lane & 31), E - 1)];
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-  auto compute = [&](int buf) {
+  bf16x8_t f0a[4], f0b[4], f1a[4], f1b[4];
+  auto issue = [&](int kt, int stage) {
+    const uint32_t base = lds0 + stage * kGStage + wave * 4096;
 #pragma unroll
-    for (int kk = 0; kk < kGK; kk += 16) {
-      const int kc = kk + 8 * (lane >> 5);
-      bf16x8_t av[2], bv[2];
+    for (int j = 0; j < 4; ++j) dma16(voa[j], xa + kt * kGK, base + j * 1024);
 #pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = *reinterpret_cast<const bf16x8_t*>(&sa[buf][wm + 32 * a + (lane & 31)][kc]);
+    for (int j = 0; j < 4; ++j) dma16(vob[j], xb + kt * kGK, base + kGOpBytes + j * 1024);
+  };
+  // one half-step: 16 MFMAs on (fa, fb), b-major (the operand read last is
+  // used last), interleaved with the 8 operand reads of the other register
+  // set and, when asked, the 8 loads of slice dk
+  auto half = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], auto rd, int rstage, uint32_t lb,
+                  bf16x8_t (&ga)[4], bf16x8_t (&gb)[4], auto dm, int dk, int dstage) {
+    const uint8_t* p = glds + rstage * kGStage + lb;
+    const uint32_t dbase = lds0 + dstage * kGStage + wave * 4096;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) bv[b] = *reinterpret_cast<const bf16x8_t*>(&sb[buf][wn + 32 * b + (lane & 31)][kc]);
+    for (int g = 0; g < 8; ++g) {
+      if constexpr (decltype(dm)::value) {
+        if (g < 4) dma16(voa[g], xa + dk * kGK, dbase + g * 1024);
+        else dma16(vob[g - 4], xb + dk * kGK, dbase + kGOpBytes + (g - 4) * 1024);
+      }
+      if constexpr (decltype(rd)::value) {
+        if (g < 4) ga[g] = *reinterpret_cast<const bf16x8_t*>(p + (wm + 32 * g) * 64);
+        else gb[g - 4] = *reinterpret_cast<const bf16x8_t*>(p + kGOpBytes + (wn + 32 * (g - 4)) * 64);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+      for (int q = 0; q < 2; ++q) {
+        const int idx = 2 * g + q, b = idx >> 2, a = idx & 3;
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  uint4 a0 = *reinterpret_cast<const uint4*>(pa), b0 = *reinterpret_cast<const uint4*>(pb);
-  float bpre[2];                                         // bias, loaded before the K loop (never null)
+  using On = std::integral_constant<bool, true>;
+  using Off = std::integral_constant<bool, false>;
+  // K loop: at the barrier of slice k every wave's loads of slice k + 1 have
+  // landed (vmcnt counts this wave's loads in order; slice k + 2 may still be
+  // in flight) and every wave has finished reading slice k - 1, whose ring
+  // slot then takes slice k + 3.
+  const int nk = H / kGK;                                // >= 4
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
 #pragma unroll
-  for (int b = 0; b < 2; ++b) bpre[b] = bias[min(n0 + wn + 32 * b + (lane & 31), E - 1)];
-  const int k1 = min(1, nk - 1) * kGK;
-  uint4 a1 = *reinterpret_cast<const uint4*>(pa + k1), b1 = *reinterpret_cast<const uint4*>(pb + k1);
-  for (int kt = 0; kt < nk; kt += 2) {
-    *reinterpret_cast<uint4*>(&sa[0][lr][lcol]) = a0;
-    *reinterpret_cast<uint4*>(&sb[0][lr][lcol]) = b0;
-    __syncthreads();
-    const int k2 = min(kt + 2, nk - 1) * kGK;
-    a0 = *reinterpret_cast<const uint4*>(pa + k2);
-    b0 = *reinterpret_cast<const uint4*>(pb + k2);
-    compute(0);
-    if (kt + 1 < nk) {
-      *reinterpret_cast<uint4*>(&sa[1][lr][lcol]) = a1;
-      *reinterpret_cast<uint4*>(&sb[1][lr][lcol]) = b1;
-      __syncthreads();
-      const int k3 = min(kt + 3, nk - 1) * kGK;
-      a1 = *reinterpret_cast<const uint4*>(pa + k3);
-      b1 = *reinterpret_cast<const uint4*>(pb + k3);
-      compute(1);
-    }
+  for (int a = 0; a < 4; ++a) f0a[a] = *reinterpret_cast<const bf16x8_t*>(glds + lb0 + (wm + 32 * a) * 64);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) f0b[b] = *reinterpret_cast<const bf16x8_t*>(glds + kGOpBytes + lb0 + (wn + 32 * b) * 64);
+  int k = 0;
+  for (; k + 3 < nk; ++k) {
+    const int S = k & 3;
+    half(f0a, f0b, On{}, S, lb1, f1a, f1b, Off{}, 0, 0);
+    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    half(f1a, f1b, On{}, (S + 1) & 3, lb0, f0a, f0b, On{}, k + 3, (S + 3) & 3);
   }
-  // epilogue: lane holds rows 8*(i/4) + 4*(lane/32) + i%4 of column lane%32 of
-  // each 32x32 accumulator; interior tiles skip every bounds check
-  const bool full = m0 + kGM <= T && n0 + kGN <= E;       // block-uniform
+  // the last three slices: nothing more to load
+  half(f0a, f0b, On{}, k & 3, lb1, f1a, f1b, Off{}, 0, 0);
+  asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  half(f1a, f1b, On{}, (k + 1) & 3, lb0, f0a, f0b, Off{}, 0, 0);
+  ++k;
+  half(f0a, f0b, On{}, k & 3, lb1, f1a, f1b, Off{}, 0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  half(f1a, f1b, On{}, (k + 1) & 3, lb0, f0a, f0b, Off{}, 0, 0);
+  ++k;
+  half(f0a, f0b, On{}, k & 3, lb1, f1a, f1b, Off{}, 0, 0);
+  half(f1a, f1b, Off{}, 0, lb0, f0a, f0b, Off{}, 0, 0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is free from here on
+
+  // epilogue: lane holds rows 8*(i/4) + 4*(lane/32) + i%4 of column lane%32
+  // of each 32x32 accumulator; interior tiles skip every bounds check
+  const bool full = m0 + kGM <= T && n0 + kGN <= E && (E % 16) == 0;   // block-uniform
   const size_t G4 = size_t(E + 3) / 4;
+  float* sg = reinterpret_cast<float*>(glds);             // group maxima [256 tokens][64 groups]
   bool bad = false;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int e = n0 + wn + 32 * b + (lane & 31);
+  for (int b = 0; b < 4; ++b) {
+    const int el = wn + 32 * b + (lane & 31), e = n0 + el;
     const double bs = (double)bpre[b];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int tb = m0 + wm + 32 * a + 4 * (lane >> 5);
+    for (int a = 0; a < 4; ++a) {
+      const int tl = wm + 32 * a + 4 * (lane >> 5);
       double v[16];
       float f[16], d[16];
 #pragma unroll
@@ -274,7 +343,8 @@ __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
         f[i] = isnan(v[i]) ? -INFINITY : f64_to_f32_up(v[i]);
       }
       // maximum over the 4 consecutive experts of lanes 4q..4q+3 (rounded up
-      // values: rounding up is monotone, so this is the rounded-up maximum)
+      // values: rounding up is monotone, so this is the rounded-up maximum;
+      // lanes past E hold a copy of expert E - 1)
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         d[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f[i]), 0xB1, 0xf, 0xf, false));
@@ -285,53 +355,62 @@ __global__ __launch_bounds__(kGThreads) void router_gemm_big_kernel(
         d[i] = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, f[i]), 0x4E, 0xf, 0xf, false));
 #pragma unroll
       for (int i = 0; i < 16; ++i) f[i] = d[i] > f[i] ? d[i] : f[i];
-      ZT* zb = z + size_t(tb) * E + min(e, E - 1);
-      float* gb = gmax + size_t(tb) * G4 + (min(e, E - 1) >> 2);
+      ZT* zb = z + size_t(m0 + tl) * E + min(e, E - 1);
       if (full) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = 8 * (i >> 2) + (i & 3);
-          zb[size_t(r) * E] = (ZT)v[i];
+          zb[size_t(8 * (i >> 2) + (i & 3)) * E] = (ZT)v[i];
           bad |= !isfinite(v[i]);
-        }
-        if ((lane & 3) == 0) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) gb[size_t(8 * (i >> 2) + (i & 3)) * G4] = f[i];
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 8 * (i >> 2) + (i & 3);
-          if (e < E && tb + r < T) {
+          if (e < E && m0 + tl + r < T) {
             zb[size_t(r) * E] = (ZT)v[i];
             bad |= !isfinite(v[i]);
-            if ((lane & 3) == 0) gb[size_t(r) * G4] = f[i];
           }
         }
+      }
+      if ((lane & 3) == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sg[(tl + 8 * (i >> 2) + (i & 3)) * 64 + (el >> 2)] = f[i];
       }
     }
   }
   if (bad) atomicOr(dev_flag, kDevNonFinite);
-  // ||x_t||^2 of this token tile: 16 groups of 16 tokens (one per wave), dealt
-  // to the tile's first expert tiles (all groups to tile 0 when nn = 1)
-  for (int g = nb; g < kGM / 16; g += nn) {
-    {
-      const int t = m0 + g * 16 + wave;
-      if (t >= T) break;
-      float q = 0.f;
-      for (int c = lane; c < H / 8; c += 64) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(X + size_t(t) * H + c * 8);
-        const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+  __syncthreads();
+  if (full) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-          q = fmaf(lo, lo, q);
-          q = fmaf(hi, hi, q);
-        }
-      }
-      q = wave_sum(q);
-      if (lane == 0) xnorm[t] = (double)q;
+    for (int u = 0; u < 16; ++u) {
+      const int q = tid + kGThreads * u, tok = q >> 4, g4 = q & 15;
+      *reinterpret_cast<float4*>(gmax + size_t(m0 + tok) * G4 + n0 / 4 + g4 * 4) =
+          *reinterpret_cast<const float4*>(&sg[tok * 64 + g4 * 4]);
     }
+  } else {
+    for (int q = tid; q < kGM * 64; q += kGThreads) {
+      const int tok = q >> 6, g = q & 63;
+      if (m0 + tok < T && size_t(n0 / 4 + g) < G4) gmax[size_t(m0 + tok) * G4 + n0 / 4 + g] = sg[q];
+    }
+  }
+  // ||x_t||^2 of this token tile: 64 groups of 4 tokens (one per wave), dealt
+  // to the tile's first expert tiles (all groups to tile 0 when nn = 1)
+  for (int g = nb; g < kGM / 4; g += nn) {
+    const int t = m0 + g * 4 + wave;
+    if (t >= T) break;
+    float q = 0.f;
+    for (int c = lane; c < H / 8; c += 64) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(X + size_t(t) * H + c * 8);
+      const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+        q = fmaf(lo, lo, q);
+        q = fmaf(hi, hi, q);
+      }
+    }
+    q = wave_sum(q);
+    if (lane == 0) xnorm[t] = (double)q;
   }
 }
 
@@ -339,9 +418,26 @@ bool router_uses_mfma(const Layer& L, int T) {
   return L.d.act_dtype == MOE_BF16 && T >= 16 && (L.d.hidden % kBK) == 0;
 }
 
-bool router_uses_big_tiles(const Layer& L, int T) { return router_uses_mfma(L, T) && T >= kBigT; }
+bool router_uses_big_tiles(const Layer& L, int T) {
+  return router_uses_mfma(L, T) && T >= kBigT && L.d.hidden >= kBigMinH;
+}
 
 bool router_logits_f32(const Layer& L, int T) { return router_uses_big_tiles(L, T); }
+
+// The big-tile kernels take kGLds bytes of dynamic LDS; allow it once per
+// process (the attribute belongs to the function, on every device).
+static hipError_t big_lds_attributes() {
+  static const hipError_t err = [] {
+    const void* fns[] = {reinterpret_cast<const void*>(&router_gemm_big_kernel<float>),
+                         reinterpret_cast<const void*>(&router_gemm_big_kernel<double>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
+  return err;
+}
 
 hipError_t launch_router_gemm(const Layer& L, const void* x, int T, void* z, bool z32, float* gmax,
                               double* xnorm, hipStream_t s) {
@@ -349,13 +445,14 @@ hipError_t launch_router_gemm(const Layer& L, const void* x, int T, void* z, boo
   const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
   const uint16_t* rb = reinterpret_cast<const uint16_t*>(L.router_eh);
   if (router_uses_big_tiles(L, T)) {
+    if (hipError_t ea = big_lds_attributes(); ea != hipSuccess) return ea;
     const int nm = (T + kGM - 1) / kGM, nn = (E + kGN - 1) / kGN, nper = (nn + 7) / 8;
     if (z32)
-      hipLaunchKernelGGL(router_gemm_big_kernel<float>, dim3(8 * nper * nm), dim3(kGThreads), 0, s, xb, rb,
+      hipLaunchKernelGGL(router_gemm_big_kernel<float>, dim3(8 * nper * nm), dim3(kGThreads), kGLds, s, xb, rb,
                          router_bias_or_zero(L), T, H, E, nm, nn, nper, static_cast<float*>(z), gmax,
                          xnorm, L.dev_flag);
     else
-      hipLaunchKernelGGL(router_gemm_big_kernel<double>, dim3(8 * nper * nm), dim3(kGThreads), 0, s, xb, rb,
+      hipLaunchKernelGGL(router_gemm_big_kernel<double>, dim3(8 * nper * nm), dim3(kGThreads), kGLds, s, xb, rb,
                          router_bias_or_zero(L), T, H, E, nm, nn, nper, static_cast<double*>(z), gmax,
                          xnorm, L.dev_flag);
     return hipGetLastError();
