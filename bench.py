@@ -389,8 +389,8 @@ def sweep_main(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported "
-                                   "(the multi-GPU sharding is a design, see DESIGN.md)"}))
+        print(json.dumps({"error": "single-GPU implementation: --gpus above 1 is not supported "
+                                   "(sharding by expert id across GPUs is not implemented)"}))
         sys.exit(2)
     import numpy as np
     import torch
