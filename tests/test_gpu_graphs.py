@@ -3,6 +3,7 @@ replayed several times, with eager calls on other inputs (through the same
 workspace) between the replays; every replay must reproduce the eager result
 bit for bit.  Covers the fused batch-1 decode, a verify window, the pair
 deduplication path, the sorted 4-bit grouped path, the MFMA grouped path
+(with the 256 x 256 router tiles and their direct-to-LDS loads at T = 600)
 and fp32 activations, so no captured path relies on workspace contents
 left by an earlier call.
 """
@@ -34,7 +35,8 @@ def device_layer(name):
 
 
 @pytest.mark.parametrize("name,T", [("wide_q4", 1), ("tiny_q4", 1), ("wide_q4", 5), ("tiny_q4", 37),
-                                    ("tiny_q4", 100), ("mfma_multi_tile", 300), ("tiny_f32", 1)])
+                                    ("tiny_q4", 100), ("mfma_multi_tile", 300), ("mfma_multi_tile", 600),
+                                    ("tiny_f32", 1)])
 def test_graph_replays_match_eager(name, T):
     torch = G.torch_mod()
     import synth.device as SD

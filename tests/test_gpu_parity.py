@@ -210,12 +210,14 @@ MFMA_SPECS = {
 
 @pytest.mark.parametrize("name,T", [("mfma_multi_tile", 300), ("mfma_ragged", 77), ("mfma_wide", 64),
                                     ("mfma_wide", 16), ("mfma_multi_tile", 600), ("mfma_ragged", 530),
-                                    ("mfma_multi_tile", 200)])
+                                    ("mfma_multi_tile", 200), ("mfma_wide", 512)])
 def test_grouped_mfma_tiles(name, T):
     """Experts with more than 32 tokens go to 64-row tiles (both grouping
     kernels: 800 pairs and more than 1024); T >= 512 also takes the 256 x 256
     router tiles (fp32 accumulation over H) with one expert tile (E = 20, 37)
-    and ragged token tiles."""
+    and ragged token tiles, or two expert tiles of which the second is
+    partial (E = 300, not a multiple of 16, so every tile takes the masked
+    epilogue)."""
     import synth.device as SD
     spec = MFMA_SPECS[name]
     G.note("grouped mfma", name, T)
