@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
     p.add_argument("--cpu-sample", type=int, default=800,
                    help="tokens the oracle is timed on (about 10 s of host work; 0: skip)")
+    p.add_argument("--layers", type=int, default=1,
+                   help="decode configs: N > 1 stacks N distinct layers (weight seeds base..base+N-1, "
+                        "N x 21.7 GB for 4-bit experts) and times every token through all of them "
+                        "(one JSON line, per layer-token cost; replaces the router copies)")
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter run: launch eagerly (no graphs), run the router alone, then "
                         "a plain copy of known size that calibrates the byte counters; prints a summary")
@@ -386,6 +390,75 @@ def sweep_main(args):
                       "sweep": rows}), flush=True)
 
 
+def layers_main(args, spec):
+    """Batch-1 decode through N distinct layers per token (each with its own
+    router, bias and expert pool), captured as one graph of K x N
+    moe_grouped_forward calls.  Every layer takes the same synthetic hidden
+    state (no residual stream or other model code between layers), so the
+    measurement is the MoE layers' own cost with real cross-layer cache
+    behaviour: N routers and N pools, far beyond the 256 MB Infinity Cache."""
+    import dataclasses
+
+    import torch
+
+    import synth.device as SD
+    K, W, N = args.steps, args.warmup, args.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    dls, layers = [], []
+    for l in range(N):
+        sl = dataclasses.replace(spec, weight_seed=spec.weight_seed + l)
+        dls.append(SD.device_layer(sl))
+        layers.append(SD.make_layer(dls[-1], max_tokens=1))
+    X = SD.device_tokens(spec, 0, W + K)
+    torch.cuda.synchronize()
+    pool = sum(d.nbytes_pool() for d in dls)
+    log(f"{N} layers ready in {time.time() - t0:.1f}s: pools {pool / 1e9:.1f} GB")
+    ws = layers[0].workspace(1)
+    idx = torch.zeros((W + K, N, spec.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((W + K, N, spec.k), dtype=torch.float32, device=dev)
+    out = torch.zeros((W + K, N, spec.H), dtype=torch.float32, device=dev)
+
+    def token(t):
+        for l in range(N):
+            layers[l].grouped_forward(X[t], 1, idx[t, l], gates[t, l], 0, out[t, l], ws)
+
+    for t in range(W):
+        token(t)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g_warm, stream=s):
+            for t in range(W):
+                token(t)
+        with torch.cuda.graph(g_main, stream=s):
+            for t in range(W, W + K):
+                token(t)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        g_warm.replay()
+        torch.cuda.synchronize()
+        ms = median_replay_ms(g_main, s)
+    errs = [L.device_error() for L in layers]
+    by = step_bytes(spec)
+    per_lt = ms / 1e3 / (K * N)
+    print(json.dumps({
+        "metric": "MoE-layer decode layer-tokens/s through N distinct layers (batch-1)",
+        "value": 1.0 / per_lt, "unit": "layer-tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": ms / K, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config} batch-1 decode through {N} distinct layers per token "
+                               f"(weight seeds {spec.weight_seed}..{spec.weight_seed + N - 1}, "
+                               f"{pool / 1e9:.1f} GB of expert pools), {K} tokens, same hidden state into "
+                               f"every layer",
+                   "layers": N, "us_per_layer_token": per_lt * 1e6, "us_per_token_all_layers": ms * 1e3 / K,
+                   "hbm_gbs": by["total"] / per_lt / 1e9, "device_errors": errs},
+    }), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -405,6 +478,8 @@ def main():
         return counters_main(args, spec)
     if spec.T > 1:
         return grouped_main(args, spec)
+    if args.layers > 1:
+        return layers_main(args, spec)
     K, W = args.steps, args.warmup
     n_rep = 3 if args.mode == "cold" else 1
     dev = torch.device("cuda:0")
