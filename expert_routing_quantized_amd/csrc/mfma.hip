@@ -207,46 +207,32 @@ constexpr int kBigMinH = 4 * kGK;                        // the K loop keeps 3 s
 __device__ __forceinline__ int gpiece(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // Direct load of 16 bytes per lane from sbase + voff into LDS at m0 + 16 lane.
-// The LDS address travels in M0, which needs one wait state after it is set.
+// The compiler cannot see the memory instruction inside the asm, so the asm
+// supplies the wait states its operands may need: 5 when a vector
+// instruction (v_readlane, v_readfirstlane, as in register-spill restores)
+// has just written the base SGPRs or M0, which also covers the one that M0
+// needs after a scalar write.
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr)
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds_addr)
                : "memory");
 }
 
-template <typename ZT>   // logits stored in binary64, or in binary32 for the selection (one more rounding)
-__global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
-    int T, int H, int E, int nm, int nn, int nper, ZT* __restrict__ z, float* __restrict__ gmax,
-    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
-  const int nb = xcd * nper + loc / nm, mb = loc % nm;
-  if (nb >= nn) return;                                  // whole block
-  const int m0 = mb * kGM, n0 = nb * kGN;
-  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
-  // slice loads: wave w, instruction j moves rows 16 (4 w + j) .. +15 of an
-  // operand; lane l lands in LDS slot l (row l / 4, stored piece l % 4).
-  // Rows past T or E repeat the last row (never stored).
-  uint32_t voa[4], vob[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 16 * (4 * wave + j) + (lane >> 2);
-    const int c = (lane & 3) ^ gpiece(r);
-    voa[j] = uint32_t((min(m0 + r, T - 1) - m0) * H + c * 8) * 2;
-    vob[j] = uint32_t((min(n0 + r, E - 1) - n0) * H + c * 8) * 2;
-  }
+// K loop of one 256 x 256 tile on 4 waves of 128 x 128 (see above).  The
+// operands are rows of two row sets: A row r is 16 bytes per lane at
+// xa + voa[j] (rows 16 (4 w + j) + lane / 4 of wave w), B likewise from xb +
+// vob[j]; the base pointers are wave-uniform and advance 32 elements per
+// slice.  A wave multiplies A rows wm .. wm + 127 with the B rows brow(b) ..
+// brow(b) + 31, b = 0..3.  On return every LDS read and slice load of the
+// block is complete and the ring may be reused.
+template <typename BRow>
+__device__ __forceinline__ void big_tile_kloop(uint8_t* glds, int wave, int lane, int nk,
+                                               const uint16_t* xa, const uint16_t* xb,
+                                               const uint32_t (&voa)[4], const uint32_t (&vob)[4],
+                                               int wm, BRow brow, f32x16_t (&acc)[4][4]) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)glds;
-  const uint16_t* xa = X + size_t(m0) * H;
-  const uint16_t* xb = R + size_t(n0) * H;
   // operand reads: row (lane & 31) of a 32-row group, logical piece 2 s + (lane >> 5)
   const int pc = (lane >> 5) ^ gpiece(lane & 31);
   const uint32_t lb0 = (lane & 31) * 64 + pc * 16, lb1 = (lane & 31) * 64 + (pc ^ 2) * 16;
-  float bpre[4];                                         // bias, loaded before the K loop (never null)
-#pragma unroll
-  for (int b = 0; b < 4; ++b) bpre[b] = bias[min(n0 + wn + 32 * b + (lane & 31), E - 1)];
-  f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -276,7 +262,7 @@ __global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
       }
       if constexpr (decltype(rd)::value) {
         if (g < 4) ga[g] = *reinterpret_cast<const bf16x8_t*>(p + (wm + 32 * g) * 64);
-        else gb[g - 4] = *reinterpret_cast<const bf16x8_t*>(p + kGOpBytes + (wn + 32 * (g - 4)) * 64);
+        else gb[g - 4] = *reinterpret_cast<const bf16x8_t*>(p + kGOpBytes + brow(g - 4) * 64);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -293,7 +279,6 @@ __global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
   // landed (vmcnt counts this wave's loads in order; slice k + 2 may still be
   // in flight) and every wave has finished reading slice k - 1, whose ring
   // slot then takes slice k + 3.
-  const int nk = H / kGK;                                // >= 4
   issue(0, 0);
   issue(1, 1);
   issue(2, 2);
@@ -301,7 +286,7 @@ __global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
 #pragma unroll
   for (int a = 0; a < 4; ++a) f0a[a] = *reinterpret_cast<const bf16x8_t*>(glds + lb0 + (wm + 32 * a) * 64);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) f0b[b] = *reinterpret_cast<const bf16x8_t*>(glds + kGOpBytes + lb0 + (wn + 32 * b) * 64);
+  for (int b = 0; b < 4; ++b) f0b[b] = *reinterpret_cast<const bf16x8_t*>(glds + kGOpBytes + lb0 + brow(b) * 64);
   int k = 0;
   for (; k + 3 < nk; ++k) {
     const int S = k & 3;
@@ -321,6 +306,39 @@ __global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
   half(f0a, f0b, On{}, k & 3, lb1, f1a, f1b, Off{}, 0, 0);
   half(f1a, f1b, Off{}, 0, lb0, f0a, f0b, Off{}, 0, 0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // the ring is free from here on
+}
+
+template <typename ZT>   // logits stored in binary64, or in binary32 for the selection (one more rounding)
+__global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, const float* __restrict__ bias,
+    int T, int H, int E, int nm, int nn, int nper, ZT* __restrict__ z, float* __restrict__ gmax,
+    double* __restrict__ xnorm, int* __restrict__ dev_flag) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t glds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int xcd = blockIdx.x % 8, loc = blockIdx.x / 8;
+  const int nb = xcd * nper + loc / nm, mb = loc % nm;
+  if (nb >= nn) return;                                  // whole block
+  const int m0 = mb * kGM, n0 = nb * kGN;
+  const int wm = (wave & 1) * 128, wn = (wave >> 1) * 128;
+  // slice loads: wave w, instruction j moves rows 16 (4 w + j) .. +15 of an
+  // operand; lane l lands in LDS slot l (row l / 4, stored piece l % 4).
+  // Rows past T or E repeat the last row (never stored).
+  uint32_t voa[4], vob[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * (4 * wave + j) + (lane >> 2);
+    const int c = (lane & 3) ^ gpiece(r);
+    voa[j] = uint32_t((min(m0 + r, T - 1) - m0) * H + c * 8) * 2;
+    vob[j] = uint32_t((min(n0 + r, E - 1) - n0) * H + c * 8) * 2;
+  }
+  const uint16_t* xa = X + size_t(m0) * H;
+  const uint16_t* xb = R + size_t(n0) * H;
+  float bpre[4];                                         // bias, loaded before the K loop (never null)
+#pragma unroll
+  for (int b = 0; b < 4; ++b) bpre[b] = bias[min(n0 + wn + 32 * b + (lane & 31), E - 1)];
+  f32x16_t acc[4][4];
+  big_tile_kloop(glds, wave, lane, H / kGK, xa, xb, voa, vob, wm, [&](int b) { return wn + 32 * b; }, acc);
 
   // epilogue: lane holds rows 8*(i/4) + 4*(lane/32) + i%4 of column lane%32
   // of each 32x32 accumulator; interior tiles skip every bounds check
