@@ -218,7 +218,18 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out, dl=None):
     base = {"value": count / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{count} tokens (tokens {first}..{first + count - 1} of the timed stream), "
                       f"float64 numpy, {dt:.1f} s; expert bytes pre-generated from the seeded generator"}
-    return base, parity
+    # the same oracle on one thread (BLAS limited to 1), first 50 tokens of the sample
+    from threadpoolctl import threadpool_limits
+    n1 = min(50, count)
+    L1 = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
+    L1._absR = L0.absR()
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        oracle.moe_tokens(X[:n1], L1)
+        d1 = time.perf_counter() - t1
+    single = {"value": n1 / d1, "unit": "tokens/s", "cores": 1,
+              "sample": f"{n1} tokens (tokens {first}..{first + n1 - 1}), float64 numpy, {d1:.1f} s"}
+    return base, parity, single
 
 
 def grouped_main(args, spec):
@@ -583,9 +594,10 @@ def main():
         gi = idx[W:W + n].cpu().numpy()
         gg = gates[W:W + n].cpu().numpy()
         go = out[W:W + n].cpu().numpy()
-        base, parity = cpu_baseline(spec, W, n, gi, gg, go, dl)
+        base, parity, single = cpu_baseline(spec, W, n, gi, gg, go, dl)
         res["cpu_baseline"] = base
         res["config"]["parity_sample"] = parity
+        res["config"]["oracle_one_thread"] = single
     print(json.dumps(res), flush=True)
 
 
