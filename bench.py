@@ -119,17 +119,34 @@ def measured_traffic():
 
 def counters_main(args, spec):
     """Eager launches for rocprofv3 --pmc runs (counter collection does not
-    need graphs): K tokens, K router-only launches, 3 calibration copies."""
+    need graphs).  Decode configs: K tokens, K router-only launches, 3
+    calibration copies; grouped configs: W + K calls on one batch."""
     import torch
 
     import synth.device as SD
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    n_rep = 3 if args.mode == "cold" else 1
+    K, W = args.steps, args.warmup
     dl = SD.device_layer(spec)
+    if spec.T > 1:
+        # grouped configs: W + K eager moe_grouped_forward calls on one batch
+        T = spec.T
+        layer = SD.make_layer(dl, max_tokens=T)
+        X = SD.device_tokens(spec, 0, T)
+        ws = layer.workspace(T)
+        idx = torch.empty((T, spec.k), dtype=torch.int32, device=dev)
+        gates = torch.empty((T, spec.k), dtype=torch.float32, device=dev)
+        out = torch.empty((T, spec.H), dtype=torch.float32, device=dev)
+        for _ in range(W + K):
+            layer.grouped_forward(X, T, idx, gates, 0, out, ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "calls": W + K, "T": T,
+                          "router_flops_per_call": 2.0 * T * spec.H * spec.E,
+                          "device_errors": layer.device_error()}), flush=True)
+        return
+    n_rep = 3 if args.mode == "cold" else 1
     routers = [dl.router_eh] + [SD.device_router(spec) for _ in range(n_rep - 1)]
     layers = [SD.make_layer(dl, max_tokens=1, router=r) for r in routers]
-    K, W = args.steps, args.warmup
     X = SD.device_tokens(spec, 0, W + K)
     ws = layers[0].workspace(1)
     idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
