@@ -394,6 +394,73 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
   }
 }
 
+// Batch-1 decode with bf16 or fp32 experts: the selection fused with the
+// dense gate/up rows, as select_gateup_q4_kernel does for 4-bit experts.
+// Block b serves pair p = b / bpp and kDecodeRowsPerBlock rows of its expert
+// with gateup_dense_kernel's per-row arithmetic (outputs bitwise equal); the
+// lane's x chunks are loaded before the selection starts.
+template <int ACT, int WD, int CPL>
+__global__ __launch_bounds__(kSelectThreads) void select_gateup_dense_kernel(SelectArgs sa, PairArgs a) {
+  constexpr int RPW = kDecodeRowsPerWave;
+  __shared__ int32_t s_idx[kMaxK];
+  __shared__ float s_gate[kMaxK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nch = a.H >> 3;
+  const int bpp = (a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock;   // blocks per pair
+  const int p = blockIdx.x / bpp, t = p / a.k, j = p - t * a.k;
+  Chunk<ACT> xc[CPL];
+#pragma unroll
+  for (int s = 0; s < CPL; ++s) xc[s].load(a.x, size_t(t) * a.H + min(s * 64 + lane, nch - 1) * 8);
+  select_block<ACT>(sa, t, s_idx, s_gate);
+  __syncthreads();
+  if (j == 0 && blockIdx.x == p * bpp && tid < a.k) {   // first block of the token
+    sa.idx[size_t(t) * a.k + tid] = s_idx[tid];
+    sa.gates[size_t(t) * a.k + tid] = s_gate[tid];
+  }
+  const int i0 = (blockIdx.x - p * bpp) * kDecodeRowsPerBlock + wave * RPW;
+  int e = s_idx[j];
+  const bool valid = e >= 0 && e < a.E;
+  e = valid ? e : 0;                                   // addresses stay in range; h becomes NaN
+  Chunk<WD> wg[RPW][CPL], wu[RPW][CPL];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const size_t row = size_t(e) * a.I + min(i0 + r, a.I - 1);
+#pragma unroll
+    for (int s = 0; s < CPL; ++s) {
+      const int c = min(s * 64 + lane, nch - 1);
+      wg[r][s].load(a.wg, row * a.H + c * 8);
+      wu[r][s].load(a.wu, row * a.H + c * 8);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r)
+#pragma unroll
+    for (int s = 0; s < CPL; ++s)
+      if (!(i0 + r < a.I && s * 64 + lane < nch)) {
+        wg[r][s].zero();
+        wu[r][s].zero();
+      }
+  float xv[CPL][8];
+#pragma unroll
+  for (int s = 0; s < CPL; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[s][i] = (s * 64 + lane < nch) ? xc[s].get(i) : 0.f;
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    float pa = 0.f, pu = 0.f;
+#pragma unroll
+    for (int s = 0; s < CPL; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pa = fmaf(wg[r][s].get(i), xv[s][i], pa);
+        pu = fmaf(wu[r][s].get(i), xv[s][i], pu);
+      }
+    const float av = wave_sum(pa), uv = wave_sum(pu);
+    const int i = i0 + r;
+    if (lane == 0 && i < a.I) a.h[size_t(p) * a.I + i] = valid ? silu_f(av) * uv : NAN;
+  }
+}
+
 // ------------------------------------------------------------ down + combine
 
 // Independent pairs: block (x, t) computes 8 output rows of token t; wave w
@@ -869,16 +936,36 @@ static hipError_t launch_pairs(const PairArgs& a, int act, int wd, hipStream_t s
 constexpr int kFusedMaxT = 1;
 
 bool decode_fused_fits(const Layer& L, int T) {
-  return L.d.expert_dtype == MOE_Q4B32 && L.d.top_k <= kMaxK && (L.d.hidden / 32 + 63) / 64 <= 4 &&
-         T >= 1 && T <= kFusedMaxT && T <= kIndependentMaxT && T * L.d.top_k <= kMaxPairs;
+  const bool q4 = L.d.expert_dtype == MOE_Q4B32;
+  const bool rows_fit = q4 ? (L.d.hidden / 32 + 63) / 64 <= 4 : (L.d.hidden / 8 + 63) / 64 <= 4;
+  return L.d.top_k <= kMaxK && rows_fit && T >= 1 && T <= kFusedMaxT && T <= kIndependentMaxT &&
+         T * L.d.top_k <= kMaxPairs;
 }
 
-hipError_t launch_decode_q4(const Layer& L, const void* x, int T, const double* z, const float* gmax,
-                            const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
-                            float* out, float* h, hipStream_t s) {
+hipError_t launch_decode_fused(const Layer& L, const void* x, int T, const double* z, const float* gmax,
+                               const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
+                               float* out, float* h, hipStream_t s) {
   if (!decode_fused_fits(L, T)) return hipErrorInvalidValue;
   const SelectArgs sa = make_select_args(L, x, z, false, gmax, xnorm, idx, gates, rb);
   const PairArgs a = pair_args(L, x, T, idx, gates, out, h);
+  if (L.d.expert_dtype != MOE_Q4B32) {
+    const int cpl = (a.H / 8 + 63) / 64, act = L.d.act_dtype, wd = L.d.expert_dtype;
+    const dim3 g1(a.P * ((a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock));
+#define MOE_DEC_D(C)                                                                                          \
+    if (cpl <= C) {                                                                                           \
+      if (act == MOE_BF16 && wd == MOE_BF16)                                                                  \
+        hipLaunchKernelGGL((select_gateup_dense_kernel<MOE_BF16, MOE_BF16, C>), g1, dim3(kSelectThreads), 0, s, sa, a); \
+      else if (act == MOE_F32 && wd == MOE_BF16)                                                              \
+        hipLaunchKernelGGL((select_gateup_dense_kernel<MOE_F32, MOE_BF16, C>), g1, dim3(kSelectThreads), 0, s, sa, a);  \
+      else                                                                                                    \
+        hipLaunchKernelGGL((select_gateup_dense_kernel<MOE_F32, MOE_F32, C>), g1, dim3(kSelectThreads), 0, s, sa, a);   \
+    } else
+    MOE_DEC_D(1) MOE_DEC_D(2) MOE_DEC_D(4) return hipErrorInvalidValue;
+#undef MOE_DEC_D
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return wd == MOE_BF16 ? launch_down_indep<MOE_BF16>(a, s) : launch_down_indep<MOE_F32>(a, s);
+  }
   const int mb = (a.H / 32 + 63) / 64;
   const dim3 g1(a.P * ((a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock));
 #define MOE_DEC_Q4(M)                                                                             \

@@ -329,14 +329,14 @@ moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
   float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
   if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T)) {
-    // decode and short verify windows with 4-bit experts: router, then the
-    // selection fused with gate/up, then down + combine
+    // batch-1 decode: router, then the selection fused with gate/up, then
+    // down + combine
     double* z = reinterpret_cast<double*>(w + W.z);
     float* gmax = reinterpret_cast<float*>(w + W.gmax);
     double* xnorm = reinterpret_cast<double*>(w + W.xnorm);
     hipError_t e = moe::launch_router(L, x, T, z, gmax, xnorm, s);
     if (e != hipSuccess) return hip_fail(e, "router launch");
-    e = moe::launch_decode_q4(L, x, T, z, gmax, xnorm, moe::router_bound(L, T), ri, rg, out,
+    e = moe::launch_decode_fused(L, x, T, z, gmax, xnorm, moe::router_bound(L, T), ri, rg, out,
                               reinterpret_cast<float*>(w + (T == 1 ? W.h : W.hm)), s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return ok();

@@ -341,7 +341,7 @@ hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32
 // selection fused with gate/up (idx, gates written), then down + combine;
 // h is [T k][I] fp32 workspace.
 bool decode_fused_fits(const Layer& L, int T);
-hipError_t launch_decode_q4(const Layer& L, const void* x, int T, const double* z, const float* gmax,
+hipError_t launch_decode_fused(const Layer& L, const void* x, int T, const double* z, const float* gmax,
                             const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
                             float* out, float* h, hipStream_t s);
 // grouped.hip: index sort, grouped experts, weighted un-permute.

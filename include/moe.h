@@ -177,7 +177,7 @@ moe_status moe_expert_decode(const moe_layer* layer, const void* x,
  * idx and gates are identical to those of moe_route on the same T tokens;
  * row t of out equals moe_expert_decode of x[t] with that routing within
  * fp32 accumulation error (bit for bit at T = 1, where the selection runs
- * fused with the 4-bit gate/up projections). */
+ * fused with the gate/up projections). */
 moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
                                int32_t* idx, float* gates, uint32_t flags,
                                float* out, void* ws, size_t ws_bytes, void* stream);

@@ -118,9 +118,13 @@ def test_decode_q4_grouped_single_token_path():
     the oracle on 16 tokens, and bitwise against moe_route +
     moe_expert_decode on all 1000 tokens of the stream (including the ones
     whose order needs exact refinement)."""
+    grouped_single_token_path("decode_q4", 1000)
+
+
+def grouped_single_token_path(name, n):
     import torch
     import synth.device as SD
-    layer, spec = layer_for("decode_q4", 1)
+    layer, spec = layer_for(name, 1)
     L = oracle_for(spec)
     first = 400
     x = SD.device_tokens(spec, first, 16)
@@ -129,8 +133,7 @@ def test_decode_q4_grouped_single_token_path():
     gates = np.concatenate([r[1] for r in rows])
     out = np.concatenate([r[2] for r in rows])
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, first, 16)
-    G.compare(idx, gates, out, o_idx, o_g, o_out, "decode_q4 grouped T=1")
-    n = 1000
+    G.compare(idx, gates, out, o_idx, o_g, o_out, f"{name} grouped T=1")
     X = SD.device_tokens(spec, 0, n)
     ws = layer.workspace(1)
     fi = torch.empty((n, spec.k), dtype=torch.int32, device=X.device)
@@ -172,6 +175,13 @@ def test_decode_bf16_decode_parity():
     r = G.compare(idx, gates, out, o_idx, o_g, o_out, "decode_bf16")
     print(f"decode_bf16: rel L2 max {r.max():.2e} median {np.median(r):.2e}")
     assert layer.device_error() == 0
+
+
+def test_decode_bf16_grouped_single_token_path():
+    """The same for the bf16 experts (selection fused with the dense gate/up
+    rows): oracle on 16 tokens, bitwise against moe_route +
+    moe_expert_decode on 300 tokens."""
+    grouped_single_token_path("decode_bf16", 300)
 
 
 def test_prefill_bf16_prefill_chunk_parity():

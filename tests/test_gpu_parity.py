@@ -136,7 +136,8 @@ FUSED_SPECS = {
 SMALL.update(FUSED_SPECS)
 
 
-@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "q4_f32x", "q4_h4096"])
+@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "q4_f32x", "q4_h4096", "tiny_bf16", "tiny_f32",
+                                  "f32_bf16x"])
 @pytest.mark.parametrize("exact", [False, True])
 def test_fused_decode_single_token(name, exact):
     """moe_grouped_forward at T = 1 against the oracle, and bitwise against
