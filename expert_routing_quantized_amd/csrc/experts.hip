@@ -1,15 +1,15 @@
 // Expert GEMVs of one token: h_j = silu(G_e x) * (U_e x) for the k selected
 // experts, then out = sum_j g_j D_e h_j.
 //
-// The pages compute the cached experts with a hand-written GEMV that is
-// "already bandwidth-bound"; their tensor-core variant was slower on every
-// real shape because a single token fills one row of a 16-row tile (hexlives
-// dispatch).  So these are vector-ALU GEMVs: every weight byte is loaded
+// The pages compute the cached experts with a hand-written GEMV whose speed
+// is set by memory bandwidth; their tensor-core variant lost on every real
+// shape because a single token fills one row of a 16-row tile (hexlives
+// dispatch, paragraph on the archived tensor-core benchmark).  So these are vector-ALU GEMVs: every weight byte is loaded
 // once with 16-byte loads, the 4-bit codes are expanded in registers and the
 // fp16 block scale is applied to each 32-element partial in fp32 (exact
 // dequantisation, nothing rounded to 16 bits).  The router weight is applied
-// only in the down/combine kernel (pyshine source tour, "The expert handoff
-// is a verified contract").
+// only in the down/combine kernel (pyshine source tour, Understanding the
+// Architecture, paragraph on the expert hand-off).
 //
 // The same kernels serve a few tokens at once (verify windows): with T
 // tokens there are P = T k token-expert pairs.  Short windows compute every

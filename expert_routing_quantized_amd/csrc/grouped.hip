@@ -1,6 +1,6 @@
 // Grouped expert path for T > 1 tokens (verify windows and prefill chunks:
-// pyshine source tour, "Guess, then check" and "Prompts are read in batched
-// pieces").  The T*k token-expert pairs are sorted by expert so that each
+// pyshine source tour, Understanding the Architecture, the paragraphs on
+// speculative decoding and on chunked prompt reading).  The T*k token-expert pairs are sorted by expert so that each
 // active expert's weights are streamed once for all of its tokens:
 //
 //   counts[e]  = #pairs routed to e            (integer atomics)

@@ -158,19 +158,19 @@ __global__ __launch_bounds__(kRThreads) void router_gemm_kernel(
     for (int r = 0; r < kRM / 8; ++r) {
       const int t = m0 + wave * (kRM / 8) + r;
       if (t >= T) break;
-      float q = 0.f;
+      double q = 0.0;   // exact squares summed in binary64 (no underflow)
       for (int c = lane; c < H / 8; c += 64) {
         const uint4 v = *reinterpret_cast<const uint4*>(X + size_t(t) * H + c * 8);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-          q = fmaf(lo, lo, q);
-          q = fmaf(hi, hi, q);
+          const double lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+          q = fma(lo, lo, q);
+          q = fma(hi, hi, q);
         }
       }
-      q = wave_sum(q);
-      if (lane == 0) xnorm[t] = (double)q;
+      q = wave_sum_f64(q);
+      if (lane == 0) xnorm[t] = q;
     }
   }
 }
@@ -416,19 +416,19 @@ __global__ __launch_bounds__(kGThreads, 1) void router_gemm_big_kernel(
   for (int g = nb; g < kGM / 4; g += nn) {
     const int t = m0 + g * 4 + wave;
     if (t >= T) break;
-    float q = 0.f;
+    double q = 0.0;   // exact squares summed in binary64 (no underflow)
     for (int c = lane; c < H / 8; c += 64) {
       const uint4 xv = *reinterpret_cast<const uint4*>(X + size_t(t) * H + c * 8);
       const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-        q = fmaf(lo, lo, q);
-        q = fmaf(hi, hi, q);
+        const double lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+        q = fma(lo, lo, q);
+        q = fma(hi, hi, q);
       }
     }
-    q = wave_sum(q);
-    if (lane == 0) xnorm[t] = (double)q;
+    q = wave_sum_f64(q);
+    if (lane == 0) xnorm[t] = q;
   }
 }
 
@@ -577,19 +577,19 @@ __device__ __forceinline__ void skinny_epilogue(double (*red)[16][17], const uin
   if ((el & 3) == 0 && live) gmax[size_t(t) * ((E + 3) / 4) + (e >> 2)] = f64_to_f32_up(m);
   if (blockIdx.x == 0) {
     for (int tt = wave; tt < T; tt += 4) {
-      float q = 0.f;
+      double q = 0.0;   // exact squares summed in binary64 (no underflow)
       for (int c = lane; c < H / 8; c += 64) {
         const uint4 xv = *reinterpret_cast<const uint4*>(X + size_t(tt) * H + c * 8);
         const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
-          q = fmaf(lo, lo, q);
-          q = fmaf(hi, hi, q);
+          const double lo = bf16_lo(w[j]), hi = bf16_hi(w[j]);
+          q = fma(lo, lo, q);
+          q = fma(hi, hi, q);
         }
       }
-      q = wave_sum(q);
-      if (lane == 0) xnorm[tt] = (double)q;
+      q = wave_sum_f64(q);
+      if (lane == 0) xnorm[tt] = q;
     }
   }
 }

@@ -1,8 +1,8 @@
 // C ABI of libmoe: argument validation, layer lifetime, workspace layout and
 // the launch sequence of each entry point.  Every check that the host can
 // make runs before anything is enqueued (a wrong expert geometry is refused
-// rather than mis-indexed: pyshine source tour, "The expert handoff is a
-// verified contract").
+// rather than mis-indexed: pyshine source tour, Understanding the
+// Architecture, paragraph on the expert hand-off).
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>

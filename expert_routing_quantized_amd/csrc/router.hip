@@ -1,7 +1,8 @@
 // Router GEMV for a few tokens: z[t][e] = fl(sum_h x[t][h] R[e][h] + b[e]).
 //
 // The pages' routing kernel scores all 24,576 experts of the pool for each
-// token (pyshine source tour, "Three tiers, one residency table"); at batch
+// token (pyshine source tour, Understanding the Architecture, paragraph on
+// the three residency tiers and the routing kernel); at batch
 // 1 this is a GEMV that only streams the router once, and the hexlives
 // dispatch reports that matrix units lose on exactly this shape, so the
 // product runs on the vector ALUs.
@@ -115,22 +116,22 @@ void router_kernel(
       if (lane == t && t < nt && live) z[size_t(t0 + t) * E + e] = v;
       if (lane == 0) zl[t][wave] = live ? v : -INFINITY;
     }
-    if (blockIdx.x == 0) {      // ||x_t||^2 of this block's tokens (binary32 sums)
+    if (blockIdx.x == 0) {      // ||x_t||^2 of this block's tokens (binary64 sums of exact squares)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t % kRouterWaves != wave || t >= nt) continue;   // wave-uniform
-        float q = 0.f;
+        double q = 0.0;
 #pragma unroll
         for (int s2 = 0; s2 < CPL; ++s2) {
           const uint32_t xw[4] = {xp[t][s2].x, xp[t][s2].y, xp[t][s2].z, xp[t][s2].w};
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float xv = (i & 1) ? bf16_hi(xw[i >> 1]) : bf16_lo(xw[i >> 1]);
-            q = fmaf(xv, xv, q);
+            const double xv = (i & 1) ? bf16_hi(xw[i >> 1]) : bf16_lo(xw[i >> 1]);
+            q = fma(xv, xv, q);
           }
         }
-        q = wave_sum(q);
-        if (lane == 0) xnorm[t0 + t] = (double)q;
+        q = wave_sum_f64(q);
+        if (lane == 0) xnorm[t0 + t] = q;
       }
     }
   } else {
@@ -192,17 +193,17 @@ void router_kernel(
     const double v = wave_sum_f64(acc[0]) + (double)b;
     if (lane == 0 && live) z[size_t(t0) * E + e] = v;
     if (lane == 0) zl[0][wave] = live ? v : -INFINITY;
-    if (blockIdx.x == 0 && wave == 0) {   // ||x||^2 (binary32 sum; the bound keeps a margin)
-      float q = 0.f;
+    if (blockIdx.x == 0 && wave == 0) {   // ||x||^2: exact squares summed in binary64 (no underflow)
+      double q = 0.0;
 #pragma unroll
       for (int s = 0; s < CPL; ++s)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float xs = xf_get(xc[s], i, s * 64 + lane < nch);
-          q = fmaf(xs, xs, q);
+          const double xs = xf_get(xc[s], i, s * 64 + lane < nch);
+          q = fma(xs, xs, q);
         }
-      q = wave_sum(q);
-      if (lane == 0) xnorm[t0] = (double)q;
+      q = wave_sum_f64(q);
+      if (lane == 0) xnorm[t0] = q;
     }
   }
   // maximum of the block's logits per token, rounded up to binary32 (an

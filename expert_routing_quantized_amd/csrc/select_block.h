@@ -1,8 +1,9 @@
 // Exact top-k selection and softmax gates, one workgroup per token.
 //
-// The pages' router "names ten experts per token" (pyshine source tour) and
-// drafts are verified "bit-for-bit identical to greedy" ("Guess, then
-// check"); here the selected experts must equal those of the exact logits
+// In the pages the router picks ten experts for every token (pyshine source
+// tour, Understanding the Architecture), and the verify window must reproduce
+// greedy decoding exactly (same section, paragraph on speculative decoding);
+// here the selected experts must equal those of the exact logits
 // (each rounded once to binary64, ties to the lower expert index).  The
 // router kernel's logits z_hat obey |z_hat - z| <= B(z_hat) with
 //   B(v) = Bt + 2^-52 |v|,
@@ -358,7 +359,9 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
       if (ps * GPASS + i * kSelectThreads + tid >= G) gv[i] = -INFINITY;
   };
   load_pass(0);
-  const double xn = sqrt(a.xnorm[t]) * (1.0 + 1e-3);   // ||x||^2 was summed in binary32
+  // ||x||^2 is a binary64 sum of exact squares (no underflow for any bf16 or
+  // fp32 input); the factor covers its rounding and the square root
+  const double xn = sqrt(a.xnorm[t]) * (1.0 + 1e-3);
   const double Bt = a.bt_unit * xn + a.bt_abs;
   const double u = a.rel;
 

@@ -2,15 +2,16 @@
  * moe.h -- C ABI of one sparse mixture-of-experts layer on an MI355X (gfx950).
  *
  * The layer is the one the Strata pages describe (pyshine source tour,
- * "Understanding the Architecture"): a router scores every expert of a large
- * pool for a token, the top experts ("the router names ten experts per
- * token") run their SwiGLU MLPs, and a device-side combine sums the expert
- * outputs weighted by the router weights ("The expert handoff is a verified
- * contract": the expert side never applies the router weight, the combine
- * does).  Decode at batch 1 is a bandwidth-bound GEMV (hexlives dispatch, the
- * archived tensor-core experiment); verify windows and prefill chunks
- * ("Guess, then check" and "Prompts are read in batched pieces") run several
- * tokens through the same layer, grouped by expert.
+ * section Understanding the Architecture): a router scores every expert of a
+ * large pool for a token, the ten best-scoring experts run their SwiGLU MLPs
+ * (the end-to-end paragraph of that section), and a device-side combine sums
+ * the expert outputs weighted by the router weights (paragraph on the expert
+ * hand-off: the expert side never applies the router weight, the combine
+ * does).  Decode at batch 1 is a GEMV limited by memory bandwidth (hexlives
+ * dispatch, paragraph on the archived tensor-core benchmark); verify windows
+ * and prefill chunks (pyshine tour, same section, the paragraphs on
+ * speculative decoding and on chunked prompt reading) run several tokens
+ * through the same layer, grouped by expert.
  *
  * Conventions shared by every call:
  *  - All data pointers are DEVICE pointers except `desc`, `out`, `bytes` and
@@ -22,9 +23,10 @@
  *  - moe_route / moe_expert_decode / moe_grouped_forward only enqueue work on
  *    `stream`: no allocation, no host synchronisation, no device-to-host read.
  *    They can therefore be captured into a HIP graph, and their per-call
- *    values live in caller-owned fixed-address buffers (the pages' per-layer
- *    captured graphs fed through fixed-address device buffers, "One driver
- *    composes one token").  Two calls may run concurrently on different
+ *    values live in caller-owned fixed-address buffers (the pages capture one
+ *    graph per layer and feed it through fixed-address device buffers: pyshine
+ *    tour, Understanding the Architecture, paragraph on the engine driver).
+ *    Two calls may run concurrently on different
  *    streams if each has its own workspace and outputs.
  *  - Faults that the host can detect return a negative moe_status before any
  *    work is enqueued and print nothing (a wrong expert geometry is refused

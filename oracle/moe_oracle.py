@@ -8,9 +8,9 @@ What it computes, per token (each step follows the pages; where the pages
 are silent the reading is stated):
 
 1. Router logits ``z_e = sum_h x_h R[h, e] + b_e`` over all E experts.  The
-   pages: the engine's routing kernel "names ten experts per token" out of
-   24,576 (pyshine source tour, "Three tiers, one residency table" and the
-   end-to-end paragraph).  Reading: ``z`` is the exact real value (inputs are
+   pages: the engine's routing kernel picks ten of the 24,576 experts for
+   every token (pyshine source tour, Understanding the Architecture, the
+   paragraph on the residency tiers and the end-to-end paragraph).  Reading: ``z`` is the exact real value (inputs are
    dyadic rationals) rounded once to f64.  A numpy f64 matmul gives every
    logit to within a proved bound; every expert that could still be in the
    top k under that bound is recomputed with ``math.fsum`` (exact, correctly
@@ -23,9 +23,9 @@ are silent the reading is stated):
 4. Each selected expert is a SwiGLU MLP without biases:
    ``h = silu(G x) * (U x)``, ``y = D h``, ``silu(a) = a / (1 + exp(-a))``.
 5. Combine: ``out = sum_j g_j y_j`` in selection order.  The router weight is
-   applied here and only here (pyshine source tour, "The expert handoff is a
-   verified contract": the expert side must not apply it; the device-side
-   combine does the weighted sum).
+   applied here and only here (pyshine source tour, Understanding the
+   Architecture, paragraph on the expert hand-off: the expert side leaves the
+   router weight to the device-side combine, which does the weighted sum).
 
 The pages' own float64 parity reference for the decode GEMV (hexlives
 dispatch, the archived tensor-core benchmark) is the precedent for checking

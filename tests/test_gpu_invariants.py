@@ -223,3 +223,51 @@ def test_ties_at_the_cut_and_inside_the_top(rank, shift, T):
     L = oracle.OracleLayer(Rh, np.zeros(spec.E), spec.k, lambda e, w: synth.expert_stored(spec, e, w))
     o_idx, o_g, _, o_out = oracle.moe_tokens(oracle.tokens_f64(spec, 0, T), L)
     G.compare(idx, gates, out, o_idx, o_g, o_out, f"ties rank {rank} shift {shift} T {T}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 20, 600])
+def test_tiny_hidden_state_near_ties(T):
+    """Hidden states scaled by 2^-80 (their squares underflow binary32) with
+    an exact tie and a near tie one bf16 ulp apart in the element where token
+    0's |x| is smallest, no bias.  The selection's error bound grows with
+    ||x||, so ||x||^2 must not underflow: the routing must still match the
+    exact logits.  T = 1, 5, 20 and 600 take the four router kernels."""
+    torch = G.torch_mod()
+    import oracle
+    import synth.device as SD
+    spec = SPEC_BF
+    dl = dev(spec)
+    scale = 2.0 ** -80
+    x = (SD.device_tokens(spec, 0, T).float() * scale).to(torch.bfloat16)
+    Xh = oracle.tokens_f64(spec, 0, T) * scale
+    assert np.array_equal(oracle.decode_bf16(SD.to_numpy_bits(x)), Xh)   # scaling is exact
+    layer = SD.make_layer(dl, max_tokens=T)
+    idx0, _, _ = G.run_grouped(layer, x)
+    top = [int(v) for v in idx0[0]]
+    R = dl.router_eh.clone()
+    dst = (top[1] + 7) % spec.E
+    while dst in top:
+        dst = (dst + 1) % spec.E
+    R[dst] = R[top[1]]                              # exact tie with rank 1
+    near = (top[0] + 3) % spec.E
+    while near in top or near == dst:
+        near = (near + 1) % spec.E
+    R[near] = R[top[0]]
+    h = int(np.argmin(np.where(Xh[0] != 0, np.abs(Xh[0]), np.inf)))
+    bits = R[near].view(torch.int16)
+    bits[h] += 1                                    # near tie: differs by x_h * one ulp
+    dl2 = SD.DeviceLayer(spec, R, dl.bias, dl.w_gate, dl.w_up, dl.w_down)
+    layer2 = SD.make_layer(dl2, max_tokens=T)
+    Rh = oracle.decode_bf16(SD.to_numpy_bits(R)).T
+    L = oracle.OracleLayer(Rh, np.zeros(spec.E), spec.k, lambda e, w: synth.expert_stored(spec, e, w))
+    o_idx, o_g, _, o_out = oracle.moe_tokens(Xh, L)
+    G.note("tiny x", T)
+    # The outputs (about 2^-160 here) lie below the binary32 range, in which
+    # h and out are kept, so they are zero or subnormal: only the routing is
+    # compared with the oracle, the outputs only checked to be finite and tiny.
+    assert np.abs(o_out).max() < 2.0 ** -140
+    for run in (G.run_grouped, G.run_route_decode):
+        idx, gates, out = run(layer2, x)
+        G.compare(idx, gates, None, o_idx, o_g, None, f"tiny x T {T}/{run.__name__}")
+        assert np.all(np.isfinite(out)) and np.abs(out).max() <= 2.0 ** -120
+    assert layer2.device_error() == 0
