@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE"
           -8: "MOE_E_DEVICE_FLAG"}
 
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
-           "moe_expert_decode", "moe_grouped_forward", "moe_device_error", "moe_router_logits",
+           "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
+           "moe_router_logits",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -65,6 +66,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_expert_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_router_logits.argtypes = [vp, vp, i32, vp, vp, sz, vp]
     lib.moe_grouped_forward.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp, sz, vp]
+    lib.moe_grouped_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp]
     lib.moe_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -72,7 +74,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_last_error_message.restype = ctypes.c_char_p
     lib.moe_abi_version.argtypes = []
     for name in ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
-                 "moe_expert_decode", "moe_grouped_forward", "moe_device_error", "moe_router_logits", "moe_abi_version"]:
+                 "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
+           "moe_router_logits", "moe_abi_version"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -163,6 +166,10 @@ class Layer:
         _check(self.lib.moe_grouped_forward(self.handle, _ptr(x), T, _ptr(idx), _ptr(gates), flags,
                                             _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0,
                                             _stream(stream)), "moe_grouped_forward")
+
+    def grouped_forward_noalloc(self, x, T, idx, gates, flags, out, stream=None):
+        _check(self.lib.moe_grouped_forward_noalloc(self.handle, _ptr(x), T, _ptr(idx), _ptr(gates), flags,
+                                                    _ptr(out), _stream(stream)), "moe_grouped_forward_noalloc")
 
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32()

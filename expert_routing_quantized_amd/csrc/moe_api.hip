@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "moe_internal.h"
@@ -117,6 +118,83 @@ moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float*
   return MOE_OK;
 }
 
+// ---------------------------------------------------------------- scratch
+// Device scratch of moe_grouped_forward_noalloc, for callers that cannot
+// allocate.  Each GPU holds its own copy until the process ends; in host
+// code the array's name is only a stand-in, so the device address of each
+// GPU's copy is looked up once, with that GPU current, and used everywhere
+// host code needs the memory.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+constexpr int kScratchMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchMaxDevices];
+
+// Device address of `scratch` on device `dev` (the current device).
+hipError_t scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+// Shared by moe_grouped_forward and moe_grouped_forward_noalloc: checks of
+// everything but the workspace, then the launch sequence.
+moe_status grouped_check(const Layer& L, const void* x, int32_t T, const int32_t* idx, const float* gates,
+                         uint32_t flags, const float* out) {
+  if (flags != MOE_ROUTE_INTERNAL && flags != MOE_ROUTE_GIVEN)
+    return fail(MOE_E_RANGE, "flags=0x%x must be MOE_ROUTE_INTERNAL or MOE_ROUTE_GIVEN", flags);
+  if (T < 0 || T > L.d.max_tokens) return fail(MOE_E_RANGE, "T=%d outside [0, max_tokens=%d]", T, L.d.max_tokens);
+  if (T == 0) return MOE_OK;
+  if (!x || !out) return fail(MOE_E_NULL, "x and out are required");
+  if (flags == MOE_ROUTE_GIVEN && (!idx || !gates))
+    return fail(MOE_E_NULL, "MOE_ROUTE_GIVEN needs idx and gates");
+  if ((idx == nullptr) != (gates == nullptr))
+    return fail(MOE_E_NULL, "idx and gates must both be given or both be NULL");
+  if (!aligned(x, 16)) return fail(MOE_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(out, 4) || (idx && (!aligned(idx, 4) || !aligned(gates, 4))))
+    return fail(MOE_E_ALIGN, "idx/gates/out must be 4-byte aligned");
+  return MOE_OK;
+}
+
+moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, float* gates,
+                        uint32_t flags, float* out, char* w, const Workspace& W, hipStream_t s) {
+  int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
+  float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
+  if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T)) {
+    // batch-1 decode: router, then the selection fused with gate/up, then
+    // down + combine
+    double* z = reinterpret_cast<double*>(w + W.z);
+    float* gmax = reinterpret_cast<float*>(w + W.gmax);
+    double* xnorm = reinterpret_cast<double*>(w + W.xnorm);
+    hipError_t e = moe::launch_router(L, x, T, z, gmax, xnorm, s);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    e = moe::launch_decode_fused(L, x, T, z, gmax, xnorm, moe::router_bound(L, T), ri, rg, out,
+                                 reinterpret_cast<float*>(w + (T == 1 ? W.h : W.hm)), s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return MOE_OK;
+  }
+  if (flags == MOE_ROUTE_INTERNAL) {
+    if (moe_status st = route_impl(L, x, T, ri, rg, w, W, s)) return st;
+  }
+  hipError_t e;
+  if (T == 1)
+    e = moe::launch_pair_experts(L, x, 1, ri, rg, out, reinterpret_cast<float*>(w + W.h), s);
+  else if (!moe::grouped_uses_mfma(L, T) && moe::pair_path_fits(L, T))
+    e = moe::launch_pair_experts(L, x, T, ri, rg, out, reinterpret_cast<float*>(w + W.hm), s);
+  else
+    e = moe::launch_grouped_experts(L, x, T, ri, rg, out, w, W, s);
+  if (e != hipSuccess) return hip_fail(e, "expert launch");
+  return MOE_OK;
+}
+
 }  // namespace
 
 namespace moe {
@@ -202,6 +280,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
     return code;
   };
   if (e != hipSuccess) return cleanup(hip_fail(e, "hipGetDevice"));
+  if ((e = scratch_address(L.device, &L.scratch)) != hipSuccess)
+    return cleanup(hip_fail(e, "hipGetSymbolAddress(scratch)"));
   if ((e = hipMalloc(&L.norms, (E + 1) * sizeof(float))) != hipSuccess)
     return cleanup(hip_fail(e, "hipMalloc(norms)"));
   if ((e = hipMalloc(&L.dev_flag, sizeof(int))) != hipSuccess)
@@ -310,48 +390,33 @@ moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
                                size_t ws_bytes, void* stream) {
   if (moe_status st = check_layer(layer)) return st;
   const Layer& L = layer->L;
-  if (flags != MOE_ROUTE_INTERNAL && flags != MOE_ROUTE_GIVEN)
-    return fail(MOE_E_RANGE, "flags=0x%x must be MOE_ROUTE_INTERNAL or MOE_ROUTE_GIVEN", flags);
-  if (T < 0 || T > L.d.max_tokens) return fail(MOE_E_RANGE, "T=%d outside [0, max_tokens=%d]", T, L.d.max_tokens);
+  if (moe_status st = grouped_check(L, x, T, idx, gates, flags, out)) return st;
   if (T == 0) return ok();
-  if (!x || !out) return fail(MOE_E_NULL, "x and out are required");
-  if (flags == MOE_ROUTE_GIVEN && (!idx || !gates))
-    return fail(MOE_E_NULL, "MOE_ROUTE_GIVEN needs idx and gates");
-  if ((idx == nullptr) != (gates == nullptr))
-    return fail(MOE_E_NULL, "idx and gates must both be given or both be NULL");
-  if (!aligned(x, 16)) return fail(MOE_E_ALIGN, "x must be 16-byte aligned");
-  if (!aligned(out, 4) || (idx && (!aligned(idx, 4) || !aligned(gates, 4))))
-    return fail(MOE_E_ALIGN, "idx/gates/out must be 4-byte aligned");
   Workspace W;
   if (moe_status st = check_ws(L, T, ws, ws_bytes, &W)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
-  float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
-  if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T)) {
-    // batch-1 decode: router, then the selection fused with gate/up, then
-    // down + combine
-    double* z = reinterpret_cast<double*>(w + W.z);
-    float* gmax = reinterpret_cast<float*>(w + W.gmax);
-    double* xnorm = reinterpret_cast<double*>(w + W.xnorm);
-    hipError_t e = moe::launch_router(L, x, T, z, gmax, xnorm, s);
-    if (e != hipSuccess) return hip_fail(e, "router launch");
-    e = moe::launch_decode_fused(L, x, T, z, gmax, xnorm, moe::router_bound(L, T), ri, rg, out,
-                              reinterpret_cast<float*>(w + (T == 1 ? W.h : W.hm)), s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    return ok();
-  }
-  if (flags == MOE_ROUTE_INTERNAL) {
-    if (moe_status st = route_impl(L, x, T, ri, rg, w, W, s)) return st;
-  }
-  hipError_t e;
-  if (T == 1)
-    e = moe::launch_pair_experts(L, x, 1, ri, rg, out, reinterpret_cast<float*>(w + W.h), s);
-  else if (!moe::grouped_uses_mfma(L, T) && moe::pair_path_fits(L, T))
-    e = moe::launch_pair_experts(L, x, T, ri, rg, out, reinterpret_cast<float*>(w + W.hm), s);
-  else
-    e = moe::launch_grouped_experts(L, x, T, ri, rg, out, w, W, s);
-  if (e != hipSuccess) return hip_fail(e, "expert launch");
+  if (moe_status st = grouped_impl(L, x, T, idx, gates, flags, out, static_cast<char*>(ws), W, s)) return st;
+  return ok();
+}
+
+moe_status moe_grouped_forward_noalloc(const moe_layer* layer, const void* x, int32_t T, int32_t* idx,
+                                       float* gates, uint32_t flags, float* out, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const Layer& L = layer->L;
+  if (moe_status st = grouped_check(L, x, T, idx, gates, flags, out)) return st;
+  if (T == 0) return ok();
+  const Workspace W = moe::workspace_layout(L, T);
+  if (W.total > kScratchBytes)
+    return fail(MOE_E_WORKSPACE, "T=%d needs %zu bytes of scratch, more than the %zu bytes of the "
+                "library's device scratch (use moe_grouped_forward with a workspace)", T, W.total, kScratchBytes);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != L.device)
+    return fail(MOE_E_RANGE, "current device %d is not the layer's device %d", dev, L.device);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (moe_status st = grouped_impl(L, x, T, idx, gates, flags, out, static_cast<char*>(L.scratch), W, s))
+    return st;
   return ok();
 }
 

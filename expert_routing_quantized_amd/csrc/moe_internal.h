@@ -35,6 +35,7 @@ struct Layer {
   float* zero_bias;         // owned: [E] zeros when the caller gives no bias, else null
   double norm_max;          // host copy of max_e ||R_e||_2 (rounded up)
   int device;
+  void* scratch;            // device address of this GPU's library scratch (moe_grouped_forward_noalloc)
 };
 
 // The router bias as the GEMV and few-token router kernels read it: never

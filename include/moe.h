@@ -184,6 +184,21 @@ moe_status moe_grouped_forward(const moe_layer* layer, const void* x, int32_t T,
                                int32_t* idx, float* gates, uint32_t flags,
                                float* out, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_grouped_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The per-call scratch lives in the
+ * library's own fixed device array of 8 MiB on each GPU (held until the
+ * process ends); the call allocates nothing and returns MOE_E_WORKSPACE when
+ * moe_workspace_bytes(T) exceeds 8 MiB (at H = 2048, E = 24,576, k = 10,
+ * I = 256 that covers decode and verify windows, T up to about 20), and
+ * MOE_E_RANGE when the current device is not the layer's.  Every call on one GPU shares that array and leaves its contents
+ * behind: calls that may overlap on one GPU (other streams, other host
+ * threads) race and must not be issued.  Arguments and results otherwise as
+ * moe_grouped_forward. */
+moe_status moe_grouped_forward_noalloc(const moe_layer* layer, const void* x, int32_t T,
+                                       int32_t* idx, float* gates, uint32_t flags,
+                                       float* out, void* stream);
+
 /* Synchronise `stream`, return the sticky device-fault bits in *code (0 when
  * clean: 1 = expert index out of range, 2 = expert repeated within a token,
  * 4 = non-finite router logit, 8 = internal range check) and clear them.
