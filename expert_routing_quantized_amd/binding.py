@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_F32, MOE_BF16, MOE_Q4B32 = 0, 1, 2
 MOE_ROUTER_HE, MOE_ROUTER_EH = 0, 1
 MOE_LAYER_FORCE_EXACT_REFINE = 1
+MOE_LAYER_SCREEN_ON = 2
+MOE_LAYER_SCREEN_OFF = 4
 MOE_ROUTE_INTERNAL, MOE_ROUTE_GIVEN = 0, 1
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE",
@@ -24,7 +26,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE"
 
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
            "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
-           "moe_router_logits",
+           "moe_router_logits", "moe_router_screen",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -65,6 +67,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_route.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
     lib.moe_expert_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_router_logits.argtypes = [vp, vp, i32, vp, vp, sz, vp]
+    lib.moe_router_screen.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
     lib.moe_grouped_forward.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp, sz, vp]
     lib.moe_grouped_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp]
     lib.moe_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
@@ -75,7 +78,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_abi_version.argtypes = []
     for name in ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
                  "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
-           "moe_router_logits", "moe_abi_version"]:
+           "moe_router_logits", "moe_router_screen", "moe_abi_version"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -156,6 +159,11 @@ class Layer:
         _check(self.lib.moe_router_logits(self.handle, _ptr(x), T, _ptr(z), _ptr(ws),
                                           ws.numel() if ws is not None else 0, _stream(stream)),
                "moe_router_logits")
+
+    def router_screen(self, x, T, v, bound, ws, stream=None):
+        _check(self.lib.moe_router_screen(self.handle, _ptr(x), T, _ptr(v), _ptr(bound), _ptr(ws),
+                                          ws.numel() if ws is not None else 0, _stream(stream)),
+               "moe_router_screen")
 
     def expert_decode(self, x, idx, gates, out, ws, stream=None):
         _check(self.lib.moe_expert_decode(self.handle, _ptr(x), _ptr(idx), _ptr(gates), _ptr(out),

@@ -61,7 +61,12 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_E_DTYPE, "fp32 experts need fp32 activations");
   if (d->router_layout != MOE_ROUTER_HE && d->router_layout != MOE_ROUTER_EH)
     return fail(MOE_E_DTYPE, "router_layout %d unsupported", d->router_layout);
-  if (d->flags & ~MOE_LAYER_FORCE_EXACT_REFINE) return fail(MOE_E_RANGE, "unknown desc.flags bits 0x%x", d->flags);
+  const uint32_t known = MOE_LAYER_FORCE_EXACT_REFINE | MOE_LAYER_SCREEN_ON | MOE_LAYER_SCREEN_OFF;
+  if (d->flags & ~known) return fail(MOE_E_RANGE, "unknown desc.flags bits 0x%x", d->flags);
+  if ((d->flags & MOE_LAYER_SCREEN_ON) && (d->flags & MOE_LAYER_SCREEN_OFF))
+    return fail(MOE_E_RANGE, "MOE_LAYER_SCREEN_ON and MOE_LAYER_SCREEN_OFF together");
+  if ((d->flags & MOE_LAYER_SCREEN_ON) && (d->act_dtype != MOE_BF16 || d->hidden % 32))
+    return fail(MOE_E_DTYPE, "the router screen needs bf16 activations and hidden %% 32 == 0");
   const int mult = (d->expert_dtype == MOE_Q4B32) ? 32 : 8;
   if (H < 8 || H > moe::kMaxH || H % mult)
     return fail(MOE_E_GEOMETRY, "hidden=%d must be a multiple of %d in [8, %d]", H, mult, moe::kMaxH);
@@ -104,6 +109,16 @@ moe_status check_ws(const Layer& L, int T, const void* ws, size_t ws_bytes, Work
 
 moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float* gates,
                       char* ws, const Workspace& W, hipStream_t s) {
+  if (T == 1 && L.screen) {     // the int8 first pass, then the selection recomputes its candidates
+    float* z8 = reinterpret_cast<float*>(ws + W.z);
+    float* g8 = reinterpret_cast<float*>(ws + W.gmax);
+    double* xq = reinterpret_cast<double*>(ws + W.xnorm);
+    hipError_t e = moe::launch_screen(L, x, 1, z8, g8, xq, nullptr, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "screen launch");
+    e = moe::launch_select_screen(L, x, 1, z8, g8, xq, idx, gates, s);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    return MOE_OK;
+  }
   // the selection reads binary32 logits from the big-tile GEMM (half the bytes to write)
   void* z = ws + W.z;
   float* gmax = reinterpret_cast<float*>(ws + W.gmax);
@@ -168,6 +183,21 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
                         uint32_t flags, float* out, char* w, const Workspace& W, hipStream_t s) {
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
   float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
+  if (flags == MOE_ROUTE_INTERNAL && T == 1 && L.screen) {
+    // batch-1 decode on the screen: the int8 first pass, then one kernel for
+    // the selection, gate/up and (when it fits) down + combine
+    float* z8 = reinterpret_cast<float*>(w + W.z);
+    float* g8 = reinterpret_cast<float*>(w + W.gmax);
+    double* xq = reinterpret_cast<double*>(w + W.xnorm);
+    unsigned long long* tags = reinterpret_cast<unsigned long long*>(w + W.tags);
+    const bool fused = moe::decode_screen_fused_down(L);
+    hipError_t e = moe::launch_screen(L, x, 1, z8, g8, xq, fused ? tags : nullptr,
+                                      fused ? L.d.top_k * L.d.inter : 0, s);
+    if (e != hipSuccess) return hip_fail(e, "screen launch");
+    e = moe::launch_decode_screen(L, x, z8, g8, xq, ri, rg, out, reinterpret_cast<float*>(w + W.h), tags, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return MOE_OK;
+  }
   if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T)) {
     // batch-1 decode: router, then the selection fused with gate/up, then
     // down + combine
@@ -212,7 +242,7 @@ Workspace workspace_layout(const Layer& L, int T) {
   };
   W.z = take(Tz * E * 8);
   W.gmax = take(Tz * ((E + 3) / 4) * 4);
-  W.xnorm = take(Tz * 8);
+  W.xnorm = take(Tz * 16);
   W.idx = take(P * 4);
   W.gates = take(P * 4);
   W.h = take(k * I * 4);
@@ -228,6 +258,7 @@ Workspace workspace_layout(const Layer& L, int T) {
     W.hm = take(P * I * 4);
     W.y = take(P * H * 4);
   }
+  W.tags = take(k * I * 8);
   W.total = off;
   return W;
 }
@@ -261,6 +292,10 @@ static void release_layer(Layer& L) {
   if (L.norms) (void)hipFree(L.norms);
   if (L.dev_flag) (void)hipFree(L.dev_flag);
   if (L.zero_bias) (void)hipFree(L.zero_bias);
+  if (L.q8) (void)hipFree(L.q8);
+  if (L.sc8) (void)hipFree(L.sc8);
+  if (L.eb8) (void)hipFree(L.eb8);
+  if (L.screen_consts) (void)hipFree(L.screen_consts);
 }
 
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out) {
@@ -304,12 +339,34 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
     L.router_eh = desc->router_w;
   }
   if ((e = moe::launch_router_norms(L, s)) != hipSuccess) return cleanup(hip_fail(e, "router norms"));
+  // the int8 first pass of the batch-1 router (layer-owned: E H bytes + 12 E)
+  L.screen = desc->act_dtype == MOE_BF16 && H % 32 == 0 && !(desc->flags & MOE_LAYER_SCREEN_OFF) &&
+             (E >= size_t(moe::kScreenMinExperts) || (desc->flags & MOE_LAYER_SCREEN_ON));
+  float sconst[3] = {0.f, 0.f, 0.f};
+  if (L.screen) {
+    if ((e = hipMalloc(&L.q8, E * H)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(screen router)"));
+    if ((e = hipMalloc(&L.sc8, E * sizeof(float))) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(screen scales)"));
+    if ((e = hipMalloc(&L.eb8, E * sizeof(float2))) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(screen norms)"));
+    if ((e = hipMalloc(&L.screen_consts, 3 * sizeof(float))) != hipSuccess)
+      return cleanup(hip_fail(e, "hipMalloc(screen maxima)"));
+    if ((e = moe::launch_screen_prep(L, L.screen_consts, s)) != hipSuccess) return cleanup(hip_fail(e, "screen prep"));
+    if ((e = hipMemcpyAsync(sconst, L.screen_consts, sizeof(sconst), hipMemcpyDeviceToHost, s)) != hipSuccess)
+      return cleanup(hip_fail(e, "screen maxima readback"));
+  }
   float nmax = 0.f;
   if ((e = hipMemcpyAsync(&nmax, L.norms + E, sizeof(float), hipMemcpyDeviceToHost, s)) != hipSuccess)
     return cleanup(hip_fail(e, "norm readback"));
   if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup(hip_fail(e, "hipStreamSynchronize"));
   if (!(nmax >= 0.f) || isinf(nmax)) return cleanup(fail(MOE_E_RANGE, "router weights are not finite"));
   L.norm_max = nmax;
+  L.screen_enmax = sconst[0];
+  L.screen_rqmax = sconst[1];
+  L.screen_bmax = sconst[2];
+  if (L.screen) {
+    if (!(isfinite(sconst[0]) && isfinite(sconst[1]) && isfinite(sconst[2])))
+      return cleanup(fail(MOE_E_RANGE, "router weights or bias are not finite"));
+    L.resident_blocks = moe::decode_screen_resident_blocks(L);
+  }
   *out = l;
   return ok();
 }
@@ -364,6 +421,29 @@ moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, d
   hipError_t e = moe::router_uses_mfma(L, T) ? moe::launch_router_gemm(L, x, T, z, false, gm, xn, s)
                                              : moe::launch_router(L, x, T, z, gm, xn, s);
   if (e != hipSuccess) return hip_fail(e, "router launch");
+  return ok();
+}
+
+moe_status moe_router_screen(const moe_layer* layer, const void* x, int32_t T, float* v, float* bound,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  const Layer& L = layer->L;
+  if (!L.screen) return fail(MOE_E_DTYPE, "this layer has no router screen (MOE_LAYER_SCREEN_ON with bf16 "
+                                         "activations and hidden %% 32 == 0)");
+  if (T < 0 || T > L.d.max_tokens) return fail(MOE_E_RANGE, "T=%d outside [0, max_tokens=%d]", T, L.d.max_tokens);
+  if (T == 0) return ok();
+  if (!x || !v) return fail(MOE_E_NULL, "x and v are required");
+  if (!aligned(x, 16)) return fail(MOE_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(v, 4) || (bound && !aligned(bound, 4))) return fail(MOE_E_ALIGN, "v and bound must be 4-byte aligned");
+  Workspace W;
+  if (moe_status st = check_ws(L, T, ws, ws_bytes, &W)) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  float* g8 = reinterpret_cast<float*>(w + W.gmax);
+  double* xq = reinterpret_cast<double*>(w + W.xnorm);
+  hipError_t e = moe::launch_screen(L, x, T, v, g8, xq, nullptr, 0, s);
+  if (e == hipSuccess && bound) e = moe::launch_screen_bounds(L, T, v, xq, bound, s);
+  if (e != hipSuccess) return hip_fail(e, "screen launch");
   return ok();
 }
 

@@ -36,7 +36,21 @@ struct Layer {
   double norm_max;          // host copy of max_e ||R_e||_2 (rounded up)
   int device;
   void* scratch;            // device address of this GPU's library scratch (moe_grouped_forward_noalloc)
+  // the router's int8 first pass (batch-1 routing), when `screen`:
+  bool screen;
+  int8_t* q8;               // owned: [E][H] int8 router
+  float* sc8;               // owned: [E] scales
+  float2* eb8;              // owned: [E] (||eps_e||, ||s_e q_e||), rounded up
+  float* screen_consts;     // owned: device maxima of the two norms and of |b|
+  double screen_enmax, screen_rqmax, screen_bmax;   // host copies
+  int resident_blocks;      // blocks of the fused screen decode kernel the device holds at once
 };
+
+// Layers screen the batch-1 router pass only with MOE_LAYER_SCREEN_ON for
+// now: measured at E = 24,576 the recompute of the ~50 undecided experts in
+// every block of the fused kernel costs more than the halved router stream
+// saves.  (The threshold stays for the automatic choice.)
+constexpr int kScreenMinExperts = 1 << 30;
 
 // The router bias as the GEMV and few-token router kernels read it: never
 // null (zeros when the caller gives none), so their loads need no branch.
@@ -48,7 +62,7 @@ inline const float* router_bias_or_zero(const Layer& L) {
 struct Workspace {
   size_t z;         // f64 [T][E] approximate logits
   size_t gmax;      // f32 [T][ceil(E/4)] maxima of 4 consecutive logits (rounded up)
-  size_t xnorm;     // f64 [T] squared norms of the hidden states
+  size_t xnorm;     // f64 [T] squared norms of the hidden states ([T][2] with the screen's ||delta||^2)
   size_t idx;       // int32 [T][k] routing (when the caller passes none)
   size_t gates;     // fp32 [T][k]
   size_t h;         // fp32 [k][I] decode intermediate
@@ -62,6 +76,7 @@ struct Workspace {
   size_t tiles_big; // int32, same layout: kBigTileRows-row tiles of experts with more than 32 pairs
   size_t hm;        // fp32 [P][I] grouped intermediate
   size_t y;         // fp32 [P][H] grouped expert outputs
+  size_t tags;      // u64 [k][I] tagged h words of the fused batch-1 screen kernel
   size_t total;
 };
 
@@ -349,6 +364,30 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, int T, const doubl
 hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const int32_t* idx,
                                   const float* gates, float* out, char* ws,
                                   const Workspace& W, hipStream_t s);
+// screen.hip: the router's int8 first pass (batch-1 routing).  prep builds
+// q8 / sc8 / eb8 and the maxima (consts[3]); screen writes the values z8
+// [T][E], their maxima of 4 g8 and ||x||^2, ||delta||^2 into xq [T][2], and
+// clears `ntags` words at `tags` (may be null) for the call's next kernel.
+hipError_t launch_screen_prep(const Layer& L, float* consts, hipStream_t s);
+hipError_t launch_screen(const Layer& L, const void* x, int T, float* z8, float* g8, double* xq,
+                         unsigned long long* tags, int ntags, hipStream_t s);
+int screen_clearable_words(const Layer& L);
+struct ScreenSelectArgs;
+ScreenSelectArgs make_screen_select_args(const Layer& L, const void* x, const float* z8, const float* g8,
+                                         const double* xq, int32_t* idx, float* gates);
+hipError_t launch_select_screen(const Layer& L, const void* x, int T, const float* z8, const float* g8,
+                                const double* xq, int32_t* idx, float* gates, hipStream_t s);
+// the screen values' error bounds B_e of tokens [0, T) (inspection)
+hipError_t launch_screen_bounds(const Layer& L, int T, const float* z8, const double* xq, float* bound,
+                                hipStream_t s);
+// experts.hip: batch-1 decode after the screen: selection + gate/up, then down
+// + combine in the same kernel when decode_screen_fused_down (h published as
+// tagged words in `tags`, cleared by the screen), else as its own launch.
+bool decode_screen_fused_down(const Layer& L);
+int decode_screen_resident_blocks(const Layer& L);
+hipError_t launch_decode_screen(const Layer& L, const void* x, const float* z8, const float* g8, const double* xq,
+                                int32_t* idx, float* gates, float* out, float* h, unsigned long long* tags,
+                                hipStream_t s);
 // prep.hip: layer creation helpers.
 hipError_t launch_transpose_router(const Layer& L, void* dst, hipStream_t s);
 hipError_t launch_router_norms(const Layer& L, hipStream_t s);

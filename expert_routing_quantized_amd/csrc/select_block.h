@@ -190,6 +190,36 @@ static __device__ double bins_round(const long long* bins) {
   return neg ? -v : v;
 }
 
+// Correctly rounded logit of expert e for token t by exact fixed-point
+// accumulation (one wave; every lane returns it).  The rare fallback of
+// refine_logit, kept out of line so the kernels' hot code stays compact.
+template <int ACT>
+__device__ __attribute__((noinline)) double exact_logit_bins(const void* R, const void* x, const float* bias, int H,
+                                                             int t, int e, long long* bins, int lane,
+                                                             int* dev_flag) {
+  const int nch = H >> 3;
+  const double b = bias ? (double)bias[e] : 0.0;
+  for (int i = lane; i < kBins; i += 64) bins[i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  int bad = 0;
+  for (int ch = lane; ch < nch; ch += 64) {
+    Chunk<ACT> xc, rc;
+    xc.load(x, size_t(t) * H + ch * 8);
+    rc.load(R, size_t(e) * H + ch * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bins_add(bins, (double)xc.get(i) * (double)rc.get(i), &bad);
+  }
+  if (lane == 0) bins_add(bins, b, &bad);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  double v = 0.0;
+  if (lane == 0) v = bins_round(bins);
+  if (bad) atomicOr(dev_flag, kDevInternal);
+  __builtin_amdgcn_wave_barrier();
+  return __shfl(v, 0);
+}
+
 // Exact logit of expert e for token t, computed by one wave (all lanes
 // return the same value).  Inlined, so the kernel's argument block is never
 // copied to private memory and its pointers keep their global address space.
@@ -255,27 +285,7 @@ __device__ __forceinline__ double refine_logit(const SelectArgs& a, int t, int e
   const double dn = r - nextafter(r, -INFINITY);
   const bool ok = !a.force_exact && isfinite(r) && (d + eps < 0.5 * up) && (d - eps > -0.5 * dn);
   if (ok) return r;
-
-  // slow path: exact fixed-point accumulation
-  for (int i = lane; i < kBins; i += 64) bins[i] = 0;
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  int bad = 0;
-  for (int ch = lane; ch < nch; ch += 64) {
-    Chunk<ACT> xc, rc;
-    xc.load(a.x, size_t(t) * a.H + ch * 8);
-    rc.load(a.R, size_t(e) * a.H + ch * 8);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) bins_add(bins, (double)xc.get(i) * (double)rc.get(i), &bad);
-  }
-  if (lane == 0) bins_add(bins, b, &bad);
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  double v = 0.0;
-  if (lane == 0) v = bins_round(bins);
-  if (bad) atomicOr(a.dev_flag, kDevInternal);
-  __builtin_amdgcn_wave_barrier();
-  return __shfl(v, 0);
+  return exact_logit_bins<ACT>(a.R, a.x, a.bias, a.H, t, e, bins, lane, a.dev_flag);
 }
 
 // ---------------------------------------------------------------- kernel
@@ -304,27 +314,297 @@ __device__ __forceinline__ double key_f64(unsigned long long k) {
   return __longlong_as_double((long long)u);
 }
 
+// LDS of one block's selection.
+struct SelectLds {
+  double s_val[kSelectMaxCand];   // survivors' values (then reused by the re-ranking)
+  int s_id[kSelectMaxCand];       // survivors' experts
+  int c_id[kSelectMaxCand];
+  double c_z[kSelectMaxCand];
+  int s_glist[kSelectMaxCand];    // listed groups
+  float s_tmax[kSelectThreads];
+  int top_e[kMaxK], new_e[kMaxK];
+  double top_z[kMaxK], new_z[kMaxK], s_w[kMaxK];
+  long long bins[kWavesSel][kBins];
+  double red[kWavesSel];
+  int s_cnt, c_cnt, s_ntop, s_done, s_ng, s_nref;
+  int s_ref[64];                  // ranks refined by the cluster pass
+  int s_rank[64];                 // fast path: each survivor's rank
+  double x_z[64];                 // their exact logits, by rank
+  double s_tau, s_th0;
+  float s_thf;                    // s_th0 in binary32, rounded down
+};
+
+// Names of the SelectLds fields inside a selection function.
+#define MOE_SELECT_LDS_NAMES(S)                                                        \
+  double* s_val = S.s_val;                                                           \
+  int* s_id = S.s_id;                                                                \
+  int* c_id = S.c_id;                                                                \
+  double* c_z = S.c_z;                                                               \
+  int* s_glist = S.s_glist;                                                          \
+  float* s_tmax = S.s_tmax;                                                          \
+  int *top_e = S.top_e, *new_e = S.new_e;                                            \
+  double *top_z = S.top_z, *new_z = S.new_z, *s_w = S.s_w;                           \
+  auto& bins = S.bins;                                                               \
+  double* red = S.red;                                                               \
+  int &s_cnt = S.s_cnt, &c_cnt = S.c_cnt, &s_ntop = S.s_ntop, &s_done = S.s_done;    \
+  int &s_ng = S.s_ng, &s_nref = S.s_nref;                                            \
+  int* s_ref = S.s_ref;                                                              \
+  double* x_z = S.x_z;                                                               \
+  double &s_tau = S.s_tau, &s_th0 = S.s_th0;                                         \
+  float& s_thf = S.s_thf;                                                            \
+  (void)s_val; (void)s_id; (void)c_id; (void)c_z; (void)s_glist; (void)s_tmax;       \
+  (void)top_e; (void)new_e; (void)top_z; (void)new_z; (void)s_w; (void)bins;         \
+  (void)red; (void)s_ref; (void)x_z
+
+// The end of a selection, shared by the full-router and the screened paths.
+// On entry S.s_val / S.s_id hold n survivors (n = kSelectMaxCand + 1: too
+// many to hold) whose values v obey |v - z| <= Btv + uv |v|, and every
+// expert outside them has an exact logit below the k-th largest.  zr(e) is
+// an approximate logit of every expert with |zr(e) - z| <= Btz + uz |zr(e)|,
+// read only when the survivors did not fit.  Certifies the order (refining
+// exactly where intervals overlap) and writes idx and gates to oi / og.
+template <int ACT, class ZR>
+__device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, SelectLds& S, double Btv,
+                                            double uv, ZR zr, double Btz, double uz, int32_t* oi, float* og) {
+  MOE_SELECT_LDS_NAMES(S);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, k = a.k;
+  const double Bt = Btv, u = uv;
+  auto bound = [&](double v) -> double { return Bt + u * fabs(v); };
+  auto lower_b = [](double tv, double B0, double uu) -> double {   // tv - B(tv), rounded down
+    if (isinf(tv)) return tv < 0 ? -INFINITY : tv;
+    const double B = B0 + uu * fabs(tv);
+    const double L = tv - B;
+    return L - 1e-15 * (fabs(tv) + B + 1.0);
+  };
+  auto lower = [&](double tv) -> double { return lower_b(tv, Bt, u); };
+
+  // 5a. fast path: the survivors' ranks (each wave counts, for every
+  //     survivor, the larger ones among 8 of the others), then one wave
+  //     certifies the order.
+  const bool fast = n <= 64 && !a.force_exact;     // block-uniform
+  if (fast) {
+    if (tid < 64) S.s_rank[tid] = 0;
+    __syncthreads();
+    const double v = (lane < n) ? s_val[lane] : -INFINITY;
+    const int e = (lane < n) ? s_id[lane] : 0x7fffffff;
+    int part = 0;
+    for (int j = wave * 8; j < min(n, wave * 8 + 8); ++j) {   // wave-uniform bounds
+      const double vj = readlane_f64(v, j);
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      part += (vj > v) || (vj == v && ej < e);
+    }
+    if (lane < n && part) atomicAdd(&S.s_rank[lane], part);
+    __syncthreads();
+  }
+  if (fast && wave == 0) {
+    const double v = (lane < n) ? s_val[lane] : -INFINITY;
+    const int e = (lane < n) ? s_id[lane] : 0x7fffffff;
+    const int rank = (lane < n) ? S.s_rank[lane] : 64;
+    if (lane < n) {
+      c_z[rank] = v;
+      c_id[rank] = e;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    // ranks r and r+1 must not overlap for r < k (order of the k, and the cut)
+    const int npair = min(k, n - 1);
+    bool bad = false;
+    if (lane < npair) {
+      const double hi = c_z[lane], lo = c_z[lane + 1];
+      bad = !(hi - bound(hi) > lo + bound(lo));
+    }
+    const unsigned long long bm = __ballot(bad);
+    const bool certified = (n >= k) && (bm == 0ull);
+    if (certified) {
+      if (lane < k) s_w[lane] = exp(c_z[lane] - c_z[0]);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < k) {
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += s_w[j];
+        oi[lane] = c_id[lane];
+        og[lane] = (float)(s_w[lane] / sum);
+      }
+      if (lane == 0) s_done = 1;
+    } else if (n >= k) {
+      // cluster pass: the ranks of every overlapping pair, and, when the
+      // cut (k-1, k) overlaps, every later rank whose interval reaches the
+      // lower end of rank k's, are refined to their exact logits
+      bool mark = lane < n && ((((bm >> lane) & 1ull) != 0) || (lane > 0 && ((bm >> (lane - 1)) & 1ull) != 0));
+      if (((bm >> (k - 1)) & 1ull) != 0 && lane > k && lane < n) {
+        const double zk = c_z[k];
+        if (c_z[lane] + bound(c_z[lane]) >= zk - bound(zk)) mark = true;
+      }
+      const unsigned long long mm = __ballot(mark);
+      if (mark) s_ref[__popcll(mm & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) s_nref = (__popcll(mm) <= 2 * kWavesSel) ? __popcll(mm) : 0;
+    }
+  }
+  __syncthreads();
+  if (s_done) return;
+  if (s_nref > 0) {
+    for (int i = wave; i < s_nref; i += kWavesSel) {
+      const double zz = refine_logit<ACT>(a, t, c_id[s_ref[i]], bins[wave], lane);
+      if (lane == 0) x_z[s_ref[i]] = zz;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // re-rank with the exact logits where known (interval of width 0)
+      bool ex = false;
+      for (int i = 0; i < s_nref; ++i) ex = ex || (s_ref[i] == lane);
+      const double v = (lane < n) ? (ex ? x_z[lane] : c_z[lane]) : -INFINITY;
+      const double bw = (lane < n && !ex) ? bound(c_z[lane]) : 0.0;
+      const int e = (lane < n) ? c_id[lane] : 0x7fffffff;
+      int rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const double vj = readlane_f64(v, j);
+        const int ej = __builtin_amdgcn_readlane(e, j);
+        rank += (vj > v) || (vj == v && ej < e);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane < n) {          // reuse the first slots of the candidate lists
+        s_val[rank] = v;
+        x_z[rank] = bw;
+        s_id[rank] = e;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // adjacent ranks r < k: disjoint intervals, or both exact (their
+      // order is then the exact order, ties by index)
+      const int npair = min(k, n - 1);
+      bool bad = false;
+      if (lane < npair) {
+        const double hv = s_val[lane], hb = x_z[lane], lv = s_val[lane + 1], lb = x_z[lane + 1];
+        bad = !((hv - hb > lv + lb) || (hb == 0.0 && lb == 0.0));
+      }
+      if (__ballot(bad) == 0ull) {
+        if (lane < k) s_w[lane] = exp(s_val[lane] - s_val[0]);
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (lane < k) {
+          double sum = 0.0;
+          for (int j = 0; j < k; ++j) sum += s_w[j];
+          oi[lane] = s_id[lane];
+          og[lane] = (float)(s_w[lane] / sum);
+        }
+        if (lane == 0) s_done = 1;
+      }
+    }
+    __syncthreads();
+    if (s_done) return;
+  }
+
+  // 5b. exact path.
+  auto process = [&](int nc) {
+    for (int i = wave; i < nc; i += kWavesSel) {
+      const double zz = refine_logit<ACT>(a, t, c_id[i], bins[wave], lane);
+      if (lane == 0) c_z[i] = zz;
+    }
+    __syncthreads();
+    const int ntop = s_ntop;
+    const int nu = ntop + nc;
+    for (int q = tid; q < nu; q += kSelectThreads) {
+      const int eu = (q < ntop) ? top_e[q] : c_id[q - ntop];
+      const double zu = (q < ntop) ? top_z[q] : c_z[q - ntop];
+      int rank = 0;
+      for (int w = 0; w < nu; ++w) {
+        const int ew = (w < ntop) ? top_e[w] : c_id[w - ntop];
+        const double zw = (w < ntop) ? top_z[w] : c_z[w - ntop];
+        rank += (zw > zu) || (zw == zu && ew < eu);
+      }
+      if (rank < k) {
+        new_e[rank] = eu;
+        new_z[rank] = zu;
+      }
+    }
+    __syncthreads();
+    const int nn = min(k, nu);
+    if (tid < nn) {
+      top_e[tid] = new_e[tid];
+      top_z[tid] = new_z[tid];
+    }
+    if (tid == 0) {
+      s_ntop = nn;
+      c_cnt = 0;
+    }
+    __syncthreads();
+  };
+
+  // the candidates near the k-th largest value, refined exactly: the
+  // survivors in one range, or (degenerate: more survivors than LDS holds)
+  // every expert, range by range, from the approximate logits zr
+  const bool degenerate = n > kSelectMaxCand;
+  double th;
+  if (!degenerate) {
+    // tau = k-th largest z_hat among the survivors, then the band around it
+    for (int i = tid; i < n; i += kSelectThreads) {
+      const double v = s_val[i];
+      int gt = 0, ge = 0;
+      for (int j = 0; j < n; ++j) {
+        gt += s_val[j] > v;
+        ge += s_val[j] >= v;
+      }
+      if (gt < k && k <= ge) s_tau = v;
+    }
+    __syncthreads();
+    th = cand_threshold(lower(s_tau), Bt, u);
+  } else {
+    // bisection on the monotone 64-bit key for tau
+    unsigned long long K = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const unsigned long long cand = K | (1ull << bit);
+      int cnt = 0;
+      for (int e = tid; e < E; e += kSelectThreads) cnt += (f64_key(zr(e)) >= cand);
+      cnt = block_sum_i(cnt, red);
+      if (cnt >= k) K = cand;
+    }
+    const double tau = (K == 0) ? -INFINITY : key_f64(K);
+    th = cand_threshold(lower_b(tau, Btz, uz), Btz, uz);
+  }
+  const int span = degenerate ? E : n;
+  for (int r0 = 0; r0 < span; r0 += kSelectMaxCand) {
+    const int r1 = min(span, r0 + kSelectMaxCand);
+    for (int i = r0 + tid; i < r1; i += kSelectThreads) {
+      if (degenerate) {
+        const double v = zr(i);
+        if (isfinite(v) && v >= th) c_id[atomicAdd(&c_cnt, 1)] = i;
+      } else if (s_val[i] >= th) {
+        c_id[atomicAdd(&c_cnt, 1)] = s_id[i];
+      }
+    }
+    __syncthreads();
+    process(c_cnt);
+  }
+
+  // 6. outputs: gates = softmax over the k exact logits (f64), one thread per gate.
+  const int nt = s_ntop;
+  if (nt == k && tid < k) s_w[tid] = exp(top_z[tid] - top_z[0]);
+  __syncthreads();
+  if (tid < k) {
+    if (nt < k) {
+      oi[tid] = (tid < nt) ? top_e[tid] : -1;
+      og[tid] = NAN;
+    } else {
+      double sum = 0.0;
+      for (int j = 0; j < k; ++j) sum += s_w[j];
+      oi[tid] = top_e[tid];
+      og[tid] = (float)(s_w[tid] / sum);
+    }
+  }
+  if (tid == 0 && nt < k) atomicOr(a.dev_flag, kDevNonFinite);
+}
+
+
 // The selection of token t by one block of kSelectThreads threads (every
 // thread must call it); idx and gates go to oi[k] and og[k], global or LDS.
 template <int ACT>
 __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t* oi, float* og) {
   constexpr int GPT = 12;                          // group maxima per thread (E <= 24,576 in one pass)
   constexpr int GPASS = kSelectThreads * GPT;      // groups per pass
-  __shared__ double s_val[kSelectMaxCand];
-  __shared__ int s_id[kSelectMaxCand];
-  __shared__ int c_id[kSelectMaxCand];
-  __shared__ double c_z[kSelectMaxCand];
-  __shared__ int s_glist[kSelectMaxCand];
-  __shared__ float s_tmax[kSelectThreads];
-  __shared__ int top_e[kMaxK], new_e[kMaxK];
-  __shared__ double top_z[kMaxK], new_z[kMaxK], s_w[kMaxK];
-  __shared__ long long bins[kWavesSel][kBins];
-  __shared__ double red[kWavesSel];
-  __shared__ int s_cnt, c_cnt, s_ntop, s_done, s_ng, s_nref;
-  __shared__ int s_ref[64];                        // ranks refined by the cluster pass
-  __shared__ double x_z[64];                       // their exact logits, by rank
-  __shared__ double s_tau, s_th0;
-  __shared__ float s_thf;                          // s_th0 in binary32, rounded down
+  __shared__ SelectLds S;
+  MOE_SELECT_LDS_NAMES(S);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k;
@@ -476,204 +756,7 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
   __syncthreads();
   const int n = (s_ng > kSelectMaxCand) ? kSelectMaxCand + 1 : s_cnt;
 
-  // 5a. fast path: one wave ranks the survivors and certifies the order.
-  if (n <= 64 && !a.force_exact && wave == 0) {
-    const double v = (lane < n) ? s_val[lane] : -INFINITY;
-    const int e = (lane < n) ? s_id[lane] : 0x7fffffff;
-    int rank = 0;
-    for (int j = 0; j < n; ++j) {
-      const double vj = readlane_f64(v, j);
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      rank += (vj > v) || (vj == v && ej < e);
-    }
-    if (lane < n) {
-      c_z[rank] = v;
-      c_id[rank] = e;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // ranks r and r+1 must not overlap for r < k (order of the k, and the cut)
-    const int npair = min(k, n - 1);
-    bool bad = false;
-    if (lane < npair) {
-      const double hi = c_z[lane], lo = c_z[lane + 1];
-      bad = !(hi - bound(hi) > lo + bound(lo));
-    }
-    const unsigned long long bm = __ballot(bad);
-    const bool certified = (n >= k) && (bm == 0ull);
-    if (certified) {
-      if (lane < k) s_w[lane] = exp(c_z[lane] - c_z[0]);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if (lane < k) {
-        double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += s_w[j];
-        oi[lane] = c_id[lane];
-        og[lane] = (float)(s_w[lane] / sum);
-      }
-      if (lane == 0) s_done = 1;
-    } else if (n >= k) {
-      // cluster pass: the ranks of every overlapping pair, and, when the
-      // cut (k-1, k) overlaps, every later rank whose interval reaches the
-      // lower end of rank k's, are refined to their exact logits
-      bool mark = lane < n && ((((bm >> lane) & 1ull) != 0) || (lane > 0 && ((bm >> (lane - 1)) & 1ull) != 0));
-      if (((bm >> (k - 1)) & 1ull) != 0 && lane > k && lane < n) {
-        const double zk = c_z[k];
-        if (c_z[lane] + bound(c_z[lane]) >= zk - bound(zk)) mark = true;
-      }
-      const unsigned long long mm = __ballot(mark);
-      if (mark) s_ref[__popcll(mm & ((1ull << lane) - 1ull))] = lane;
-      if (lane == 0) s_nref = (__popcll(mm) <= 2 * kWavesSel) ? __popcll(mm) : 0;
-    }
-  }
-  __syncthreads();
-  if (s_done) return;
-  if (s_nref > 0) {
-    for (int i = wave; i < s_nref; i += kWavesSel) {
-      const double zz = refine_logit<ACT>(a, t, c_id[s_ref[i]], bins[wave], lane);
-      if (lane == 0) x_z[s_ref[i]] = zz;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // re-rank with the exact logits where known (interval of width 0)
-      bool ex = false;
-      for (int i = 0; i < s_nref; ++i) ex = ex || (s_ref[i] == lane);
-      const double v = (lane < n) ? (ex ? x_z[lane] : c_z[lane]) : -INFINITY;
-      const double bw = (lane < n && !ex) ? bound(c_z[lane]) : 0.0;
-      const int e = (lane < n) ? c_id[lane] : 0x7fffffff;
-      int rank = 0;
-      for (int j = 0; j < n; ++j) {
-        const double vj = readlane_f64(v, j);
-        const int ej = __builtin_amdgcn_readlane(e, j);
-        rank += (vj > v) || (vj == v && ej < e);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if (lane < n) {          // reuse the first slots of the candidate lists
-        s_val[rank] = v;
-        x_z[rank] = bw;
-        s_id[rank] = e;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      // adjacent ranks r < k: disjoint intervals, or both exact (their
-      // order is then the exact order, ties by index)
-      const int npair = min(k, n - 1);
-      bool bad = false;
-      if (lane < npair) {
-        const double hv = s_val[lane], hb = x_z[lane], lv = s_val[lane + 1], lb = x_z[lane + 1];
-        bad = !((hv - hb > lv + lb) || (hb == 0.0 && lb == 0.0));
-      }
-      if (__ballot(bad) == 0ull) {
-        if (lane < k) s_w[lane] = exp(s_val[lane] - s_val[0]);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (lane < k) {
-          double sum = 0.0;
-          for (int j = 0; j < k; ++j) sum += s_w[j];
-          oi[lane] = s_id[lane];
-          og[lane] = (float)(s_w[lane] / sum);
-        }
-        if (lane == 0) s_done = 1;
-      }
-    }
-    __syncthreads();
-    if (s_done) return;
-  }
-
-  // 5b. exact path.
-  auto process = [&](int nc) {
-    for (int i = wave; i < nc; i += kWavesSel) {
-      const double zz = refine_logit<ACT>(a, t, c_id[i], bins[wave], lane);
-      if (lane == 0) c_z[i] = zz;
-    }
-    __syncthreads();
-    const int ntop = s_ntop;
-    const int nu = ntop + nc;
-    for (int q = tid; q < nu; q += kSelectThreads) {
-      const int eu = (q < ntop) ? top_e[q] : c_id[q - ntop];
-      const double zu = (q < ntop) ? top_z[q] : c_z[q - ntop];
-      int rank = 0;
-      for (int w = 0; w < nu; ++w) {
-        const int ew = (w < ntop) ? top_e[w] : c_id[w - ntop];
-        const double zw = (w < ntop) ? top_z[w] : c_z[w - ntop];
-        rank += (zw > zu) || (zw == zu && ew < eu);
-      }
-      if (rank < k) {
-        new_e[rank] = eu;
-        new_z[rank] = zu;
-      }
-    }
-    __syncthreads();
-    const int nn = min(k, nu);
-    if (tid < nn) {
-      top_e[tid] = new_e[tid];
-      top_z[tid] = new_z[tid];
-    }
-    if (tid == 0) {
-      s_ntop = nn;
-      c_cnt = 0;
-    }
-    __syncthreads();
-  };
-
-  if (n <= kSelectMaxCand) {
-    // tau = k-th largest z_hat among the survivors, then the band around it
-    for (int i = tid; i < n; i += kSelectThreads) {
-      const double v = s_val[i];
-      int gt = 0, ge = 0;
-      for (int j = 0; j < n; ++j) {
-        gt += s_val[j] > v;
-        ge += s_val[j] >= v;
-      }
-      if (gt < k && k <= ge) s_tau = v;
-    }
-    __syncthreads();
-    const double th = cand_threshold(lower(s_tau), Bt, u);
-    for (int i = tid; i < n; i += kSelectThreads)
-      if (s_val[i] >= th) c_id[atomicAdd(&c_cnt, 1)] = s_id[i];
-    __syncthreads();
-    process(c_cnt);
-  } else {
-    // degenerate: more survivors than LDS holds.  Bisection on the monotone
-    // 64-bit key for tau, then the candidates range by range.
-    unsigned long long K = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const unsigned long long cand = K | (1ull << bit);
-      int cnt = 0;
-      for (int e = tid; e < E; e += kSelectThreads) cnt += (f64_key(zr(e)) >= cand);
-      cnt = block_sum_i(cnt, red);
-      if (cnt >= k) K = cand;
-    }
-    const double tau = (K == 0) ? -INFINITY : key_f64(K);
-    const double th = cand_threshold(lower(tau), Bt, u);
-    for (int r0 = 0; r0 < E; r0 += kSelectMaxCand) {
-      const int r1 = min(E, r0 + kSelectMaxCand);
-      for (int e = r0 + tid; e < r1; e += kSelectThreads) {
-        const double v = zr(e);
-        if (isfinite(v) && v >= th) c_id[atomicAdd(&c_cnt, 1)] = e;
-      }
-      __syncthreads();
-      process(c_cnt);
-    }
-  }
-
-  // 6. outputs: gates = softmax over the k exact logits (f64), one thread per gate.
-  const int nt = s_ntop;
-  if (nt == k && tid < k) s_w[tid] = exp(top_z[tid] - top_z[0]);
-  __syncthreads();
-  if (tid < k) {
-    if (nt < k) {
-      oi[tid] = (tid < nt) ? top_e[tid] : -1;
-      og[tid] = NAN;
-    } else {
-      double sum = 0.0;
-      for (int j = 0; j < k; ++j) sum += s_w[j];
-      oi[tid] = top_e[tid];
-      og[tid] = (float)(s_w[tid] / sum);
-    }
-  }
-  if (tid == 0 && nt < k) atomicOr(a.dev_flag, kDevNonFinite);
+  select_tail<ACT>(a, t, n, S, Bt, u, zr, Bt, u, oi, og);
 }
 
 // SelectArgs of a layer for one call (host).

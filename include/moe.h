@@ -91,6 +91,8 @@ typedef enum {
 /* desc.flags */
 #define MOE_LAYER_FORCE_EXACT_REFINE 1u  /* debug: every near-tie logit goes through
                                             the slow integer accumulator */
+#define MOE_LAYER_SCREEN_ON  2u  /* build the router screen (see moe_router_screen) */
+#define MOE_LAYER_SCREEN_OFF 4u  /* never build it (batch-1 routing reads the bf16 router) */
 
 typedef struct {
   int32_t hidden;         /* H: multiple of 8 (of 32 for MOE_Q4B32), 8 <= H <= 8192 */
@@ -117,8 +119,12 @@ typedef struct moe_layer moe_layer;   /* opaque; immutable after creation */
 /* Validate `desc` and build a layer.  The only call that allocates device
  * memory (an expert-major router copy when router_layout is MOE_ROUTER_HE,
  * the per-expert router row norms used to bound rounding errors, the sticky
- * device-error word) and the only one that synchronises `stream`.  On error
- * *out is set to NULL. */
+ * device-error word, and -- with MOE_LAYER_SCREEN_ON (bf16 activations, H a
+ * multiple of 32) -- the router screen: an int8 copy
+ * of the router with a per-expert scale and residual norms, E H + 12 E
+ * bytes, see moe_router_screen) and the only one that synchronises `stream`.
+ * Returns MOE_E_RANGE when the router weights or the bias are not finite.
+ * On error *out is set to NULL. */
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out);
 
 /* Free what moe_layer_create allocated.  NULL is accepted.  The caller must
@@ -160,6 +166,25 @@ moe_status moe_route(const moe_layer* layer, const void* x, int32_t T,
  * batch-1 decode.
  *   x [T][H] act_dtype; z f64 [T][E] out (8-byte aligned); ws as for moe_route. */
 moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, double* z,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* The router's int8 first pass ("screen"), which moe_route and
+ * moe_grouped_forward use for T = 1 on layers that have one.  The pages'
+ * routing kernel scores every expert for each token (pyshine tour,
+ * Understanding the Architecture, paragraph on the residency tiers); at
+ * batch 1 that pass is bound by the router bytes it reads, so the screen
+ * reads an int8 copy (q_e = rint(R_e / s_e), s_e = max|R_e| / 127) with the
+ * hidden state in a 15-bit fixed point, and
+ *   v[t][e] = s_e 2^-m sum_h q_eh X_th + b_e     (exact integer dot products),
+ *   |v - z| <= bound[t][e] = ||x_t|| ||R_e - s_e q_e|| + ||delta_t|| ||s_e q_e||
+ *                            + 2^-23 |v| + 2^-52 max|b| + 2^-140,
+ * where z is the exact logit and delta_t the rounding of x_t to the fixed
+ * point.  The routing recomputes exactly the experts whose interval reaches
+ * the k-th largest lower end, so idx and gates do not depend on the screen.
+ *   x [T][H] bf16; v fp32 [T][E] out; bound fp32 [T][E] out or NULL (then
+ *   one kernel runs: the screen alone); ws as for moe_route.
+ * Returns MOE_E_DTYPE for a layer without a screen. */
+moe_status moe_router_screen(const moe_layer* layer, const void* x, int32_t T, float* v, float* bound,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* Experts of one token: out[H] = sum_j gates[j] * expert_{idx[j]}(x).

@@ -66,7 +66,9 @@ def create(desc):
     (dict(max_tokens=0), -2), (dict(max_tokens=70000), -2),
     (dict(act_dtype=2), -3), (dict(act_dtype=7), -3), (dict(expert_dtype=9), -3),
     (dict(expert_dtype=B.MOE_F32), -3),                       # fp32 experts with bf16 x
-    (dict(router_layout=5), -3), (dict(flags=4), -6),
+    (dict(router_layout=5), -3), (dict(flags=8), -6),
+    (dict(flags=B.MOE_LAYER_SCREEN_ON | B.MOE_LAYER_SCREEN_OFF), -6),
+    (dict(flags=B.MOE_LAYER_SCREEN_ON, act_dtype=B.MOE_F32, expert_dtype=B.MOE_F32), -3),   # screen needs bf16 x
     (dict(router_w=0), -1), (dict(w_down=0), -1),
     (dict(expert_dtype=B.MOE_Q4B32), -1),                     # 4-bit without scales
     (dict(expert_dtype=B.MOE_Q4B32, hidden=264, s_gate=8, s_up=8, s_down=8), -2),  # H % 32
@@ -93,6 +95,8 @@ def test_entry_points_refuse_null_layer():
     assert lib.moe_route(None, 1, 1, 1, 1, 1, 1, None) == -1
     assert lib.moe_expert_decode(None, 1, 1, 1, 1, 1, 1, None) == -1
     assert lib.moe_grouped_forward(None, 1, 1, 1, 1, 0, 1, 1, 1, None) == -1
+    assert lib.moe_grouped_forward_noalloc(None, 1, 1, 1, 1, 0, 1, None) == -1
+    assert lib.moe_router_screen(None, 1, 1, 1, 1, 1, 1, None) == -1
     code = ctypes.c_int32()
     assert lib.moe_device_error(None, None, ctypes.byref(code)) == -1
     assert lib.moe_layer_destroy(None) == 0

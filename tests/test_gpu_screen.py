@@ -1,0 +1,251 @@
+"""The router's int8 first pass (screen) on the GPU: its per-expert error
+bound holds for every expert, and routing through it gives the oracle's
+indices and gates -- at full size, on small layers that force it on, and on
+the edge cases (ties, near ties, all-equal logits, tiny and non-finite
+hidden states).  The batch-1 fused kernel's output must equal moe_route +
+moe_expert_decode bit for bit."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny_q4": synth.small_spec(H=256, E=200, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                                bias_alpha=0.37, weight_seed=23, token_seed=24, name="tiny_q4"),
+    "tiny_bf16": synth.small_spec(H=256, E=200, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_BF16,
+                                  bias_alpha=0.37, weight_seed=21, token_seed=22, name="tiny_bf16"),
+    "wide_q4": synth.small_spec(H=2048, E=130, k=10, I=256, act=synth.DT_BF16, expert=synth.DT_Q4,
+                                bias_alpha=0.37, weight_seed=25, token_seed=26, name="wide_q4"),
+    "odd_q4": synth.small_spec(H=96, E=70, k=3, I=32, act=synth.DT_BF16, expert=synth.DT_Q4,
+                               bias_alpha=None, weight_seed=27, token_seed=28, name="odd_q4"),
+    "q4_h4096": synth.small_spec(H=4096, E=70, k=8, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                                 bias_alpha=0.37, weight_seed=83, token_seed=84, name="q4_h4096"),
+    "k20_q4": synth.small_spec(H=512, E=3000, k=20, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                               bias_alpha=0.37, weight_seed=53, token_seed=54, name="k20_q4"),
+}
+_cache = {}
+
+
+def setup(name):
+    if name not in _cache:
+        import synth.device as SD
+        spec = SMALL[name]
+        _cache[name] = (spec, SD.device_layer(spec), G.host_oracle(spec))
+    return _cache[name]
+
+
+def screen_flags(extra=0):
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_ON
+    return MOE_LAYER_SCREEN_ON | extra
+
+
+def per_token(layer, x, n):
+    """moe_grouped_forward one token at a time, then moe_route +
+    moe_expert_decode one token at a time (both T = 1, the screened path)."""
+    torch = G.torch_mod()
+    dev = x.device
+    ws = layer.workspace(1)
+    fi = torch.empty((n, layer.k), dtype=torch.int32, device=dev)
+    fg = torch.empty((n, layer.k), dtype=torch.float32, device=dev)
+    fo = torch.empty((n, layer.H), dtype=torch.float32, device=dev)
+    si, sg, so = torch.empty_like(fi), torch.empty_like(fg), torch.empty_like(fo)
+    for t in range(n):
+        layer.grouped_forward(x[t], 1, fi[t], fg[t], 0, fo[t], ws)
+        layer.route(x[t], 1, si[t], sg[t], ws)
+        layer.expert_decode(x[t], si[t], sg[t], so[t], ws)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in (fi, fg, fo, si, sg, so)]
+
+
+def check_bitwise(fi, fg, fo, si, sg, so):
+    assert np.array_equal(fi, si)
+    assert np.array_equal(fg.view(np.uint32), sg.view(np.uint32))
+    assert np.array_equal(fo.view(np.uint32), so.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("exact", [False, True])
+def test_screened_decode_small(name, exact):
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_FORCE_EXACT_REFINE
+    spec, dl, L = setup(name)
+    G.note("screen small", name, exact)
+    n = 8 if exact else 24
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags(MOE_LAYER_FORCE_EXACT_REFINE if exact else 0))
+    x = SD.device_tokens(spec, 300, n)
+    fi, fg, fo, si, sg, so = per_token(layer, x, n)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 300, n)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, f"screen {name}")
+    check_bitwise(fi, fg, fo, si, sg, so)
+    assert layer.device_error() == 0
+
+
+def _exact_logits(spec, first, n, R=None, b=None):
+    X = oracle.tokens_f64(spec, first, n)
+    if R is None:
+        L = oracle.layer_from_spec(spec)
+        R, b = L.R, L.b
+    return X, X @ R + b[None, :]
+
+
+@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "q4_h4096"])
+def test_screen_bound_small(name):
+    """|v - z| <= bound for every expert of 16 tokens (z: float64, whose own
+    error is below 1e-12 here)."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, _ = setup(name)
+    layer = SD.make_layer(dl, max_tokens=16, flags=screen_flags())
+    x = SD.device_tokens(spec, 40, 16)
+    v = torch.empty((16, spec.E), dtype=torch.float32, device="cuda")
+    bd = torch.empty_like(v)
+    layer.router_screen(x, 16, v, bd, layer.workspace(16))
+    torch.cuda.synchronize()
+    _, Z = _exact_logits(spec, 40, 16)
+    err = np.abs(v.cpu().numpy().astype(np.float64) - Z)
+    ratio = err / bd.cpu().numpy()
+    print(f"{name}: screen |err|/bound max {ratio.max():.3f}, bound mean {bd.cpu().numpy().mean():.3e}")
+    assert ratio.max() < 1.0
+
+
+def test_screen_bound_fullsize():
+    """The 4-bit decode layer at full size: every expert of 6 tokens."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec = synth.CONFIGS["decode_q4"]
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=6, flags=screen_flags())
+    x = SD.device_tokens(spec, 10, 6)
+    v = torch.empty((6, spec.E), dtype=torch.float32, device="cuda")
+    bd = torch.empty_like(v)
+    layer.router_screen(x, 6, v, bd, layer.workspace(6))
+    torch.cuda.synchronize()
+    G.note("screen bound full size: oracle logits")
+    _, Z = _exact_logits(spec, 10, 6)
+    vv, bb = v.cpu().numpy().astype(np.float64), bd.cpu().numpy().astype(np.float64)
+    err = np.abs(vv - Z)
+    ratio = err / bb
+    # experts the bound leaves undecided (what the selection recomputes)
+    k = spec.k
+    lo = np.sort(vv - bb, axis=1)[:, -k]
+    ncand = ((vv + bb) >= lo[:, None]).sum(axis=1)
+    print(f"full size: |err|/bound max {ratio.max():.3f}; bound mean {bb.mean():.3f}; "
+          f"max |err| {err.max():.3e}; experts left undecided per token {ncand.tolist()}")
+    assert ratio.max() < 1.0
+    assert ncand.max() <= 256
+    del layer, dl
+
+
+def test_screen_ties_and_near_ties():
+    """Copies of the rank-1 and rank-k-1 experts (exact ties: lower index
+    first) and a row one bf16 ulp from the top expert, routed through the
+    screen (their screen values are equal or nearly so, and the recomputed
+    logits decide)."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec = synth.small_spec(H=256, E=96, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_BF16,
+                            bias_alpha=None, weight_seed=43, token_seed=44, name="inv_bf16")
+    dl = SD.device_layer(spec)
+    x = SD.device_tokens(spec, 0, 6)
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    idx0, _, _ = G.run_grouped(layer, x[0:1])
+    top = [int(v) for v in idx0[0]]
+    R = dl.router_eh.clone()
+    used = set(top)
+    for src, shift in ((top[1], 9), (top[spec.k - 1], -5)):
+        dst = (src + shift) % spec.E
+        while dst in used:
+            dst = (dst + 1) % spec.E
+        R[dst] = R[src]
+        used.add(dst)
+    near = (top[0] + 3) % spec.E
+    while near in used:
+        near = (near + 1) % spec.E
+    R[near] = R[top[0]]
+    R[near].view(torch.int16)[37] += 1
+    dl2 = SD.DeviceLayer(spec, R, dl.bias, dl.w_gate, dl.w_up, dl.w_down)
+    layer2 = SD.make_layer(dl2, max_tokens=1, flags=screen_flags())
+    fi, fg, fo, si, sg, so = per_token(layer2, x, 6)
+    Rh = oracle.decode_bf16(SD.to_numpy_bits(R)).T
+    L = oracle.OracleLayer(Rh, np.zeros(spec.E), spec.k, lambda e, w: synth.expert_stored(spec, e, w))
+    o_idx, o_g, _, o_out = oracle.moe_tokens(oracle.tokens_f64(spec, 0, 6), L)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, "screen ties")
+    check_bitwise(fi, fg, fo, si, sg, so)
+    assert layer2.device_error() == 0
+
+
+def test_screen_all_equal_logits():
+    """x = 0, no bias: 3000 equal logits -- the screen decides nothing and
+    the selection falls back to scanning every screen value."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec = synth.small_spec(H=256, E=3000, k=6, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                            bias_alpha=None, weight_seed=51, token_seed=52, name="equal")
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    x = torch.zeros((2, spec.H), dtype=torch.bfloat16, device="cuda")
+    fi, fg, fo, si, sg, so = per_token(layer, x, 2)
+    assert np.array_equal(fi, np.tile(np.arange(spec.k), (2, 1)))
+    assert np.all(fg == np.float32(1.0 / spec.k))
+    assert np.all(fo == 0.0)
+    check_bitwise(fi, fg, fo, si, sg, so)
+    assert layer.device_error() == 0
+
+
+def test_screen_nan_hidden_state():
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup("tiny_q4")
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    x = SD.device_tokens(spec, 0, 3)
+    x[1, 17] = float("nan")
+    fi, fg, fo, si, sg, so = per_token(layer, x, 3)
+    assert layer.device_error() & 4
+    for a in (fi, si):
+        assert np.all(a[1] == -1)
+    for a in (fg, fo, sg, so):
+        assert np.all(np.isnan(a[1]))
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, 3)
+    G.compare(fi[[0, 2]], fg[[0, 2]], fo[[0, 2]], o_idx[[0, 2]], o_g[[0, 2]], o_out[[0, 2]], "screen nan/others")
+
+
+def test_screen_tiny_hidden_state():
+    """Hidden states scaled by 2^-80 through the screen: routing as the oracle's."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup("tiny_q4")
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    scale = 2.0 ** -80
+    x = (SD.device_tokens(spec, 0, 8).float() * scale).to(torch.bfloat16)
+    Xh = oracle.tokens_f64(spec, 0, 8) * scale
+    assert np.array_equal(oracle.decode_bf16(SD.to_numpy_bits(x)), Xh)
+    fi, fg, fo, si, sg, so = per_token(layer, x, 8)
+    o_idx, o_g, _, _ = oracle.moe_tokens(Xh, L)
+    G.compare(fi, fg, None, o_idx, o_g, None, "screen tiny x")
+    check_bitwise(fi, fg, fo, si, sg, so)
+    assert layer.device_error() == 0
+
+
+def test_screen_off_flag_and_refusals():
+    torch = G.torch_mod()
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_OFF, MOE_LAYER_SCREEN_ON
+    from expert_routing_quantized_amd.binding import MoeError
+    spec, dl, L = setup("tiny_q4")
+    off = SD.make_layer(dl, max_tokens=1, flags=MOE_LAYER_SCREEN_OFF)
+    x = SD.device_tokens(spec, 0, 1)
+    v = torch.empty((1, spec.E), dtype=torch.float32, device="cuda")
+    with pytest.raises(MoeError) as e:
+        off.router_screen(x, 1, v, None, off.workspace(1))
+    assert e.value.status == -3
+    with pytest.raises(MoeError) as e:
+        SD.make_layer(dl, max_tokens=1, flags=MOE_LAYER_SCREEN_ON | MOE_LAYER_SCREEN_OFF)
+    assert e.value.status == -6
+    f32 = synth.CONFIGS["tiny_f32"]
+    with pytest.raises(MoeError) as e:
+        SD.make_layer(SD.device_layer(f32), max_tokens=1, flags=MOE_LAYER_SCREEN_ON)
+    assert e.value.status == -3
