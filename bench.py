@@ -56,6 +56,9 @@ def parse():
                    help="cost table of moe_grouped_forward over T: 1-8 tokens through the 4-bit layer, "
                         "16-8192 through the bf16 layer (one JSON line)")
     p.add_argument("--mode", default="cold", choices=["cold", "warm"])
+    p.add_argument("--screen", default="on", choices=["on", "off"],
+                   help="batch-1 decode through the router's int8 screen (cold: 6 layer copies, "
+                        "so the int8 routers too exceed the 256 MB last-level cache)")
     p.add_argument("--cpu-sample", type=int, default=800,
                    help="tokens the oracle is timed on (about 10 s of host work; 0: skip)")
     p.add_argument("--layers", type=int, default=1,
@@ -144,9 +147,12 @@ def counters_main(args, spec):
                           "router_flops_per_call": 2.0 * T * spec.H * spec.E,
                           "device_errors": layer.device_error()}), flush=True)
         return
-    n_rep = 3 if args.mode == "cold" else 1
+    screen = args.screen == "on"
+    n_rep = (6 if screen else 3) if args.mode == "cold" else 1
     routers = [dl.router_eh] + [SD.device_router(spec) for _ in range(n_rep - 1)]
-    layers = [SD.make_layer(dl, max_tokens=1, router=r) for r in routers]
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_OFF, MOE_LAYER_SCREEN_ON
+    lflags = MOE_LAYER_SCREEN_ON if screen else MOE_LAYER_SCREEN_OFF
+    layers = [SD.make_layer(dl, max_tokens=1, router=r, flags=lflags) for r in routers]
     X = SD.device_tokens(spec, 0, W + K)
     ws = layers[0].workspace(1)
     idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
@@ -509,14 +515,17 @@ def main():
     if args.layers > 1:
         return layers_main(args, spec)
     K, W = args.steps, args.warmup
-    n_rep = 3 if args.mode == "cold" else 1
+    screen = args.screen == "on"
+    n_rep = (6 if screen else 3) if args.mode == "cold" else 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     t0 = time.time()
     dl = SD.device_layer(spec)
     routers = [dl.router_eh] + [SD.device_router(spec) for _ in range(n_rep - 1)]
-    layers = [SD.make_layer(dl, max_tokens=1, router=r) for r in routers]
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_OFF, MOE_LAYER_SCREEN_ON
+    lflags = MOE_LAYER_SCREEN_ON if screen else MOE_LAYER_SCREEN_OFF
+    layers = [SD.make_layer(dl, max_tokens=1, router=r, flags=lflags) for r in routers]
     X = SD.device_tokens(spec, 0, W + K)
     torch.cuda.synchronize()
     log(f"layer ready in {time.time() - t0:.1f}s: pool {dl.nbytes_pool() / 1e9:.2f} GB, "

@@ -72,6 +72,7 @@ struct PairArgs {
   float* out;        // [T][H]
   int H, I, E, k, T, P;
   int* dev_flag;
+  HintWords* hint;   // batch-1 screen list: the down kernel advances it (block 0), else null
 };
 
 // Expert of pair p if pair p is the first pair naming it (else -1): the
@@ -261,20 +262,22 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(Screen
   const int nblk = a.H >> 5;
   const int bpp = (a.I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock;   // blocks per pair
   const int p = blockIdx.x / bpp, t = p / a.k, j = p - t * a.k;
-  {   // the token's x into LDS (ordered before its reads by the selection's barriers)
-    const int nc = nblk * CK;
+  // the token's x: loaded first, stored to LDS once the selection is done
+  // (a store here would wait for the load before the selection's own loads)
+  const int nc = nblk * CK;
+  constexpr int NU = (64 * MB * CK + kSelectThreads - 1) / kSelectThreads;
+  uint4 xr[NU];
+  {
     const uint4* xs = reinterpret_cast<const uint4*>(a.x) + size_t(t) * nc;
-    constexpr int NU = (64 * MB * CK + kSelectThreads - 1) / kSelectThreads;
-    uint4 xr[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) xr[u] = xs[min(tid + kSelectThreads * u, nc - 1)];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = tid + kSelectThreads * u;
-      if (c < nc) sx[(c / CK) * PK + c % CK] = xr[u];
-    }
   }
   select_policy<ACT, CPLR, SCREEN>(sb, t, s_idx, s_gate);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int c = tid + kSelectThreads * u;
+    if (c < nc) sx[(c / CK) * PK + c % CK] = xr[u];
+  }
   __syncthreads();
   if (j == 0 && blockIdx.x == p * bpp && tid < a.k) {   // first block of the token
     sa.idx[size_t(t) * a.k + tid] = s_idx[tid];
@@ -341,222 +344,6 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(Screen
     const float av = wave_sum(pa), uv = wave_sum(pu);
     const int i = i0 + r;
     if (lane == 0 && i < a.I) a.h[size_t(p) * a.I + i] = valid ? silu_f(av) * uv : NAN;
-  }
-}
-
-// ------------------------------------------- decode: screen select + gate/up + down
-// Batch-1 decode with 4-bit experts after the router's int8 screen: one
-// launch does the selection (select_screen_block, in every block), the
-// gate/up rows of the block's expert, and the down projection with the
-// weighted combine for a slice of the output rows.
-//
-// Block b (of NB = k * bpp) computes kDecodeRowsPerBlock intermediate rows
-// of the expert at rank b / bpp, as select_gateup_q4_kernel does, and then
-// output rows [b H / NB, (b + 1) H / NB) of the combine: 8 lanes per
-// (output row, expert) pair, lane g covering quant block g of the down row.
-// Right after the selection every block issues both its gate/up loads and
-// the down-row loads of its output slice, so the down weights arrive while
-// gate/up computes.  The down projection needs h of all k experts, which 16
-// blocks each compute a part of: each h value is published as one 64-bit
-// word (the value and a tag 1) with a device-scope atomic store, and every
-// block polls the k I words with device-scope atomic loads until it has
-// seen all of them (the tags were cleared by the screen kernel of the same
-// call, which runs before this one on the stream).  All NB blocks are
-// resident together (NB <= 256 blocks of one CU's worth of LDS each, on a
-// part with 256 CUs), every block publishes before it waits, and the wait is
-// bounded: after kPollLimit rounds the block gives up, raises the internal
-// fault bit and writes NaN.  The per-(row, expert) partials and the
-// combine's summation order are those of down_combine_single_kernel, so the
-// output equals moe_route + moe_expert_decode bit for bit.
-constexpr int kPollLimit = 1 << 21;
-constexpr int kFusedDownMaxI = 256;                  // one quant block per lane of a row group
-constexpr int kFusedDownMaxWords = 4096;             // k I tagged h words at most (8 per thread)
-// h of expert j, quant block g, element i sits at sh[j * kShExpert + g * kShBlock + i]:
-// the padding puts the 8 lanes of a row group (8 blocks of one expert) and
-// neighbouring experts on different LDS banks
-constexpr int kShBlock = 36;
-constexpr int kShExpert = (kFusedDownMaxI / 32) * kShBlock + 4;
-
-__device__ __forceinline__ unsigned long long tag_word(float v) {
-  return (1ull << 32) | (unsigned long long)__float_as_uint(v);
-}
-
-template <int ACT, int MB, int CPL, int UD>
-__global__ __launch_bounds__(kSelectThreads) void decode_screen_q4_kernel(ScreenSelectArgs sb, PairArgs a,
-                                                                         unsigned long long* tags) {
-  constexpr int RPW = kDecodeRowsPerWave;
-  constexpr int CK = XStage<ACT>::kChunks, PK = XStage<ACT>::kPitch;
-  constexpr int kPoll = kFusedDownMaxWords / kSelectThreads;
-  __shared__ uint4 sx[(kMaxH / 32) * PK];
-  __shared__ int32_t s_idx[kMaxK];
-  __shared__ float s_gate[kMaxK];
-  __shared__ __attribute__((aligned(16))) float sh[(kFusedDownMaxWords / kFusedDownMaxI + 1) * kShExpert];   // h of the k experts
-  __shared__ float part[64 * UD];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int H = a.H, I = a.I, k = a.k;
-  const int nblk = H >> 5;
-  const int bpp = (I + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock;
-  const int NB = k * bpp;
-  const int j = blockIdx.x / bpp;
-  {   // the token's x into LDS (ordered before its reads by the selection's barriers)
-    const int nc = nblk * CK;
-    const uint4* xs = reinterpret_cast<const uint4*>(a.x);
-    constexpr int NU = (64 * MB * CK + kSelectThreads - 1) / kSelectThreads;
-    uint4 xr[NU];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) xr[u] = xs[min(tid + kSelectThreads * u, nc - 1)];
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const int c = tid + kSelectThreads * u;
-      if (c < nc) sx[(c / CK) * PK + c % CK] = xr[u];
-    }
-  }
-  select_screen_block<ACT, CPL>(sb, 0, s_idx, s_gate);
-  __syncthreads();
-  if (blockIdx.x == 0 && tid < k) {
-    sb.sel.idx[tid] = s_idx[tid];
-    sb.sel.gates[tid] = s_gate[tid];
-  }
-  // gate/up loads of rows i0, i0 + 1 of the rank-j expert
-  const int i0 = (blockIdx.x - j * bpp) * kDecodeRowsPerBlock + wave * RPW;
-  int e = s_idx[j];
-  const bool valid = e >= 0 && e < a.E;
-  e = valid ? e : 0;                                   // addresses stay in range; h becomes NaN
-  const size_t rowb = size_t(H) / 2;
-  uint4 wg[RPW][MB], wu[RPW][MB];
-  float dg[RPW][MB], du[RPW][MB];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int i = min(i0 + r, I - 1);
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const int b = min(m * 64 + lane, nblk - 1);
-      const size_t row = size_t(e) * I + i;
-      wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * rowb + b * 16);
-      wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * rowb + b * 16);
-      dg[r][m] = f16_to_f32(a.sg[row * nblk + b]);
-      du[r][m] = f16_to_f32(a.su[row * nblk + b]);
-    }
-  }
-  // down loads of this block's (output row, expert) pairs: pair pd is row
-  // o0 + pd % R of the expert at rank pd / R, so the row groups of a wave
-  // share an expert (their h reads in LDS coincide or fall on other banks)
-  const int o0 = int((long long)blockIdx.x * H / NB), o1 = int((long long)(blockIdx.x + 1) * H / NB);
-  const int R = o1 - o0;
-  const int npd = R * k;
-  const int g = lane & 7, grp = tid >> 3;
-  const int dblk = I >> 5;                             // quant blocks of a down row (<= 8)
-  uint4 wd[UD];
-  float dd[UD];
-#pragma unroll
-  for (int u = 0; u < UD; ++u) {
-    const int pd = min(grp + 64 * u, npd - 1);
-    const int jj = pd / R, o = o0 + pd - jj * R;
-    const int ej = s_idx[jj];
-    const int ec = (ej >= 0 && ej < a.E) ? ej : 0;
-    const size_t row = size_t(ec) * H + o;
-    const int gb = min(g, dblk - 1);
-    wd[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + gb * 16);
-    dd[u] = f16_to_f32(a.sd[row * dblk + gb]);
-  }
-  // gate/up arithmetic of gateup_q4_kernel, h published as tagged words
-#pragma unroll
-  for (int r = 0; r < RPW; ++r)
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-      if (!(i0 + r < I && m * 64 + lane < nblk)) dg[r][m] = du[r][m] = 0.f;
-  {
-    float xv[MB][32];
-    float xsum[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      const int b = m * 64 + lane;
-      xsum[m] = 0.f;
-      Chunk<ACT> ch[4];
-      const uint4* sbx = sx + min(b, nblk - 1) * PK;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if constexpr (ACT == MOE_BF16) {
-          ch[c].v = sbx[c];
-        } else {
-          const uint4 p0 = sbx[2 * c], p1 = sbx[2 * c + 1];
-          ch[c].a = make_float4(__uint_as_float(p0.x), __uint_as_float(p0.y), __uint_as_float(p0.z), __uint_as_float(p0.w));
-          ch[c].b = make_float4(__uint_as_float(p1.x), __uint_as_float(p1.y), __uint_as_float(p1.z), __uint_as_float(p1.w));
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xv[m][c * 8 + i] = (b < nblk) ? ch[c].get(i) : 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) xsum[m] += xv[m][i];
-    }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      float pa = 0.f, pu = 0.f;
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        pa = fmaf(dg[r][m], q4_block_dot(wg[r][m], xv[m]) - 8.f * xsum[m], pa);
-        pu = fmaf(du[r][m], q4_block_dot(wu[r][m], xv[m]) - 8.f * xsum[m], pu);
-      }
-      const float av = wave_sum(pa), uv = wave_sum(pu);
-      const int i = i0 + r;
-      if (lane == 0 && i < I)
-        __hip_atomic_store(tags + size_t(j) * I + i, tag_word(valid ? silu_f(av) * uv : NAN),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  // wait for h of every expert (this thread's words: tid, tid + 512, ...);
-  // two rounds of polls in flight: round r + 1 is issued before round r is
-  // read, so a word published just after a round left is seen one round
-  // trip later instead of two
-  const int nw = k * I;
-  unsigned pending = 0u;
-#pragma unroll
-  for (int v = 0; v < kPoll; ++v)
-    if (tid + kSelectThreads * v < nw) pending |= 1u << v;
-  auto poll = [&](unsigned long long (&got)[kPoll], unsigned pend) {
-#pragma unroll
-    for (int v = 0; v < kPoll; ++v)
-      got[v] = ((pend >> v) & 1u)
-                   ? __hip_atomic_load(tags + tid + kSelectThreads * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                   : 0ull;
-  };
-  bool timed_out = false;
-  unsigned long long cur[kPoll], nxt[kPoll];
-  poll(cur, pending);
-  for (int it = 0;; ++it) {
-    poll(nxt, pending);
-#pragma unroll
-    for (int v = 0; v < kPoll; ++v)
-      if (((pending >> v) & 1u) && (cur[v] >> 32) == 1ull) {
-        const int w = tid + kSelectThreads * v, jw = w / I, iw = w - jw * I;
-        sh[jw * kShExpert + (iw >> 5) * kShBlock + (iw & 31)] = __uint_as_float(unsigned(cur[v]));
-        pending &= ~(1u << v);
-      }
-    if (__syncthreads_and(pending == 0u)) break;
-    if (it >= kPollLimit) {                            // block-uniform
-      timed_out = true;
-      break;
-    }
-#pragma unroll
-    for (int v = 0; v < kPoll; ++v) cur[v] = nxt[v];
-  }
-  if (timed_out && tid == 0) atomicOr(a.dev_flag, kDevInternal);
-  // down partials of this block's pairs, then each output row over the experts in order
-#pragma unroll
-  for (int u = 0; u < UD; ++u) {
-    const int pd = grp + 64 * u;
-    const int jj = min(pd, npd - 1) / R;
-    float y = (g < dblk) ? down_lane_partial_q4(wd[u], dd[u], sh + jj * kShExpert + g * kShBlock) : 0.f;
-    y = group8_sum(y);
-    if (g == 0 && pd < npd) part[pd] = y;
-  }
-  __syncthreads();
-  for (int oo = tid; oo < R; oo += kSelectThreads) {
-    float s = 0.f;
-    for (int jj = 0; jj < k; ++jj) s = fmaf(s_gate[jj], part[jj * R + oo], s);
-    a.out[o0 + oo] = timed_out ? NAN : s;
   }
 }
 
@@ -713,7 +500,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_dense_kernel(Scr
 // registers, so the weights, the scales and h are all in flight together.
 // Each (row, expert) partial y_j is summed over its 8 lanes, and each output
 // row is sum_j g_j y_j in selection order (fmaf chain), the arithmetic of
-// the window kernel and of the fused batch-1 kernel.
+// the window kernel.
 template <int WD>
 __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   __shared__ float part[kMaxK][8];
@@ -729,6 +516,9 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   const int nblk = I >> 5;
   const int32_t* ti = a.idx + size_t(t) * k;
   if (threadIdx.x == 0) s_bad = 0;
+  const bool ends = a.hint != nullptr && blockIdx.x == 0 && t == 0 && wave == 0;   // this wave ends the call
+  HintRead hr{};
+  if (ends) hr = hint_read(a.hint, lane);
   // every wave holds the token's k indices, one per lane (k <= 32), and
   // checks its own experts with a ballot (no dependent loads before the
   // weight loads)
@@ -775,6 +565,7 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
     for (int j = 0; j < k; ++j) s = fmaf(a.gates[size_t(t) * k + j], part[j][threadIdx.x], s);
     a.out[size_t(t) * a.H + blockIdx.x * 8 + threadIdx.x] = s_bad ? NAN : s;
   }
+  if (ends) hint_write(a.hint, hr, lane);
 }
 
 // Short windows (2 <= T <= 8 tokens, P = T k pairs): one block per 8 output
@@ -806,6 +597,9 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
   const int o = blockIdx.x * 8 + grp;
   const int oc = min(o, a.H - 1);
   const int nsl = I >> 5, nblk = I >> 5;
+  const bool ends = a.hint != nullptr && blockIdx.x == 0 && wave == 0;   // this wave ends the call
+  HintRead hr{};
+  if (ends) hr = hint_read(a.hint, lane);
   // 1. h of every pair: all loads in flight (P I / 4 <= 64 kWindowWaves UG)
   const int n4 = P * I / 4;
   float4 hv4[UG];
@@ -886,6 +680,7 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
     for (int j = 0; j < k; ++j) s = fmaf(a.gates[t * k + j], part[t * k + j][r], s);
     a.out[size_t(t) * a.H + blockIdx.x * 8 + r] = s_bad[t] ? NAN : s;
   }
+  if (ends) hint_write(a.hint, hr, lane);
 }
 
 // The window kernels take up to kWindowHLdsBytes of dynamic LDS; allow it
@@ -1070,6 +865,7 @@ static PairArgs pair_args(const Layer& L, const void* x, int T, const int32_t* i
   a.T = T;
   a.P = T * a.k;
   a.dev_flag = L.dev_flag;
+  a.hint = nullptr;
   return a;
 }
 
@@ -1234,63 +1030,15 @@ hipError_t launch_decode_fused(const Layer& L, const void* x, int T, const doubl
   return launch_select_gateup<false>(L, sb, a, s);
 }
 
-// Blocks of the fused screen kernel for a layer (k experts x blocks per expert).
-static int screen_fused_blocks(const Layer& L) {
-  return L.d.top_k * ((L.d.inter + kDecodeRowsPerBlock - 1) / kDecodeRowsPerBlock);
-}
-
-static int screen_fused_ud(const Layer& L) {
-  const int NB = screen_fused_blocks(L);
-  const int rows = (L.d.hidden + NB - 1) / NB;
-  return (rows * L.d.top_k + 63) / 64;
-}
-
-bool decode_screen_fused_down(const Layer& L) {
-  const int NB = screen_fused_blocks(L);
-  return L.screen && L.d.expert_dtype == MOE_Q4B32 && L.d.act_dtype == MOE_BF16 && L.d.inter <= kFusedDownMaxI &&
-         L.d.inter % 32 == 0 && screen_fused_ud(L) <= 4 && NB <= L.resident_blocks &&
-         (L.d.hidden / 8 + 63) / 64 <= 4 && L.d.top_k * L.d.inter <= kFusedDownMaxWords &&
-         L.d.top_k * L.d.inter <= screen_clearable_words(L);
-}
-
-template <int C, int U>
-static const void* decode_screen_kernel() {
-  return reinterpret_cast<const void*>(&decode_screen_q4_kernel<MOE_BF16, 1, C, U>);
-}
-
-// The instantiation of decode_screen_q4_kernel a layer launches (null if none).
-static const void* decode_screen_kernel_for(const Layer& L) {
-  const int cplr = (L.d.hidden / 8 + 63) / 64, ud = screen_fused_ud(L);
-  if (ud > 4) return nullptr;
-  if (cplr <= 1) return ud <= 2 ? decode_screen_kernel<1, 2>() : decode_screen_kernel<1, 4>();
-  if (cplr <= 2) return ud <= 2 ? decode_screen_kernel<2, 2>() : decode_screen_kernel<2, 4>();
-  if (cplr <= 4) return ud <= 2 ? decode_screen_kernel<4, 2>() : ud <= 3 ? decode_screen_kernel<4, 3>()
-                                                                         : decode_screen_kernel<4, 4>();
-  return nullptr;
-}
-
-// Blocks of the layer's fused screen kernel the device holds at once (its
-// blocks wait for each other, so all of them must be resident).
-int decode_screen_resident_blocks(const Layer& L) {
-  const void* f = decode_screen_kernel_for(L);
-  int per_cu = 0, cus = 0;
-  if (!f || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kSelectThreads, 0) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, L.device) != hipSuccess) return 0;
-  return per_cu * cus;
-}
-
 hipError_t launch_decode_screen(const Layer& L, const void* x, const float* z8, const float* g8, const double* xq,
-                                int32_t* idx, float* gates, float* out, float* h, unsigned long long* tags,
+                                const ScreenList* list, int32_t* idx, float* gates, float* out, float* h,
                                 hipStream_t s) {
-  const ScreenSelectArgs sb = make_screen_select_args(L, x, z8, g8, xq, idx, gates);
-  const PairArgs a = pair_args(L, x, 1, idx, gates, out, h);
-  if (!decode_screen_fused_down(L)) return launch_select_gateup<true>(L, sb, a, s);
-  const void* f = decode_screen_kernel_for(L);
-  if (!f) return hipErrorInvalidValue;
-  ScreenSelectArgs sbv = sb;
-  PairArgs av = a;
-  void* args[] = {&sbv, &av, &tags};
-  return hipLaunchKernel(f, dim3(screen_fused_blocks(L)), dim3(kSelectThreads), args, 0, s);
+  if (list == nullptr) return hipErrorInvalidValue;
+  ScreenSelectArgs sb = make_screen_select_args(L, x, z8, g8, xq, idx, gates);
+  PairArgs a = pair_args(L, x, 1, idx, gates, out, h);
+  set_screen_list(sb, L, list, false);
+  a.hint = list->hint;              // the down kernel ends the call
+  return launch_select_gateup<true>(L, sb, a, s);
 }
 
 }  // namespace moe

@@ -11,7 +11,7 @@
 #include <mutex>
 #include <string>
 
-#include "moe_internal.h"
+#include "select_screen.h"
 
 using moe::Layer;
 using moe::Workspace;
@@ -107,15 +107,24 @@ moe_status check_ws(const Layer& L, int T, const void* ws, size_t ws_bytes, Work
   return MOE_OK;
 }
 
+moe::ScreenList screen_list(char* ws, const Workspace& W) {
+  moe::ScreenList l;
+  l.hint = reinterpret_cast<moe::HintWords*>(ws + W.hint);
+  l.cnt8 = reinterpret_cast<unsigned char*>(ws + W.cnt8);
+  l.list = reinterpret_cast<ulonglong2*>(ws + W.list);
+  return l;
+}
+
 moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float* gates,
                       char* ws, const Workspace& W, hipStream_t s) {
   if (T == 1 && L.screen) {     // the int8 first pass, then the selection recomputes its candidates
     float* z8 = reinterpret_cast<float*>(ws + W.z);
     float* g8 = reinterpret_cast<float*>(ws + W.gmax);
     double* xq = reinterpret_cast<double*>(ws + W.xnorm);
-    hipError_t e = moe::launch_screen(L, x, 1, z8, g8, xq, nullptr, 0, s);
+    const moe::ScreenList list = screen_list(ws, W);
+    hipError_t e = moe::launch_screen(L, x, 1, z8, g8, xq, &list, s);
     if (e != hipSuccess) return hip_fail(e, "screen launch");
-    e = moe::launch_select_screen(L, x, 1, z8, g8, xq, idx, gates, s);
+    e = moe::launch_select_screen(L, x, 1, z8, g8, xq, &list, idx, gates, s);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     return MOE_OK;
   }
@@ -184,17 +193,15 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
   float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
   if (flags == MOE_ROUTE_INTERNAL && T == 1 && L.screen) {
-    // batch-1 decode on the screen: the int8 first pass, then one kernel for
-    // the selection, gate/up and (when it fits) down + combine
+    // batch-1 decode on the screen: the int8 first pass (with the list),
+    // the selection fused with gate/up, then down + combine
     float* z8 = reinterpret_cast<float*>(w + W.z);
     float* g8 = reinterpret_cast<float*>(w + W.gmax);
     double* xq = reinterpret_cast<double*>(w + W.xnorm);
-    unsigned long long* tags = reinterpret_cast<unsigned long long*>(w + W.tags);
-    const bool fused = moe::decode_screen_fused_down(L);
-    hipError_t e = moe::launch_screen(L, x, 1, z8, g8, xq, fused ? tags : nullptr,
-                                      fused ? L.d.top_k * L.d.inter : 0, s);
+    const moe::ScreenList list = screen_list(w, W);
+    hipError_t e = moe::launch_screen(L, x, 1, z8, g8, xq, &list, s);
     if (e != hipSuccess) return hip_fail(e, "screen launch");
-    e = moe::launch_decode_screen(L, x, z8, g8, xq, ri, rg, out, reinterpret_cast<float*>(w + W.h), tags, s);
+    e = moe::launch_decode_screen(L, x, z8, g8, xq, &list, ri, rg, out, reinterpret_cast<float*>(w + W.h), s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return MOE_OK;
   }
@@ -240,6 +247,11 @@ Workspace workspace_layout(const Layer& L, int T) {
     off = round_up(off + bytes, 256);
     return o;
   };
+  if (L.screen) {      // first, at the same place for every T (the hint outlives the call)
+    W.hint = take(sizeof(moe::HintWords));
+    W.cnt8 = take(size_t(moe::screen_waves(L)) + 16);
+    W.list = take(size_t(moe::kListSlots) * 16);
+  }
   W.z = take(Tz * E * 8);
   W.gmax = take(Tz * ((E + 3) / 4) * 4);
   W.xnorm = take(Tz * 16);
@@ -258,7 +270,6 @@ Workspace workspace_layout(const Layer& L, int T) {
     W.hm = take(P * I * 4);
     W.y = take(P * H * 4);
   }
-  W.tags = take(k * I * 8);
   W.total = off;
   return W;
 }
@@ -347,7 +358,8 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
     if ((e = hipMalloc(&L.q8, E * H)) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(screen router)"));
     if ((e = hipMalloc(&L.sc8, E * sizeof(float))) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(screen scales)"));
     if ((e = hipMalloc(&L.eb8, E * sizeof(float2))) != hipSuccess) return cleanup(hip_fail(e, "hipMalloc(screen norms)"));
-    if ((e = hipMalloc(&L.screen_consts, 3 * sizeof(float))) != hipSuccess)
+    // 256 bytes: the three maxima, and a stand-in the screen reads in place of a hint
+    if ((e = hipMalloc(&L.screen_consts, 256)) != hipSuccess)
       return cleanup(hip_fail(e, "hipMalloc(screen maxima)"));
     if ((e = moe::launch_screen_prep(L, L.screen_consts, s)) != hipSuccess) return cleanup(hip_fail(e, "screen prep"));
     if ((e = hipMemcpyAsync(sconst, L.screen_consts, sizeof(sconst), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -365,7 +377,6 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
   if (L.screen) {
     if (!(isfinite(sconst[0]) && isfinite(sconst[1]) && isfinite(sconst[2])))
       return cleanup(fail(MOE_E_RANGE, "router weights or bias are not finite"));
-    L.resident_blocks = moe::decode_screen_resident_blocks(L);
   }
   *out = l;
   return ok();
@@ -428,8 +439,8 @@ moe_status moe_router_screen(const moe_layer* layer, const void* x, int32_t T, f
                              void* ws, size_t ws_bytes, void* stream) {
   if (moe_status st = check_layer(layer)) return st;
   const Layer& L = layer->L;
-  if (!L.screen) return fail(MOE_E_DTYPE, "this layer has no router screen (MOE_LAYER_SCREEN_ON with bf16 "
-                                         "activations and hidden %% 32 == 0)");
+  if (!L.screen) return fail(MOE_E_DTYPE, "this layer has no router screen (bf16 activations, hidden %% 32 == 0, "
+                                         "E >= %d or MOE_LAYER_SCREEN_ON)", moe::kScreenMinExperts);
   if (T < 0 || T > L.d.max_tokens) return fail(MOE_E_RANGE, "T=%d outside [0, max_tokens=%d]", T, L.d.max_tokens);
   if (T == 0) return ok();
   if (!x || !v) return fail(MOE_E_NULL, "x and v are required");
@@ -441,7 +452,7 @@ moe_status moe_router_screen(const moe_layer* layer, const void* x, int32_t T, f
   char* w = static_cast<char*>(ws);
   float* g8 = reinterpret_cast<float*>(w + W.gmax);
   double* xq = reinterpret_cast<double*>(w + W.xnorm);
-  hipError_t e = moe::launch_screen(L, x, T, v, g8, xq, nullptr, 0, s);
+  hipError_t e = moe::launch_screen(L, x, T, v, g8, xq, nullptr, s);
   if (e == hipSuccess && bound) e = moe::launch_screen_bounds(L, T, v, xq, bound, s);
   if (e != hipSuccess) return hip_fail(e, "screen launch");
   return ok();

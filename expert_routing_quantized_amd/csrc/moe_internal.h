@@ -43,14 +43,13 @@ struct Layer {
   float2* eb8;              // owned: [E] (||eps_e||, ||s_e q_e||), rounded up
   float* screen_consts;     // owned: device maxima of the two norms and of |b|
   double screen_enmax, screen_rqmax, screen_bmax;   // host copies
-  int resident_blocks;      // blocks of the fused screen decode kernel the device holds at once
 };
 
-// Layers screen the batch-1 router pass only with MOE_LAYER_SCREEN_ON for
-// now: measured at E = 24,576 the recompute of the ~50 undecided experts in
-// every block of the fused kernel costs more than the halved router stream
-// saves.  (The threshold stays for the automatic choice.)
-constexpr int kScreenMinExperts = 1 << 30;
+// Layers with at least this many experts (bf16 activations, H a multiple of
+// 32) screen the batch-1 router pass unless MOE_LAYER_SCREEN_OFF: the int8
+// stream is half the bf16 router's bytes; with fewer experts the router is
+// short enough that the extra kernel work does not pay.
+constexpr int kScreenMinExperts = 4096;
 
 // The router bias as the GEMV and few-token router kernels read it: never
 // null (zeros when the caller gives none), so their loads need no branch.
@@ -76,7 +75,9 @@ struct Workspace {
   size_t tiles_big; // int32, same layout: kBigTileRows-row tiles of experts with more than 32 pairs
   size_t hm;        // fp32 [P][I] grouped intermediate
   size_t y;         // fp32 [P][H] grouped expert outputs
-  size_t tags;      // u64 [k][I] tagged h words of the fused batch-1 screen kernel
+  size_t hint;      // batch-1 screen list: HintWords (128 B; state carried from call to call)
+  size_t cnt8;      // u8 [screen waves] entries each screen wave listed
+  size_t list;      // 16 B [kListSlots] the listed experts' recomputed logits
   size_t total;
 };
 
@@ -366,27 +367,32 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
                                   const Workspace& W, hipStream_t s);
 // screen.hip: the router's int8 first pass (batch-1 routing).  prep builds
 // q8 / sc8 / eb8 and the maxima (consts[3]); screen writes the values z8
-// [T][E], their maxima of 4 g8 and ||x||^2, ||delta||^2 into xq [T][2], and
-// clears `ntags` words at `tags` (may be null) for the call's next kernel.
+// [T][E], their maxima of 4 g8 and ||x||^2, ||delta||^2 into xq [T][2], and,
+// with a list at T = 1, the listed experts' recomputed logits.
+struct HintWords;
+struct ScreenList {            // workspace regions of the batch-1 list
+  HintWords* hint;
+  unsigned char* cnt8;
+  ulonglong2* list;
+};
 hipError_t launch_screen_prep(const Layer& L, float* consts, hipStream_t s);
 hipError_t launch_screen(const Layer& L, const void* x, int T, float* z8, float* g8, double* xq,
-                         unsigned long long* tags, int ntags, hipStream_t s);
-int screen_clearable_words(const Layer& L);
+                         const ScreenList* list, hipStream_t s);
+int screen_waves(const Layer& L);
 struct ScreenSelectArgs;
 ScreenSelectArgs make_screen_select_args(const Layer& L, const void* x, const float* z8, const float* g8,
                                          const double* xq, int32_t* idx, float* gates);
+void set_screen_list(ScreenSelectArgs& b, const Layer& L, const ScreenList* list, bool advance);
 hipError_t launch_select_screen(const Layer& L, const void* x, int T, const float* z8, const float* g8,
-                                const double* xq, int32_t* idx, float* gates, hipStream_t s);
+                                const double* xq, const ScreenList* list, int32_t* idx, float* gates,
+                                hipStream_t s);
 // the screen values' error bounds B_e of tokens [0, T) (inspection)
 hipError_t launch_screen_bounds(const Layer& L, int T, const float* z8, const double* xq, float* bound,
                                 hipStream_t s);
-// experts.hip: batch-1 decode after the screen: selection + gate/up, then down
-// + combine in the same kernel when decode_screen_fused_down (h published as
-// tagged words in `tags`, cleared by the screen), else as its own launch.
-bool decode_screen_fused_down(const Layer& L);
-int decode_screen_resident_blocks(const Layer& L);
+// experts.hip: batch-1 decode after the screen: selection + gate/up, then
+// down + combine (which ends the call: it advances the list's hint).
 hipError_t launch_decode_screen(const Layer& L, const void* x, const float* z8, const float* g8, const double* xq,
-                                int32_t* idx, float* gates, float* out, float* h, unsigned long long* tags,
+                                const ScreenList* list, int32_t* idx, float* gates, float* out, float* h,
                                 hipStream_t s);
 // prep.hip: layer creation helpers.
 hipError_t launch_transpose_router(const Layer& L, void* dst, hipStream_t s);

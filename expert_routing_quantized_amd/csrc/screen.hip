@@ -138,10 +138,42 @@ struct ScreenArgs {
   float* z8;              // [T][E]
   float* g8;              // [T][ceil(E/4)]
   double* xq;             // [T][2]: ||x||^2, ||delta||^2
-  unsigned long long* tags;   // words cleared for the next kernel of the call (or null)
-  int ntags;
   int* dev_flag;
+  // the list (batch 1; hint null: none)
+  const uint16_t* R;      // [E][H] bf16 router
+  const float2* eb8;      // [E] residual norms, rounded up
+  double u8, babs8;       // the bound's relative and absolute terms
+  double rqmax;           // max_e ||s_e q_e|| (rounded up)
+  const HintWords* hint;  // the call's hint, null: no list
+  const HintWords* hsrc;  // never null: hint, or a readable stand-in (read unconditionally)
+  unsigned char* cnt8;    // [waves]
+  ulonglong2* list;       // [kListSlots]
 };
+
+// Puts (e, z) in the table under `tag` (lane 0 of a wave calls it): linear
+// probing from a hash of e; a slot is free unless it holds this call's tag.
+// Every failed compare-and-swap means another wave took that slot, so the
+// probe ends within 2 kListSlots steps; false when the table is full.
+__device__ bool list_insert(ulonglong2* list, unsigned long long tag, int e, double z) {
+  unsigned long long* w = reinterpret_cast<unsigned long long*>(list);
+  const unsigned long long key = (tag << 24) | (unsigned long long)(e + 1);
+  unsigned s = (unsigned(e) * 2654435761u) >> 24;    // 8 bits: kListSlots = 256
+  unsigned long long old = __hip_atomic_load(w + 2 * s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; it < 2 * kListSlots; ++it) {
+    if ((old >> 24) == tag && (old & 0xffffffull) != 0ull) {   // taken in this call
+      s = (s + 1) & (kListSlots - 1);
+      old = __hip_atomic_load(w + 2 * s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      continue;
+    }
+    const unsigned long long seen = atomicCAS(w + 2 * s, old, key);
+    if (seen == old) {
+      w[2 * s + 1] = (unsigned long long)__double_as_longlong(z);
+      return true;
+    }
+    old = seen;
+  }
+  return false;
+}
 
 // One wave owns RPW consecutive rows (RPW a multiple of 4: whole groups of 4
 // experts), WPB waves per block; CH = 16-byte chunks per lane of an int8 row
@@ -149,17 +181,16 @@ struct ScreenArgs {
 // loads the hidden-state elements of its own row chunks l, l + 64, ...
 // (together the wave holds all of x), takes the maximum with a DPP
 // reduction, and writes those elements' digits straight into registers.
-template <int RPW, int WPB, int CH>
+template <int NB, int WPB, int CH>
 __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
-  static_assert(RPW % 4 == 0, "a wave holds whole groups of 4 experts");
+  constexpr int RB = 2, RPW = RB * NB;               // rows per batch, per wave
+  static_assert((WPB * RPW) % 4 == 0, "a block holds whole groups of 4 experts");
+  __shared__ float s_v[WPB * RPW];                   // the block's values (NaN, past E: -inf)
+  __shared__ float s_vf[WPB * RPW], s_eb[WPB * RPW];  // values and ||eps_e|| (for the list)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, E = a.E, t = blockIdx.y;
-  if (a.tags != nullptr && t == 0) {                 // words the call's next kernel waits on start cleared
-    const int w = blockIdx.x * WPB * 64 + tid;
-    if (w < a.ntags) a.tags[w] = 0ull;
-  }
   const int e0 = (blockIdx.x * WPB + wave) * RPW;
-  if (e0 >= E) return;                               // wave-uniform
+  const bool live = e0 < E;                          // wave-uniform (every wave reaches the barrier)
   const int nch = H >> 4;                            // 16-byte chunks of an int8 row
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   // 1. the lane's x first (loads complete in order, so its digits are
@@ -172,21 +203,31 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
     xr[s][0] = xp[0];
     xr[s][1] = xp[1];
   }
-  u32x4 r[RPW][CH];
+  // the hint (read whether or not it is used: a load under a branch would
+  // wait for every load before it)
+  const float ring_v = a.hsrc->ring[lane & (kHintRing - 1)];
+  const unsigned long long epoch_v = a.hsrc->epoch;
+  // rows in batches of RB, two batches in flight: batch b + 2 is issued
+  // into the buffer batch b frees (registers for 2 RB rows whatever NB is,
+  // so one wave per row group of RPW rows stays resident)
+  u32x4 r[2][RB][CH];
+  float scv[2][RB], bv[2][RB], ebv[2][RB];           // scale, bias, ||eps_e|| (the list's bound)
+  auto issue = [&](int bt, int buf) {
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int e = min(e0 + i, E - 1);
+    for (int i = 0; i < RB; ++i) {
+      const int e = min(e0 + bt * RB + i, E - 1);
 #pragma unroll
-    for (int s = 0; s < CH; ++s)
-      r[i][s] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(a.q8 + size_t(e) * H) + min(s * 64 + lane, nch - 1));
-  }
-  float scv[RPW], bv[RPW];
-#pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    scv[i] = a.sc8[min(e0 + i, E - 1)];
-    bv[i] = a.bias[min(e0 + i, E - 1)];
-  }
+      for (int s = 0; s < CH; ++s)
+        r[buf][i][s] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.q8 + size_t(e) * H) + min(s * 64 + lane, nch - 1));
+      scv[buf][i] = a.sc8[e];
+      bv[buf][i] = a.bias[e];
+      ebv[buf][i] = a.eb8[e].x;                      // (a load under a branch would wait for all)
+    }
+  };
+  issue(0, 0);
+  if (NB > 1) issue(1, 1);
+  const bool listing = a.hint != nullptr && t == 0;  // uniform
   // 2. max |x| over the wave (= all of x) on the magnitude bits: a non-finite
   //    element has magnitude bits >= 0x7f80
   uint32_t mb = 0u;
@@ -210,32 +251,10 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
   // x 2^m in binary32, exact: two power-of-two factors, neither over- nor underflowing
   const int m1 = m > 100 ? 100 : (m < -100 ? -100 : m);
   const float sc1 = ldexpf(1.f, m1), sc2 = ldexpf(1.f, m - m1);
-  // 3. the digits of the lane's chunks (zero past the row, so the clamped
-  //    row loads add nothing); block 0's first wave also sums ||x||^2 and
-  //    ||delta||^2 exactly in binary64
+  // 3. block 0's first wave sums ||x||^2 and ||delta||^2 exactly in
+  //    binary64; then the digits of the lane's chunks (zero past the row, so
+  //    the clamped row loads add nothing)
   const double isc = ldexp(1.0, -m);
-  int dh[CH][4], dl[CH][4];
-#pragma unroll
-  for (int s = 0; s < CH; ++s) {
-    const bool in = s * 64 + lane < nch;
-    const uint32_t w[8] = {xr[s][0].x, xr[s][0].y, xr[s][0].z, xr[s][0].w,
-                           xr[s][1].x, xr[s][1].y, xr[s][1].z, xr[s][1].w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t hw = 0u, lw = 0u;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int el = 4 * q + b;                    // element of the chunk
-        const uint32_t word = w[el >> 1];
-        const float v = (el & 1) ? bf16_hi(word) : bf16_lo(word);
-        const int Xi = (int)rintf((v * sc1) * sc2);  // |Xi| <= 2^13
-        hw |= (uint32_t(Xi >> 7) & 0xffu) << (8 * b);          // floor(Xi / 128), in [-64, 64]
-        lw |= uint32_t(Xi & 127) << (8 * b);                   // in [0, 127]
-      }
-      dh[s][q] = (in && !xbad) ? (int)hw : 0;
-      dl[s][q] = (in && !xbad) ? (int)lw : 0;
-    }
-  }
   if (blockIdx.x == 0 && wave == 0) {                // wave-uniform
     double sx2 = 0.0, sd2 = 0.0;
 #pragma unroll
@@ -259,57 +278,164 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
       if (xbad) atomicOr(a.dev_flag, kDevNonFinite);
     }
   }
-  // 4. exact integer dot products, one binary64 evaluation per row, the
-  //    values and the maxima of every 4 consecutive experts (NaN: -inf)
-  const int G = (E + 3) / 4;
-  float gm = -INFINITY;
+  int dh[CH][4], dl[CH][4];
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    int HI = 0, LO = 0;
+  for (int s = 0; s < CH; ++s) {
+    const bool in = s * 64 + lane < nch;
+    const uint32_t w[8] = {xr[s][0].x, xr[s][0].y, xr[s][0].z, xr[s][0].w,
+                           xr[s][1].x, xr[s][1].y, xr[s][1].z, xr[s][1].w};
 #pragma unroll
-    for (int s = 0; s < CH; ++s) {
-      const unsigned w[4] = {r[i][s].x, r[i][s].y, r[i][s].z, r[i][s].w};
+    for (int q = 0; q < 4; ++q) {
+      uint32_t hw = 0u, lw = 0u;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        HI = __builtin_amdgcn_sdot4((int)w[q], dh[s][q], HI, false);
-        LO = __builtin_amdgcn_sdot4((int)w[q], dl[s][q], LO, false);
+      for (int b = 0; b < 4; ++b) {
+        const int el = 4 * q + b;                    // element of the chunk
+        const uint32_t word = w[el >> 1];
+        const float v = (el & 1) ? bf16_hi(word) : bf16_lo(word);
+        const int Xi = (int)rintf((v * sc1) * sc2);  // |Xi| <= 2^13
+        hw |= (uint32_t(Xi >> 7) & 0xffu) << (8 * b);          // floor(Xi / 128), in [-64, 64]
+        lw |= uint32_t(Xi & 127) << (8 * b);                   // in [0, 127]
       }
-    }
-    HI = wave_sum_i32(HI);
-    LO = wave_sum_i32(LO);
-    const int e = e0 + i;
-    const double v = (double)scv[i] * (128.0 * (double)HI + (double)LO) * isc + (double)bv[i];
-    const float vf = xbad ? NAN : (float)v;
-    if (e < E && !isnan(vf)) gm = fmaxf(gm, vf);
-    if (lane == 0) {
-      if (e < E) a.z8[size_t(t) * E + e] = vf;
-      if (e < E && !xbad && !isfinite(vf)) atomicOr(a.dev_flag, kDevNonFinite);
-    }
-    if ((i & 3) == 3) {
-      const int g = (e0 + i) >> 2;
-      if (lane == 0 && g < G) a.g8[size_t(t) * G + g] = gm;
-      gm = -INFINITY;
+      dh[s][q] = (in && !xbad) ? (int)hw : 0;
+      dl[s][q] = (in && !xbad) ? (int)lw : 0;
     }
   }
+  // the list's theta and upper bounds on ||x|| and ||delta||, worked out
+  // while the rows stream.  With X the digits' integers (x 2^m = X + d,
+  // |d_h| <= 1/2): ||x|| 2^m <= ||X|| + sqrt(H) / 2 and ||delta|| 2^m <=
+  // sqrt(H) / 2, where ||X||^2 = 2^14 sum hi^2 + 2^8 sum hi lo + sum lo^2
+  // (three exact integer dot products of the digits).  Binary32 with a
+  // (1 + 2^-20) margin per result: a handful of roundings each.
+  float theta = INFINITY, xnu = 0.f, dnu = 0.f;
+  unsigned long long tag = 0ull;
+  if (listing) {
+    theta = xbad ? INFINITY : hint_threshold_lanes(ring_v);
+    const unsigned ep_lo = __builtin_amdgcn_readfirstlane((unsigned)epoch_v);
+    const unsigned ep_hi = __builtin_amdgcn_readfirstlane((unsigned)(epoch_v >> 32));
+    tag = list_tag(((unsigned long long)ep_hi << 32) | ep_lo);
+    int shh = 0, shl = 0, sll = 0;
+#pragma unroll
+    for (int s = 0; s < CH; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        shh = __builtin_amdgcn_sdot4(dh[s][q], dh[s][q], shh, false);
+        shl = __builtin_amdgcn_sdot4(dh[s][q], dl[s][q], shl, false);
+        sll = __builtin_amdgcn_sdot4(dl[s][q], dl[s][q], sll, false);
+      }
+    shh = wave_sum_i32(shh);
+    shl = wave_sum_i32(shl);
+    sll = wave_sum_i32(sll);
+    // exact in 64-bit integers (the middle term can be negative), one rounding to binary32
+    const long long X2i = 16384ll * shh + 256ll * shl + (long long)sll;
+    const float X2 = (float)X2i * (1.f + 0x1p-20f);
+    const float iscf = ldexpf(1.f, -m);              // 2^-m (m <= 150: normal or subnormal, exact)
+    const float hd = 0.5f * sqrtf((float)H) * (1.f + 0x1p-20f);
+    xnu = ((sqrtf(X2) * (1.f + 0x1p-20f) + hd) * (1.f + 0x1p-20f)) * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
+    dnu = hd * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
+  }
+  const float rqmax = (float)a.rqmax * (1.f + 0x1p-20f), u8f = (float)a.u8 * (1.f + 0x1p-20f);
+  const float babs8f = (float)a.babs8 * (1.f + 0x1p-20f) + 0x1p-149f;
+  unsigned listed = 0u;                              // rows whose upper end reaches theta (uniform)
+
+  // 4. exact integer dot products, one binary64 evaluation per row, the
+  //    values (and, for the list, whether v + B reaches theta)
+#pragma unroll
+  for (int bt = 0; bt < NB; ++bt) {
+    const int buf = bt & 1;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      int HI = 0, LO = 0;
+#pragma unroll
+      for (int s = 0; s < CH; ++s) {
+        const unsigned w[4] = {r[buf][i][s].x, r[buf][i][s].y, r[buf][i][s].z, r[buf][i][s].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          HI = __builtin_amdgcn_sdot4((int)w[q], dh[s][q], HI, false);
+          LO = __builtin_amdgcn_sdot4((int)w[q], dl[s][q], LO, false);
+        }
+      }
+      HI = wave_sum_i32(HI);
+      LO = wave_sum_i32(LO);
+      const int ri = bt * RB + i, e = e0 + ri;
+      const double v = (double)scv[buf][i] * (128.0 * (double)HI + (double)LO) * isc + (double)bv[buf][i];
+      const float vf = xbad ? NAN : (float)v;
+      if (lane == 0) {
+        s_v[wave * RPW + ri] = (e < E && !isnan(vf)) ? vf : -INFINITY;
+        s_vf[wave * RPW + ri] = (e < E) ? vf : NAN;
+        s_eb[wave * RPW + ri] = ebv[buf][i];
+        if (e < E) a.z8[size_t(t) * E + e] = vf;
+        if (e < E && !xbad && !isfinite(vf)) atomicOr(a.dev_flag, kDevNonFinite);
+      }
+    }
+    if (bt + 2 < NB) {
+      __builtin_amdgcn_sched_barrier(0);             // keep the next loads after this batch (registers)
+      issue(bt + 2, buf);
+    }
+  }
+  // the maxima of every 4 consecutive experts of the block (NaN: -inf)
+  __syncthreads();
+  {
+    const int G = (E + 3) / 4;
+    const int g = blockIdx.x * (WPB * RPW / 4) + tid;
+    if (tid < WPB * RPW / 4 && g < G)
+      a.g8[size_t(t) * G + g] = fmaxf(fmaxf(s_v[4 * tid], s_v[4 * tid + 1]), fmaxf(s_v[4 * tid + 2], s_v[4 * tid + 3]));
+  }
+  if (!listing || !live) return;
+  // rows whose upper end v + B reaches theta (binary32, rounded up: every
+  // term of B is positive, so (1 + 2^-20) covers its few roundings and
+  // 2^-147 those in the subnormal range; the 2^-22 |U| + 2^-149 slack covers
+  // the rounding of U and of the slack's own sum)
+#pragma unroll
+  for (int ri = 0; ri < RPW; ++ri) {
+    const float vf = s_vf[wave * RPW + ri];
+    const float B = fmaf(xnu, s_eb[wave * RPW + ri], fmaf(dnu, rqmax, fmaf(u8f, fabsf(vf), babs8f))) *
+                        (1.f + 0x1p-20f) + 0x1p-147f;
+    const float U = vf + B;
+    if (isfinite(vf) && U + fabsf(U) * 0x1p-22f + 0x1p-149f >= theta) listed |= 1u << ri;
+  }
+  // the listed rows' logits recomputed from the bf16 rows as the selection
+  // would (8-element chunks, dot2 chains), into the table
+  if (listed != 0u) {
+    constexpr int CPLR = 2 * CH;
+    const int n8 = H >> 3;
+    uint4 xc[CPLR];
+#pragma unroll
+    for (int s = 0; s < CPLR; ++s)
+      xc[s] = *reinterpret_cast<const uint4*>(a.x + size_t(t) * H + min(s * 64 + lane, n8 - 1) * 8);
+    for (unsigned m = listed; m != 0u; m &= m - 1u) {   // one row at a time (registers)
+      const int e = e0 + __builtin_ctz(m);
+      uint4 rr[CPLR];
+#pragma unroll
+      for (int s = 0; s < CPLR; ++s)
+        rr[s] = *reinterpret_cast<const uint4*>(a.R + size_t(e) * H + min(s * 64 + lane, n8 - 1) * 8);
+      const double z = dot2_logit<CPLR>(xc, rr, n8, a.bias[e], lane);
+      if (lane == 0) list_insert(a.list, tag, e, z);
+    }
+  }
+  if (lane == 0) a.cnt8[blockIdx.x * WPB + wave] = (unsigned char)__popc(listed);
 }
 
-// Launch shape of the screen: rows per wave and waves per block.
-constexpr int kScreenRowsPerWave = 4;
+// Launch shape of the screen: batches of 2 rows per wave, waves per block
+// (6 rows per wave: 1024 blocks of 4 waves at E = 24,576, one per SIMD slot
+// of the part at the kernel's occupancy, so no wave waits for another's slot).
+constexpr int kScreenBatches = 3;
+constexpr int kScreenRowsPerWave = 2 * kScreenBatches;
 constexpr int kScreenWavesPerBlock = 4;
 
-template <int RPW, int WPB>
-static int screen_blocks(int E) { return (E + WPB * RPW - 1) / (WPB * RPW); }
+static int screen_blocks(int E) {
+  return (E + kScreenWavesPerBlock * kScreenRowsPerWave - 1) / (kScreenWavesPerBlock * kScreenRowsPerWave);
+}
 
-template <int RPW, int WPB, int CH>
+template <int CH>
 static hipError_t launch_screen_shape(const ScreenArgs& sa, hipStream_t s) {
-  if (sa.tags != nullptr && sa.ntags > screen_blocks<RPW, WPB>(sa.E) * WPB * 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((screen_kernel<RPW, WPB, CH>), dim3(screen_blocks<RPW, WPB>(sa.E), sa.T), dim3(WPB * 64), 0, s, sa);
+  hipLaunchKernelGGL((screen_kernel<kScreenBatches, kScreenWavesPerBlock, CH>), dim3(screen_blocks(sa.E), sa.T),
+                     dim3(kScreenWavesPerBlock * 64), 0, s, sa);
   return hipGetLastError();
 }
 
 hipError_t launch_screen(const Layer& L, const void* x, int T, float* z8, float* g8, double* xq,
-                         unsigned long long* tags, int ntags, hipStream_t s) {
-  ScreenArgs a;
+                         const ScreenList* list, hipStream_t s) {
+  ScreenArgs a{};
   a.q8 = L.q8;
   a.sc8 = L.sc8;
   a.bias = router_bias_or_zero(L);
@@ -320,25 +446,41 @@ hipError_t launch_screen(const Layer& L, const void* x, int T, float* z8, float*
   a.z8 = z8;
   a.g8 = g8;
   a.xq = xq;
-  a.tags = tags;
-  a.ntags = ntags;
   a.dev_flag = L.dev_flag;
-  constexpr int R = kScreenRowsPerWave, W = kScreenWavesPerBlock;
+  a.eb8 = L.eb8;
+  a.hsrc = reinterpret_cast<const HintWords*>(L.screen_consts);   // 256 bytes, read and ignored
+  if (list != nullptr && T == 1) {
+    a.R = reinterpret_cast<const uint16_t*>(L.router_eh);
+    const ScreenSelectArgs b = make_screen_select_args(L, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+    a.u8 = b.u8;
+    a.babs8 = b.babs8;
+    a.rqmax = b.rqmax;
+    a.hint = list->hint;
+    a.hsrc = list->hint;
+    a.cnt8 = list->cnt8;
+    a.list = list->list;
+  }
   const int ch = (a.H / 16 + 63) / 64;
-  if (ch <= 2) return launch_screen_shape<R, W, 2>(a, s);
-  if (ch <= 4) return launch_screen_shape<R, W, 4>(a, s);
-  if (ch <= 8) return launch_screen_shape<R, W, 8>(a, s);
+  if (ch <= 2) return launch_screen_shape<2>(a, s);
+  if (ch <= 4) return launch_screen_shape<4>(a, s);
+  if (ch <= 8) return launch_screen_shape<8>(a, s);
   return hipErrorInvalidValue;
 }
 
-// Words of `tags` the screen kernel can clear for a layer (its grid's threads).
-int screen_clearable_words(const Layer& L) {
-  return screen_blocks<kScreenRowsPerWave, kScreenWavesPerBlock>(L.d.n_experts) * kScreenWavesPerBlock * 64;
+// Waves of the screen kernel that own rows (one count byte each in the list).
+int screen_waves(const Layer& L) { return (L.d.n_experts + kScreenRowsPerWave - 1) / kScreenRowsPerWave; }
+
+void set_screen_list(ScreenSelectArgs& b, const Layer& L, const ScreenList* list, bool advance) {
+  b.hint = list->hint;
+  b.cnt8 = list->cnt8;
+  b.list = list->list;
+  b.nw = screen_waves(L);
+  b.advance = advance ? 1 : 0;
 }
 
 ScreenSelectArgs make_screen_select_args(const Layer& L, const void* x, const float* z8, const float* g8,
                                          const double* xq, int32_t* idx, float* gates) {
-  ScreenSelectArgs b;
+  ScreenSelectArgs b{};
   RouterBound rb = router_bound(L, 1);
   rb.d32 = 8;                     // the recomputed logits' chains of four v_dot2_f32_bf16
   b.sel = make_select_args(L, x, nullptr, false, nullptr, xq, idx, gates, rb);
@@ -388,8 +530,11 @@ __global__ __launch_bounds__(kSelectThreads) void select_screen_kernel(ScreenSel
 }
 
 hipError_t launch_select_screen(const Layer& L, const void* x, int T, const float* z8, const float* g8,
-                                const double* xq, int32_t* idx, float* gates, hipStream_t s) {
-  const ScreenSelectArgs b = make_screen_select_args(L, x, z8, g8, xq, idx, gates);
+                                const double* xq, const ScreenList* list, int32_t* idx, float* gates,
+                                hipStream_t s) {
+  if (list == nullptr || T != 1) return hipErrorInvalidValue;     // batch 1, with the list
+  ScreenSelectArgs b = make_screen_select_args(L, x, z8, g8, xq, idx, gates);
+  set_screen_list(b, L, list, true);   // this kernel ends the call
   const int cpl = (L.d.hidden / 8 + 63) / 64;
 #define MOE_SEL_SCREEN(C)                                                                             \
   if (cpl <= C) {                                                                                     \

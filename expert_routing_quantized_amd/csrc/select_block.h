@@ -45,6 +45,7 @@
 namespace moe {
 
 constexpr int kWavesSel = kSelectThreads / 64;
+static_assert(kWavesSel * 8 >= 64, "the 64-survivor rank gives each wave 8 survivors");
 constexpr int kBins = 48;
 constexpr int kQBase = -352;   // lowest binary exponent of an fp32 x fp32 product lsb, rounded down
 
@@ -290,6 +291,7 @@ __device__ __forceinline__ double refine_logit(const SelectArgs& a, int t, int e
 
 // ---------------------------------------------------------------- kernel
 constexpr int kTauSteps = 12;   // bisection steps for tau0
+constexpr int kFastMax = 256;   // survivors the ranking fast path takes
 
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
   return __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
@@ -328,9 +330,12 @@ struct SelectLds {
   double red[kWavesSel];
   int s_cnt, c_cnt, s_ntop, s_done, s_ng, s_nref;
   int s_ref[64];                  // ranks refined by the cluster pass
-  int s_rank[64];                 // fast path: each survivor's rank
+  int s_rankp[kWavesSel][kFastMax];   // fast path: each wave's part of each survivor's rank
   double x_z[64];                 // their exact logits, by rank
   double s_tau, s_th0;
+  double s_kth;                   // approximate logit of the k-th expert chosen (when all k are)
+  int s_red3[3][kWavesSel];       // per-wave partial sums
+  int s_nf;                       // survivors the fast path keeps (-1: none, go exact)
   float s_thf;                    // s_th0 in binary32, rounded down
 };
 
@@ -363,12 +368,23 @@ struct SelectLds {
 // an approximate logit of every expert with |zr(e) - z| <= Btz + uz |zr(e)|,
 // read only when the survivors did not fit.  Certifies the order (refining
 // exactly where intervals overlap) and writes idx and gates to oi / og.
-template <int ACT, class ZR>
-__device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, SelectLds& S, double Btv,
-                                            double uv, ZR zr, double Btz, double uz, int32_t* oi, float* og) {
+//
+// The result depends on the input alone, not on which survivors were
+// passed: the order is the exact order (ties by index), and the gates are
+// the softmax of the k chosen experts' approximate logits v (the values the
+// survivors carry; zt(S) writes them to S.new_z[0..k) for S.top_e[0..k)
+// when the exact path chose), in that order.  S.s_kth gets the k-th one.
+// The rest of select_tail when the fast path has not certified the order:
+// the cluster pass's refinements and re-rank, then the exact path.  (Out of
+// line it measured slower: the lambdas' captures then live in scratch.)
+template <int ACT, class ZR, class ZT>
+__device__ __forceinline__ void select_tail_slow(const SelectArgs& a, int t, int n, int nf, SelectLds& S,
+                                                           double Btv, double uv, ZR zr, double Btz, double uz,
+                                                           ZT zt, int32_t* oi, float* og) {
   MOE_SELECT_LDS_NAMES(S);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = a.E, k = a.k;
+  n = __builtin_amdgcn_readfirstlane(n);           // block-uniform: scalar loop bounds
   const double Bt = Btv, u = uv;
   auto bound = [&](double v) -> double { return Bt + u * fabs(v); };
   auto lower_b = [](double tv, double B0, double uu) -> double {   // tv - B(tv), rounded down
@@ -378,72 +394,22 @@ __device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, S
     return L - 1e-15 * (fabs(tv) + B + 1.0);
   };
   auto lower = [&](double tv) -> double { return lower_b(tv, Bt, u); };
+  // gates of the k ranked experts from their approximate logits zv[0..k) (lanes < k of one wave)
+  auto write_gates = [&](const double* zv, const int* ev) {
+    // (the sum over the k weights in the fixed order of wave_sum_f64's tree)
+    const double w = (lane < k) ? exp(zv[min(lane, k - 1)] - zv[0]) : 0.0;
+    const double sum = wave_sum_f64(w);
+    if (lane < k) {
+      oi[lane] = ev[lane];
+      og[lane] = (float)(w / sum);
+    }
+    if (lane == 0) {
+      S.s_kth = zv[k - 1];
+      s_done = 1;
+    }
+  };
 
-  // 5a. fast path: the survivors' ranks (each wave counts, for every
-  //     survivor, the larger ones among 8 of the others), then one wave
-  //     certifies the order.
-  const bool fast = n <= 64 && !a.force_exact;     // block-uniform
-  if (fast) {
-    if (tid < 64) S.s_rank[tid] = 0;
-    __syncthreads();
-    const double v = (lane < n) ? s_val[lane] : -INFINITY;
-    const int e = (lane < n) ? s_id[lane] : 0x7fffffff;
-    int part = 0;
-    for (int j = wave * 8; j < min(n, wave * 8 + 8); ++j) {   // wave-uniform bounds
-      const double vj = readlane_f64(v, j);
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      part += (vj > v) || (vj == v && ej < e);
-    }
-    if (lane < n && part) atomicAdd(&S.s_rank[lane], part);
-    __syncthreads();
-  }
-  if (fast && wave == 0) {
-    const double v = (lane < n) ? s_val[lane] : -INFINITY;
-    const int e = (lane < n) ? s_id[lane] : 0x7fffffff;
-    const int rank = (lane < n) ? S.s_rank[lane] : 64;
-    if (lane < n) {
-      c_z[rank] = v;
-      c_id[rank] = e;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    // ranks r and r+1 must not overlap for r < k (order of the k, and the cut)
-    const int npair = min(k, n - 1);
-    bool bad = false;
-    if (lane < npair) {
-      const double hi = c_z[lane], lo = c_z[lane + 1];
-      bad = !(hi - bound(hi) > lo + bound(lo));
-    }
-    const unsigned long long bm = __ballot(bad);
-    const bool certified = (n >= k) && (bm == 0ull);
-    if (certified) {
-      if (lane < k) s_w[lane] = exp(c_z[lane] - c_z[0]);
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if (lane < k) {
-        double sum = 0.0;
-        for (int j = 0; j < k; ++j) sum += s_w[j];
-        oi[lane] = c_id[lane];
-        og[lane] = (float)(s_w[lane] / sum);
-      }
-      if (lane == 0) s_done = 1;
-    } else if (n >= k) {
-      // cluster pass: the ranks of every overlapping pair, and, when the
-      // cut (k-1, k) overlaps, every later rank whose interval reaches the
-      // lower end of rank k's, are refined to their exact logits
-      bool mark = lane < n && ((((bm >> lane) & 1ull) != 0) || (lane > 0 && ((bm >> (lane - 1)) & 1ull) != 0));
-      if (((bm >> (k - 1)) & 1ull) != 0 && lane > k && lane < n) {
-        const double zk = c_z[k];
-        if (c_z[lane] + bound(c_z[lane]) >= zk - bound(zk)) mark = true;
-      }
-      const unsigned long long mm = __ballot(mark);
-      if (mark) s_ref[__popcll(mm & ((1ull << lane) - 1ull))] = lane;
-      if (lane == 0) s_nref = (__popcll(mm) <= 2 * kWavesSel) ? __popcll(mm) : 0;
-    }
-  }
-  __syncthreads();
-  if (s_done) return;
-  if (s_nref > 0) {
+  if (nf >= 0 && s_nref > 0) {
     for (int i = wave; i < s_nref; i += kWavesSel) {
       const double zz = refine_logit<ACT>(a, t, c_id[s_ref[i]], bins[wave], lane);
       if (lane == 0) x_z[s_ref[i]] = zz;
@@ -453,14 +419,15 @@ __device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, S
       // re-rank with the exact logits where known (interval of width 0)
       bool ex = false;
       for (int i = 0; i < s_nref; ++i) ex = ex || (s_ref[i] == lane);
-      const double v = (lane < n) ? (ex ? x_z[lane] : c_z[lane]) : -INFINITY;
-      const double bw = (lane < n && !ex) ? bound(c_z[lane]) : 0.0;
+      const double va = (lane < n) ? c_z[lane] : -INFINITY;    // approximate logit (gates)
+      const double v = (lane < n) ? (ex ? x_z[lane] : va) : -INFINITY;
+      const double bw = (lane < n && !ex) ? bound(va) : 0.0;
       const int e = (lane < n) ? c_id[lane] : 0x7fffffff;
       int rank = 0;
       for (int j = 0; j < n; ++j) {
         const double vj = readlane_f64(v, j);
         const int ej = __builtin_amdgcn_readlane(e, j);
-        rank += (vj > v) || (vj == v && ej < e);
+        rank += int((vj > v) | ((vj == v) & (ej < e)));
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -468,6 +435,10 @@ __device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, S
         s_val[rank] = v;
         x_z[rank] = bw;
         s_id[rank] = e;
+        if (rank < k) {
+          new_z[rank] = va;
+          new_e[rank] = e;
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -479,18 +450,7 @@ __device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, S
         const double hv = s_val[lane], hb = x_z[lane], lv = s_val[lane + 1], lb = x_z[lane + 1];
         bad = !((hv - hb > lv + lb) || (hb == 0.0 && lb == 0.0));
       }
-      if (__ballot(bad) == 0ull) {
-        if (lane < k) s_w[lane] = exp(s_val[lane] - s_val[0]);
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        if (lane < k) {
-          double sum = 0.0;
-          for (int j = 0; j < k; ++j) sum += s_w[j];
-          oi[lane] = s_id[lane];
-          og[lane] = (float)(s_w[lane] / sum);
-        }
-        if (lane == 0) s_done = 1;
-      }
+      if (__ballot(bad) == 0ull) write_gates(new_z, new_e);
     }
     __syncthreads();
     if (s_done) return;
@@ -512,7 +472,7 @@ __device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, S
       for (int w = 0; w < nu; ++w) {
         const int ew = (w < ntop) ? top_e[w] : c_id[w - ntop];
         const double zw = (w < ntop) ? top_z[w] : c_z[w - ntop];
-        rank += (zw > zu) || (zw == zu && ew < eu);
+        rank += int((zw > zu) | ((zw == zu) & (ew < eu)));
       }
       if (rank < k) {
         new_e[rank] = eu;
@@ -578,22 +538,166 @@ __device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, S
     process(c_cnt);
   }
 
-  // 6. outputs: gates = softmax over the k exact logits (f64), one thread per gate.
+  // 6. outputs: the k experts in exact order; gates = softmax over their
+  //    approximate logits (zt), or over the exact ones when one of those is
+  //    not finite.
   const int nt = s_ntop;
-  if (nt == k && tid < k) s_w[tid] = exp(top_z[tid] - top_z[0]);
-  __syncthreads();
-  if (tid < k) {
-    if (nt < k) {
-      oi[tid] = (tid < nt) ? top_e[tid] : -1;
-      og[tid] = NAN;
-    } else {
-      double sum = 0.0;
-      for (int j = 0; j < k; ++j) sum += s_w[j];
-      oi[tid] = top_e[tid];
-      og[tid] = (float)(s_w[tid] / sum);
+  if (nt == k) {
+    zt(S);                       // S.new_z[0..k) for S.top_e[0..k) (every thread calls it)
+    __syncthreads();
+    if (wave == 0) {
+      const bool fin = __ballot(lane < k && !isfinite(new_z[lane])) == 0ull;
+      write_gates(fin ? new_z : top_z, top_e);
     }
+  } else if (tid < k) {
+    oi[tid] = (tid < nt) ? top_e[tid] : -1;
+    og[tid] = NAN;
   }
   if (tid == 0 && nt < k) atomicOr(a.dev_flag, kDevNonFinite);
+}
+
+template <int ACT, class ZR, class ZT>
+__device__ __forceinline__ void select_tail(const SelectArgs& a, int t, int n, SelectLds& S, double Btv,
+                                            double uv, ZR zr, double Btz, double uz, ZT zt, int32_t* oi,
+                                            float* og) {
+  MOE_SELECT_LDS_NAMES(S);
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = a.E, k = a.k;
+  n = __builtin_amdgcn_readfirstlane(n);           // block-uniform: scalar loop bounds
+  const double Bt = Btv, u = uv;
+  auto bound = [&](double v) -> double { return Bt + u * fabs(v); };
+  auto lower_b = [](double tv, double B0, double uu) -> double {   // tv - B(tv), rounded down
+    if (isinf(tv)) return tv < 0 ? -INFINITY : tv;
+    const double B = B0 + uu * fabs(tv);
+    const double L = tv - B;
+    return L - 1e-15 * (fabs(tv) + B + 1.0);
+  };
+  auto lower = [&](double tv) -> double { return lower_b(tv, Bt, u); };
+  // gates of the k ranked experts from their approximate logits zv[0..k) (lanes < k of one wave)
+  auto write_gates = [&](const double* zv, const int* ev) {
+    // (the sum over the k weights in the fixed order of wave_sum_f64's tree)
+    const double w = (lane < k) ? exp(zv[min(lane, k - 1)] - zv[0]) : 0.0;
+    const double sum = wave_sum_f64(w);
+    if (lane < k) {
+      oi[lane] = ev[lane];
+      og[lane] = (float)(w / sum);
+    }
+    if (lane == 0) {
+      S.s_kth = zv[k - 1];
+      s_done = 1;
+    }
+  };
+
+  // 5a. fast path: the survivors' ranks by v (each wave counts, for every
+  //     survivor, the larger ones among its share of the others), then one
+  //     wave certifies the order.  Past 64 survivors, ranks 64 and on are
+  //     dropped when they lie strictly below rank k-1's interval (none of
+  //     them can then be among the k).
+  constexpr int Q = kFastMax / 64;
+  const bool fast = n <= kFastMax && !a.force_exact;     // block-uniform
+  if (fast) {
+    double v[Q];
+    int e[Q], part[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int i = lane + 64 * q;
+      v[q] = (i < n) ? s_val[i] : -INFINITY;
+      e[q] = (i < n) ? s_id[i] : 0x7fffffff;
+      part[q] = 0;
+    }
+    if (n <= 64) {
+      // wave w compares every survivor (one per lane) with survivors 8 w ..
+      // 8 w + 7, read from LDS at one address per instruction (broadcast)
+      double vj[8];
+      int ej[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {                    // unconditional loads (no branch between them)
+        const int j = min(wave * 8 + u, n - 1);
+        vj[u] = s_val[j];
+        ej[u] = s_id[j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        part[0] += int((wave * 8 + u < n) & ((vj[u] > v[0]) | ((vj[u] == v[0]) & (ej[u] < e[0]))));
+    } else {
+    const int J = (n + kWavesSel - 1) / kWavesSel;
+    const int j0 = wave * J, j1 = min(n, j0 + J);
+    const int nq = (n + 63) >> 6;                      // lane groups in use
+#pragma unroll
+    for (int qj = 0; qj < Q; ++qj) {
+      const int lo = max(j0, 64 * qj), hi = min(j1, 64 * qj + 64);   // wave-uniform
+      for (int j = lo; j < hi; ++j) {
+        const double vj = readlane_f64(v[qj], j - 64 * qj);
+        const int ej = __builtin_amdgcn_readlane(e[qj], j - 64 * qj);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)      // (bitwise operators: no branches)
+          if (q < nq) part[q] += int((vj > v[q]) | ((vj == v[q]) & (ej < e[q])));
+      }
+    }
+    }
+    // per-wave partial ranks (no initialisation, no atomics), summed by wave 0
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+      if (q == 0 || lane + 64 * q < n) S.s_rankp[wave][lane + 64 * q] = part[q];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const int i = lane + 64 * q;
+        if (i < n) {
+          int rank = 0;
+#pragma unroll
+          for (int w = 0; w < kWavesSel; ++w) rank += S.s_rankp[w][i];
+          c_z[rank] = v[q];
+          c_id[rank] = e[q];
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      int m = n;
+      if (n > 64) {
+        const double zk = c_z[k - 1], z64 = c_z[64];
+        m = (z64 + bound(z64) < lower(zk)) ? 64 : -1;
+        if (m == 64) {          // the kept ranks become the survivors (for the exact path too)
+          s_val[lane] = c_z[lane];
+          s_id[lane] = c_id[lane];
+        }
+      }
+      if (lane == 0) S.s_nf = m;
+    }
+    __syncthreads();
+  }
+  const int nf = fast ? __builtin_amdgcn_readfirstlane(S.s_nf) : -1;   // block-uniform
+  if (nf > 0) n = nf;
+  if (nf >= 0 && wave == 0) {
+    // ranks r and r+1 must not overlap for r < k (order of the k, and the cut)
+    const int npair = min(k, n - 1);
+    bool bad = false;
+    if (lane < npair) {
+      const double hi = c_z[lane], lo = c_z[lane + 1];
+      bad = !(hi - bound(hi) > lo + bound(lo));
+    }
+    const unsigned long long bm = __ballot(bad);
+    const bool certified = (n >= k) && (bm == 0ull);
+    if (certified) {
+      write_gates(c_z, c_id);
+    } else if (n >= k) {
+      // cluster pass: the ranks of every overlapping pair, and, when the
+      // cut (k-1, k) overlaps, every later rank whose interval reaches the
+      // lower end of rank k's, are refined to their exact logits
+      bool mark = lane < n && ((((bm >> lane) & 1ull) != 0) || (lane > 0 && ((bm >> (lane - 1)) & 1ull) != 0));
+      if (((bm >> (k - 1)) & 1ull) != 0 && lane > k && lane < n) {
+        const double zk = c_z[k];
+        if (c_z[lane] + bound(c_z[lane]) >= zk - bound(zk)) mark = true;
+      }
+      const unsigned long long mm = __ballot(mark);
+      if (mark) s_ref[__popcll(mm & ((1ull << lane) - 1ull))] = lane;
+      if (lane == 0) s_nref = (__popcll(mm) <= 2 * kWavesSel) ? __popcll(mm) : 0;
+    }
+  }
+  __syncthreads();
+  if (s_done) return;
+  select_tail_slow<ACT>(a, t, n, nf, S, Btv, uv, zr, Btz, uz, zt, oi, og);
 }
 
 
@@ -756,7 +860,10 @@ __device__ __forceinline__ void select_block(const SelectArgs& a, int t, int32_t
   __syncthreads();
   const int n = (s_ng > kSelectMaxCand) ? kSelectMaxCand + 1 : s_cnt;
 
-  select_tail<ACT>(a, t, n, S, Bt, u, zr, Bt, u, oi, og);
+  auto zt = [&](SelectLds& S2) {   // the chosen experts' logits as the router gave them
+    if (tid < k) S2.new_z[tid] = zr(S2.top_e[tid]);
+  };
+  select_tail<ACT>(a, t, n, S, Bt, u, zr, Bt, u, zt, oi, og);
 }
 
 // SelectArgs of a layer for one call (host).

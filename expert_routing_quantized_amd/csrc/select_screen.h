@@ -39,6 +39,102 @@ namespace moe {
 
 constexpr int kScreenMaxCand = 256;   // experts recomputed from the bf16 rows at most
 
+// ---------------------------------------------------------------- the list
+// At batch 1 the screen can also do the recompute itself, for the experts
+// whose upper end v + B reaches a threshold theta taken from recent tokens
+// (their k-th largest logit: consecutive tokens' values spread little, so
+// the k experts of the next token nearly always lie above it).  Each such
+// expert's logit is recomputed by the screen wave that owns its row and
+// put in a small open-addressing table; every wave also writes how many it
+// put there.  The selection then reads about 10 KB instead of the screen
+// values, and accepts the table only when it can prove it complete:
+//  - the entries tagged for this call number exactly the waves' counts (so
+//    none was lost and no stale or stray entry is counted), fewer than the
+//    table's size;
+//  - at least k entries have a lower end z - B >= theta, so the k-th
+//    largest exact logit is >= theta, above every expert left out (those
+//    have z <= v + B < theta).
+// Otherwise it selects from the screen values as before; either way the
+// result is the same (select_tail's output depends on the input alone).
+// The workspace carries the state from call to call: a call counter whose
+// hash tags the call's entries (so no clearing is needed, and workspace
+// contents from elsewhere are only ever a slower call), and the ring of
+// recent k-th logits.  The last kernel of each call moves the call's k-th
+// logit into the ring and advances the counter.
+constexpr int kHintRing = 16;
+constexpr int kListSlots = 256;           // table size (a power of 2, <= kFastMax)
+
+struct HintWords {                        // 128 bytes of the workspace
+  unsigned long long epoch;               // calls so far (from any start value)
+  float kth;                              // this call's k-th logit (NaN: none)
+  unsigned int listed_calls;              // calls whose selection took the table (statistics)
+  float pad[12];
+  float ring[kHintRing];                  // k-th logits of recent calls
+};
+static_assert(sizeof(HintWords) <= 256, "the screen reads a 256-byte stand-in in place of a hint");
+
+// theta from the ring: its minimum less a quarter of its range (+inf, i.e.
+// no list, while the ring holds a value that is not finite).  0.25 (mx - mn)
+// is exact, so the result does not depend on contraction into an fma.
+__device__ __forceinline__ float hint_threshold(const HintWords* h) {
+  float mn = INFINITY, mx = -INFINITY;
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < kHintRing; ++j) {
+    const float r = h->ring[j];
+    ok = ok && isfinite(r);
+    mn = fminf(mn, r);
+    mx = fmaxf(mx, r);
+  }
+  const float th = mn - 0.25f * (mx - mn);
+  return (ok && isfinite(th)) ? th : INFINITY;
+}
+
+// hint_threshold for one wave: lane l holds ring[l % 16]; minimum and
+// maximum are exact in any order, so every lane gets the same value as
+// hint_threshold.
+__device__ __forceinline__ float hint_threshold_lanes(float r) {   // r = ring[lane % 16]
+  const bool ok = __ballot(!isfinite(r)) == 0ull;
+  const float rr = ok ? r : 0.f;
+  const float mx = wave_max(rr), mn = -wave_max(-rr);
+  const float th = mn - 0.25f * (mx - mn);
+  return (ok && isfinite(th)) ? th : INFINITY;
+}
+
+// 40-bit tag of a call: the splitmix64 finaliser of its counter.
+__device__ __forceinline__ unsigned long long list_tag(unsigned long long epoch) {
+  unsigned long long z = epoch + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  return z >> 24;
+}
+
+// End of a call, by one wave of the call's last kernel: the k-th logit into
+// the ring (every slot while the ring is not all finite), then the next
+// counter value.  hint_read issues the loads where the kernel starts and
+// hint_write only stores, so the wave never waits on them.
+struct HintRead {
+  unsigned long long epoch;
+  float kth;
+  float ring;              // ring[lane % 16]
+};
+__device__ __forceinline__ HintRead hint_read(const HintWords* h, int lane) {
+  HintRead r;
+  r.epoch = h->epoch;
+  r.kth = h->kth;
+  r.ring = h->ring[lane & (kHintRing - 1)];
+  return r;
+}
+__device__ __forceinline__ void hint_write(HintWords* h, const HintRead& r, int lane) {   // all 64 lanes
+  const bool ok = __ballot(!isfinite(r.ring)) == 0ull;
+  if (isfinite(r.kth) && lane < kHintRing && (!ok || int(r.epoch % kHintRing) == lane)) h->ring[lane] = r.kth;
+  if (lane == 0) {
+    h->kth = NAN;
+    h->epoch = r.epoch + 1;
+  }
+}
+
 struct ScreenSelectArgs {
   SelectArgs sel;          // router rows, bias, x, idx/gates, the recomputed logits' bound;
                            // sel.xnorm -> [T][2]: ||x_t||^2, ||delta_t||^2
@@ -47,6 +143,11 @@ struct ScreenSelectArgs {
   const float2* eb8;       // [E]: (||eps_e|| rounded up, ||Rq_e|| rounded up)
   double enmax, rqmax;     // maxima of the two norms over the experts
   double u8, babs8;        // relative and absolute terms of the screen bound
+  HintWords* hint;         // batch 1 with the list (else null): the call's state
+  const unsigned char* cnt8;   // [nw] entries each screen wave put in the table
+  const ulonglong2* list;  // [kListSlots] (tag << 24 | e + 1, logit bits)
+  int nw;                  // screen waves
+  int advance;             // this kernel ends the call: advance the hint (block 0)
 };
 
 typedef __bf16 sel_bf16x2_t __attribute__((ext_vector_type(2)));
@@ -123,11 +224,11 @@ __device__ __forceinline__ void recompute_logits(const SelectArgs& a, int t, int
 // it); idx and gates go to oi[k] and og[k].  CPL = 8-element chunks per lane
 // of a router row, as in the batch-1 router kernel.
 template <int ACT, int CPL>
-__device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, int t, int32_t* oi, float* og) {
+__device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, int t, SelectLds& S, int32_t* oi,
+                                                   float* og) {
   constexpr int GPT = 12;                          // group maxima per thread (E <= 24,576 in one pass)
   constexpr int GPASS = kSelectThreads * GPT;
   const SelectArgs& a = b.sel;
-  __shared__ SelectLds S;
   MOE_SELECT_LDS_NAMES(S);
   __shared__ float s_bnd[kSelectMaxCand];          // screen bound of each listed survivor
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -146,6 +247,113 @@ __device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, i
     s_tau = -INFINITY;
     s_th0 = -INFINITY;
     s_thf = -INFINITY;
+    S.s_kth = NAN;
+  }
+  // every load of the list path first (one round trip): ||x||^2 and
+  // ||delta||^2, the hint, this thread's table slot and count words
+  const double xn2 = a.xnorm[2 * t], dn2 = a.xnorm[2 * t + 1];
+  const float ring_v = b.hint->ring[lane & (kHintRing - 1)];
+  const unsigned long long epoch = b.hint->epoch;
+  const ulonglong2 ent = b.list[min(tid, kListSlots - 1)];
+  const int nw16 = (b.nw + 15) >> 4;               // 16-byte words of counts
+  constexpr int kCw = 2;                           // words per thread loaded up front (E <= 65,536)
+  uint4 cwv[kCw];
+#pragma unroll
+  for (int u = 0; u < kCw; ++u) cwv[u] = reinterpret_cast<const uint4*>(b.cnt8)[min(tid + u * kSelectThreads, nw16 - 1)];
+  // (a non-finite hidden state is handled once these loads have all been
+  // used: an early return here would let the compiler sink them past its wait)
+  // binary64 sums of exact squares; the factor covers their rounding and the roots
+  const double xn = sqrt(xn2) * (1.0 + 1e-3), dn = sqrt(dn2) * (1.0 + 1e-3);
+  const double Btg = xn * b.enmax + dn * b.rqmax + b.babs8;   // screen bound without the relative term
+  const double u8 = b.u8;
+  const double Btr = a.bt_unit * xn + a.bt_abs;   // bound of the recomputed logits
+  auto zr = [&](int e) -> double { return (double)zs[e]; };
+  auto zt = [&](SelectLds& S2) {   // the chosen experts' logits recomputed from the bf16 rows
+    if (tid < k) S2.c_id[tid] = S2.top_e[tid];
+    __syncthreads();
+    recompute_logits<CPL>(a, t, k, S2);
+    __syncthreads();
+    if (tid < k) S2.new_z[tid] = S2.s_val[tid];
+  };
+
+  // 0. the screen's table, when it can be proved complete
+  {
+    const float theta = hint_threshold_lanes(ring_v);
+    const unsigned long long tag = list_tag(epoch);
+    int csum = 0;
+#pragma unroll
+    for (int u = 0; u < kCw; ++u) {
+      const int w = tid + u * kSelectThreads;
+      const int nb = (w < nw16) ? b.nw - 16 * w : 0;   // bytes of this word that are counts
+      const uint32_t cw[4] = {cwv[u].x, cwv[u].y, cwv[u].z, cwv[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int valid = min(max(nb - 4 * j, 0), 4);
+        const uint32_t m = (valid >= 4) ? 0xffffffffu : ((1u << (8 * valid)) - 1u);
+        csum = (int)__builtin_amdgcn_udot4(cw[j] & m, 0x01010101u, (uint32_t)csum, false);
+      }
+    }
+    for (int w = tid + kCw * kSelectThreads; w < nw16; w += kSelectThreads) {   // E > 65,536 only
+      const uint4 c = reinterpret_cast<const uint4*>(b.cnt8)[w];
+      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+      const int nb = b.nw - 16 * w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int valid = min(max(nb - 4 * j, 0), 4);
+        const uint32_t m = (valid >= 4) ? 0xffffffffu : ((1u << (8 * valid)) - 1u);
+        csum = (int)__builtin_amdgcn_udot4(cw[j] & m, 0x01010101u, (uint32_t)csum, false);
+      }
+    }
+    const bool match = tid < kListSlots && (ent.x >> 24) == tag && (ent.x & 0xffffffull) != 0ull;
+    const int e = int(ent.x & 0xffffffull) - 1;
+    const bool bad = match && e >= E;
+    const double zv = __longlong_as_double((long long)ent.y);
+    const double Bz = Btr + a.rel * fabs(zv);      // the recomputed logit's lower end, rounded down
+    const bool low_ok = match && !bad && (zv - Bz) - 1e-15 * (fabs(zv) + Bz + 1.0) >= (double)theta;
+    __syncthreads();                               // s_cnt cleared
+    const unsigned long long mm = __ballot(match && !bad);
+    if (mm) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&s_cnt, __popcll(mm));
+      base = __builtin_amdgcn_readfirstlane(base);
+      if (match && !bad) {
+        const int p = base + lanes_below(mm);
+        s_val[p] = zv;
+        s_id[p] = e;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) csum += __shfl_xor(csum, m);
+    const int nl = __popcll(__ballot(low_ok)), nb = __popcll(__ballot(bad));
+    if (lane == 0) {
+      S.s_red3[0][wave] = csum;
+      S.s_red3[1][wave] = nl;
+      S.s_red3[2][wave] = nb;
+    }
+    __syncthreads();                               // the appends and the per-wave sums
+    int tc = 0, tl = 0, tb = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesSel; ++w) {
+      tc += S.s_red3[0][w];
+      tl += S.s_red3[1][w];
+      tb += S.s_red3[2][w];
+    }
+    const int found = s_cnt;
+    if (!(isfinite(xn2) && isfinite(dn2))) {       // non-finite hidden state: no routing
+      if (tid < k) {
+        oi[tid] = -1;
+        og[tid] = NAN;
+      }
+      if (tid == 0) atomicOr(a.dev_flag, kDevNonFinite);
+      return;
+    }
+    if (theta < INFINITY && tb == 0 && found == tc && found < kListSlots && tl >= k) {
+      if (tid == 0 && blockIdx.x == 0) atomicAdd(&b.hint->listed_calls, 1u);
+      select_tail<ACT>(a, t, found, S, Btr, a.rel, zr, Btg, u8, zt, oi, og);
+      return;
+    }
+    __syncthreads();
+    if (tid == 0) s_cnt = 0;
   }
   float gv[GPT];
   auto load_pass = [&](int ps) {
@@ -156,19 +364,6 @@ __device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, i
       if (ps * GPASS + i * kSelectThreads + tid >= G) gv[i] = -INFINITY;
   };
   load_pass(0);
-  const double xn2 = a.xnorm[2 * t], dn2 = a.xnorm[2 * t + 1];
-  if (!(isfinite(xn2) && isfinite(dn2))) {         // non-finite hidden state: no routing
-    if (tid < k) {
-      oi[tid] = -1;
-      og[tid] = NAN;
-    }
-    if (tid == 0) atomicOr(a.dev_flag, kDevNonFinite);
-    return;
-  }
-  // binary64 sums of exact squares; the factor covers their rounding and the roots
-  const double xn = sqrt(xn2) * (1.0 + 1e-3), dn = sqrt(dn2) * (1.0 + 1e-3);
-  const double Btg = xn * b.enmax + dn * b.rqmax + b.babs8;   // screen bound without the relative term
-  const double u8 = b.u8;
   auto lower8 = [&](double tv) -> double {
     if (isinf(tv)) return tv < 0 ? -INFINITY : tv;
     const double B = Btg + u8 * fabs(tv);
@@ -278,8 +473,6 @@ __device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, i
   }
   __syncthreads();
   const int n1 = (s_ng > kSelectMaxCand) ? kSelectMaxCand + 1 : s_cnt;
-  auto zr = [&](int e) -> double { return (double)zs[e]; };
-  const double Btr = a.bt_unit * xn + a.bt_abs;   // bound of the recomputed logits
   int nc = kSelectMaxCand + 1;                     // degenerate unless the recompute set is small
   if (n1 <= kSelectMaxCand) {
     // tau: a value that at least k lower ends v - B reach, by a bisection in
@@ -336,7 +529,26 @@ __device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, i
   //    otherwise scan every screen value with exact refinement
   if (nc <= kScreenMaxCand) recompute_logits<CPL>(a, t, nc, S);
   __syncthreads();
-  select_tail<ACT>(a, t, nc, S, Btr, a.rel, zr, Btg, u8, oi, og);
+  select_tail<ACT>(a, t, nc, S, Btr, a.rel, zr, Btg, u8, zt, oi, og);
+}
+
+// The selection of token t from the screen; with the list, block 0 records
+// the call's k-th logit (and, when this kernel ends the call, advances the
+// hint).
+template <int ACT, int CPL>
+__device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, int t, int32_t* oi, float* og) {
+  __shared__ SelectLds S;
+  const bool ends = b.advance && blockIdx.x == 0 && threadIdx.x < 64;   // wave-uniform
+  HintRead hr{};
+  if (ends) hr = hint_read(b.hint, threadIdx.x);
+  select_screen_core<ACT, CPL>(b, t, S, oi, og);
+  __syncthreads();
+  if (ends) {
+    hr.kth = (float)S.s_kth;
+    hint_write(b.hint, hr, threadIdx.x);
+  } else if (threadIdx.x == 0 && blockIdx.x == 0) {
+    b.hint->kth = (float)S.s_kth;
+  }
 }
 
 }  // namespace moe

@@ -91,7 +91,7 @@ typedef enum {
 /* desc.flags */
 #define MOE_LAYER_FORCE_EXACT_REFINE 1u  /* debug: every near-tie logit goes through
                                             the slow integer accumulator */
-#define MOE_LAYER_SCREEN_ON  2u  /* build the router screen (see moe_router_screen) */
+#define MOE_LAYER_SCREEN_ON  2u  /* build the router screen even when E < 4096 */
 #define MOE_LAYER_SCREEN_OFF 4u  /* never build it (batch-1 routing reads the bf16 router) */
 
 typedef struct {
@@ -119,8 +119,9 @@ typedef struct moe_layer moe_layer;   /* opaque; immutable after creation */
 /* Validate `desc` and build a layer.  The only call that allocates device
  * memory (an expert-major router copy when router_layout is MOE_ROUTER_HE,
  * the per-expert router row norms used to bound rounding errors, the sticky
- * device-error word, and -- with MOE_LAYER_SCREEN_ON (bf16 activations, H a
- * multiple of 32) -- the router screen: an int8 copy
+ * device-error word, and -- for bf16 activations, H a multiple of 32 and
+ * E >= 4096 unless MOE_LAYER_SCREEN_OFF, or with MOE_LAYER_SCREEN_ON -- the
+ * router screen: an int8 copy
  * of the router with a per-expert scale and residual norms, E H + 12 E
  * bytes, see moe_router_screen) and the only one that synchronises `stream`.
  * Returns MOE_E_RANGE when the router weights or the bias are not finite.

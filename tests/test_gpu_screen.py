@@ -249,3 +249,152 @@ def test_screen_off_flag_and_refusals():
     with pytest.raises(MoeError) as e:
         SD.make_layer(SD.device_layer(f32), max_tokens=1, flags=MOE_LAYER_SCREEN_ON)
     assert e.value.status == -3
+
+
+# ---------------------------------------------------------------- the list
+HINT_BYTES = 128
+
+
+def hint_state(ws):
+    """The batch-1 list's state at the start of the workspace: call counter,
+    calls whose selection took the table, and the ring of recent k-th logits."""
+    b = ws[:HINT_BYTES].cpu().numpy()
+    return int(b[0:8].view(np.uint64)[0]), int(b[12:16].view(np.uint32)[0]), b[64:128].view(np.float32).copy()
+
+
+def poison_ring(ws, value):
+    torch = G.torch_mod()
+    ws[64:128].view(torch.float32).fill_(value)
+
+
+def grouped_tokens(layer, x, n, ws, before=None):
+    torch = G.torch_mod()
+    fi = torch.empty((n, layer.k), dtype=torch.int32, device=x.device)
+    fg = torch.empty((n, layer.k), dtype=torch.float32, device=x.device)
+    fo = torch.empty((n, layer.H), dtype=torch.float32, device=x.device)
+    for t in range(n):
+        if before is not None:
+            before(t)
+        layer.grouped_forward(x[t], 1, fi[t], fg[t], 0, fo[t], ws)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in (fi, fg, fo)]
+
+
+@pytest.mark.parametrize("name", ["wide_q4", "k20_q4", "tiny_bf16", "q4_h4096"])
+def test_list_taken_and_equal_to_the_full_screen_path(name):
+    """Most calls select from the screen's table once the ring has warmed up;
+    the results equal, bit for bit, those of calls whose ring is poisoned
+    (theta = +inf: no table), and the oracle's."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup(name)
+    G.note("list", name)
+    n = 24
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    x = SD.device_tokens(spec, 500, n)
+    ws = layer.workspace(1)
+    ws.zero_()
+    fi, fg, fo = grouped_tokens(layer, x, n, ws)
+    ep, listed, ring = hint_state(ws)
+    print(f"{name}: {listed} of {n} calls took the table; ring {ring[:4]}")
+    assert ep == n and listed >= n // 2
+    ws2 = layer.workspace(1)
+    ws2.zero_()
+    gi, gg, go = grouped_tokens(layer, x, n, ws2, before=lambda t: poison_ring(ws2, float("nan")))
+    assert hint_state(ws2)[1] == 0
+    check_bitwise(fi, fg, fo, gi, gg, go)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 500, n)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, f"list {name}")
+    assert layer.device_error() == 0
+
+
+def test_list_route_path_and_low_theta():
+    """moe_route through the table equals the grouped forward; a ring far
+    below the logits lists every expert (table full: the full path)."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup("k20_q4")
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    x = SD.device_tokens(spec, 900, 12)
+    fi, fg, fo, si, sg, so = per_token(layer, x, 12)
+    check_bitwise(fi, fg, fo, si, sg, so)
+    ws = layer.workspace(1)
+    ws.zero_()
+    gi, gg, go = grouped_tokens(layer, x, 12, ws, before=lambda t: poison_ring(ws, -1e30))
+    assert hint_state(ws)[1] == 0
+    check_bitwise(fi, fg, fo, gi, gg, go)
+
+
+def test_list_stale_entries_are_not_taken():
+    """Setting the call counter back makes the previous call's entries look
+    current: the counts no longer match and the call selects without the
+    table (same result as a fresh workspace)."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup("wide_q4")
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    x = SD.device_tokens(spec, 700, 8)
+    ref = grouped_tokens(layer, x, 8, layer.workspace(1))
+    ws = layer.workspace(1)
+    ws.zero_()
+    out = []
+    for t in range(8):
+        ep0, listed0, _ = hint_state(ws)
+        r = grouped_tokens(layer, x[t:t + 1], 1, ws)
+        out.append(r)
+        ep1, listed1, _ = hint_state(ws)
+        assert ep1 == ep0 + 1
+        if t >= 2 and t % 2 == 0:
+            # replay token t+1 under token t's counter: token t's entries
+            # (its screen waves' counts sit right after the 256-byte hint
+            # region) now look current
+            nw = (spec.E + 3) // 4
+            stale = int(ws[256:256 + nw].cpu().numpy().astype(np.int64).sum())
+            ws[0:8].view(torch.int64).fill_(ep0)
+            r2 = grouped_tokens(layer, x[t + 1:t + 2], 1, ws)
+            check_bitwise(*[a for a in r2], *[a[t + 1:t + 2] for a in ref])
+            if stale > 0:
+                assert hint_state(ws)[1] == listed1
+    for t in range(8):
+        check_bitwise(*out[t], *[a[t:t + 1] for a in ref])
+
+
+def test_list_garbage_workspace():
+    """A workspace full of random bytes: correct results from the first call."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup("tiny_q4")
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    x = SD.device_tokens(spec, 40, 10)
+    ws = layer.workspace(1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=g))
+    fi, fg, fo = grouped_tokens(layer, x, 10, ws)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 40, 10)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, "list garbage ws")
+    assert layer.device_error() == 0
+
+
+def test_list_fullsize_decode():
+    """The 4-bit decode layer at full size: the table serves most tokens and
+    routing equals the oracle's."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec = synth.CONFIGS["decode_q4"]
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=1, flags=screen_flags())
+    n = 48
+    x = SD.device_tokens(spec, 2000, n)
+    ws = layer.workspace(1)
+    ws.zero_()
+    fi, fg, fo = grouped_tokens(layer, x, n, ws)
+    ep, listed, ring = hint_state(ws)
+    print(f"full size: {listed} of {n} calls took the table; ring min {ring.min():.4f} max {ring.max():.4f}")
+    assert listed >= n * 3 // 4
+    G.note("list full size: oracle")
+    L = G.host_oracle(spec)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 2000, 8)
+    G.compare(fi[:8], fg[:8], fo[:8], o_idx, o_g, o_out, "list full size")
+    assert layer.device_error() == 0
+    del layer, dl
