@@ -73,6 +73,10 @@ def parse():
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "router_gemv_decode_q4_traffic.md")
 TRAFFIC_SOURCES = ["expert_routing_quantized_amd/csrc/router.hip", "expert_routing_quantized_amd/csrc/moe_internal.h"]
+SCREEN_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "screen_decode_q4_traffic.md")
+SCREEN_TRAFFIC_SOURCES = ["expert_routing_quantized_amd/csrc/screen.hip",
+                          "expert_routing_quantized_amd/csrc/select_screen.h",
+                          "expert_routing_quantized_amd/csrc/moe_internal.h"]
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
@@ -93,27 +97,28 @@ def median_replay_ms(graph, stream, reps=5):
     return statistics.median(times)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the sources the router GEMV is compiled from."""
+def kernel_source_hash(screen=False) -> str:
+    """sha256 over the sources the dominant kernel (the router GEMV, or the
+    screen) is compiled from."""
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in (SCREEN_TRAFFIC_SOURCES if screen else TRAFFIC_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per router launch from the committed counter summary, or
-    None when the summary is missing or the kernel sources changed since."""
+def measured_traffic(screen=False):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when it is missing or the kernel sources changed since."""
     try:
         fields = {}
-        with open(TRAFFIC_PROFILE) as f:
+        with open(SCREEN_TRAFFIC_PROFILE if screen else TRAFFIC_PROFILE) as f:
             for line in f:
                 if line.startswith("- ") and ": " in line:
                     k, v = line[2:].split(": ", 1)
                     fields[k.strip()] = v.strip().strip("`")
-        if fields.get("source_sha256") != kernel_source_hash():
+        if fields.get("source_sha256") != kernel_source_hash(screen):
             return None
         return float(fields["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -161,24 +166,38 @@ def counters_main(args, spec):
     zbuf = torch.empty((spec.E,), dtype=torch.float64, device=dev)
     for t in range(W + K):
         layers[t % n_rep].grouped_forward(X[t], 1, idx[t], gates[t], 0, out[t], ws)
+    vbuf = torch.empty((spec.E,), dtype=torch.float32, device=dev)
     for t in range(W, W + K):
-        layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
+        if screen:
+            layers[t % n_rep].router_screen(X[t], 1, vbuf, None, ws)
+        else:
+            layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
     src = torch.empty(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"counters_run": True, "tokens": W + K, "router_launches": K,
+    print(json.dumps({"counters_run": True, "tokens": W + K, "router_launches": K, "screen": screen,
                       "copy_bytes": COPY_CALIBRATION_BYTES, "copies": 3,
-                      "router_bytes_per_launch": step_bytes(spec)["router"],
-                      "source_sha256": kernel_source_hash()}), flush=True)
+                      "dominant_kernel_bytes_per_launch": screen_bytes(spec) if screen else step_bytes(spec)["router"],
+                      "source_sha256": kernel_source_hash(screen)}), flush=True)
 
 
-def step_bytes(spec) -> dict:
-    """Algorithmic bytes of one decode token (what the method must move)."""
+def screen_bytes(spec) -> int:
+    """Bytes one launch of the screen reads: the int8 router, per expert its
+    scale, bias and residual norm, and x."""
+    act = 2 if spec.act == 1 else 4
+    return spec.E * spec.H + 12 * spec.E + spec.H * act
+
+
+def step_bytes(spec, screen=False, listed=0.0) -> dict:
+    """Algorithmic bytes of one decode token (what the method must move);
+    with the screen, the int8 pass plus the `listed` bf16 rows recomputed."""
     H, E, k, I = spec.H, spec.E, spec.k, spec.I
     act = 2 if spec.act == 1 else 4
     router = E * H * act + E * 4 + H * act            # weights + bias + x
+    if screen:
+        router = screen_bytes(spec) + int(round(listed * H * act))
     if spec.expert == 2:
         per_expert = 3 * I * H // 2 + 3 * I * (H // 32) * 2
     else:
@@ -228,7 +247,11 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out, dl=None):
         if 0 <= e < spec.E:
             for which in ("gate", "up", "down"):
                 fetch(int(e), which)
-    # timed pass: a fresh oracle over the same stored bytes
+    # untimed warm-up over the sample's first tokens (thread pools, caches),
+    # then the timed pass: a fresh oracle over the same stored bytes
+    Lw = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
+    Lw._absR = L0.absR()
+    oracle.moe_tokens(X[:min(16, count)], Lw)
     Lt = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch)
     Lt._absR = L0.absR()
     t0 = time.perf_counter()
@@ -250,8 +273,10 @@ def cpu_baseline(spec, first, count, gpu_idx, gpu_gates, gpu_out, dl=None):
         t1 = time.perf_counter()
         oracle.moe_tokens(X[:n1], L1)
         d1 = time.perf_counter() - t1
-    single = {"value": n1 / d1, "unit": "tokens/s", "cores": 1,
+    single = {"value": n1 / d1, "unit": "tokens/s", "cores": 1, "kind": "oracle",
               "sample": f"{n1} tokens (tokens {first}..{first + n1 - 1}), float64 numpy, {d1:.1f} s"}
+    if single["value"] > base["value"]:          # report the faster configuration as the baseline
+        base, single = single, base
     return base, parity, single
 
 
@@ -526,16 +551,21 @@ def main():
     from expert_routing_quantized_amd import MOE_LAYER_SCREEN_OFF, MOE_LAYER_SCREEN_ON
     lflags = MOE_LAYER_SCREEN_ON if screen else MOE_LAYER_SCREEN_OFF
     layers = [SD.make_layer(dl, max_tokens=1, router=r, flags=lflags) for r in routers]
-    X = SD.device_tokens(spec, 0, W + K)
+    # tokens: W warm-up, K timed, and as many after them as the oracle's
+    # sample needs beyond the timed ones (run eagerly after the timing)
+    n_cpu = max(args.cpu_sample, 0)
+    NT = W + max(K, n_cpu)
+    X = SD.device_tokens(spec, 0, NT)
     torch.cuda.synchronize()
     log(f"layer ready in {time.time() - t0:.1f}s: pool {dl.nbytes_pool() / 1e9:.2f} GB, "
         f"{n_rep} router copies")
 
     ws = layers[0].workspace(1)
-    idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
-    gates = torch.zeros((W + K, spec.k), dtype=torch.float32, device=dev)
-    out = torch.zeros((W + K, spec.H), dtype=torch.float32, device=dev)
+    idx = torch.zeros((NT, spec.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((NT, spec.k), dtype=torch.float32, device=dev)
+    out = torch.zeros((NT, spec.H), dtype=torch.float32, device=dev)
     zbuf = torch.empty((spec.E,), dtype=torch.float64, device=dev)
+    vbuf = torch.empty((spec.E,), dtype=torch.float32, device=dev)
 
     def token(t):
         # one moe_grouped_forward call per token (at T = 1 with 4-bit experts
@@ -559,7 +589,10 @@ def main():
                 token(t)
         with torch.cuda.graph(g_router, stream=s):
             for t in range(W, W + K):
-                layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
+                if screen:       # the screen kernel alone (router_screen without bounds)
+                    layers[t % n_rep].router_screen(X[t], 1, vbuf, None, ws)
+                else:
+                    layers[t % n_rep].router_logits(X[t], 1, zbuf, ws)
     torch.cuda.synchronize()
 
     with torch.cuda.stream(s):
@@ -570,13 +603,29 @@ def main():
         g_router.replay()
         torch.cuda.synchronize()
         ms_router = median_replay_ms(g_router, s)
+    # the sample's tokens past the timed ones, eagerly (outputs for the parity check)
+    for t in range(W + K, NT):
+        token(t)
+    listed = 0.0
+    if screen:
+        # rows the screen recomputed per token (its waves' counts in the
+        # workspace), over 32 eager tokens after the timed ones
+        from expert_routing_quantized_amd import binding as B
+        nw = (spec.E + 5) // 6
+        cnt = []
+        for t in range(W, W + min(32, K)):
+            token(t)
+            cnt.append(int(ws[256:256 + nw].to(torch.int64).sum().item()))
+        listed = sum(cnt) / len(cnt)
+    torch.cuda.synchronize()
     errs = [L.device_error() for L in layers]
 
     per_tok_s = ms / 1e3 / K
     tok_s = K / (ms / 1e3)
-    by = step_bytes(spec)
+    by = step_bytes(spec, screen, listed)
     router_s = ms_router / 1e3 / K
-    router_gbs = by["router"] / router_s / 1e9
+    dom_bytes = screen_bytes(spec) if screen else by["router"]
+    router_gbs = dom_bytes / router_s / 1e9
     res = {
         "metric": "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, 4-bit experts)"
                   if args.config == "decode_q4" else "MoE-layer decode tokens/s and achieved HBM GB/s (batch-1, bf16 experts)",
@@ -595,9 +644,13 @@ def main():
             "workload": (f"{args.config} batch-1 decode: H={spec.H}, E={spec.E}, top-{spec.k}, I={spec.I}, "
                          + ("4-bit experts (32-blocks, fp16 scales)" if spec.expert == 2 else "bf16 experts")
                          + f", bf16 router and hidden states, {K} sequential tokens, "
-                         + f"{args.mode} router ({n_rep} cop{'ies' if n_rep > 1 else 'y'})"),
-            "operands": "x bf16, router bf16, experts " + ("q4b32" if spec.expert == 2 else "bf16")
+                         + f"{args.mode} router ({n_rep} cop{'ies' if n_rep > 1 else 'y'})"
+                         + (", routed through the int8 screen" if screen else "")),
+            "operands": "x bf16, router bf16" + (" (int8 screen, exact integer dot products, then the listed "
+                                                 "rows in bf16)" if screen else "")
+                        + ", experts " + ("q4b32" if spec.expert == 2 else "bf16")
                         + ", fp32 accumulation, f64 near-tie refinement",
+            "screen_rows_recomputed_per_token": listed if screen else None,
             "bytes_per_token": by["total"],
             "hbm_gbs": by["total"] / per_tok_s / 1e9,
             "us_per_token": per_tok_s * 1e6,
@@ -605,25 +658,26 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "router GEMV (moe::router_kernel<bf16, CPL=4, NT=1>)",
+            "kernel": ("router screen (moe::screen_kernel<3, 4, 2>: int8 router, exact integer dot products)"
+                       if screen else "router GEMV (moe::router_kernel<bf16, CPL=4, NT=1>)"),
             "achieved": router_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": router_gbs / HBM_PEAK_GBS,
-            "traffic": measured_traffic() if args.mode == "cold" and args.config == "decode_q4" else None,
+            "traffic": measured_traffic(screen) if args.mode == "cold" and args.config == "decode_q4" else None,
             "avg_launch_us": router_s * 1e6,
-            "bytes_per_launch": by["router"],
+            "bytes_per_launch": dom_bytes,
         },
     }
     if args.cpu_sample > 0:
-        n = min(args.cpu_sample, K)
+        n = args.cpu_sample
         gi = idx[W:W + n].cpu().numpy()
         gg = gates[W:W + n].cpu().numpy()
         go = out[W:W + n].cpu().numpy()
         base, parity, single = cpu_baseline(spec, W, n, gi, gg, go, dl)
         res["cpu_baseline"] = base
         res["config"]["parity_sample"] = parity
-        res["config"]["oracle_one_thread"] = single
+        res["config"]["oracle_other_threads"] = single
     print(json.dumps(res), flush=True)
 
 
