@@ -611,7 +611,7 @@ def main():
         # rows the screen recomputed per token (its waves' counts in the
         # workspace), over 32 eager tokens after the timed ones
         from expert_routing_quantized_amd import binding as B
-        nw = (spec.E + 5) // 6
+        nw = (spec.E + 23) // 24                   # screen blocks: one count byte each
         cnt = []
         for t in range(W, W + min(32, K)):
             token(t)
@@ -658,7 +658,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("router screen (moe::screen_kernel<3, 4, 2>: int8 router, exact integer dot products)"
+            "kernel": ("router screen (moe::screen_kernel<6, 4, 2, 1, 2>: int8 router, exact integer dot products)"
                        if screen else "router GEMV (moe::router_kernel<bf16, CPL=4, NT=1>)"),
             "achieved": router_gbs,
             "peak": HBM_PEAK_GBS,

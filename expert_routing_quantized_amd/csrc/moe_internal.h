@@ -76,7 +76,7 @@ struct Workspace {
   size_t hm;        // fp32 [P][I] grouped intermediate
   size_t y;         // fp32 [P][H] grouped expert outputs
   size_t hint;      // batch-1 screen list: HintWords (128 B; state carried from call to call)
-  size_t cnt8;      // u8 [screen waves] entries each screen wave listed
+  size_t cnt8;      // u8 [screen blocks] rows each block of the screen listed
   size_t list;      // 16 B [kListSlots] the listed experts' recomputed logits
   size_t total;
 };

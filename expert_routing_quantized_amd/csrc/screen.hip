@@ -146,34 +146,10 @@ struct ScreenArgs {
   double rqmax;           // max_e ||s_e q_e|| (rounded up)
   const HintWords* hint;  // the call's hint, null: no list
   const HintWords* hsrc;  // never null: hint, or a readable stand-in (read unconditionally)
+  unsigned int* lcount;   // the list's counter (in the hint)
   unsigned char* cnt8;    // [waves]
-  ulonglong2* list;       // [kListSlots]
+  ulonglong2* list;       // [kListSlots]: (e, logit bits)
 };
-
-// Puts (e, z) in the table under `tag` (lane 0 of a wave calls it): linear
-// probing from a hash of e; a slot is free unless it holds this call's tag.
-// Every failed compare-and-swap means another wave took that slot, so the
-// probe ends within 2 kListSlots steps; false when the table is full.
-__device__ bool list_insert(ulonglong2* list, unsigned long long tag, int e, double z) {
-  unsigned long long* w = reinterpret_cast<unsigned long long*>(list);
-  const unsigned long long key = (tag << 24) | (unsigned long long)(e + 1);
-  unsigned s = (unsigned(e) * 2654435761u) >> 24;    // 8 bits: kListSlots = 256
-  unsigned long long old = __hip_atomic_load(w + 2 * s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int it = 0; it < 2 * kListSlots; ++it) {
-    if ((old >> 24) == tag && (old & 0xffffffull) != 0ull) {   // taken in this call
-      s = (s + 1) & (kListSlots - 1);
-      old = __hip_atomic_load(w + 2 * s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      continue;
-    }
-    const unsigned long long seen = atomicCAS(w + 2 * s, old, key);
-    if (seen == old) {
-      w[2 * s + 1] = (unsigned long long)__double_as_longlong(z);
-      return true;
-    }
-    old = seen;
-  }
-  return false;
-}
 
 // One wave owns RPW consecutive rows (RPW a multiple of 4: whole groups of 4
 // experts), WPB waves per block; CH = 16-byte chunks per lane of an int8 row
@@ -181,16 +157,16 @@ __device__ bool list_insert(ulonglong2* list, unsigned long long tag, int e, dou
 // loads the hidden-state elements of its own row chunks l, l + 64, ...
 // (together the wave holds all of x), takes the maximum with a DPP
 // reduction, and writes those elements' digits straight into registers.
-template <int NB, int WPB, int CH>
+template <int NB, int WPB, int CH, int RB = 2, int NBUF = 2>
 __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
-  constexpr int RB = 2, RPW = RB * NB;               // rows per batch, per wave
+  constexpr int RPW = RB * NB;                       // rows per wave
   static_assert((WPB * RPW) % 4 == 0, "a block holds whole groups of 4 experts");
   __shared__ float s_v[WPB * RPW];                   // the block's values (NaN, past E: -inf)
   __shared__ float s_vf[WPB * RPW], s_eb[WPB * RPW];  // values and ||eps_e|| (for the list)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = a.H, E = a.E, t = blockIdx.y;
   const int e0 = (blockIdx.x * WPB + wave) * RPW;
-  const bool live = e0 < E;                          // wave-uniform (every wave reaches the barrier)
+  // (waves past E compute clamped rows and discard them: every wave reaches the barrier)
   const int nch = H >> 4;                            // 16-byte chunks of an int8 row
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   // 1. the lane's x first (loads complete in order, so its digits are
@@ -206,12 +182,12 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
   // the hint (read whether or not it is used: a load under a branch would
   // wait for every load before it)
   const float ring_v = a.hsrc->ring[lane & (kHintRing - 1)];
-  const unsigned long long epoch_v = a.hsrc->epoch;
-  // rows in batches of RB, two batches in flight: batch b + 2 is issued
-  // into the buffer batch b frees (registers for 2 RB rows whatever NB is,
-  // so one wave per row group of RPW rows stays resident)
-  u32x4 r[2][RB][CH];
-  float scv[2][RB], bv[2][RB], ebv[2][RB];           // scale, bias, ||eps_e|| (the list's bound)
+  // rows in batches of RB, NBUF batches in flight: batch b + NBUF is issued
+  // into the buffer batch b frees (registers for NBUF RB rows whatever NB
+  // is, so one wave per row group of RPW rows stays resident; issuing every
+  // batch up front measured slower)
+  u32x4 r[NBUF][RB][CH];
+  float scv[NBUF][RB], bv[NBUF][RB], ebv[NBUF][RB];  // scale, bias, ||eps_e|| (the list's bound)
   auto issue = [&](int bt, int buf) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -225,8 +201,8 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
       ebv[buf][i] = a.eb8[e].x;                      // (a load under a branch would wait for all)
     }
   };
-  issue(0, 0);
-  if (NB > 1) issue(1, 1);
+#pragma unroll
+  for (int bt = 0; bt < NBUF; ++bt) issue(bt, bt);
   const bool listing = a.hint != nullptr && t == 0;  // uniform
   // 2. max |x| over the wave (= all of x) on the magnitude bits: a non-finite
   //    element has magnitude bits >= 0x7f80
@@ -306,13 +282,10 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
   // sqrt(H) / 2, where ||X||^2 = 2^14 sum hi^2 + 2^8 sum hi lo + sum lo^2
   // (three exact integer dot products of the digits).  Binary32 with a
   // (1 + 2^-20) margin per result: a handful of roundings each.
+  // (wave 0 of each block only: the block's list decisions are its job)
   float theta = INFINITY, xnu = 0.f, dnu = 0.f;
-  unsigned long long tag = 0ull;
-  if (listing) {
+  if (listing && wave == 0) {
     theta = xbad ? INFINITY : hint_threshold_lanes(ring_v);
-    const unsigned ep_lo = __builtin_amdgcn_readfirstlane((unsigned)epoch_v);
-    const unsigned ep_hi = __builtin_amdgcn_readfirstlane((unsigned)(epoch_v >> 32));
-    tag = list_tag(((unsigned long long)ep_hi << 32) | ep_lo);
     int shh = 0, shl = 0, sll = 0;
 #pragma unroll
     for (int s = 0; s < CH; ++s)
@@ -333,15 +306,12 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
     xnu = ((sqrtf(X2) * (1.f + 0x1p-20f) + hd) * (1.f + 0x1p-20f)) * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
     dnu = hd * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
   }
-  const float rqmax = (float)a.rqmax * (1.f + 0x1p-20f), u8f = (float)a.u8 * (1.f + 0x1p-20f);
-  const float babs8f = (float)a.babs8 * (1.f + 0x1p-20f) + 0x1p-149f;
-  unsigned listed = 0u;                              // rows whose upper end reaches theta (uniform)
 
   // 4. exact integer dot products, one binary64 evaluation per row, the
   //    values (and, for the list, whether v + B reaches theta)
 #pragma unroll
   for (int bt = 0; bt < NB; ++bt) {
-    const int buf = bt & 1;
+    const int buf = bt % NBUF;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       int HI = 0, LO = 0;
@@ -367,9 +337,9 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
         if (e < E && !xbad && !isfinite(vf)) atomicOr(a.dev_flag, kDevNonFinite);
       }
     }
-    if (bt + 2 < NB) {
+    if (bt + NBUF < NB) {
       __builtin_amdgcn_sched_barrier(0);             // keep the next loads after this batch (registers)
-      issue(bt + 2, buf);
+      issue(bt + NBUF, buf);
     }
   }
   // the maxima of every 4 consecutive experts of the block (NaN: -inf)
@@ -380,46 +350,62 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
     if (tid < WPB * RPW / 4 && g < G)
       a.g8[size_t(t) * G + g] = fmaxf(fmaxf(s_v[4 * tid], s_v[4 * tid + 1]), fmaxf(s_v[4 * tid + 2], s_v[4 * tid + 3]));
   }
-  if (!listing || !live) return;
-  // rows whose upper end v + B reaches theta (binary32, rounded up: every
+  // the list, by wave 0 of the block: lane l decides for the block's row l
+  // whether its upper end v + B reaches theta (binary32, rounded up: every
   // term of B is positive, so (1 + 2^-20) covers its few roundings and
   // 2^-147 those in the subnormal range; the 2^-22 |U| + 2^-149 slack covers
-  // the rounding of U and of the slack's own sum)
-#pragma unroll
-  for (int ri = 0; ri < RPW; ++ri) {
-    const float vf = s_vf[wave * RPW + ri];
-    const float B = fmaf(xnu, s_eb[wave * RPW + ri], fmaf(dnu, rqmax, fmaf(u8f, fabsf(vf), babs8f))) *
-                        (1.f + 0x1p-20f) + 0x1p-147f;
+  // the rounding of U and of the slack's own sum), then recomputes the
+  // listed rows' logits from the bf16 rows as the selection would
+  // (8-element chunks, dot2 chains) and appends them: one atomic add takes
+  // the block's slots, in flight while the rows load
+  if (!listing || wave != 0) return;
+  constexpr int BR = WPB * RPW;                      // rows of the block (<= 64)
+  static_assert(BR <= 64, "one lane per row of the block");
+  const int eb0 = blockIdx.x * BR;
+  unsigned long long listed = 0ull;
+  {
+    const float rqmax = (float)a.rqmax * (1.f + 0x1p-20f), u8f = (float)a.u8 * (1.f + 0x1p-20f);
+    const float babs8f = (float)a.babs8 * (1.f + 0x1p-20f) + 0x1p-149f;
+    const float vf = (lane < BR) ? s_vf[lane] : NAN;    // NaN past E
+    const float eb = (lane < BR) ? s_eb[lane] : 0.f;
+    const float B = fmaf(xnu, eb, fmaf(dnu, rqmax, fmaf(u8f, fabsf(vf), babs8f))) * (1.f + 0x1p-20f) + 0x1p-147f;
     const float U = vf + B;
-    if (isfinite(vf) && U + fabsf(U) * 0x1p-22f + 0x1p-149f >= theta) listed |= 1u << ri;
+    listed = __ballot(lane < BR && isfinite(vf) && U + fabsf(U) * 0x1p-22f + 0x1p-149f >= theta);
   }
-  // the listed rows' logits recomputed from the bf16 rows as the selection
-  // would (8-element chunks, dot2 chains), into the table
-  if (listed != 0u) {
+  if (listed != 0ull) {
     constexpr int CPLR = 2 * CH;
     const int n8 = H >> 3;
+    unsigned slot = 0u;
+    if (lane == 0) slot = atomicAdd(a.lcount, (unsigned)__popcll(listed));
     uint4 xc[CPLR];
 #pragma unroll
     for (int s = 0; s < CPLR; ++s)
       xc[s] = *reinterpret_cast<const uint4*>(a.x + size_t(t) * H + min(s * 64 + lane, n8 - 1) * 8);
-    for (unsigned m = listed; m != 0u; m &= m - 1u) {   // one row at a time (registers)
-      const int e = e0 + __builtin_ctz(m);
+    for (unsigned long long m = listed; m != 0ull; m &= m - 1ull) {   // one row at a time (registers)
+      const int e = eb0 + __builtin_ctzll(m);
       uint4 rr[CPLR];
 #pragma unroll
       for (int s = 0; s < CPLR; ++s)
         rr[s] = *reinterpret_cast<const uint4*>(a.R + size_t(e) * H + min(s * 64 + lane, n8 - 1) * 8);
       const double z = dot2_logit<CPLR>(xc, rr, n8, a.bias[e], lane);
-      if (lane == 0) list_insert(a.list, tag, e, z);
+      if (lane == 0 && slot < (unsigned)kListSlots)    // a full list: the selection falls back
+        a.list[slot] = make_ulonglong2((unsigned long long)e, (unsigned long long)__double_as_longlong(z));
+      ++slot;
     }
   }
-  if (lane == 0) a.cnt8[blockIdx.x * WPB + wave] = (unsigned char)__popc(listed);
+  if (lane == 0) a.cnt8[blockIdx.x] = (unsigned char)__popcll(listed);
 }
 
-// Launch shape of the screen: batches of 2 rows per wave, waves per block
-// (6 rows per wave: 1024 blocks of 4 waves at E = 24,576, one per SIMD slot
-// of the part at the kernel's occupancy, so no wave waits for another's slot).
-constexpr int kScreenBatches = 3;
-constexpr int kScreenRowsPerWave = 2 * kScreenBatches;
+// Launch shape of the screen: 6 rows per wave, one row per batch, two
+// batches in flight, 4 waves per block (1024 blocks at E = 24,576, all
+// resident at once).  Measured in a sweep of shapes (screen alone, graph of
+// launches over six router copies): 10.8-11.0 us per launch against 11.7
+// for two-row batches and 12.1 with every batch issued up front; one batch
+// in flight 13.5, 4 or 8 rows per wave 11.6-11.8.
+constexpr int kScreenBatches = 6;
+constexpr int kScreenRowsPerBatch = 1;
+constexpr int kScreenBuffers = 2;
+constexpr int kScreenRowsPerWave = kScreenRowsPerBatch * kScreenBatches;
 constexpr int kScreenWavesPerBlock = 4;
 
 static int screen_blocks(int E) {
@@ -428,7 +414,8 @@ static int screen_blocks(int E) {
 
 template <int CH>
 static hipError_t launch_screen_shape(const ScreenArgs& sa, hipStream_t s) {
-  hipLaunchKernelGGL((screen_kernel<kScreenBatches, kScreenWavesPerBlock, CH>), dim3(screen_blocks(sa.E), sa.T),
+  hipLaunchKernelGGL((screen_kernel<kScreenBatches, kScreenWavesPerBlock, CH, kScreenRowsPerBatch, kScreenBuffers>),
+                     dim3(screen_blocks(sa.E), sa.T),
                      dim3(kScreenWavesPerBlock * 64), 0, s, sa);
   return hipGetLastError();
 }
@@ -457,6 +444,7 @@ hipError_t launch_screen(const Layer& L, const void* x, int T, float* z8, float*
     a.rqmax = b.rqmax;
     a.hint = list->hint;
     a.hsrc = list->hint;
+    a.lcount = &list->hint->list_count;
     a.cnt8 = list->cnt8;
     a.list = list->list;
   }
@@ -467,8 +455,8 @@ hipError_t launch_screen(const Layer& L, const void* x, int T, float* z8, float*
   return hipErrorInvalidValue;
 }
 
-// Waves of the screen kernel that own rows (one count byte each in the list).
-int screen_waves(const Layer& L) { return (L.d.n_experts + kScreenRowsPerWave - 1) / kScreenRowsPerWave; }
+// Blocks of the screen kernel (one count byte each in the list).
+int screen_waves(const Layer& L) { return screen_blocks(L.d.n_experts); }
 
 void set_screen_list(ScreenSelectArgs& b, const Layer& L, const ScreenList* list, bool advance) {
   b.hint = list->hint;

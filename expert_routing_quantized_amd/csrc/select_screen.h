@@ -44,31 +44,34 @@ constexpr int kScreenMaxCand = 256;   // experts recomputed from the bf16 rows a
 // whose upper end v + B reaches a threshold theta taken from recent tokens
 // (their k-th largest logit: consecutive tokens' values spread little, so
 // the k experts of the next token nearly always lie above it).  Each such
-// expert's logit is recomputed by the screen wave that owns its row and
-// put in a small open-addressing table; every wave also writes how many it
-// put there.  The selection then reads about 10 KB instead of the screen
-// values, and accepts the table only when it can prove it complete:
-//  - the entries tagged for this call number exactly the waves' counts (so
-//    none was lost and no stale or stray entry is counted), fewer than the
-//    table's size;
+// expert's logit is recomputed by the screen block that owns its row and
+// appended to a list in the workspace: each block that lists rows takes
+// consecutive slots with one atomic add on the list's counter, and every
+// block also writes how many rows it listed.  The selection then reads
+// about 6 KB instead of the screen values, and accepts the list only when
+// it can prove it complete:
+//  - the counter equals the sum of the blocks' counts and fits the list: the
+//    counter started this call at 0, so slots [0, counter) were all written
+//    by this call, and no listed row was dropped;
 //  - at least k entries have a lower end z - B >= theta, so the k-th
 //    largest exact logit is >= theta, above every expert left out (those
 //    have z <= v + B < theta).
 // Otherwise it selects from the screen values as before; either way the
 // result is the same (select_tail's output depends on the input alone).
-// The workspace carries the state from call to call: a call counter whose
-// hash tags the call's entries (so no clearing is needed, and workspace
-// contents from elsewhere are only ever a slower call), and the ring of
-// recent k-th logits.  The last kernel of each call moves the call's k-th
-// logit into the ring and advances the counter.
+// The workspace carries the state from call to call: the list's counter,
+// which the last kernel of each call sets back to 0 (a counter that did not
+// start at 0 -- a workspace's first use -- only makes that call take the
+// slower path), a call counter, and the ring of recent k-th logits, into
+// which the last kernel moves the call's k-th logit.
 constexpr int kHintRing = 16;
 constexpr int kListSlots = 256;           // table size (a power of 2, <= kFastMax)
 
 struct HintWords {                        // 128 bytes of the workspace
   unsigned long long epoch;               // calls so far (from any start value)
   float kth;                              // this call's k-th logit (NaN: none)
-  unsigned int listed_calls;              // calls whose selection took the table (statistics)
-  float pad[12];
+  unsigned int listed_calls;              // calls whose selection took the list (statistics)
+  unsigned int list_count;                // entries appended to the list in this call
+  float pad[11];
   float ring[kHintRing];                  // k-th logits of recent calls
 };
 static_assert(sizeof(HintWords) <= 256, "the screen reads a 256-byte stand-in in place of a hint");
@@ -101,15 +104,6 @@ __device__ __forceinline__ float hint_threshold_lanes(float r) {   // r = ring[l
   return (ok && isfinite(th)) ? th : INFINITY;
 }
 
-// 40-bit tag of a call: the splitmix64 finaliser of its counter.
-__device__ __forceinline__ unsigned long long list_tag(unsigned long long epoch) {
-  unsigned long long z = epoch + 0x9E3779B97F4A7C15ull;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  z ^= z >> 31;
-  return z >> 24;
-}
-
 // End of a call, by one wave of the call's last kernel: the k-th logit into
 // the ring (every slot while the ring is not all finite), then the next
 // counter value.  hint_read issues the loads where the kernel starts and
@@ -131,6 +125,7 @@ __device__ __forceinline__ void hint_write(HintWords* h, const HintRead& r, int 
   if (isfinite(r.kth) && lane < kHintRing && (!ok || int(r.epoch % kHintRing) == lane)) h->ring[lane] = r.kth;
   if (lane == 0) {
     h->kth = NAN;
+    h->list_count = 0u;
     h->epoch = r.epoch + 1;
   }
 }
@@ -144,9 +139,9 @@ struct ScreenSelectArgs {
   double enmax, rqmax;     // maxima of the two norms over the experts
   double u8, babs8;        // relative and absolute terms of the screen bound
   HintWords* hint;         // batch 1 with the list (else null): the call's state
-  const unsigned char* cnt8;   // [nw] entries each screen wave put in the table
-  const ulonglong2* list;  // [kListSlots] (tag << 24 | e + 1, logit bits)
-  int nw;                  // screen waves
+  const unsigned char* cnt8;   // [nw] rows each screen block listed
+  const ulonglong2* list;  // [kListSlots] (e, logit bits)
+  int nw;                  // screen blocks
   int advance;             // this kernel ends the call: advance the hint (block 0)
 };
 
@@ -253,7 +248,7 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
   // ||delta||^2, the hint, this thread's table slot and count words
   const double xn2 = a.xnorm[2 * t], dn2 = a.xnorm[2 * t + 1];
   const float ring_v = b.hint->ring[lane & (kHintRing - 1)];
-  const unsigned long long epoch = b.hint->epoch;
+  const unsigned list_n = b.hint->list_count;
   const ulonglong2 ent = b.list[min(tid, kListSlots - 1)];
   const int nw16 = (b.nw + 15) >> 4;               // 16-byte words of counts
   constexpr int kCw = 2;                           // words per thread loaded up front (E <= 65,536)
@@ -279,7 +274,6 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
   // 0. the screen's table, when it can be proved complete
   {
     const float theta = hint_threshold_lanes(ring_v);
-    const unsigned long long tag = list_tag(epoch);
     int csum = 0;
 #pragma unroll
     for (int u = 0; u < kCw; ++u) {
@@ -304,9 +298,9 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
         csum = (int)__builtin_amdgcn_udot4(cw[j] & m, 0x01010101u, (uint32_t)csum, false);
       }
     }
-    const bool match = tid < kListSlots && (ent.x >> 24) == tag && (ent.x & 0xffffffull) != 0ull;
-    const int e = int(ent.x & 0xffffffull) - 1;
-    const bool bad = match && e >= E;
+    const bool match = tid < kListSlots && (unsigned)tid < list_n;
+    const int e = int(ent.x & 0xffffffffull);
+    const bool bad = match && (ent.x >= (unsigned long long)E);
     const double zv = __longlong_as_double((long long)ent.y);
     const double Bz = Btr + a.rel * fabs(zv);      // the recomputed logit's lower end, rounded down
     const bool low_ok = match && !bad && (zv - Bz) - 1e-15 * (fabs(zv) + Bz + 1.0) >= (double)theta;
@@ -338,7 +332,7 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
       tl += S.s_red3[1][w];
       tb += S.s_red3[2][w];
     }
-    const int found = s_cnt;
+    const int found = s_cnt;                       // = min(list_n, kListSlots) when no entry is bad
     if (!(isfinite(xn2) && isfinite(dn2))) {       // non-finite hidden state: no routing
       if (tid < k) {
         oi[tid] = -1;
@@ -347,7 +341,7 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
       if (tid == 0) atomicOr(a.dev_flag, kDevNonFinite);
       return;
     }
-    if (theta < INFINITY && tb == 0 && found == tc && found < kListSlots && tl >= k) {
+    if (theta < INFINITY && tb == 0 && (int)list_n == tc && list_n <= (unsigned)kListSlots && tl >= k) {
       if (tid == 0 && blockIdx.x == 0) atomicAdd(&b.hint->listed_calls, 1u);
       select_tail<ACT>(a, t, found, S, Btr, a.rel, zr, Btg, u8, zt, oi, og);
       return;

@@ -325,10 +325,10 @@ def test_list_route_path_and_low_theta():
     check_bitwise(fi, fg, fo, gi, gg, go)
 
 
-def test_list_stale_entries_are_not_taken():
-    """Setting the call counter back makes the previous call's entries look
-    current: the counts no longer match and the call selects without the
-    table (same result as a fresh workspace)."""
+def test_list_counter_not_reset():
+    """A list counter that did not start the call at 0 (as a workspace's
+    first use may leave it) makes that call select without the list, with
+    the same result; the call sets it back, so the next one uses the list."""
     torch = G.torch_mod()
     import synth.device as SD
     spec, dl, L = setup("wide_q4")
@@ -337,26 +337,17 @@ def test_list_stale_entries_are_not_taken():
     ref = grouped_tokens(layer, x, 8, layer.workspace(1))
     ws = layer.workspace(1)
     ws.zero_()
-    out = []
     for t in range(8):
-        ep0, listed0, _ = hint_state(ws)
+        if t % 2 == 1:
+            ws[16:20].view(torch.int32).fill_(3 + t)        # the list's counter
+        _, listed0, _ = hint_state(ws)
         r = grouped_tokens(layer, x[t:t + 1], 1, ws)
-        out.append(r)
-        ep1, listed1, _ = hint_state(ws)
-        assert ep1 == ep0 + 1
-        if t >= 2 and t % 2 == 0:
-            # replay token t+1 under token t's counter: token t's entries
-            # (its screen waves' counts sit right after the 256-byte hint
-            # region) now look current
-            nw = (spec.E + 3) // 4
-            stale = int(ws[256:256 + nw].cpu().numpy().astype(np.int64).sum())
-            ws[0:8].view(torch.int64).fill_(ep0)
-            r2 = grouped_tokens(layer, x[t + 1:t + 2], 1, ws)
-            check_bitwise(*[a for a in r2], *[a[t + 1:t + 2] for a in ref])
-            if stale > 0:
-                assert hint_state(ws)[1] == listed1
-    for t in range(8):
-        check_bitwise(*out[t], *[a[t:t + 1] for a in ref])
+        check_bitwise(*r, *[a[t:t + 1] for a in ref])
+        _, listed1, _ = hint_state(ws)
+        assert int(ws[16:20].view(torch.int32).item()) == 0
+        if t % 2 == 1:
+            assert listed1 == listed0
+    assert hint_state(ws)[1] >= 2
 
 
 def test_list_garbage_workspace():
