@@ -65,6 +65,10 @@ def parse():
                    help="decode configs: N > 1 stacks N distinct layers (weight seeds base..base+N-1, "
                         "N x 21.7 GB for 4-bit experts) and times every token through all of them "
                         "(one JSON line, per layer-token cost; replaces the router copies)")
+    p.add_argument("--parity-stream", action="store_true",
+                   help="whole-stream parity against the oracle: 1000 tokens of the tiny fp32 layer and of "
+                        "both batch-1 decode layers, 1000 verify steps (T = 5), one 2048-token prefill chunk; "
+                        "one JSON line per workload (the exact-refinement counts included)")
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter run: launch eagerly (no graphs), run the router alone, then "
                         "a plain copy of known size that calibrates the byte counters; prints a summary")
@@ -518,6 +522,81 @@ def layers_main(args, spec):
     }), flush=True)
 
 
+def parity_main(args):
+    """Every output of whole workloads against the oracle (float64), on the
+    seeded synthetic inputs: indices exactly, gates and outputs within the
+    tolerances of the parity tests; also the exact-refinement counts and, at
+    batch 1 through the screen, how many calls selected from its list."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    import synth.device as SD
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    plan = [("tiny_f32", 1, 1000), ("decode_bf16", 1, 1000), ("decode_q4", 1, 1000),
+            ("verify_q4", 5, 1000), ("prefill_bf16", 2048, 1)]
+    for name, T, steps in plan:
+        spec = synth.CONFIGS[name]
+        t0 = time.time()
+        dl = SD.device_layer(spec)
+        layer = SD.make_layer(dl, max_tokens=T)
+        n = T * steps
+        X = SD.device_tokens(spec, 0, n)
+        ws = layer.workspace(T)
+        ws.zero_()
+        idx = torch.empty((n, spec.k), dtype=torch.int32, device=dev)
+        gates = torch.empty((n, spec.k), dtype=torch.float32, device=dev)
+        out = torch.empty((n, spec.H), dtype=torch.float32, device=dev)
+        r0 = layer.exact_refinements()
+        for st in range(steps):
+            a, b = st * T, (st + 1) * T
+            layer.grouped_forward(X[a:b], T, idx[a:b], gates[a:b], 0, out[a:b], ws)
+        torch.cuda.synchronize()
+        nref = layer.exact_refinements() - r0
+        listed = int(ws[12:16].view(torch.int32).item()) if (T == 1 and spec.act == synth.DT_BF16) else None
+        errs = layer.device_error()
+        gi, gg, go = idx.cpu().numpy(), gates.cpu().numpy(), out.cpu().numpy()
+        log(f"{name}: {steps} calls of T={T} on the GPU in {time.time() - t0:.1f} s; oracle ...")
+
+        stored = {}
+
+        def fetch(e, which, dl=dl, spec=spec, stored=stored):
+            key = (e, which)
+            if key not in stored:
+                w = {"gate": dl.w_gate, "up": dl.w_up, "down": dl.w_down}[which][e]
+                if spec.expert == synth.DT_Q4:
+                    sc = {"gate": dl.s_gate, "up": dl.s_up, "down": dl.s_down}[which][e]
+                    stored[key] = ("q4", (w.cpu().numpy(), sc.cpu().numpy().view(np.uint16)))
+                elif spec.expert == synth.DT_BF16:
+                    stored[key] = ("bf16", w.view(torch.int16).cpu().numpy().view(np.uint16))
+                else:
+                    stored[key] = ("f32", w.cpu().numpy())
+            return stored[key]
+        L0 = oracle.layer_from_spec(spec)
+        L = oracle.OracleLayer(L0.R, L0.b, spec.k, fetch, cache_size=4096)
+        Xh = oracle.tokens_f64(spec, 0, n)
+        o_idx = np.empty((n, spec.k), np.int64)
+        o_g = np.empty((n, spec.k))
+        o_out = np.empty((n, spec.H))
+        for c0 in range(0, n, 256):
+            c1 = min(n, c0 + 256)
+            o_idx[c0:c1], o_g[c0:c1], _, o_out[c0:c1] = oracle.moe_tokens(Xh[c0:c1], L)
+            log(f"{name}: oracle {c1}/{n} tokens")
+        rel = np.linalg.norm(go.astype(np.float64) - o_out, axis=1) / np.maximum(np.linalg.norm(o_out, axis=1), 1e-300)
+        print(json.dumps({
+            "workload": name, "T": T, "calls": steps, "tokens": n,
+            "idx_mismatched_tokens": int((gi != o_idx).any(axis=1).sum()),
+            "gate_max_abs_err": float(np.abs(gg.astype(np.float64) - o_g).max()),
+            "out_rel_l2_max": float(rel.max()), "out_rel_l2_median": float(np.median(rel)),
+            "exact_refinements": int(nref), "exact_refinements_per_token": nref / n,
+            "calls_selected_from_the_screen_list": listed, "device_errors": errs,
+            "seconds": round(time.time() - t0, 1)}), flush=True)
+        del layer, dl, X, ws, idx, gates, out, L, L0, stored
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -532,6 +611,8 @@ def main():
 
     if args.sweep:
         return sweep_main(args)
+    if args.parity_stream:
+        return parity_main(args)
     spec = synth.CONFIGS[args.config]
     if args.counters:
         return counters_main(args, spec)

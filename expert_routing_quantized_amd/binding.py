@@ -26,7 +26,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE"
 
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
            "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
-           "moe_router_logits", "moe_router_screen",
+           "moe_router_logits", "moe_router_screen", "moe_layer_stats",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -71,6 +71,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_grouped_forward.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp, sz, vp]
     lib.moe_grouped_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp]
     lib.moe_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
+    lib.moe_layer_stats.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint64)]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -78,7 +79,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_abi_version.argtypes = []
     for name in ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
                  "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
-           "moe_router_logits", "moe_router_screen", "moe_abi_version"]:
+           "moe_router_logits", "moe_router_screen", "moe_layer_stats", "moe_abi_version"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -178,6 +179,11 @@ class Layer:
     def grouped_forward_noalloc(self, x, T, idx, gates, flags, out, stream=None):
         _check(self.lib.moe_grouped_forward_noalloc(self.handle, _ptr(x), T, _ptr(idx), _ptr(gates), flags,
                                                     _ptr(out), _stream(stream)), "moe_grouped_forward_noalloc")
+
+    def exact_refinements(self, stream=None) -> int:
+        n = ctypes.c_uint64()
+        _check(self.lib.moe_layer_stats(self.handle, _stream(stream), ctypes.byref(n)), "moe_layer_stats")
+        return n.value
 
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32()

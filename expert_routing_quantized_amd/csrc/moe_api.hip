@@ -330,9 +330,10 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
     return cleanup(hip_fail(e, "hipGetSymbolAddress(scratch)"));
   if ((e = hipMalloc(&L.norms, (E + 1) * sizeof(float))) != hipSuccess)
     return cleanup(hip_fail(e, "hipMalloc(norms)"));
-  if ((e = hipMalloc(&L.dev_flag, sizeof(int))) != hipSuccess)
+  // the sticky fault word, then (8-byte aligned) the count of exact refinements
+  if ((e = hipMalloc(&L.dev_flag, moe::kDevWordsBytes)) != hipSuccess)
     return cleanup(hip_fail(e, "hipMalloc(flag)"));
-  if ((e = hipMemsetAsync(L.dev_flag, 0, sizeof(int), s)) != hipSuccess)
+  if ((e = hipMemsetAsync(L.dev_flag, 0, moe::kDevWordsBytes, s)) != hipSuccess)
     return cleanup(hip_fail(e, "hipMemsetAsync(flag)"));
   if (!desc->router_bias) {
     if ((e = hipMalloc(&L.zero_bias, E * sizeof(float))) != hipSuccess)
@@ -522,6 +523,18 @@ moe_status moe_device_error(const moe_layer* layer, void* stream, int32_t* code)
   if (e != hipSuccess) return hip_fail(e, "moe_device_error");
   *code = v;
   if (v) return fail(MOE_E_DEVICE_FLAG, "device fault bits 0x%x", v);
+  return ok();
+}
+
+moe_status moe_layer_stats(const moe_layer* layer, void* stream, uint64_t* exact_refinements) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (!exact_refinements) return fail(MOE_E_NULL, "exact_refinements is NULL");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned long long v = 0;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(&v, moe::refine_counter(layer->L.dev_flag), sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "moe_layer_stats");
+  *exact_refinements = v;
   return ok();
 }
 

@@ -31,7 +31,7 @@ struct Layer {
   const void* router_eh;    // expert-major router actually read by the kernels
   void* router_copy;        // owned copy when the caller's layout is [H][E]
   float* norms;             // owned: [E] router row 2-norms (rounded up), then [1] max
-  int* dev_flag;            // owned: sticky device fault word
+  int* dev_flag;            // owned: sticky device fault word, then the refinement counter
   float* zero_bias;         // owned: [E] zeros when the caller gives no bias, else null
   double norm_max;          // host copy of max_e ||R_e||_2 (rounded up)
   int device;
@@ -44,6 +44,13 @@ struct Layer {
   float* screen_consts;     // owned: device maxima of the two norms and of |b|
   double screen_enmax, screen_rqmax, screen_bmax;   // host copies
 };
+
+// The layer's device words: the sticky fault bits (int), then at byte 8 the
+// count of exact refinements (unsigned long long, statistics).
+constexpr size_t kDevWordsBytes = 16;
+__host__ __device__ inline unsigned long long* refine_counter(int* dev_flag) {
+  return reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(dev_flag) + 8);
+}
 
 // Layers with at least this many experts (bf16 activations, H a multiple of
 // 32) screen the batch-1 router pass unless MOE_LAYER_SCREEN_OFF: the int8

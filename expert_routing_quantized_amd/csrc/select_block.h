@@ -286,6 +286,7 @@ __device__ __forceinline__ double refine_logit(const SelectArgs& a, int t, int e
   const double dn = r - nextafter(r, -INFINITY);
   const bool ok = !a.force_exact && isfinite(r) && (d + eps < 0.5 * up) && (d - eps > -0.5 * dn);
   if (ok) return r;
+  if (lane == 0) atomicAdd(refine_counter(a.dev_flag), 1ull);   // statistics (moe_layer_stats)
   return exact_logit_bins<ACT>(a.R, a.x, a.bias, a.H, t, e, bins, lane, a.dev_flag);
 }
 

@@ -231,6 +231,13 @@ moe_status moe_grouped_forward_noalloc(const moe_layer* layer, const void* x, in
  * Returns MOE_E_DEVICE_FLAG when *code != 0. */
 moe_status moe_device_error(const moe_layer* layer, void* stream, int32_t* code);
 
+/* Statistics: synchronise `stream` and return in *exact_refinements how many
+ * logits the layer's selections have refined exactly since it was created
+ * (the integer-bin accumulation run when a logit's error interval overlaps
+ * a neighbour's at the order of the k chosen experts or at the cut; see the
+ * selection's certification).  Host pointer; MOE_E_NULL when it is NULL. */
+moe_status moe_layer_stats(const moe_layer* layer, void* stream, uint64_t* exact_refinements);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

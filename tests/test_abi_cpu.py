@@ -99,6 +99,8 @@ def test_entry_points_refuse_null_layer():
     assert lib.moe_router_screen(None, 1, 1, 1, 1, 1, 1, None) == -1
     code = ctypes.c_int32()
     assert lib.moe_device_error(None, None, ctypes.byref(code)) == -1
+    nref = ctypes.c_uint64()
+    assert lib.moe_layer_stats(None, None, ctypes.byref(nref)) == -1
     assert lib.moe_layer_destroy(None) == 0
 
 

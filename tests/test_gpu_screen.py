@@ -82,6 +82,8 @@ def test_screened_decode_small(name, exact):
     G.compare(fi, fg, fo, o_idx, o_g, o_out, f"screen {name}")
     check_bitwise(fi, fg, fo, si, sg, so)
     assert layer.device_error() == 0
+    if exact:      # every selection refined its candidates exactly (moe_layer_stats counts them)
+        assert layer.exact_refinements() >= 2 * n * spec.k
 
 
 def _exact_logits(spec, first, n, R=None, b=None):
