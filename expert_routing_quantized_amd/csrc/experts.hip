@@ -504,6 +504,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_dense_kernel(Scr
 template <int WD>
 __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   __shared__ float part[kMaxK][8];
+  __shared__ float s_g[kMaxK];
   __shared__ int s_bad;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
@@ -523,6 +524,9 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   // checks its own experts with a ballot (no dependent loads before the
   // weight loads)
   const int vi = (lane < k) ? ti[lane] : -1;
+  // the gates with the indices (the combine after the barrier would
+  // otherwise wait for one more round trip)
+  if (wave == 0 && lane < k) s_g[lane] = a.gates[size_t(t) * k + lane];
   __syncthreads();
   for (int j = wave; j < k; j += nw) {
     int e = __shfl(vi, j);
@@ -562,7 +566,7 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   __syncthreads();
   if (threadIdx.x < 8 && blockIdx.x * 8 + (int)threadIdx.x < a.H) {
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s = fmaf(a.gates[size_t(t) * k + j], part[j][threadIdx.x], s);
+    for (int j = 0; j < k; ++j) s = fmaf(s_g[j], part[j][threadIdx.x], s);
     a.out[size_t(t) * a.H + blockIdx.x * 8 + threadIdx.x] = s_bad ? NAN : s;
   }
   if (ends) hint_write(a.hint, hr, lane);
@@ -590,6 +594,7 @@ template <int UG>
 __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kernel(PairArgs a) {
   extern __shared__ __attribute__((aligned(16))) float sh_h[];   // [P][I]
   __shared__ float part[kMaxPairs][8];
+  __shared__ float s_g[kMaxPairs];
   __shared__ int s_bad[kMaxPairs];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane & 7, grp = lane >> 3;
@@ -600,6 +605,7 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
   const bool ends = a.hint != nullptr && blockIdx.x == 0 && wave == 0;   // this wave ends the call
   HintRead hr{};
   if (ends) hr = hint_read(a.hint, lane);
+  const float gq = (tid < P) ? a.gates[tid] : 0.f;  // the gates, read now (P <= 128 threads)
   // 1. h of every pair: all loads in flight (P I / 4 <= 64 kWindowWaves UG)
   const int n4 = P * I / 4;
   float4 hv4[UG];
@@ -639,6 +645,7 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
     const int c = tid + i * 64 * kWindowWaves;
     if (c < n4) reinterpret_cast<float4*>(sh_h)[c] = hv4[i];
   }
+  if (tid < P) s_g[tid] = gq;
   if (tid < a.T) s_bad[tid] = 0;
   __syncthreads();
 #pragma unroll
@@ -677,7 +684,7 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
     const int t = c >> 3, r = c & 7;
     if (blockIdx.x * 8 + r >= a.H) continue;
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s = fmaf(a.gates[t * k + j], part[t * k + j][r], s);
+    for (int j = 0; j < k; ++j) s = fmaf(s_g[t * k + j], part[t * k + j][r], s);
     a.out[size_t(t) * a.H + blockIdx.x * 8 + r] = s_bad[t] ? NAN : s;
   }
   if (ends) hint_write(a.hint, hr, lane);
@@ -719,6 +726,7 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
   __shared__ int s_uniq[kMaxPairs];
   __shared__ int s_bad[kMaxPairs];
   __shared__ int s_next[kMaxPairs];     // next pair naming the same expert, or -1
+  __shared__ float s_g[kMaxPairs];
   __shared__ int s_nu;
   constexpr int UG = SPL == 1 ? 4 : (SPL <= 4 ? 2 : 1);   // experts prefetched per wave
   constexpr int kElems = (WD == MOE_Q4B32) ? 32 : 8;
@@ -738,7 +746,10 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
     for (int c = threadIdx.x; c < P * I / 4; c += blockDim.x) dst[c] = src[c];
   }
   if (threadIdx.x == 0) s_nu = 0;
-  for (int q = threadIdx.x; q < P; q += blockDim.x) s_idx[q] = a.idx[q];
+  for (int q = threadIdx.x; q < P; q += blockDim.x) {
+    s_idx[q] = a.idx[q];
+    s_g[q] = a.gates[q];                  // read now: the combine after the barriers needs them
+  }
   for (int t = threadIdx.x; t < a.T; t += blockDim.x) s_bad[t] = 0;
   __syncthreads();
   for (int q = threadIdx.x; q < P; q += blockDim.x) {
@@ -826,7 +837,7 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
     const int t = c >> 3, r = c & 7;
     if (blockIdx.x * 8 + r >= a.H) continue;
     float s = 0.f;
-    for (int j = 0; j < k; ++j) s = fmaf(a.gates[t * k + j], part[t * k + j][r], s);
+    for (int j = 0; j < k; ++j) s = fmaf(s_g[t * k + j], part[t * k + j][r], s);
     a.out[size_t(t) * a.H + blockIdx.x * 8 + r] = s_bad[t] ? NAN : s;
   }
 }
