@@ -81,6 +81,9 @@ SCREEN_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "screen_decode_q4_traffi
 SCREEN_TRAFFIC_SOURCES = ["expert_routing_quantized_amd/csrc/screen.hip",
                           "expert_routing_quantized_amd/csrc/select_screen.h",
                           "expert_routing_quantized_amd/csrc/moe_internal.h"]
+# the whole decode step (screen, fused selection + gate/up, down + combine)
+STEP_TRAFFIC_SOURCES = SCREEN_TRAFFIC_SOURCES + ["expert_routing_quantized_amd/csrc/experts.hip",
+                                                 "expert_routing_quantized_amd/csrc/select_block.h"]
 COPY_CALIBRATION_BYTES = 256 << 20
 
 
@@ -101,12 +104,13 @@ def median_replay_ms(graph, stream, reps=5):
     return statistics.median(times)
 
 
-def kernel_source_hash(screen=False) -> str:
+def kernel_source_hash(screen=False, step=False) -> str:
     """sha256 over the sources the dominant kernel (the router GEMV, or the
-    screen) is compiled from."""
+    screen) -- or, with step, every kernel of the screened decode step -- is
+    compiled from."""
     import hashlib
     h = hashlib.sha256()
-    for rel in (SCREEN_TRAFFIC_SOURCES if screen else TRAFFIC_SOURCES):
+    for rel in (STEP_TRAFFIC_SOURCES if step else SCREEN_TRAFFIC_SOURCES if screen else TRAFFIC_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -125,6 +129,23 @@ def measured_traffic(screen=False):
         if fields.get("source_sha256") != kernel_source_hash(screen):
             return None
         return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def measured_step_traffic():
+    """HBM bytes of one whole screened decode step (all three kernels) from
+    the committed counter summary, or None when missing or stale."""
+    try:
+        fields = {}
+        with open(SCREEN_TRAFFIC_PROFILE) as f:
+            for line in f:
+                if line.startswith("- ") and ": " in line:
+                    k, v = line[2:].split(": ", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("step_source_sha256") != kernel_source_hash(step=True):
+            return None
+        return float(fields["step_traffic_bytes_per_token"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -733,6 +754,8 @@ def main():
                         + ", fp32 accumulation, f64 near-tie refinement",
             "screen_rows_recomputed_per_token": listed if screen else None,
             "bytes_per_token": by["total"],
+            "hbm_bytes_per_token_measured": (measured_step_traffic() if screen and args.mode == "cold"
+                                             and args.config == "decode_q4" else None),
             "hbm_gbs": by["total"] / per_tok_s / 1e9,
             "us_per_token": per_tok_s * 1e6,
             "device_errors": errs,
