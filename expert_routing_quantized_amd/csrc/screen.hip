@@ -187,7 +187,6 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
   // is, so one wave per row group of RPW rows stays resident; issuing every
   // batch up front measured slower)
   u32x4 r[NBUF][RB][CH];
-  float scv[NBUF][RB], bv[NBUF][RB], ebv[NBUF][RB];  // scale, bias, ||eps_e|| (the list's bound)
   auto issue = [&](int bt, int buf) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -196,13 +195,15 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
       for (int s = 0; s < CH; ++s)
         r[buf][i][s] = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(a.q8 + size_t(e) * H) + min(s * 64 + lane, nch - 1));
-      scv[buf][i] = a.sc8[e];
-      bv[buf][i] = a.bias[e];
-      ebv[buf][i] = a.eb8[e].x;                      // (a load under a branch would wait for all)
     }
   };
 #pragma unroll
   for (int bt = 0; bt < NBUF; ++bt) issue(bt, bt);
+  // scale, bias and ||eps_e|| (the list's bound) of the wave's rows: lane l
+  // holds row e0 + l's (the rows' values are evaluated together at the end)
+  static_assert(RPW <= 64, "one lane per row of the wave");
+  const int el = min(e0 + min(lane, RPW - 1), E - 1);
+  const float my_sc = a.sc8[el], my_b = a.bias[el], my_eb = a.eb8[el].x;
   const bool listing = a.hint != nullptr && t == 0;  // uniform
   // 2. max |x| over the wave (= all of x) on the magnitude bits: a non-finite
   //    element has magnitude bits >= 0x7f80
@@ -307,8 +308,10 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
     dnu = hd * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
   }
 
-  // 4. exact integer dot products, one binary64 evaluation per row, the
+  // 4. exact integer dot products per row (lane ri keeps row ri's sums),
+  //    then one binary64 evaluation of every row of the wave at once, the
   //    values (and, for the list, whether v + B reaches theta)
+  int dacc = 0, hacc = 0, lacc = 0;
 #pragma unroll
   for (int bt = 0; bt < NB; ++bt) {
     const int buf = bt % NBUF;
@@ -324,23 +327,35 @@ __global__ __launch_bounds__(WPB * 64) void screen_kernel(ScreenArgs a) {
           LO = __builtin_amdgcn_sdot4((int)w[q], dl[s][q], LO, false);
         }
       }
-      HI = wave_sum_i32(HI);
-      LO = wave_sum_i32(LO);
-      const int ri = bt * RB + i, e = e0 + ri;
-      const double v = (double)scv[buf][i] * (128.0 * (double)HI + (double)LO) * isc + (double)bv[buf][i];
-      const float vf = xbad ? NAN : (float)v;
-      if (lane == 0) {
-        s_v[wave * RPW + ri] = (e < E && !isnan(vf)) ? vf : -INFINITY;
-        s_vf[wave * RPW + ri] = (e < E) ? vf : NAN;
-        s_eb[wave * RPW + ri] = ebv[buf][i];
-        if (e < E) a.z8[size_t(t) * E + e] = vf;
-        if (e < E && !xbad && !isfinite(vf)) atomicOr(a.dev_flag, kDevNonFinite);
+      const int ri = bt * RB + i;
+      if constexpr (CH <= 2) {
+        // H <= 2048: sum_h |q_eh X_h| <= 2048 * 127 * 2^13 < 2^31, so 128 HI + LO
+        // and every partial sum of it are exact in int32: one wave sum
+        const int D = wave_sum_i32(128 * HI + LO);
+        dacc = (lane == ri) ? D : dacc;
+      } else {
+        const int HS = wave_sum_i32(HI), LS = wave_sum_i32(LO);
+        hacc = (lane == ri) ? HS : hacc;
+        lacc = (lane == ri) ? LS : lacc;
       }
     }
     if (bt + NBUF < NB) {
       __builtin_amdgcn_sched_barrier(0);             // keep the next loads after this batch (registers)
       issue(bt + NBUF, buf);
     }
+  }
+  {
+    const int ri = lane, e = e0 + ri;
+    const double D = (CH <= 2) ? (double)dacc : 128.0 * (double)hacc + (double)lacc;   // exact
+    const double v = (double)my_sc * D * isc + (double)my_b;
+    const float vf = xbad ? NAN : (float)v;
+    if (ri < RPW) {
+      s_v[wave * RPW + ri] = (e < E && !isnan(vf)) ? vf : -INFINITY;
+      s_vf[wave * RPW + ri] = (e < E) ? vf : NAN;
+      s_eb[wave * RPW + ri] = my_eb;
+      if (e < E) a.z8[size_t(t) * E + e] = vf;
+    }
+    if (__ballot(ri < RPW && e < E && !xbad && !isfinite(vf)) != 0ull && lane == 0) atomicOr(a.dev_flag, kDevNonFinite);
   }
   // the maxima of every 4 consecutive experts of the block (NaN: -inf)
   __syncthreads();
