@@ -27,6 +27,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE"
 EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
            "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
            "moe_router_logits", "moe_router_screen", "moe_layer_stats",
+           "moe_decoder_create", "moe_decoder_destroy", "moe_decoder_buffers", "moe_decoder_step",
+           "moe_decoder_doorbell",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -77,9 +79,17 @@ def load_library(path: str = LIB_PATH):
     lib.moe_last_error_message.argtypes = []
     lib.moe_last_error_message.restype = ctypes.c_char_p
     lib.moe_abi_version.argtypes = []
+    lib.moe_decoder_create.argtypes = [ctypes.POINTER(vp), i32, vp, ctypes.POINTER(vp)]
+    lib.moe_decoder_destroy.argtypes = [vp]
+    lib.moe_decoder_buffers.argtypes = [vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                        ctypes.POINTER(vp)]
+    lib.moe_decoder_step.argtypes = [vp, vp, i32]
+    lib.moe_decoder_doorbell.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint64)]
     for name in ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_route",
                  "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
-           "moe_router_logits", "moe_router_screen", "moe_layer_stats", "moe_abi_version"]:
+                 "moe_router_logits", "moe_router_screen", "moe_layer_stats", "moe_abi_version",
+                 "moe_decoder_create", "moe_decoder_destroy", "moe_decoder_buffers", "moe_decoder_step",
+                 "moe_decoder_doorbell"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -191,3 +201,44 @@ class Layer:
         if st not in (0, -8):
             _check(st, "moe_device_error")
         return code.value
+
+
+class Decoder:
+    """Batch-1 decode through a stack of layers, one captured graph per layer
+    (moe_decoder_*).  Keeps references to the layers, which must outlive it."""
+
+    def __init__(self, layers, stream=None):
+        self.lib = load_library()
+        self.layers = list(layers)
+        arr = (ctypes.c_void_p * len(self.layers))(*[L.handle for L in self.layers])
+        h = ctypes.c_void_p()
+        _check(self.lib.moe_decoder_create(arr, len(self.layers), _stream(stream), ctypes.byref(h)),
+               "moe_decoder_create")
+        self.handle = h
+
+    def buffers(self, layer):
+        """(x, out, idx, gates) device addresses of `layer` (None where absent)."""
+        x, out, idx, gates = (ctypes.c_void_p() for _ in range(4))
+        _check(self.lib.moe_decoder_buffers(self.handle, layer, ctypes.byref(x), ctypes.byref(out),
+                                            ctypes.byref(idx), ctypes.byref(gates)), "moe_decoder_buffers")
+        return x.value, out.value, idx.value, gates.value
+
+    def step(self, wait_doorbell=False, stream=None):
+        _check(self.lib.moe_decoder_step(self.handle, _stream(stream), 1 if wait_doorbell else 0),
+               "moe_decoder_step")
+
+    def doorbell(self, layer) -> int:
+        v = ctypes.c_uint64()
+        _check(self.lib.moe_decoder_doorbell(self.handle, layer, ctypes.byref(v)), "moe_decoder_doorbell")
+        return v.value
+
+    def close(self):
+        if self.handle:
+            _check(self.lib.moe_decoder_destroy(self.handle), "moe_decoder_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

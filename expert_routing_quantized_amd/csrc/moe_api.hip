@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <mutex>
 #include <string>
 
@@ -235,6 +236,27 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
 }  // namespace
 
 namespace moe {
+
+moe_status api_fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+moe_status api_ok() { return ok(); }
+
+const moe_layer_desc& layer_desc(const moe_layer* layer) { return layer->L.d; }
+
+int layer_device(const moe_layer* layer) { return layer->L.device; }
+
+long long host_clock_us() {
+  return std::chrono::duration_cast<std::chrono::microseconds>(std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
 
 Workspace workspace_layout(const Layer& L, int T) {
   Workspace W{};

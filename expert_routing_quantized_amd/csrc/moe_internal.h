@@ -365,6 +365,14 @@ hipError_t launch_pair_experts(const Layer& L, const void* x, int T, const int32
 // selection fused with gate/up (idx, gates written), then down + combine;
 // h is [T k][I] fp32 workspace.
 bool decode_fused_fits(const Layer& L, int T);
+
+// ---- host helpers shared by the entry points (moe_api.hip) and the decoder
+constexpr int kMaxDecoderLayers = 64;
+moe_status api_fail(moe_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status api_ok();
+const moe_layer_desc& layer_desc(const moe_layer* layer);
+int layer_device(const moe_layer* layer);
+long long host_clock_us();
 hipError_t launch_decode_fused(const Layer& L, const void* x, int T, const double* z, const float* gmax,
                             const double* xnorm, const RouterBound& rb, int32_t* idx, float* gates,
                             float* out, float* h, hipStream_t s);

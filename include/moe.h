@@ -238,6 +238,56 @@ moe_status moe_device_error(const moe_layer* layer, void* stream, int32_t* code)
  * selection's certification).  Host pointer; MOE_E_NULL when it is NULL. */
 moe_status moe_layer_stats(const moe_layer* layer, void* stream, uint64_t* exact_refinements);
 
+/* ---- Batch-1 decode through a stack of layers, one captured graph per layer.
+ *
+ * The pages' engine composes each token from one captured graph per layer:
+ * a graph bakes in its arguments, so per-token values arrive through
+ * fixed-address device buffers, and the host decides when each layer's graph
+ * runs, signalled by a doorbell (pyshine source tour, paragraph on the driver
+ * that composes one token).
+ *
+ * A decoder chains n_layers layers (bf16 activations, one hidden size H, one
+ * device) through a residual stream.  Layer l reads its input slot x_l (bf16
+ * [H]), runs moe_grouped_forward (T = 1, routed inside, its own workspace)
+ * into idx_l (int32 [k]), gates_l (fp32 [k]) and out_l (fp32 [H]), then its
+ * epilogue writes x_{l+1} = bf16(x_l + out_l) (the fp32 sum rounded to
+ * nearest even) into slot l + 1 -- slot n_layers is the decoder's result --
+ * and rings the layer's doorbell: a host-pinned word that receives the step
+ * number (1, 2, ...) once the layer's stores are in memory. */
+typedef struct moe_decoder moe_decoder;
+
+/* Allocate the fixed buffers (device memory, zeroed; doorbells in
+ * host-pinned memory) and capture one graph per layer.  Synchronises
+ * `stream` first; the layers must outlive the decoder.  The current device
+ * must be the layers'.  MOE_E_RANGE for n_layers outside [1, 64] or layers on
+ * another device; MOE_E_DTYPE for fp32 activations; MOE_E_GEOMETRY for
+ * differing hidden sizes. */
+moe_status moe_decoder_create(const moe_layer* const* layers, int32_t n_layers, void* stream,
+                              moe_decoder** out);
+
+/* Synchronise the device, then free everything the decoder owns.  NULL is a
+ * no-op. */
+moe_status moe_decoder_destroy(moe_decoder* decoder);
+
+/* The fixed device addresses of layer `layer` (0 <= layer <= n_layers): its
+ * input slot (bf16 [H]) and its outputs out (fp32 [H]), idx (int32 [k]),
+ * gates (fp32 [k]); layer n_layers has only the result slot (the others are
+ * set to NULL).  Any output pointer may be NULL.  A caller writes the
+ * token's hidden state into slot 0 on the stream it steps on. */
+moe_status moe_decoder_buffers(const moe_decoder* decoder, int32_t layer, void** x, float** out,
+                               int32_t** idx, float** gates);
+
+/* One token on `stream`.  wait_doorbell == 0: one launch of a graph that
+ * holds every layer's graph in order (the host returns at once).
+ * wait_doorbell != 0: the layers' graphs one launch each, the host launching
+ * layer l + 1 only after layer l's doorbell shows this step (a bounded spin:
+ * MOE_E_HIP after 2 s).  Calls on one decoder must not overlap. */
+moe_status moe_decoder_step(moe_decoder* decoder, void* stream, int32_t wait_doorbell);
+
+/* The last step layer `layer` has rung (0 before the first); a host read,
+ * no synchronisation. */
+moe_status moe_decoder_doorbell(const moe_decoder* decoder, int32_t layer, uint64_t* step);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

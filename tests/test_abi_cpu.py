@@ -104,6 +104,23 @@ def test_entry_points_refuse_null_layer():
     assert lib.moe_layer_destroy(None) == 0
 
 
+def test_decoder_entry_points_refuse_null_and_range():
+    lib = moe.load_library()
+    h = ctypes.c_void_p(0x1234)
+    assert lib.moe_decoder_create(None, 1, None, ctypes.byref(h)) == -1
+    assert h.value is None                                   # cleared on failure
+    layers = (ctypes.c_void_p * 1)(None)
+    assert lib.moe_decoder_create(layers, 1, None, None) == -1
+    assert lib.moe_decoder_create(layers, 1, None, ctypes.byref(h)) == -1    # a NULL layer
+    assert lib.moe_decoder_create(layers, 0, None, ctypes.byref(h)) == -6
+    assert lib.moe_decoder_create(layers, 65, None, ctypes.byref(h)) == -6
+    assert lib.moe_decoder_buffers(None, 0, None, None, None, None) == -1
+    assert lib.moe_decoder_step(None, None, 0) == -1
+    v = ctypes.c_uint64()
+    assert lib.moe_decoder_doorbell(None, 0, ctypes.byref(v)) == -1
+    assert lib.moe_decoder_destroy(None) == 0
+
+
 def test_binding_raises_typed_errors():
     with pytest.raises(B.MoeError) as ei:
         B._check(-2, "where")
