@@ -391,3 +391,34 @@ def test_list_fullsize_decode():
     G.compare(fi[:8], fg[:8], fo[:8], o_idx, o_g, o_out, "list full size")
     assert layer.device_error() == 0
     del layer, dl
+
+
+@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "q4_h4096"])
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+def test_windows_and_batch1_share_a_screened_workspace(name, T):
+    """On a layer with the screen, verify windows (2 <= T <= 8: the bf16
+    router) and batch-1 calls (the screen with its list) alternate through
+    one workspace: every window and every single token against the oracle,
+    moe_grouped_forward and moe_route."""
+    import synth.device as SD
+    spec, dl, L = setup(name)
+    G.note("screened layer, windows and batch 1", name, T)
+    layer = SD.make_layer(dl, max_tokens=8, flags=screen_flags())
+    first = 700 + 11 * T
+    n = 3 * T + 3
+    x = SD.device_tokens(spec, first, n)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, first, n)
+    ws = layer.workspace(T)
+    pos = 0
+    for w in range(3):
+        sl = slice(pos, pos + T)
+        fi, fg, fo = G.run_grouped(layer, x[sl], ws=ws)
+        G.compare(fi, fg, fo, o_idx[sl], o_g[sl], o_out[sl], f"window {name} T={T} w={w}")
+        ri, rg, _ = G.run_route_decode(layer, x[sl], ws=ws)
+        G.compare(ri, rg, None, o_idx[sl], o_g[sl], None, f"window route {name} T={T} w={w}")
+        pos += T
+        one = slice(pos, pos + 1)            # then one batch-1 token through the same workspace
+        fi, fg, fo = G.run_grouped(layer, x[one], ws=ws)
+        G.compare(fi, fg, fo, o_idx[one], o_g[one], o_out[one], f"batch 1 after window {name} T={T} w={w}")
+        pos += 1
+    assert layer.device_error() == 0
