@@ -252,6 +252,7 @@ __device__ __forceinline__ void select_policy(const ScreenSelectArgs& sb, int t,
 
 template <int ACT, int MB, int CPLR, bool SCREEN>
 __global__ __launch_bounds__(kSelectThreads) void select_gateup_q4_kernel(ScreenSelectArgs sb, PairArgs a) {
+  kernarg_lines<sizeof(ScreenSelectArgs) + sizeof(PairArgs)>();
   const SelectArgs& sa = sb.sel;
   constexpr int RPW = kDecodeRowsPerWave;
   constexpr int CK = XStage<ACT>::kChunks, PK = XStage<ACT>::kPitch;
@@ -430,6 +431,7 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
 // lane's x chunks are loaded before the selection starts.
 template <int ACT, int WD, int CPL, bool SCREEN>
 __global__ __launch_bounds__(kSelectThreads) void select_gateup_dense_kernel(ScreenSelectArgs sb, PairArgs a) {
+  kernarg_lines<sizeof(ScreenSelectArgs) + sizeof(PairArgs)>();
   const SelectArgs& sa = sb.sel;
   constexpr int RPW = kDecodeRowsPerWave;
   __shared__ int32_t s_idx[kMaxK];
@@ -503,6 +505,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_gateup_dense_kernel(Scr
 // the window kernel.
 template <int WD>
 __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
+  kernarg_lines<sizeof(PairArgs)>();
   __shared__ float part[kMaxK][8];
   __shared__ float s_g[kMaxK];
   __shared__ int s_bad;
