@@ -520,16 +520,21 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
   const int nblk = I >> 5;
   const int32_t* ti = a.idx + size_t(t) * k;
   if (threadIdx.x == 0) s_bad = 0;
-  const bool ends = a.hint != nullptr && blockIdx.x == 0 && t == 0 && wave == 0;   // this wave ends the call
-  HintRead hr{};
-  if (ends) hr = hint_read(a.hint, lane);
   // every wave holds the token's k indices, one per lane (k <= 32), and
   // checks its own experts with a ballot (no dependent loads before the
-  // weight loads)
-  const int vi = (lane < k) ? ti[lane] : -1;
-  // the gates with the indices (the combine after the barrier would
-  // otherwise wait for one more round trip)
-  if (wave == 0 && lane < k) s_g[lane] = a.gates[size_t(t) * k + lane];
+  // weight loads); the gates come with them (the combine after the barrier
+  // would otherwise wait for one more round trip).  Both loads issue
+  // unconditionally and first: a load under a branch makes the wave wait
+  // at the join for every load before it.
+  const int v0 = ti[min(lane, k - 1)];
+  const float g0 = a.gates[size_t(t) * k + min(lane, k - 1)];
+  const int vi = (lane < k) ? v0 : -1;
+  // the wave that ends the call reads the hint after them (its wait at the
+  // join then comes with theirs)
+  const bool ends = a.hint != nullptr && blockIdx.x == 0 && t == 0 && wave == 0;
+  HintRead hr{};
+  if (ends) hr = hint_read(a.hint, lane);
+  if (wave == 0) s_g[min(lane, k - 1)] = g0;         // lanes past k store gate k - 1 again
   __syncthreads();
   for (int j = wave; j < k; j += nw) {
     int e = __shfl(vi, j);
