@@ -18,6 +18,7 @@ MOE_ROUTER_HE, MOE_ROUTER_EH = 0, 1
 MOE_LAYER_FORCE_EXACT_REFINE = 1
 MOE_LAYER_SCREEN_ON = 2
 MOE_LAYER_SCREEN_OFF = 4
+MOE_LAYER_WINDOW_SCREEN_OFF = 8
 MOE_ROUTE_INTERNAL, MOE_ROUTE_GIVEN = 0, 1
 
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_GEOMETRY", -3: "MOE_E_DTYPE",

@@ -62,7 +62,8 @@ moe_status validate_desc(const moe_layer_desc* d) {
     return fail(MOE_E_DTYPE, "fp32 experts need fp32 activations");
   if (d->router_layout != MOE_ROUTER_HE && d->router_layout != MOE_ROUTER_EH)
     return fail(MOE_E_DTYPE, "router_layout %d unsupported", d->router_layout);
-  const uint32_t known = MOE_LAYER_FORCE_EXACT_REFINE | MOE_LAYER_SCREEN_ON | MOE_LAYER_SCREEN_OFF;
+  const uint32_t known =
+      MOE_LAYER_FORCE_EXACT_REFINE | MOE_LAYER_SCREEN_ON | MOE_LAYER_SCREEN_OFF | MOE_LAYER_WINDOW_SCREEN_OFF;
   if (d->flags & ~known) return fail(MOE_E_RANGE, "unknown desc.flags bits 0x%x", d->flags);
   if ((d->flags & MOE_LAYER_SCREEN_ON) && (d->flags & MOE_LAYER_SCREEN_OFF))
     return fail(MOE_E_RANGE, "MOE_LAYER_SCREEN_ON and MOE_LAYER_SCREEN_OFF together");
@@ -116,8 +117,29 @@ moe::ScreenList screen_list(char* ws, const Workspace& W) {
   return l;
 }
 
+moe::WinList win_list(char* ws, const Workspace& W) {
+  moe::WinList l;
+  l.hint = reinterpret_cast<moe::HintWords*>(ws + W.hint);
+  l.wcnt = reinterpret_cast<unsigned char*>(ws + W.wcnt);
+  l.wlist = reinterpret_cast<ulonglong2*>(ws + W.wlist);
+  return l;
+}
+
+bool window_on_screen(const Layer& L, int T) { return L.screen_win && T >= 2 && T <= moe::kWinMaxT; }
+
 moe_status route_impl(const Layer& L, const void* x, int T, int32_t* idx, float* gates,
                       char* ws, const Workspace& W, hipStream_t s) {
+  if (window_on_screen(L, T)) {   // verify windows: the int8 screen on MFMA, one list per token
+    float* z8 = reinterpret_cast<float*>(ws + W.z);
+    float* g8 = reinterpret_cast<float*>(ws + W.gmax);
+    double* xq = reinterpret_cast<double*>(ws + W.xnorm);
+    const moe::WinList list = win_list(ws, W);
+    hipError_t e = moe::launch_screen_window(L, x, T, z8, g8, xq, &list, s);
+    if (e != hipSuccess) return hip_fail(e, "window screen launch");
+    e = moe::launch_select_screen_window(L, x, T, z8, g8, xq, &list, idx, gates, s);
+    if (e != hipSuccess) return hip_fail(e, "window select launch");
+    return MOE_OK;
+  }
   if (T == 1 && L.screen) {     // the int8 first pass, then the selection recomputes its candidates
     float* z8 = reinterpret_cast<float*>(ws + W.z);
     float* g8 = reinterpret_cast<float*>(ws + W.gmax);
@@ -274,6 +296,10 @@ Workspace workspace_layout(const Layer& L, int T) {
     W.cnt8 = take(size_t(moe::screen_waves(L)) + 16);
     W.list = take(size_t(moe::kListSlots) * 16);
   }
+  if (L.screen_win && T >= 2 && T <= moe::kWinMaxT) {
+    W.wcnt = take(Tz * size_t(moe::screen_window_cstride(L)));
+    W.wlist = take(Tz * size_t(moe::kListSlots) * 16);
+  }
   W.z = take(Tz * E * 8);
   W.gmax = take(Tz * ((E + 3) / 4) * 4);
   W.xnorm = take(Tz * 16);
@@ -329,6 +355,7 @@ static void release_layer(Layer& L) {
   if (L.sc8) (void)hipFree(L.sc8);
   if (L.eb8) (void)hipFree(L.eb8);
   if (L.screen_consts) (void)hipFree(L.screen_consts);
+  if (L.q8w) (void)hipFree(L.q8w);
 }
 
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out) {
@@ -387,6 +414,13 @@ moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer*
     if ((e = moe::launch_screen_prep(L, L.screen_consts, s)) != hipSuccess) return cleanup(hip_fail(e, "screen prep"));
     if ((e = hipMemcpyAsync(sconst, L.screen_consts, sizeof(sconst), hipMemcpyDeviceToHost, s)) != hipSuccess)
       return cleanup(hip_fail(e, "screen maxima readback"));
+    // verify windows' screen: the same int8 router in MFMA operand order
+    if (moe::screen_window_fits(*desc)) {
+      if ((e = hipMalloc(&L.q8w, moe::screen_window_bytes(*desc))) != hipSuccess)
+        return cleanup(hip_fail(e, "hipMalloc(window screen router)"));
+      if ((e = moe::launch_screen_window_prep(L, s)) != hipSuccess) return cleanup(hip_fail(e, "window screen prep"));
+      L.screen_win = true;
+    }
   }
   float nmax = 0.f;
   if ((e = hipMemcpyAsync(&nmax, L.norms + E, sizeof(float), hipMemcpyDeviceToHost, s)) != hipSuccess)
@@ -475,7 +509,8 @@ moe_status moe_router_screen(const moe_layer* layer, const void* x, int32_t T, f
   char* w = static_cast<char*>(ws);
   float* g8 = reinterpret_cast<float*>(w + W.gmax);
   double* xq = reinterpret_cast<double*>(w + W.xnorm);
-  hipError_t e = moe::launch_screen(L, x, T, v, g8, xq, nullptr, s);
+  hipError_t e = window_on_screen(L, T) ? moe::launch_screen_window(L, x, T, v, g8, xq, nullptr, s)
+                                         : moe::launch_screen(L, x, T, v, g8, xq, nullptr, s);
   if (e == hipSuccess && bound) e = moe::launch_screen_bounds(L, T, v, xq, bound, s);
   if (e != hipSuccess) return hip_fail(e, "screen launch");
   return ok();

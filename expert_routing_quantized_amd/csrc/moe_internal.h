@@ -71,7 +71,14 @@ struct Layer {
   float2* eb8;              // owned: [E] (||eps_e||, ||s_e q_e||), rounded up
   float* screen_consts;     // owned: device maxima of the two norms and of |b|
   double screen_enmax, screen_rqmax, screen_bmax;   // host copies
+  // the verify windows' screen (2 <= T <= kWinMaxT), when `screen_win`:
+  bool screen_win;
+  int8_t* q8w;              // owned: the int8 router in MFMA operand order (screen_window.hip)
 };
+
+// Verify windows of up to this many tokens route through the int8 screen
+// (one 16-row MFMA operand holds two digit planes of each token).
+constexpr int kWinMaxT = 8;
 
 // The layer's device words: the sticky fault bits (int), then at byte 8 the
 // count of exact refinements (unsigned long long, statistics).
@@ -113,6 +120,8 @@ struct Workspace {
   size_t hint;      // batch-1 screen list: HintWords (128 B; state carried from call to call)
   size_t cnt8;      // u8 [screen blocks] rows each block of the screen listed
   size_t list;      // 16 B [kListSlots] the listed experts' recomputed logits
+  size_t wcnt;      // verify windows on the screen: u8 [T][cstride] entries each screen wave listed
+  size_t wlist;     // 16 B [T][kListSlots] the windows' per-token lists
   size_t total;
 };
 
@@ -432,6 +441,23 @@ hipError_t launch_select_screen(const Layer& L, const void* x, int T, const floa
 // the screen values' error bounds B_e of tokens [0, T) (inspection)
 hipError_t launch_screen_bounds(const Layer& L, int T, const float* z8, const double* xq, float* bound,
                                 hipStream_t s);
+// screen_window.hip: the screen for verify windows (2 <= T <= kWinMaxT) on
+// MFMA, with one list per token (lists null: values only).
+struct WinList {               // workspace regions of the windows' lists
+  HintWords* hint;
+  unsigned char* wcnt;
+  ulonglong2* wlist;
+};
+bool screen_window_fits(const moe_layer_desc& d);
+size_t screen_window_bytes(const moe_layer_desc& d);
+int screen_window_waves(const Layer& L);
+int screen_window_cstride(const Layer& L);
+hipError_t launch_screen_window_prep(const Layer& L, hipStream_t s);
+hipError_t launch_screen_window(const Layer& L, const void* x, int T, float* z8, float* g8, double* xq,
+                                const WinList* list, hipStream_t s);
+hipError_t launch_select_screen_window(const Layer& L, const void* x, int T, const float* z8, const float* g8,
+                                       const double* xq, const WinList* list, int32_t* idx, float* gates,
+                                       hipStream_t s);
 // experts.hip: batch-1 decode after the screen: selection + gate/up, then
 // down + combine (which ends the call: it advances the list's hint).
 hipError_t launch_decode_screen(const Layer& L, const void* x, const float* z8, const float* g8, const double* xq,

@@ -1,0 +1,412 @@
+// The router's int8 first pass for verify windows (2 <= T <= 8 tokens).
+//
+// A verify window scores a few drafted tokens against the whole router in one
+// call (pyshine source tour, Understanding the Architecture, the paragraph on
+// guessing and then checking drafted tokens); its router pass is the same
+// stream as at batch 1, read once for all T tokens.  The screen's arithmetic
+// (screen.hip) is unchanged -- int8 router rows, the hidden state as two
+// int8 digit planes of a 15-bit fixed point per token, exact int32 sums,
+// v = fl32(s_e 2^-m (128 HI + LO) + b_e), bounded by B_e -- but with T tokens
+// the integer sums form a dense product [16 planes] x [H] x [E] and run on the
+// matrix cores: v_mfma_i32_16x16x64_i8 with the 2 T digit planes as the
+// 16-row operand and 16 experts' rows as the 16-column operand.  Products
+// and sums are exact integers, so the values equal the batch-1 screen's bit
+// for bit, whatever the order of accumulation.
+//
+// The int8 router is stored a second time in the operands' lane order (q8w):
+// group G of 16 experts and slab s of 64 hidden positions fill one 1 KB
+// block at (s ngroups + G) 1024, lane L's 16 bytes at 16 L holding expert
+// 16 G + (L & 15) at positions 64 s + 16 (L >> 4) + [0, 16) -- the lane and
+// byte to reduction-index map of the operands is the same for both, so only
+// the row/column lanes matter.  One wave streams its group's NS blocks, all
+// in flight at once; slab-major order puts the blocks that all waves ask
+// for at the same moment next to one another (group-major order, every wave
+// starting 32 KB from the next, ran at half the rate).  The wave's block
+// builds the digit planes in LDS in the same order while they arrive.
+//
+// After the product, lane L holds the exact sums of planes 4 (L >> 4) + r
+// (r = 0..3: hi and lo of tokens 2 (L >> 4) and 2 (L >> 4) + 1) for expert
+// 16 G + (L & 15), so every value comes out without a cross-lane reduction.
+// Per token the kernel also writes the maxima of 4 consecutive values and,
+// with a list, recomputes the logits of the experts whose upper end reaches
+// the ring's threshold (as at batch 1) into that token's list.
+#include "select_screen.h"
+
+namespace moe {
+
+constexpr int kWinWaves = 4;       // waves per block, one group of 16 experts each
+constexpr int kWinMaxH = 2048;     // 32 slabs of 64: the whole group in flight in 128 VGPRs
+
+bool screen_window_fits(const moe_layer_desc& d) {
+  return d.hidden <= kWinMaxH && d.max_tokens >= 2 && !(d.flags & MOE_LAYER_WINDOW_SCREEN_OFF);
+}
+
+static int win_slabs(int H) { return H <= 512 ? 8 : (H <= 1024 ? 16 : 32); }
+static int win_groups(int E) { return (E + 15) / 16; }
+
+size_t screen_window_bytes(const moe_layer_desc& d) {
+  return size_t(win_groups(d.n_experts)) * win_slabs(d.hidden) * 1024;
+}
+
+int screen_window_waves(const Layer& L) { return win_groups(L.d.n_experts); }
+int screen_window_cstride(const Layer& L) { return (win_groups(L.d.n_experts) + 15) / 16 * 16; }
+
+// ------------------------------------------------------------------ layout
+// One thread per 16-byte operand chunk (zero past E and past H: H is a
+// multiple of 32, so a chunk lies wholly inside or outside the row).
+__global__ __launch_bounds__(256) void screen_swizzle_kernel(const int8_t* __restrict__ q8, int H, int E, int ngroups,
+                                                             size_t nchunks, int8_t* __restrict__ q8w) {
+  const size_t c = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const int L = int(c & 63);
+  const size_t sg = c >> 6;                          // slab-major: block s ngroups + G
+  const int G = int(sg % size_t(ngroups));
+  const int s = int(sg / size_t(ngroups));
+  const int e = 16 * G + (L & 15);
+  const int h0 = 64 * s + 16 * (L >> 4);
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (e < E && h0 < H) v = *reinterpret_cast<const uint4*>(q8 + size_t(e) * H + h0);
+  reinterpret_cast<uint4*>(q8w)[c] = v;
+}
+
+hipError_t launch_screen_window_prep(const Layer& L, hipStream_t s) {
+  const int NS = win_slabs(L.d.hidden);
+  const size_t n = size_t(win_groups(L.d.n_experts)) * NS * 64;
+  hipLaunchKernelGGL(screen_swizzle_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, L.q8, L.d.hidden,
+                     L.d.n_experts, win_groups(L.d.n_experts), n, L.q8w);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ screen
+__device__ __forceinline__ uint32_t win_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+struct WinScreenArgs {
+  const int8_t* q8w;      // operand-order int8 router
+  const float* sc8;       // [E]
+  const float* bias;      // [E], never null
+  const float2* eb8;      // [E]
+  const uint16_t* x;      // [T][H] bf16
+  const uint16_t* R;      // [E][H] bf16 router (the listed rows' recompute)
+  int H, E, T, ngroups;
+  float* z8;              // [T][E]
+  float* g8;              // [T][ceil(E/4)]
+  double* xq;             // [T][2]: ||x||^2, ||delta||^2
+  int* dev_flag;
+  double u8, babs8, rqmax;   // the bound's terms, as at batch 1
+  const HintWords* hsrc;  // never null: the call's hint, or a readable stand-in
+  int listing;            // lists wanted (then hsrc is the hint)
+  unsigned int* wcount;   // [kWinMaxT] the lists' counters (in the hint)
+  unsigned char* wcnt;    // [T][cstride]
+  ulonglong2* wlist;      // [T][kListSlots]
+  int cstride;
+};
+
+template <int NS, int CPL>
+__global__ __launch_bounds__(kWinWaves * 64) void screen_window_kernel(WinScreenArgs a) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  constexpr int NCH = NS * 8;                        // 8-element chunks of a padded row
+  constexpr int XP = NS * 64;                        // elements of a padded row
+  __shared__ __attribute__((aligned(16))) unsigned char s_dig[NS * 1024];   // digit planes, operand order
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWinMaxT * XP];      // the tokens' x (zero past H)
+  __shared__ uint32_t s_mb[kWinWaves][kWinMaxT];
+  __shared__ double s_red[kWinWaves][kWinMaxT][3];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.H, E = a.E, T = a.T;
+  const int Gw = blockIdx.x * kWinWaves + wave;      // this wave's group of 16 experts
+  const int G = min(Gw, a.ngroups - 1);              // (waves past the last group compute it and discard it)
+  // 1. the tokens' x first (chunk c = tid of every token, zero past H and
+  //    past T; every load unconditional, at clamped addresses): loads
+  //    complete in order, so the digits are worked out while the group's
+  //    slabs stream; then the slabs, all in flight (streamed once per call)
+  static_assert(NCH <= kWinWaves * 64, "one 8-element chunk of each token per thread");
+  const int n8 = H >> 3;
+  const int c = tid;
+  uint4 xr[kWinMaxT];
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t)
+    xr[t] = *reinterpret_cast<const uint4*>(a.x + size_t(min(t, T - 1)) * H + min(c, n8 - 1) * 8);
+  i32x4 bq[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    bq[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.q8w) + (size_t(s) * a.ngroups + G) * 64 + lane);
+  const int jl = lane & 15, gl = lane >> 4;          // expert column, plane quad
+  const int e = 16 * G + jl, ec = min(e, E - 1);
+  const float my_sc = a.sc8[ec], my_b = a.bias[ec], my_eb = a.eb8[ec].x;
+  const float ring_v = a.hsrc->ring[lane & (kHintRing - 1)];   // read whether or not it is used
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t)
+    if (!(t < T && c < n8)) xr[t] = make_uint4(0u, 0u, 0u, 0u);
+  // max |x_t| on the magnitude bits (a non-finite element has bits >= 0x7f80)
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t) {
+    uint32_t mb = 0u;
+    const uint32_t w[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mb = max(mb, max(w[q] & 0x7fffu, (w[q] >> 16) & 0x7fffu));
+    mb = win_max_u32(mb);
+    if (lane == 0) s_mb[wave][t] = mb;
+  }
+  __syncthreads();
+  // per token: the fixed point's exponent m (|x 2^m| < 2^13), as at batch 1
+  int mt[kWinMaxT];
+  bool bad[kWinMaxT];
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t) {
+    uint32_t mb = s_mb[0][t];
+#pragma unroll
+    for (int w = 1; w < kWinWaves; ++w) mb = max(mb, s_mb[w][t]);
+    bad[t] = mb >= 0x7f80u;
+    const float mx = __uint_as_float(mb << 16);
+    int m = 0;
+    if (mx > 0.f && !bad[t]) {
+      int ex;
+      frexpf(mx, &ex);
+      m = 13 - ex;
+    }
+    mt[t] = m;
+  }
+  // 3. per token: digits into LDS in operand order (plane 2t: hi, 2t + 1:
+  //    lo), x into LDS for the recompute, the exact sum of X^2, and in block 0
+  //    the binary64 sums of x^2 and delta^2 (as at batch 1).  The planes of
+  //    tokens past T are left as they are: their sums are never used.
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t) {
+    if (t >= T) continue;                              // uniform
+    const int m = mt[t];
+    const int m1 = m > 100 ? 100 : (m < -100 ? -100 : m);
+    const float sc1 = ldexpf(1.f, m1), sc2 = ldexpf(1.f, m - m1);
+    const double isc = ldexp(1.0, -m);
+    const bool use = !bad[t];
+    double pxx = 0.0, pdd = 0.0;
+    int x2 = 0;
+    if (c < NCH) {
+      const uint32_t w[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+      uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+#pragma unroll
+      for (int el = 0; el < 8; ++el) {
+        const float v = (el & 1) ? bf16_hi(w[el >> 1]) : bf16_lo(w[el >> 1]);
+        const int Xi = use ? (int)rintf((v * sc1) * sc2) : 0;   // |Xi| <= 2^13
+        hw[el >> 2] |= (uint32_t(Xi >> 7) & 0xffu) << (8 * (el & 3));
+        lw[el >> 2] |= uint32_t(Xi & 127) << (8 * (el & 3));
+        x2 += Xi * Xi;                                          // <= 8 * 2^26: exact
+        if (blockIdx.x == 0) {                                  // uniform
+          const double d = (double)v - (double)Xi * isc;        // exact
+          pxx = fma((double)v, (double)v, pxx);
+          pdd = fma(d, d, pdd);
+        }
+      }
+      const int s = c >> 3, gq = (c & 7) >> 1, p0 = 8 * (c & 1);
+      *reinterpret_cast<uint2*>(s_dig + s * 1024 + 16 * (2 * t + 16 * gq) + p0) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(s_dig + s * 1024 + 16 * (2 * t + 1 + 16 * gq) + p0) = make_uint2(lw[0], lw[1]);
+      *reinterpret_cast<uint4*>(s_x + t * XP + 8 * c) = xr[t];
+    }
+    const double sx = wave_sum_f64((double)x2);        // exact: integers below 2^53
+    double sxx = 0.0, sdd = 0.0;
+    if (blockIdx.x == 0) {                             // uniform
+      sxx = wave_sum_f64(pxx);
+      sdd = wave_sum_f64(pdd);
+    }
+    if (lane == 0) {
+      s_red[wave][t][0] = sx;
+      s_red[wave][t][1] = sxx;
+      s_red[wave][t][2] = sdd;
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid < T) {
+    double sxx = 0.0, sdd = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWinWaves; ++w) {
+      sxx += s_red[w][tid][1];
+      sdd += s_red[w][tid][2];
+    }
+    bool xb = false;
+#pragma unroll
+    for (int t = 0; t < kWinMaxT; ++t) xb = (t == tid) ? bad[t] : xb;
+    a.xq[2 * tid] = xb ? NAN : sxx;
+    a.xq[2 * tid + 1] = xb ? NAN : sdd;
+    if (xb) atomicOr(a.dev_flag, kDevNonFinite);
+  }
+  // 4. the product: 16 planes by 16 experts over the NS slabs
+  i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const i32x4 av = *reinterpret_cast<const i32x4*>(s_dig + s * 1024 + 16 * lane);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bq[s], acc, 0, 0, 0);
+  }
+  // 5. values of tokens 2 gl and 2 gl + 1 for expert e, their maxima of 4,
+  //    and whether the list takes them
+  const int G4 = (E + 3) / 4;
+  const float theta = a.listing ? hint_threshold_lanes(ring_v) : INFINITY;
+  const float rqmaxf = (float)a.rqmax * (1.f + 0x1p-20f), u8f = (float)a.u8 * (1.f + 0x1p-20f);
+  const float babs8f = (float)a.babs8 * (1.f + 0x1p-20f) + 0x1p-149f;
+  const float hd = 0.5f * sqrtf((float)H) * (1.f + 0x1p-20f);
+  bool lst[2];
+  bool nonfin = false;
+#pragma unroll
+  for (int r2 = 0; r2 < 2; ++r2) {
+    const int t = 2 * gl + r2;                       // lane-dependent (a select over the unrolled tokens)
+    int m = 0;
+    bool xb = false;
+    double x2 = 0.0;
+#pragma unroll
+    for (int tt = 0; tt < kWinMaxT; ++tt) {
+      if (tt == t) {
+        m = mt[tt];
+        xb = bad[tt];
+      }
+    }
+    if (t < T) {
+#pragma unroll
+      for (int w = 0; w < kWinWaves; ++w) x2 += s_red[w][t][0];
+    }
+    const double D = 128.0 * (double)acc[2 * r2] + (double)acc[2 * r2 + 1];   // exact
+    const double v = (double)my_sc * D * ldexp(1.0, -m) + (double)my_b;
+    const float vf = xb ? NAN : (float)v;
+    const bool in = t < T && e < E;
+    if (in) a.z8[size_t(t) * E + e] = vf;
+    nonfin = nonfin || (in && !xb && !isfinite(vf));
+    float gm = (in && !isnan(vf)) ? vf : -INFINITY;
+    gm = fmaxf(gm, MOE_DPP_F32(gm, 0xB1, 0xf));      // quads of lanes: 4 consecutive experts
+    gm = fmaxf(gm, MOE_DPP_F32(gm, 0x4E, 0xf));
+    if (in && (jl & 3) == 0) a.g8[size_t(t) * G4 + (e >> 2)] = gm;
+    // the upper end v + B against theta, in binary32 rounded up (as at batch 1)
+    const float X2 = (float)x2 * (1.f + 0x1p-20f);
+    const float iscf = ldexpf(1.f, -m);
+    const float xnu = ((sqrtf(X2) * (1.f + 0x1p-20f) + hd) * (1.f + 0x1p-20f)) * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
+    const float dnu = hd * iscf * (1.f + 0x1p-20f) + 0x1p-149f;
+    const float B = fmaf(xnu, my_eb, fmaf(dnu, rqmaxf, fmaf(u8f, fabsf(vf), babs8f))) * (1.f + 0x1p-20f) + 0x1p-147f;
+    const float U = vf + B;
+    lst[r2] = in && isfinite(vf) && U + fabsf(U) * 0x1p-22f + 0x1p-149f >= theta;
+  }
+  if (__ballot(nonfin) != 0ull && lane == 0) atomicOr(a.dev_flag, kDevNonFinite);
+  if (!a.listing || Gw >= a.ngroups) return;          // uniform
+  // 6. the lists: per token, the wave's count and (one atomic add) its slots;
+  //    each listed expert's row is read once and dotted with every token
+  //    that lists it (x from LDS)
+  const unsigned long long m0 = __ballot(lst[0]), m1 = __ballot(lst[1]);
+  uint32_t tm[kWinMaxT];
+  uint32_t any = 0u;
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t) {
+    tm[t] = (t < T) ? uint32_t((((t & 1) ? m1 : m0) >> (16 * (t >> 1))) & 0xffffull) : 0u;
+    any |= tm[t];
+  }
+  if (lane < T) {
+    uint32_t mine = 0u;
+#pragma unroll
+    for (int t = 0; t < kWinMaxT; ++t) mine = (t == lane) ? tm[t] : mine;
+    a.wcnt[size_t(lane) * a.cstride + Gw] = (unsigned char)__popc(mine);
+  }
+  if (any == 0u) return;
+  // (the slots come back while the first row loads: lane t holds token t's first slot)
+  unsigned mine = 0u;
+  {
+    uint32_t cnt = 0u;
+#pragma unroll
+    for (int t = 0; t < kWinMaxT; ++t) cnt = (t == lane) ? tm[t] : cnt;
+    if (lane < T && cnt != 0u) mine = atomicAdd(&a.wcount[lane], (unsigned)__popc(cnt));
+  }
+  unsigned used[kWinMaxT];
+#pragma unroll
+  for (int t = 0; t < kWinMaxT; ++t) used[t] = 0u;
+  for (uint32_t mj = any; mj != 0u; mj &= mj - 1u) {   // one row at a time (registers)
+    const int j = __builtin_ctz(mj);
+    const int er = 16 * G + j;
+    uint4 rr[CPL];
+#pragma unroll
+    for (int s = 0; s < CPL; ++s)
+      rr[s] = *reinterpret_cast<const uint4*>(a.R + size_t(er) * H + min(s * 64 + lane, n8 - 1) * 8);
+    const float br = a.bias[er];
+#pragma unroll
+    for (int t = 0; t < kWinMaxT; ++t) {
+      if (!((tm[t] >> j) & 1u)) continue;            // uniform
+      uint4 xc[CPL];
+#pragma unroll
+      for (int s = 0; s < CPL; ++s)
+        xc[s] = *reinterpret_cast<const uint4*>(s_x + t * XP + min(s * 64 + lane, NCH - 1) * 8);
+      const double z = dot2_logit<CPL>(xc, rr, n8, br, lane);
+      const unsigned slot = (unsigned)__builtin_amdgcn_readlane((int)mine, t) + used[t];
+      if (lane == 0 && slot < (unsigned)kListSlots)      // a full list: the selection falls back
+        a.wlist[size_t(t) * kListSlots + slot] =
+            make_ulonglong2((unsigned long long)er, (unsigned long long)__double_as_longlong(z));
+      ++used[t];
+    }
+  }
+}
+
+hipError_t launch_screen_window(const Layer& L, const void* x, int T, float* z8, float* g8, double* xq,
+                                const WinList* list, hipStream_t s) {
+  if (!L.screen_win || T < 2 || T > kWinMaxT) return hipErrorInvalidValue;
+  WinScreenArgs a{};
+  a.q8w = L.q8w;
+  a.sc8 = L.sc8;
+  a.bias = router_bias_or_zero(L);
+  a.eb8 = L.eb8;
+  a.x = reinterpret_cast<const uint16_t*>(x);
+  a.R = reinterpret_cast<const uint16_t*>(L.router_eh);
+  a.H = L.d.hidden;
+  a.E = L.d.n_experts;
+  a.T = T;
+  a.ngroups = win_groups(a.E);
+  a.z8 = z8;
+  a.g8 = g8;
+  a.xq = xq;
+  a.dev_flag = L.dev_flag;
+  const ScreenSelectArgs b = make_screen_select_args(L, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr);
+  a.u8 = b.u8;
+  a.babs8 = b.babs8;
+  a.rqmax = b.rqmax;
+  a.hsrc = reinterpret_cast<const HintWords*>(L.screen_consts);   // 256 bytes, read and ignored
+  if (list != nullptr) {
+    a.hsrc = list->hint;
+    a.listing = 1;
+    a.wcount = list->hint->win_count;
+    a.wcnt = list->wcnt;
+    a.wlist = list->wlist;
+    a.cstride = screen_window_cstride(L);
+  }
+  const dim3 grid((a.ngroups + kWinWaves - 1) / kWinWaves);
+  switch (win_slabs(a.H)) {
+    case 8: hipLaunchKernelGGL((screen_window_kernel<8, 1>), grid, dim3(kWinWaves * 64), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((screen_window_kernel<16, 2>), grid, dim3(kWinWaves * 64), 0, s, a); break;
+    default: hipLaunchKernelGGL((screen_window_kernel<32, 4>), grid, dim3(kWinWaves * 64), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ select
+template <int ACT, int CPL>
+__global__ __launch_bounds__(kSelectThreads) void select_screen_window_kernel(ScreenSelectArgs b) {
+  const int t = blockIdx.x;
+  select_screen_block<ACT, CPL>(b, t, b.sel.idx + size_t(t) * b.sel.k, b.sel.gates + size_t(t) * b.sel.k);
+}
+
+hipError_t launch_select_screen_window(const Layer& L, const void* x, int T, const float* z8, const float* g8,
+                                       const double* xq, const WinList* list, int32_t* idx, float* gates,
+                                       hipStream_t s) {
+  if (list == nullptr || T < 2 || T > kWinMaxT) return hipErrorInvalidValue;
+  ScreenSelectArgs b = make_screen_select_args(L, x, z8, g8, xq, idx, gates);
+  b.hint = list->hint;
+  b.cnt8 = list->wcnt;
+  b.list = list->wlist;
+  b.nw = screen_window_waves(L);
+  b.advance = 1;                      // block 0 advances the ring; block t clears its counter
+  b.wcount = list->hint->win_count;
+  b.cstride = screen_window_cstride(L);
+  const int cpl = (L.d.hidden / 8 + 63) / 64;
+  if (cpl <= 1) hipLaunchKernelGGL((select_screen_window_kernel<MOE_BF16, 1>), dim3(T), dim3(kSelectThreads), 0, s, b);
+  else if (cpl <= 2) hipLaunchKernelGGL((select_screen_window_kernel<MOE_BF16, 2>), dim3(T), dim3(kSelectThreads), 0, s, b);
+  else hipLaunchKernelGGL((select_screen_window_kernel<MOE_BF16, 4>), dim3(T), dim3(kSelectThreads), 0, s, b);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -71,7 +71,8 @@ struct HintWords {                        // 128 bytes of the workspace
   float kth;                              // this call's k-th logit (NaN: none)
   unsigned int listed_calls;              // calls whose selection took the list (statistics)
   unsigned int list_count;                // entries appended to the list in this call
-  float pad[11];
+  unsigned int win_count[8];              // verify windows: entries appended to token t's list
+  float pad[3];
   float ring[kHintRing];                  // k-th logits of recent calls
 };
 static_assert(sizeof(HintWords) <= 256, "the screen reads a 256-byte stand-in in place of a hint");
@@ -138,11 +139,13 @@ struct ScreenSelectArgs {
   const float2* eb8;       // [E]: (||eps_e|| rounded up, ||Rq_e|| rounded up)
   double enmax, rqmax;     // maxima of the two norms over the experts
   double u8, babs8;        // relative and absolute terms of the screen bound
-  HintWords* hint;         // batch 1 with the list (else null): the call's state
-  const unsigned char* cnt8;   // [nw] rows each screen block listed
-  const ulonglong2* list;  // [kListSlots] (e, logit bits)
-  int nw;                  // screen blocks
+  HintWords* hint;         // with the list (else null): the call's state
+  const unsigned char* cnt8;   // [nw] rows each screen block listed (windows: [T][cstride])
+  const ulonglong2* list;  // [kListSlots] (e, logit bits) (windows: [T][kListSlots])
+  int nw;                  // screen blocks (windows: screen waves)
   int advance;             // this kernel ends the call: advance the hint (block 0)
+  unsigned int* wcount;    // verify windows: token t's counter is wcount[t] (else null: batch 1)
+  int cstride;             // verify windows: bytes of counts per token (a multiple of 16)
 };
 
 typedef __bf16 sel_bf16x2_t __attribute__((ext_vector_type(2)));
@@ -247,14 +250,18 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
   // every load of the list path first (one round trip): ||x||^2 and
   // ||delta||^2, the hint, this thread's table slot and count words
   const double xn2 = a.xnorm[2 * t], dn2 = a.xnorm[2 * t + 1];
+  // (a verify window keeps one list, counter and row of counts per token)
+  const bool win = b.wcount != nullptr;
+  const ulonglong2* tlist = win ? b.list + size_t(t) * kListSlots : b.list;
+  const unsigned char* tcnt8 = win ? b.cnt8 + size_t(t) * b.cstride : b.cnt8;
   const float ring_v = b.hint->ring[lane & (kHintRing - 1)];
-  const unsigned list_n = b.hint->list_count;
-  const ulonglong2 ent = b.list[min(tid, kListSlots - 1)];
+  const unsigned list_n = win ? b.wcount[t] : b.hint->list_count;
+  const ulonglong2 ent = tlist[min(tid, kListSlots - 1)];
   const int nw16 = (b.nw + 15) >> 4;               // 16-byte words of counts
   constexpr int kCw = 2;                           // words per thread loaded up front (E <= 65,536)
   uint4 cwv[kCw];
 #pragma unroll
-  for (int u = 0; u < kCw; ++u) cwv[u] = reinterpret_cast<const uint4*>(b.cnt8)[min(tid + u * kSelectThreads, nw16 - 1)];
+  for (int u = 0; u < kCw; ++u) cwv[u] = reinterpret_cast<const uint4*>(tcnt8)[min(tid + u * kSelectThreads, nw16 - 1)];
   // (a non-finite hidden state is handled once these loads have all been
   // used: an early return here would let the compiler sink them past its wait)
   // binary64 sums of exact squares; the factor covers their rounding and the roots
@@ -288,7 +295,7 @@ __device__ __forceinline__ void select_screen_core(const ScreenSelectArgs& b, in
       }
     }
     for (int w = tid + kCw * kSelectThreads; w < nw16; w += kSelectThreads) {   // E > 65,536 only
-      const uint4 c = reinterpret_cast<const uint4*>(b.cnt8)[w];
+      const uint4 c = reinterpret_cast<const uint4*>(tcnt8)[w];
       const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
       const int nb = b.nw - 16 * w;
 #pragma unroll
@@ -537,6 +544,10 @@ __device__ __forceinline__ void select_screen_block(const ScreenSelectArgs& b, i
   if (ends) hr = hint_read(b.hint, threadIdx.x);
   select_screen_core<ACT, CPL>(b, t, S, oi, og);
   __syncthreads();
+  // a verify window's selection kernel has one block per token, and only it
+  // reads the token's counter: back to 0 for the next call (every thread
+  // has read it before the barrier above)
+  if (b.wcount != nullptr && threadIdx.x == 0) b.wcount[t] = 0u;
   if (ends) {
     hr.kth = (float)S.s_kth;
     hint_write(b.hint, hr, threadIdx.x);

@@ -93,6 +93,8 @@ typedef enum {
                                             the slow integer accumulator */
 #define MOE_LAYER_SCREEN_ON  2u  /* build the router screen even when E < 4096 */
 #define MOE_LAYER_SCREEN_OFF 4u  /* never build it (batch-1 routing reads the bf16 router) */
+#define MOE_LAYER_WINDOW_SCREEN_OFF 8u  /* verify windows (2 <= T <= 8) route on the bf16
+                                           router even when the layer has the screen */
 
 typedef struct {
   int32_t hidden;         /* H: multiple of 8 (of 32 for MOE_Q4B32), 8 <= H <= 8192 */

@@ -66,7 +66,7 @@ def create(desc):
     (dict(max_tokens=0), -2), (dict(max_tokens=70000), -2),
     (dict(act_dtype=2), -3), (dict(act_dtype=7), -3), (dict(expert_dtype=9), -3),
     (dict(expert_dtype=B.MOE_F32), -3),                       # fp32 experts with bf16 x
-    (dict(router_layout=5), -3), (dict(flags=8), -6),
+    (dict(router_layout=5), -3), (dict(flags=16), -6),
     (dict(flags=B.MOE_LAYER_SCREEN_ON | B.MOE_LAYER_SCREEN_OFF), -6),
     (dict(flags=B.MOE_LAYER_SCREEN_ON, act_dtype=B.MOE_F32, expert_dtype=B.MOE_F32), -3),   # screen needs bf16 x
     (dict(router_w=0), -1), (dict(w_down=0), -1),

@@ -396,9 +396,10 @@ def test_list_fullsize_decode():
 @pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "q4_h4096"])
 @pytest.mark.parametrize("T", [2, 3, 5, 8])
 def test_windows_and_batch1_share_a_screened_workspace(name, T):
-    """On a layer with the screen, verify windows (2 <= T <= 8: the bf16
-    router) and batch-1 calls (the screen with its list) alternate through
-    one workspace: every window and every single token against the oracle,
+    """On a layer with the screen, verify windows (2 <= T <= 8: the window
+    screen with its per-token lists, or the bf16 router past H = 2048) and
+    batch-1 calls (the screen with its list) alternate through one
+    workspace: every window and every single token against the oracle,
     moe_grouped_forward and moe_route."""
     import synth.device as SD
     spec, dl, L = setup(name)
@@ -422,3 +423,200 @@ def test_windows_and_batch1_share_a_screened_workspace(name, T):
         G.compare(fi, fg, fo, o_idx[one], o_g[one], o_out[one], f"batch 1 after window {name} T={T} w={w}")
         pos += 1
     assert layer.device_error() == 0
+
+
+# ---------------------------------------------------------------- windows
+WIN_T = [2, 5, 8]
+WIN_COUNTS = slice(20, 52)      # the windows' per-token list counters in the hint
+
+
+def windows(layer, x, T, nwin, ws, before=None):
+    """nwin consecutive windows of T tokens through moe_grouped_forward."""
+    torch = G.torch_mod()
+    n = nwin * T
+    fi = torch.empty((n, layer.k), dtype=torch.int32, device=x.device)
+    fg = torch.empty((n, layer.k), dtype=torch.float32, device=x.device)
+    fo = torch.empty((n, layer.H), dtype=torch.float32, device=x.device)
+    for w in range(nwin):
+        if before is not None:
+            before(w)
+        sl = slice(w * T, (w + 1) * T)
+        layer.grouped_forward(x[sl], T, fi[sl], fg[sl], 0, fo[sl], ws)
+    torch.cuda.synchronize()
+    return [a.cpu().numpy() for a in (fi, fg, fo)]
+
+
+@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "odd_q4", "k20_q4"])
+@pytest.mark.parametrize("T", WIN_T)
+def test_window_screen_values_equal_batch1(name, T):
+    """The window screen (all T tokens in one pass, on the matrix cores)
+    gives every expert of every token the value the batch-1 screen gives it,
+    bit for bit, and its bounds hold against the float64 logits."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, _ = setup(name)
+    G.note("window screen values", name, T)
+    layer = SD.make_layer(dl, max_tokens=8, flags=screen_flags())
+    first = 60 + T
+    x = SD.device_tokens(spec, first, T)
+    v = torch.empty((T, spec.E), dtype=torch.float32, device="cuda")
+    bd = torch.empty_like(v)
+    layer.router_screen(x, T, v, bd, layer.workspace(T))
+    v1 = torch.empty_like(v)
+    b1 = torch.empty_like(v)
+    ws1 = layer.workspace(1)
+    for t in range(T):
+        layer.router_screen(x[t], 1, v1[t], b1[t], ws1)
+    torch.cuda.synchronize()
+    vw, v1h = v.cpu().numpy(), v1.cpu().numpy()
+    assert np.array_equal(vw.view(np.uint32), v1h.view(np.uint32))
+    _, Z = _exact_logits(spec, first, T)
+    ratio = np.abs(vw.astype(np.float64) - Z) / bd.cpu().numpy()
+    print(f"{name} T={T}: window screen |err|/bound max {ratio.max():.3f}")
+    assert ratio.max() < 1.0
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("name", ["tiny_q4", "wide_q4", "k20_q4", "tiny_bf16"])
+@pytest.mark.parametrize("T", WIN_T)
+def test_window_lists_taken_and_equal_to_the_full_screen_path(name, T):
+    """Windows on the screen select from their per-token lists once the ring
+    has warmed up; the results equal, bit for bit, those of windows whose
+    ring is poisoned (no lists), and the oracle's; each call leaves the
+    counters at 0."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup(name)
+    G.note("window lists", name, T)
+    nwin = 10
+    layer = SD.make_layer(dl, max_tokens=8, flags=screen_flags())
+    x = SD.device_tokens(spec, 900, nwin * T)
+    ws = layer.workspace(T)
+    ws.zero_()
+    fi, fg, fo = windows(layer, x, T, nwin, ws)
+    ep, listed, ring = hint_state(ws)
+    print(f"{name} T={T}: {listed} of {nwin} windows took the lists")
+    assert ep == nwin and listed >= nwin // 2
+    assert np.all(ws[WIN_COUNTS].cpu().numpy() == 0)
+    ws2 = layer.workspace(T)
+    ws2.zero_()
+    gi, gg, go = windows(layer, x, T, nwin, ws2, before=lambda w: poison_ring(ws2, float("nan")))
+    assert hint_state(ws2)[1] == 0
+    check_bitwise(fi, fg, fo, gi, gg, go)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 900, nwin * T)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, f"window lists {name} T={T}")
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("T", WIN_T)
+def test_window_screen_off_flag_same_routing(T):
+    """MOE_LAYER_WINDOW_SCREEN_OFF routes windows on the bf16 router: the
+    same indices as the window screen, gates within the tolerance."""
+    from expert_routing_quantized_amd import MOE_LAYER_WINDOW_SCREEN_OFF
+    import synth.device as SD
+    spec, dl, L = setup("wide_q4")
+    on = SD.make_layer(dl, max_tokens=8, flags=screen_flags())
+    off = SD.make_layer(dl, max_tokens=8, flags=screen_flags(MOE_LAYER_WINDOW_SCREEN_OFF))
+    x = SD.device_tokens(spec, 1300, 4 * T)
+    a = windows(on, x, T, 4, on.workspace(T))
+    b = windows(off, x, T, 4, off.workspace(T))
+    assert np.array_equal(a[0], b[0])
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 1300, 4 * T)
+    G.compare(*a, o_idx, o_g, o_out, f"window screen on T={T}")
+    G.compare(*b, o_idx, o_g, o_out, f"window screen off T={T}")
+
+
+@pytest.mark.parametrize("T", [3, 6])
+def test_window_counters_not_reset_and_garbage_workspace(T):
+    """Window counters that did not start at 0, and a workspace of random
+    bytes: the same results (those calls select without the lists), and
+    the window's counters are back at 0 after the calls."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec, dl, L = setup("wide_q4")
+    G.note("window counters", T)
+    layer = SD.make_layer(dl, max_tokens=8, flags=screen_flags())
+    nwin = 6
+    x = SD.device_tokens(spec, 1700, nwin * T)
+    ref = windows(layer, x, T, nwin, layer.workspace(T))
+    ws = layer.workspace(T)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda", generator=g))
+
+    def bump(w):
+        if w % 2 == 1:
+            ws[WIN_COUNTS].view(torch.int32).fill_(5 + w)
+    r = windows(layer, x, T, nwin, ws, before=bump)
+    check_bitwise(*r, *ref)
+    # the call clears the counters of its own tokens (those past T keep what they held)
+    assert np.all(ws[WIN_COUNTS].view(torch.int32).cpu().numpy()[:T] == 0)
+    assert layer.device_error() == 0
+
+
+@pytest.mark.parametrize("T", [2, 5, 8])
+def test_window_screen_edges(T):
+    """Windows through the screen: exact ties and a near tie (copied router
+    rows), a window of all-zero hidden states (every logit equal), a
+    non-finite token inside a window, and hidden states scaled by 2^-80."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    G.note("window edges", T)
+    # ties: copies of ranked experts and a row one bf16 ulp from the top one
+    spec = synth.small_spec(H=256, E=96, k=4, I=64, act=synth.DT_BF16, expert=synth.DT_BF16,
+                            bias_alpha=None, weight_seed=43, token_seed=44, name="inv_bf16")
+    dl = SD.device_layer(spec)
+    x = SD.device_tokens(spec, 0, T)
+    layer = SD.make_layer(dl, max_tokens=8, flags=screen_flags())
+    idx0, _, _ = G.run_grouped(layer, x[0:1])
+    top = [int(v) for v in idx0[0]]
+    R = dl.router_eh.clone()
+    used = set(top)
+    for src, shift in ((top[1], 9), (top[spec.k - 1], -5)):
+        dst = (src + shift) % spec.E
+        while dst in used:
+            dst = (dst + 1) % spec.E
+        R[dst] = R[src]
+        used.add(dst)
+    near = (top[0] + 3) % spec.E
+    while near in used:
+        near = (near + 1) % spec.E
+    R[near] = R[top[0]]
+    R[near].view(torch.int16)[37] += 1
+    dl2 = SD.DeviceLayer(spec, R, dl.bias, dl.w_gate, dl.w_up, dl.w_down)
+    layer2 = SD.make_layer(dl2, max_tokens=8, flags=screen_flags())
+    fi, fg, fo = G.run_grouped(layer2, x)
+    Rh = oracle.decode_bf16(SD.to_numpy_bits(R)).T
+    L2 = oracle.OracleLayer(Rh, np.zeros(spec.E), spec.k, lambda e, w: synth.expert_stored(spec, e, w))
+    o_idx, o_g, _, o_out = oracle.moe_tokens(oracle.tokens_f64(spec, 0, T), L2)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, f"window ties T={T}")
+    assert layer2.device_error() == 0
+    # all-zero hidden states: every logit equal, the lower indices win
+    spec_e = synth.small_spec(H=256, E=3000, k=6, I=64, act=synth.DT_BF16, expert=synth.DT_Q4,
+                              bias_alpha=None, weight_seed=51, token_seed=52, name="equal")
+    le = SD.make_layer(SD.device_layer(spec_e), max_tokens=8, flags=screen_flags())
+    fi, fg, fo = G.run_grouped(le, torch.zeros((T, spec_e.H), dtype=torch.bfloat16, device="cuda"))
+    assert np.array_equal(fi, np.tile(np.arange(spec_e.k), (T, 1)))
+    assert np.all(fg == np.float32(1.0 / spec_e.k)) and np.all(fo == 0.0)
+    assert le.device_error() == 0
+    # a non-finite token inside the window; the others as the oracle's
+    spec_t, dl_t, L_t = setup("tiny_q4")
+    lt = SD.make_layer(dl_t, max_tokens=8, flags=screen_flags())
+    x = SD.device_tokens(spec_t, 0, T)
+    bad = T // 2
+    x[bad, 17] = float("nan")
+    fi, fg, fo = G.run_grouped(lt, x)
+    assert lt.device_error() & 4
+    assert np.all(fi[bad] == -1) and np.all(np.isnan(fg[bad])) and np.all(np.isnan(fo[bad]))
+    keep = [t for t in range(T) if t != bad]
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec_t, L_t, 0, T)
+    G.compare(fi[keep], fg[keep], fo[keep], o_idx[keep], o_g[keep], o_out[keep], f"window nan/others T={T}")
+    # hidden states scaled by 2^-80
+    scale = 2.0 ** -80
+    x = (SD.device_tokens(spec_t, 0, T).float() * scale).to(torch.bfloat16)
+    Xh = oracle.tokens_f64(spec_t, 0, T) * scale
+    assert np.array_equal(oracle.decode_bf16(SD.to_numpy_bits(x)), Xh)
+    fi, fg, fo = G.run_grouped(lt, x)
+    o_idx, o_g, _, _ = oracle.moe_tokens(Xh, L_t)
+    G.compare(fi, fg, None, o_idx, o_g, None, f"window tiny x T={T}")
+    assert lt.device_error() == 0
