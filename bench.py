@@ -328,13 +328,21 @@ def grouped_main(args, spec):
 
     from expert_routing_quantized_amd import MOE_ROUTE_GIVEN
     zbuf = torch.empty((T, spec.E), dtype=torch.float64, device=dev)
+    # windows of 2-8 tokens on a layer with the router screen (bf16 x, H a
+    # multiple of 32 and at most 2048, E >= 4096) route through the window
+    # screen: its launch alone is the router's roofline
+    win_screen = 2 <= T <= 8 and spec.act == 1 and spec.H % 32 == 0 and spec.H <= 2048 and spec.E >= 4096
+    vbuf = torch.empty((T, spec.E), dtype=torch.float32, device=dev)
 
     def step(i):
         b = i % nseq
         layer.grouped_forward(X[b], T, idx[b], gates[b], 0, out[b], ws)
 
     def router_only(i):
-        layer.router_logits(X[i % nseq], T, zbuf, ws)
+        if win_screen:
+            layer.router_screen(X[i % nseq], T, vbuf, None, ws)
+        else:
+            layer.router_logits(X[i % nseq], T, zbuf, ws)
 
     def experts_only(i):
         b = i % nseq
@@ -392,6 +400,13 @@ def grouped_main(args, spec):
                 "achieved": router_flops / router_s / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
                 "frac": router_flops / router_s / 1e12 / 2500.0, "traffic": None,
                 "avg_launch_us": router_s * 1e6, "flops_per_launch": router_flops}
+    elif win_screen:
+        sbytes = screen_bytes(spec) + (T - 1) * spec.H * act
+        roof = {"bound": "hbm", "kernel": ("window screen (moe::screen_window_kernel<32, 4, 4>: int8 router on "
+                                           "v_mfma_i32_16x16x64_i8, exact integer sums)"),
+                "achieved": sbytes / router_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": sbytes / router_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
+                "avg_launch_us": router_s * 1e6, "bytes_per_launch": sbytes}
     else:
         roof = {"bound": "hbm", "kernel": "router (moe::router_skinny_lds_kernel, 16x16x32 MFMA tiles)",
                 "achieved": router_bytes / router_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",

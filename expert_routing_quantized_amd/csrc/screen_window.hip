@@ -34,7 +34,14 @@
 
 namespace moe {
 
-constexpr int kWinWaves = 4;       // waves per block, one group of 16 experts each
+constexpr int kWinWaves = 4;       // groups of 16 experts per block
+constexpr int kWinSplit = 2;       // waves per group (each streams a part of the slabs)
+// Slabs each wave keeps in flight (a ring; the next slab's load is issued as
+// each product is taken).  Measured on the 24,576-expert router, screen
+// alone, T = 2 / 5 / 8: 4 slabs 11.5 / 13.0 / 15.2 us, 2 slabs 12.4 / 14.4 /
+// 16.5, 8 slabs 12.3 / 12.8 / 15.6, all 16 slabs of the wave 12.1 / 14.0 /
+// 16.5; one wave per group with all 32 slabs in flight 11.6 / 13.2 / 15.2.
+constexpr int kWinSlabsInFlight = 4;
 constexpr int kWinMaxH = 2048;     // 32 slabs of 64: the whole group in flight in 128 VGPRs
 
 bool screen_window_fits(const moe_layer_desc& d) {
@@ -109,104 +116,118 @@ struct WinScreenArgs {
   int cstride;
 };
 
-template <int NS, int CPL>
-__global__ __launch_bounds__(kWinWaves * 64) void screen_window_kernel(WinScreenArgs a) {
+// Block: kWinWaves groups of 16 experts, each split over kWinSplit waves by
+// slab range (wave w: group w % kWinWaves, slabs of part w / kWinWaves), so
+// each wave streams NS / kWinSplit blocks and the block's digit work is
+// spread over kWinWaves * kWinSplit waves; the parts' integer sums are added
+// in LDS (exactly) by the first part's waves, which finish the group.
+template <int NS, int CPL, int NBUF>
+__global__ __launch_bounds__(kWinWaves * kWinSplit * 64, 4) void screen_window_kernel(WinScreenArgs a) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
-  constexpr int NCH = NS * 8;                        // 8-element chunks of a padded row
-  constexpr int XP = NS * 64;                        // elements of a padded row
+  constexpr int NT = kWinWaves * kWinSplit * 64;     // threads
+  constexpr int NWV = kWinWaves * kWinSplit;         // waves
+  constexpr int NSP = NS / kWinSplit;                // slabs per wave
+  constexpr int EPT = (NS * 64 / NT) < 2 ? 2 : NS * 64 / NT;   // elements of a padded row per thread (per token)
+  static_assert((EPT == 2 || EPT == 4) && NT * EPT >= NS * 64, "2 or 4 elements per thread cover the row");
   __shared__ __attribute__((aligned(16))) unsigned char s_dig[NS * 1024];   // digit planes, operand order
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWinMaxT * XP];      // the tokens' x (zero past H)
-  __shared__ uint32_t s_mb[kWinWaves][kWinMaxT];
-  __shared__ double s_red[kWinWaves][kWinMaxT][3];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWinMaxT][NT * EPT];  // the tokens' x (zero past H, T)
+  __shared__ i32x4 s_acc[kWinSplit - 1][kWinWaves][64];                     // the other parts' sums
+  __shared__ uint32_t s_mb[NWV][kWinMaxT];
+  __shared__ int s_m[kWinMaxT];                                             // per token: m, or INT_MIN if bad
+  __shared__ double s_red[NWV][kWinMaxT][3];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = wave % kWinWaves, part = wave / kWinWaves;
   const int H = a.H, E = a.E, T = a.T;
-  const int Gw = blockIdx.x * kWinWaves + wave;      // this wave's group of 16 experts
+  const int Gw = blockIdx.x * kWinWaves + q;         // this wave's group of 16 experts
   const int G = min(Gw, a.ngroups - 1);              // (waves past the last group compute it and discard it)
-  // 1. the tokens' x first (chunk c = tid of every token, zero past H and
-  //    past T; every load unconditional, at clamped addresses): loads
-  //    complete in order, so the digits are worked out while the group's
-  //    slabs stream; then the slabs, all in flight (streamed once per call)
-  static_assert(NCH <= kWinWaves * 64, "one 8-element chunk of each token per thread");
-  const int n8 = H >> 3;
-  const int c = tid;
-  uint4 xr[kWinMaxT];
+  // 1. the tokens' x first (EPT elements c * EPT .. of every token, zero
+  //    past H and past T; every load unconditional, at clamped addresses):
+  //    loads complete in order, so the digits are worked out while the
+  //    slabs stream; then the wave's slabs, all in flight
+  const int c = tid;                                 // element group of the padded row
+  const bool cin = c * EPT < H;                      // H is a multiple of 32
+  typedef uint32_t xw_t __attribute__((ext_vector_type(EPT / 2)));
+  xw_t xr[kWinMaxT];
 #pragma unroll
   for (int t = 0; t < kWinMaxT; ++t)
-    xr[t] = *reinterpret_cast<const uint4*>(a.x + size_t(min(t, T - 1)) * H + min(c, n8 - 1) * 8);
-  i32x4 bq[NS];
+    xr[t] = *reinterpret_cast<const xw_t*>(a.x + size_t(min(t, T - 1)) * H + min(c * EPT, H - EPT));
+  constexpr int NB = NBUF < NSP ? NBUF : NSP;      // slabs in flight per wave
+  const i32x4* qsrc = reinterpret_cast<const i32x4*>(a.q8w) + (size_t(part * NSP) * a.ngroups + G) * 64 + lane;
+  const size_t qstride = size_t(a.ngroups) * 64;
+  i32x4 bq[NB];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    bq[s] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(a.q8w) + (size_t(s) * a.ngroups + G) * 64 + lane);
+  for (int s = 0; s < NB; ++s) bq[s] = __builtin_nontemporal_load(qsrc + s * qstride);
   const int jl = lane & 15, gl = lane >> 4;          // expert column, plane quad
   const int e = 16 * G + jl, ec = min(e, E - 1);
   const float my_sc = a.sc8[ec], my_b = a.bias[ec], my_eb = a.eb8[ec].x;
   const float ring_v = a.hsrc->ring[lane & (kHintRing - 1)];   // read whether or not it is used
-#pragma unroll
-  for (int t = 0; t < kWinMaxT; ++t)
-    if (!(t < T && c < n8)) xr[t] = make_uint4(0u, 0u, 0u, 0u);
-  // max |x_t| on the magnitude bits (a non-finite element has bits >= 0x7f80)
+  // max |x_t| on the magnitude bits (a non-finite element has bits >= 0x7f80);
+  // x into LDS (its registers are free from here on)
 #pragma unroll
   for (int t = 0; t < kWinMaxT; ++t) {
     uint32_t mb = 0u;
-    const uint32_t w[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
+    xw_t xv;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) mb = max(mb, max(w[q] & 0x7fffu, (w[q] >> 16) & 0x7fffu));
+    for (int w = 0; w < EPT / 2; ++w) {
+      xv[w] = (t < T && cin) ? xr[t][w] : 0u;
+      mb = max(mb, max(xv[w] & 0x7fffu, (xv[w] >> 16) & 0x7fffu));
+    }
+    *reinterpret_cast<xw_t*>(&s_x[t][c * EPT]) = xv;
     mb = win_max_u32(mb);
     if (lane == 0) s_mb[wave][t] = mb;
   }
   __syncthreads();
-  // per token: the fixed point's exponent m (|x 2^m| < 2^13), as at batch 1
-  int mt[kWinMaxT];
-  bool bad[kWinMaxT];
+  // 2. per token: the fixed point's exponent m (|x 2^m| < 2^13, as at batch
+  //    1), digits into LDS in operand order (plane 2t: hi, 2t + 1: lo), the
+  //    exact sum of X^2, and in block 0 the binary64 sums of x^2 and
+  //    delta^2.  The planes of tokens past T are left as they are: their
+  //    sums are never used.
+  const int h0 = c * EPT;
+  const int doff = (h0 >> 6) * 1024 + 16 * 16 * ((h0 & 63) >> 4) + (h0 & 15);
 #pragma unroll
   for (int t = 0; t < kWinMaxT; ++t) {
+    if (t >= T) continue;                              // uniform
     uint32_t mb = s_mb[0][t];
 #pragma unroll
-    for (int w = 1; w < kWinWaves; ++w) mb = max(mb, s_mb[w][t]);
-    bad[t] = mb >= 0x7f80u;
+    for (int w = 1; w < NWV; ++w) mb = max(mb, s_mb[w][t]);
+    const bool bad = mb >= 0x7f80u;
     const float mx = __uint_as_float(mb << 16);
     int m = 0;
-    if (mx > 0.f && !bad[t]) {
+    if (mx > 0.f && !bad) {
       int ex;
       frexpf(mx, &ex);
       m = 13 - ex;
     }
-    mt[t] = m;
-  }
-  // 3. per token: digits into LDS in operand order (plane 2t: hi, 2t + 1:
-  //    lo), x into LDS for the recompute, the exact sum of X^2, and in block 0
-  //    the binary64 sums of x^2 and delta^2 (as at batch 1).  The planes of
-  //    tokens past T are left as they are: their sums are never used.
-#pragma unroll
-  for (int t = 0; t < kWinMaxT; ++t) {
-    if (t >= T) continue;                              // uniform
-    const int m = mt[t];
+    if (tid == 0) s_m[t] = bad ? INT_MIN : m;
     const int m1 = m > 100 ? 100 : (m < -100 ? -100 : m);
     const float sc1 = ldexpf(1.f, m1), sc2 = ldexpf(1.f, m - m1);
     const double isc = ldexp(1.0, -m);
-    const bool use = !bad[t];
+    const xw_t xv = *reinterpret_cast<const xw_t*>(&s_x[t][c * EPT]);
     double pxx = 0.0, pdd = 0.0;
     int x2 = 0;
-    if (c < NCH) {
-      const uint32_t w[4] = {xr[t].x, xr[t].y, xr[t].z, xr[t].w};
-      uint32_t hw[2] = {0u, 0u}, lw[2] = {0u, 0u};
+    uint32_t hw = 0u, lw = 0u;
 #pragma unroll
-      for (int el = 0; el < 8; ++el) {
-        const float v = (el & 1) ? bf16_hi(w[el >> 1]) : bf16_lo(w[el >> 1]);
-        const int Xi = use ? (int)rintf((v * sc1) * sc2) : 0;   // |Xi| <= 2^13
-        hw[el >> 2] |= (uint32_t(Xi >> 7) & 0xffu) << (8 * (el & 3));
-        lw[el >> 2] |= uint32_t(Xi & 127) << (8 * (el & 3));
-        x2 += Xi * Xi;                                          // <= 8 * 2^26: exact
-        if (blockIdx.x == 0) {                                  // uniform
-          const double d = (double)v - (double)Xi * isc;        // exact
-          pxx = fma((double)v, (double)v, pxx);
-          pdd = fma(d, d, pdd);
-        }
+    for (int el = 0; el < EPT; ++el) {
+      const uint32_t word = xv[el >> 1];
+      const float v = bad ? 0.f : ((el & 1) ? bf16_hi(word) : bf16_lo(word));
+      const int Xi = (int)rintf((v * sc1) * sc2);             // |Xi| <= 2^13
+      hw |= (uint32_t(Xi >> 7) & 0xffu) << (8 * el);
+      lw |= uint32_t(Xi & 127) << (8 * el);
+      x2 += Xi * Xi;                                          // <= 4 * 2^26: exact
+      if (blockIdx.x == 0) {                                  // uniform
+        const double d = (double)v - (double)Xi * isc;        // exact
+        pxx = fma((double)v, (double)v, pxx);
+        pdd = fma(d, d, pdd);
       }
-      const int s = c >> 3, gq = (c & 7) >> 1, p0 = 8 * (c & 1);
-      *reinterpret_cast<uint2*>(s_dig + s * 1024 + 16 * (2 * t + 16 * gq) + p0) = make_uint2(hw[0], hw[1]);
-      *reinterpret_cast<uint2*>(s_dig + s * 1024 + 16 * (2 * t + 1 + 16 * gq) + p0) = make_uint2(lw[0], lw[1]);
-      *reinterpret_cast<uint4*>(s_x + t * XP + 8 * c) = xr[t];
+    }
+    if (c * EPT < NS * 64) {
+      if constexpr (EPT == 4) {
+        *reinterpret_cast<uint32_t*>(s_dig + doff + 16 * (2 * t)) = hw;
+        *reinterpret_cast<uint32_t*>(s_dig + doff + 16 * (2 * t + 1)) = lw;
+      } else {
+        *reinterpret_cast<uint16_t*>(s_dig + doff + 16 * (2 * t)) = (uint16_t)hw;
+        *reinterpret_cast<uint16_t*>(s_dig + doff + 16 * (2 * t + 1)) = (uint16_t)lw;
+      }
     }
     const double sx = wave_sum_f64((double)x2);        // exact: integers below 2^53
     double sxx = 0.0, sdd = 0.0;
@@ -224,25 +245,33 @@ __global__ __launch_bounds__(kWinWaves * 64) void screen_window_kernel(WinScreen
   if (blockIdx.x == 0 && tid < T) {
     double sxx = 0.0, sdd = 0.0;
 #pragma unroll
-    for (int w = 0; w < kWinWaves; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       sxx += s_red[w][tid][1];
       sdd += s_red[w][tid][2];
     }
-    bool xb = false;
-#pragma unroll
-    for (int t = 0; t < kWinMaxT; ++t) xb = (t == tid) ? bad[t] : xb;
+    const bool xb = s_m[tid] == INT_MIN;
     a.xq[2 * tid] = xb ? NAN : sxx;
     a.xq[2 * tid + 1] = xb ? NAN : sdd;
     if (xb) atomicOr(a.dev_flag, kDevNonFinite);
   }
-  // 4. the product: 16 planes by 16 experts over the NS slabs
+  // 3. the product: 16 planes by 16 experts over the wave's slabs; the
+  //    other parts hand their sums to the first part's wave of the group
   i32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const i32x4 av = *reinterpret_cast<const i32x4*>(s_dig + s * 1024 + 16 * lane);
-    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bq[s], acc, 0, 0, 0);
+  for (int s = 0; s < NSP; ++s) {
+    const i32x4 av = *reinterpret_cast<const i32x4*>(s_dig + (part * NSP + s) * 1024 + 16 * lane);
+    acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bq[s % NB], acc, 0, 0, 0);
+    if (s + NB < NSP) {
+      __builtin_amdgcn_sched_barrier(0);             // the next slab's load after this product
+      bq[s % NB] = __builtin_nontemporal_load(qsrc + (s + NB) * qstride);
+    }
   }
-  // 5. values of tokens 2 gl and 2 gl + 1 for expert e, their maxima of 4,
+  if (part > 0) s_acc[part - 1][q][lane] = acc;
+  __syncthreads();
+  if (part > 0) return;                              // uniform per wave
+#pragma unroll
+  for (int p = 0; p < kWinSplit - 1; ++p) acc += s_acc[p][q][lane];   // exact int32 sums
+  // 4. values of tokens 2 gl and 2 gl + 1 for expert e, their maxima of 4,
   //    and whether the list takes them
   const int G4 = (E + 3) / 4;
   const float theta = a.listing ? hint_threshold_lanes(ring_v) : INFINITY;
@@ -253,20 +282,14 @@ __global__ __launch_bounds__(kWinWaves * 64) void screen_window_kernel(WinScreen
   bool nonfin = false;
 #pragma unroll
   for (int r2 = 0; r2 < 2; ++r2) {
-    const int t = 2 * gl + r2;                       // lane-dependent (a select over the unrolled tokens)
-    int m = 0;
-    bool xb = false;
+    const int t = 2 * gl + r2;                       // lane-dependent
+    const int mraw = (t < T) ? s_m[t] : 0;
+    const bool xb = mraw == INT_MIN;
+    const int m = xb ? 0 : mraw;
     double x2 = 0.0;
-#pragma unroll
-    for (int tt = 0; tt < kWinMaxT; ++tt) {
-      if (tt == t) {
-        m = mt[tt];
-        xb = bad[tt];
-      }
-    }
     if (t < T) {
 #pragma unroll
-      for (int w = 0; w < kWinWaves; ++w) x2 += s_red[w][t][0];
+      for (int w = 0; w < NWV; ++w) x2 += s_red[w][t][0];
     }
     const double D = 128.0 * (double)acc[2 * r2] + (double)acc[2 * r2 + 1];   // exact
     const double v = (double)my_sc * D * ldexp(1.0, -m) + (double)my_b;
@@ -289,9 +312,10 @@ __global__ __launch_bounds__(kWinWaves * 64) void screen_window_kernel(WinScreen
   }
   if (__ballot(nonfin) != 0ull && lane == 0) atomicOr(a.dev_flag, kDevNonFinite);
   if (!a.listing || Gw >= a.ngroups) return;          // uniform
-  // 6. the lists: per token, the wave's count and (one atomic add) its slots;
+  // 5. the lists: per token, the wave's count and (one atomic add) its slots;
   //    each listed expert's row is read once and dotted with every token
-  //    that lists it (x from LDS)
+  //    that lists it
+  const int n8 = H >> 3;
   const unsigned long long m0 = __ballot(lst[0]), m1 = __ballot(lst[1]);
   uint32_t tm[kWinMaxT];
   uint32_t any = 0u;
@@ -332,7 +356,7 @@ __global__ __launch_bounds__(kWinWaves * 64) void screen_window_kernel(WinScreen
       uint4 xc[CPL];
 #pragma unroll
       for (int s = 0; s < CPL; ++s)
-        xc[s] = *reinterpret_cast<const uint4*>(s_x + t * XP + min(s * 64 + lane, NCH - 1) * 8);
+        xc[s] = *reinterpret_cast<const uint4*>(a.x + size_t(t) * H + min(s * 64 + lane, n8 - 1) * 8);
       const double z = dot2_logit<CPL>(xc, rr, n8, br, lane);
       const unsigned slot = (unsigned)__builtin_amdgcn_readlane((int)mine, t) + used[t];
       if (lane == 0 && slot < (unsigned)kListSlots)      // a full list: the selection falls back
@@ -375,10 +399,11 @@ hipError_t launch_screen_window(const Layer& L, const void* x, int T, float* z8,
     a.cstride = screen_window_cstride(L);
   }
   const dim3 grid((a.ngroups + kWinWaves - 1) / kWinWaves);
+  constexpr int NT = kWinWaves * kWinSplit * 64;
   switch (win_slabs(a.H)) {
-    case 8: hipLaunchKernelGGL((screen_window_kernel<8, 1>), grid, dim3(kWinWaves * 64), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((screen_window_kernel<16, 2>), grid, dim3(kWinWaves * 64), 0, s, a); break;
-    default: hipLaunchKernelGGL((screen_window_kernel<32, 4>), grid, dim3(kWinWaves * 64), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((screen_window_kernel<8, 1, kWinSlabsInFlight>), grid, dim3(NT), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((screen_window_kernel<16, 2, kWinSlabsInFlight>), grid, dim3(NT), 0, s, a); break;
+    default: hipLaunchKernelGGL((screen_window_kernel<32, 4, kWinSlabsInFlight>), grid, dim3(NT), 0, s, a); break;
   }
   return hipGetLastError();
 }
