@@ -69,6 +69,10 @@ def parse():
                    help="whole-stream parity against the oracle: 1000 tokens of the tiny fp32 layer and of "
                         "both batch-1 decode layers, 1000 verify steps (T = 5), one 2048-token prefill chunk; "
                         "one JSON line per workload (the exact-refinement counts included)")
+    p.add_argument("--hot", type=int, default=0,
+                   help="decode configs: copy the N experts most chosen over a 400-token calibration stream "
+                        "into the layer's hot region and time the decode stream with it, with a region that "
+                        "catches nothing, and without a region")
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter run: launch eagerly (no graphs), run the router alone, then "
                         "a plain copy of known size that calibrates the byte counters; prints a summary")
@@ -684,6 +688,95 @@ def parity_main(args):
         torch.cuda.empty_cache()
 
 
+def hot_main(args, spec):
+    """Batch-1 decode with the hot-expert region: calibration counts over a
+    separate token stream, the top-N experts copied into the region of every
+    layer copy, then the same timed stream three ways (graph replays, cold
+    router copies as in the default run): no region (the fused decode
+    kernels), the region of the top N, and a region holding one expert that
+    the stream never chooses (the same few-token kernels, no hits)."""
+    import numpy as np
+    import torch
+
+    import synth.device as SD
+    K, W, N = args.steps, args.warmup, args.hot
+    n_rep = 6 if args.mode == "cold" else 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dl = SD.device_layer(spec)
+    routers = [dl.router_eh] + [SD.device_router(spec) for _ in range(n_rep - 1)]
+    layers = [SD.make_layer(dl, max_tokens=1, router=r) for r in routers]
+    ws = layers[0].workspace(1)
+    ncal = 400
+    C = SD.device_tokens(spec, 100000, ncal)
+    X = SD.device_tokens(spec, 0, W + K)
+    idx = torch.zeros((W + K, spec.k), dtype=torch.int32, device=dev)
+    gates = torch.zeros((W + K, spec.k), dtype=torch.float32, device=dev)
+    out = torch.zeros((W + K, spec.H), dtype=torch.float32, device=dev)
+    ci = torch.zeros((ncal, spec.k), dtype=torch.int32, device=dev)
+    cg = torch.zeros((ncal, spec.k), dtype=torch.float32, device=dev)
+    co = torch.zeros((ncal, spec.H), dtype=torch.float32, device=dev)
+    for t in range(ncal):
+        layers[0].grouped_forward(C[t], 1, ci[t], cg[t], 0, co[t], ws)
+    counts = torch.zeros(spec.E, dtype=torch.int32, device=dev)
+    layers[0].expert_counts(ci, ncal * spec.k, counts)
+    hist = counts.cpu().numpy()
+    order = np.lexsort((np.arange(spec.E), -hist))
+    hot = [int(e) for e in order[:N]]
+
+    def run(tag):
+        def token(t):
+            layers[t % n_rep].grouped_forward(X[t], 1, idx[t], gates[t], 0, out[t], ws)
+        for t in range(W):
+            token(t)
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for t in range(W, W + K):
+                    token(t)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            g.replay()
+            torch.cuda.synchronize()
+            ms = median_replay_ms(g, s)
+        res = {"us_per_token": ms * 1e3 / K, "outputs": out[W:W + K].clone(), "idx": idx[W:W + K].cpu().numpy()}
+        log(f"{tag}: {res['us_per_token']:.2f} us per token")
+        return res
+
+    base = run("no region (fused decode kernels)")
+    for L in layers:
+        L.set_hot_experts(hot)
+    with_region = run(f"region of the top {N}")
+    cold = [int(order[-1])]
+    for L in layers:
+        L.set_hot_experts(cold)
+    no_hits = run("region with no hits (few-token kernels)")
+    for L in layers:
+        L.set_hot_experts([])
+    same = bool(torch.equal(base["outputs"].view(torch.int32), with_region["outputs"].view(torch.int32)) and
+                torch.equal(base["outputs"].view(torch.int32), no_hits["outputs"].view(torch.int32)))
+    hit = float(np.isin(with_region["idx"], hot).mean())
+    per_expert = 3 * spec.I * spec.H // 2 + 3 * spec.I * (spec.H // 32) * 2 if spec.expert == 2 else \
+        3 * spec.I * spec.H * (2 if spec.expert == 1 else 4)
+    res = {
+        "metric": f"MoE-layer decode us per token with a hot-expert region ({spec.name})",
+        "value": with_region["us_per_token"], "unit": "us per token", "n_gpus": 1, "steps": K, "warmup": W,
+        "higher_is_better": False, "data": "synthetic",
+        "config": {"workload": f"{spec.name}: batch-1 decode, {K} tokens, {n_rep} router copies; region of the "
+                               f"{N} experts most chosen over {ncal} calibration tokens "
+                               f"({N * per_expert / 1e6:.0f} MB)",
+                   "hit_rate": hit,
+                   "us_per_token_no_region_fused": base["us_per_token"],
+                   "us_per_token_region_no_hits": no_hits["us_per_token"],
+                   "outputs_bitwise_equal": same,
+                   "device_errors": layers[0].device_error()},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -707,6 +800,8 @@ def main():
         return grouped_main(args, spec)
     if args.layers > 1:
         return layers_main(args, spec)
+    if args.hot > 0:
+        return hot_main(args, spec)
     K, W = args.steps, args.warmup
     screen = args.screen == "on"
     n_rep = (6 if screen else 3) if args.mode == "cold" else 1

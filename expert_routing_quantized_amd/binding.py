@@ -29,7 +29,7 @@ EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_
            "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
            "moe_router_logits", "moe_router_screen", "moe_layer_stats",
            "moe_decoder_create", "moe_decoder_destroy", "moe_decoder_buffers", "moe_decoder_step",
-           "moe_decoder_doorbell",
+           "moe_decoder_doorbell", "moe_expert_counts", "moe_layer_set_hot_experts",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_grouped_forward_noalloc.argtypes = [vp, vp, i32, vp, vp, u32, vp, vp]
     lib.moe_device_error.argtypes = [vp, vp, ctypes.POINTER(i32)]
     lib.moe_layer_stats.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint64)]
+    lib.moe_expert_counts.argtypes = [vp, vp, i32, vp, vp]
+    lib.moe_layer_set_hot_experts.argtypes = [vp, ctypes.POINTER(i32), i32, vp]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -90,7 +92,7 @@ def load_library(path: str = LIB_PATH):
                  "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
                  "moe_router_logits", "moe_router_screen", "moe_layer_stats", "moe_abi_version",
                  "moe_decoder_create", "moe_decoder_destroy", "moe_decoder_buffers", "moe_decoder_step",
-                 "moe_decoder_doorbell"]:
+                 "moe_decoder_doorbell", "moe_expert_counts", "moe_layer_set_hot_experts"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -195,6 +197,20 @@ class Layer:
         n = ctypes.c_uint64()
         _check(self.lib.moe_layer_stats(self.handle, _stream(stream), ctypes.byref(n)), "moe_layer_stats")
         return n.value
+
+    def expert_counts(self, idx, n, counts, stream=None):
+        """counts[e] += 1 (uint32 device tensor [E]) for each of the first n
+        indices of the device int32 tensor idx."""
+        _check(self.lib.moe_expert_counts(self.handle, _ptr(idx), n, _ptr(counts), _stream(stream)),
+               "moe_expert_counts")
+
+    def set_hot_experts(self, ids, stream=None):
+        """Copy the listed experts (host sequence of ints) into the layer's hot
+        region; an empty sequence removes it."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(e) for e in ids])
+        _check(self.lib.moe_layer_set_hot_experts(self.handle, arr if n else None, n, _stream(stream)),
+               "moe_layer_set_hot_experts")
 
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32()

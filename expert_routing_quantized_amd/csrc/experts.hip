@@ -73,7 +73,28 @@ struct PairArgs {
   int H, I, E, k, T, P;
   int* dev_flag;
   HintWords* hint;   // batch-1 screen list: the down kernel advances it (block 0), else null
+  const ExpertTiers* tiers;   // the layer's hot-expert region (device memory), else null
 };
+
+// Where expert e's weights are read: the hot region's copy when the layer
+// has one that holds e (e then becomes its slot there), else the pool.  With
+// no region this is a uniform branch and no load.
+struct PoolView {
+  const void *wg, *wu, *wd;
+  const uint16_t *sg, *su, *sd;
+};
+__device__ __forceinline__ PoolView pool_view(const PairArgs& a, int& e) {
+  PoolView v{a.wg, a.wu, a.wd, a.sg, a.su, a.sd};
+  if (a.tiers != nullptr) {
+    const ExpertTiers* t = a.tiers;
+    const int slot = t->loc[e];
+    if (slot >= 0) {
+      v = PoolView{t->wg, t->wu, t->wd, t->sg, t->su, t->sd};
+      e = slot;
+    }
+  }
+  return v;
+}
 
 // Expert of pair p if pair p is the first pair naming it (else -1): the
 // block that owns the first occurrence computes every pair of that expert,
@@ -128,6 +149,7 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
   constexpr int kRowsPerWave = RPW;
   const int i0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
   const size_t rowb = size_t(a.H) / 2;
+  const PoolView pv = pool_view(a, e);
   uint4 wg[kRowsPerWave][MB], wu[kRowsPerWave][MB];
   float dg[kRowsPerWave][MB], du[kRowsPerWave][MB];
   // clamped indices: every load issues unconditionally; out-of-range lanes
@@ -139,10 +161,10 @@ __global__ __launch_bounds__(256) void gateup_q4_kernel(PairArgs a) {
     for (int m = 0; m < MB; ++m) {
       const int b = min(m * 64 + lane, nblk - 1);
       const size_t row = size_t(e) * a.I + i;
-      wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wg) + row * rowb + b * 16);
-      wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wu) + row * rowb + b * 16);
-      dg[r][m] = f16_to_f32(a.sg[row * nblk + b]);
-      du[r][m] = f16_to_f32(a.su[row * nblk + b]);
+      wg[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pv.wg) + row * rowb + b * 16);
+      wu[r][m] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pv.wu) + row * rowb + b * 16);
+      dg[r][m] = f16_to_f32(pv.sg[row * nblk + b]);
+      du[r][m] = f16_to_f32(pv.su[row * nblk + b]);
     }
   }
 #pragma unroll
@@ -367,6 +389,7 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
   const int nch = a.H >> 3;
   constexpr int kRowsPerWave = 2;
   const int i0 = (blockIdx.x * 4 + wave) * kRowsPerWave;
+  const PoolView pv = pool_view(a, e);
   Chunk<WD> wg[kRowsPerWave][CPL], wu[kRowsPerWave][CPL];
 #pragma unroll
   for (int r = 0; r < kRowsPerWave; ++r) {
@@ -374,8 +397,8 @@ __global__ __launch_bounds__(256) void gateup_dense_kernel(PairArgs a) {
 #pragma unroll
     for (int s = 0; s < CPL; ++s) {
       const int c = min(s * 64 + lane, nch - 1);
-      wg[r][s].load(a.wg, row * a.H + c * 8);
-      wu[r][s].load(a.wu, row * a.H + c * 8);
+      wg[r][s].load(pv.wg, row * a.H + c * 8);
+      wu[r][s].load(pv.wu, row * a.H + c * 8);
     }
   }
 #pragma unroll
@@ -546,13 +569,14 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
       if (blockIdx.x == 0) atomicOr(a.dev_flag, bad);
     }
     e = inval ? 0 : e;                                 // addresses stay in range
+    const PoolView pv = pool_view(a, e);
     const size_t row = size_t(e) * a.H + oc;
     const float* hj = a.h + (size_t(t) * k + j) * I;
     float y = 0.f;
     for (int sl = g; sl < nsl; sl += 8) {
       if constexpr (WD == MOE_Q4B32) {
-        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + sl * 16);
-        const float d = f16_to_f32(a.sd[row * nblk + sl]);
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pv.wd) + row * (I / 2) + sl * 16);
+        const float d = f16_to_f32(pv.sd[row * nblk + sl]);
         y += down_lane_partial_q4(w, d, hj + sl * 32);
       } else {
         float hv[8];
@@ -561,7 +585,7 @@ __global__ __launch_bounds__(1024) void down_combine_single_kernel(PairArgs a) {
         hv[0] = h0.x; hv[1] = h0.y; hv[2] = h0.z; hv[3] = h0.w;
         hv[4] = h1.x; hv[5] = h1.y; hv[6] = h1.z; hv[7] = h1.w;
         Chunk<WD> w;
-        w.load(a.wd, row * I + sl * 8);
+        w.load(pv.wd, row * I + sl * 8);
         float p = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) p = fmaf(w.get(i), hv[i], p);
@@ -642,10 +666,11 @@ __global__ __launch_bounds__(64 * kWindowWaves) void down_combine_window_q4_kern
     const bool dup = __ballot(lane < j && vi[u] == e) != 0ull;
     badu[u] = inval ? kDevBadIndex : (dup ? kDevDupIndex : 0);
     e = inval ? 0 : e;                                 // addresses stay in range
+    const PoolView pv = pool_view(a, e);
     const size_t row = size_t(e) * a.H + oc;
     const int sl = min(g, nsl - 1);
-    w[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + sl * 16);
-    d[u] = f16_to_f32(a.sd[row * nblk + sl]);
+    w[u] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pv.wd) + row * (I / 2) + sl * 16);
+    d[u] = f16_to_f32(pv.sd[row * nblk + sl]);
   }
   // 3. h into LDS, flags cleared
 #pragma unroll
@@ -796,15 +821,17 @@ __global__ __launch_bounds__(1024) void down_combine_kernel(PairArgs a) {
       const int u = min(u0 + ug * nw, nu - 1);            // clamped: loads stay in range
       qu[ug] = s_uniq[u];
       eu[ug] = s_idx[qu[ug]];
-      const size_t row = size_t(eu[ug]) * a.H + oc;
+      int ev = eu[ug];
+      const PoolView pv = pool_view(a, ev);
+      const size_t row = size_t(ev) * a.H + oc;
 #pragma unroll
       for (int sp = 0; sp < SPL; ++sp) {
         const int sl = min(g + 8 * sp, nsl - 1);
         if constexpr (WD == MOE_Q4B32) {
-          w[ug][sp].v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.wd) + row * (I / 2) + sl * 16);
-          d[ug][sp] = f16_to_f32(a.sd[row * nblk + sl]);
+          w[ug][sp].v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(pv.wd) + row * (I / 2) + sl * 16);
+          d[ug][sp] = f16_to_f32(pv.sd[row * nblk + sl]);
         } else {
-          w[ug][sp].load(a.wd, row * I + sl * 8);
+          w[ug][sp].load(pv.wd, row * I + sl * 8);
           d[ug][sp] = 1.f;
         }
       }
@@ -885,6 +912,7 @@ static PairArgs pair_args(const Layer& L, const void* x, int T, const int32_t* i
   a.P = T * a.k;
   a.dev_flag = L.dev_flag;
   a.hint = nullptr;
+  a.tiers = L.tiers;
   return a;
 }
 

@@ -11,6 +11,7 @@
 #include <chrono>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "select_screen.h"
 
@@ -215,7 +216,7 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
                         uint32_t flags, float* out, char* w, const Workspace& W, hipStream_t s) {
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
   float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
-  if (flags == MOE_ROUTE_INTERNAL && T == 1 && L.screen) {
+  if (flags == MOE_ROUTE_INTERNAL && T == 1 && L.screen && L.n_hot == 0) {
     // batch-1 decode on the screen: the int8 first pass (with the list),
     // the selection fused with gate/up, then down + combine
     float* z8 = reinterpret_cast<float*>(w + W.z);
@@ -228,7 +229,7 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return MOE_OK;
   }
-  if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T)) {
+  if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T) && L.n_hot == 0) {
     // batch-1 decode: router, then the selection fused with gate/up, then
     // down + combine
     double* z = reinterpret_cast<double*>(w + W.z);
@@ -356,6 +357,7 @@ static void release_layer(Layer& L) {
   if (L.eb8) (void)hipFree(L.eb8);
   if (L.screen_consts) (void)hipFree(L.screen_consts);
   if (L.q8w) (void)hipFree(L.q8w);
+  if (L.hot_buf) (void)hipFree(L.hot_buf);
 }
 
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out) {
@@ -566,6 +568,86 @@ moe_status moe_grouped_forward_noalloc(const moe_layer* layer, const void* x, in
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (moe_status st = grouped_impl(L, x, T, idx, gates, flags, out, static_cast<char*>(L.scratch), W, s))
     return st;
+  return ok();
+}
+
+moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32_t n, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  Layer& L = layer->L;
+  const int E = L.d.n_experts;
+  if (n < 0 || n > E) return fail(MOE_E_RANGE, "n=%d outside [0, n_experts=%d]", n, E);
+  if (n > 0 && !ids) return fail(MOE_E_NULL, "ids is NULL");
+  std::vector<int32_t> loc(size_t(E), -1);
+  for (int i = 0; i < n; ++i) {
+    const int e = ids[i];
+    if (e < 0 || e >= E) return fail(MOE_E_RANGE, "ids[%d]=%d outside [0, %d)", i, e, E);
+    if (loc[e] >= 0) return fail(MOE_E_RANGE, "ids[%d]=%d repeats ids[%d]", i, e, loc[e]);
+    loc[e] = i;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);            // earlier calls may still read the old region
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  if (L.hot_buf) (void)hipFree(L.hot_buf);
+  L.hot_buf = nullptr;
+  L.tiers = nullptr;
+  L.n_hot = 0;
+  if (n == 0) return ok();
+  // per-expert bytes of each array, in the pool's own layout
+  const size_t H = L.d.hidden, I = L.d.inter, N = size_t(n);
+  const bool q4 = L.d.expert_dtype == MOE_Q4B32;
+  const size_t elt = L.d.expert_dtype == MOE_F32 ? 4 : 2;
+  const size_t gu = q4 ? I * H / 2 : I * H * elt, dn = q4 ? H * I / 2 : H * I * elt;
+  const size_t sgu = q4 ? I * (H / 32) * 2 : 0, sdn = q4 ? H * (I / 32) * 2 : 0;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + bytes, 256);
+    return o;
+  };
+  const size_t o_rec = take(sizeof(moe::ExpertTiers)), o_loc = take(size_t(E) * 4), o_ids = take(N * 4);
+  const size_t o_wg = take(N * gu), o_wu = take(N * gu), o_wd = take(N * dn);
+  const size_t o_sg = take(N * sgu), o_su = take(N * sgu), o_sd = take(N * sdn);
+  char* buf = nullptr;
+  if ((e = hipMalloc(reinterpret_cast<void**>(&buf), off)) != hipSuccess) return hip_fail(e, "hipMalloc(hot region)");
+  moe::ExpertTiers rec{};
+  rec.loc = reinterpret_cast<const int32_t*>(buf + o_loc);
+  rec.wg = buf + o_wg;
+  rec.wu = buf + o_wu;
+  rec.wd = buf + o_wd;
+  rec.sg = q4 ? reinterpret_cast<const uint16_t*>(buf + o_sg) : nullptr;
+  rec.su = q4 ? reinterpret_cast<const uint16_t*>(buf + o_su) : nullptr;
+  rec.sd = q4 ? reinterpret_cast<const uint16_t*>(buf + o_sd) : nullptr;
+  const int32_t* dids = reinterpret_cast<const int32_t*>(buf + o_ids);
+  if ((e = hipMemcpyAsync(buf + o_loc, loc.data(), size_t(E) * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(buf + o_ids, ids, N * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(buf + o_rec, &rec, sizeof(rec), hipMemcpyHostToDevice, s)) != hipSuccess ||
+      (e = moe::launch_gather_experts(L.d.w_gate, buf + o_wg, gu, dids, n, s)) != hipSuccess ||
+      (e = moe::launch_gather_experts(L.d.w_up, buf + o_wu, gu, dids, n, s)) != hipSuccess ||
+      (e = moe::launch_gather_experts(L.d.w_down, buf + o_wd, dn, dids, n, s)) != hipSuccess ||
+      (q4 && (e = moe::launch_gather_experts(L.d.s_gate, buf + o_sg, sgu, dids, n, s)) != hipSuccess) ||
+      (q4 && (e = moe::launch_gather_experts(L.d.s_up, buf + o_su, sgu, dids, n, s)) != hipSuccess) ||
+      (q4 && (e = moe::launch_gather_experts(L.d.s_down, buf + o_sd, sdn, dids, n, s)) != hipSuccess) ||
+      (e = hipStreamSynchronize(s)) != hipSuccess) {
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(buf);
+    return hip_fail(e, "hot region copies");
+  }
+  L.hot_buf = buf;
+  L.tiers = reinterpret_cast<const moe::ExpertTiers*>(buf + o_rec);
+  L.n_hot = n;
+  return ok();
+}
+
+moe_status moe_expert_counts(const moe_layer* layer, const int32_t* idx, int32_t n, uint32_t* counts,
+                             void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  if (n < 0) return fail(MOE_E_RANGE, "n=%d is negative", n);
+  if (n == 0) return ok();
+  if (!idx || !counts) return fail(MOE_E_NULL, "idx and counts are required");
+  if (!aligned(idx, 4) || !aligned(counts, 4)) return fail(MOE_E_ALIGN, "idx and counts must be 4-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipError_t e = moe::launch_expert_counts(idx, n, layer->L.d.n_experts, counts, s);
+  if (e != hipSuccess) return hip_fail(e, "expert counts launch");
   return ok();
 }
 

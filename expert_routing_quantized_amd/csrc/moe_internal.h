@@ -54,6 +54,15 @@ __device__ __forceinline__ void kernarg_lines() {
 }
 
 // ------------------------------------------------------------------ layer
+// The hot-expert region (moe_layer_set_hot_experts): compact copies of
+// chosen experts' weights in the pool's own per-expert layout, slot s
+// holding expert ids[s], and where each expert is read from.  Device memory.
+struct ExpertTiers {
+  const int32_t* loc;       // [E]: slot of e in the region, or -1 (read from the pool)
+  const void *wg, *wu, *wd; // [n][I][H], [n][I][H], [n][H][I] in the pool's element format
+  const uint16_t *sg, *su, *sd;   // 4-bit scales per slot (else null)
+};
+
 struct Layer {
   moe_layer_desc d;         // caller's description (pointers to caller weights)
   const void* router_eh;    // expert-major router actually read by the kernels
@@ -74,6 +83,10 @@ struct Layer {
   // the verify windows' screen (2 <= T <= kWinMaxT), when `screen_win`:
   bool screen_win;
   int8_t* q8w;              // owned: the int8 router in MFMA operand order (screen_window.hip)
+  // the hot-expert region, when n_hot > 0 (the few-token path reads through it)
+  int n_hot;
+  void* hot_buf;            // owned: loc table, the ExpertTiers record and the copies
+  const ExpertTiers* tiers; // inside hot_buf (null without a region)
 };
 
 // Verify windows of up to this many tokens route through the int8 screen
@@ -463,6 +476,11 @@ hipError_t launch_select_screen_window(const Layer& L, const void* x, int T, con
 hipError_t launch_decode_screen(const Layer& L, const void* x, const float* z8, const float* g8, const double* xq,
                                 const ScreenList* list, int32_t* idx, float* gates, float* out, float* h,
                                 hipStream_t s);
+// prep.hip: the hot region's copies (rows of `bytes` bytes of src for each
+// listed expert, into consecutive slots of dst) and per-expert counts.
+hipError_t launch_gather_experts(const void* src, void* dst, size_t bytes, const int32_t* ids, int n,
+                                 hipStream_t s);
+hipError_t launch_expert_counts(const int32_t* idx, int n, int E, uint32_t* counts, hipStream_t s);
 // prep.hip: layer creation helpers.
 hipError_t launch_transpose_router(const Layer& L, void* dst, hipStream_t s);
 hipError_t launch_router_norms(const Layer& L, hipStream_t s);

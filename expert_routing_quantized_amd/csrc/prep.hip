@@ -71,3 +71,53 @@ hipError_t launch_router_norms(const Layer& L, hipStream_t s) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// ------------------------------------------------------------ hot region
+// dst slot s <- src expert ids[s]: `bytes` bytes each, copied in units of U
+// (the host picks the widest unit that the pointers' alignment and `bytes`
+// allow).  Grid: (units / 256 rounded up, n).
+template <typename U>
+__global__ __launch_bounds__(256) void gather_experts_kernel(const U* __restrict__ src, U* __restrict__ dst,
+                                                             size_t units, const int32_t* __restrict__ ids) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= units) return;
+  const int slot = blockIdx.y;
+  dst[size_t(slot) * units + i] = src[size_t(ids[slot]) * units + i];
+}
+
+hipError_t launch_gather_experts(const void* src, void* dst, size_t bytes, const int32_t* ids, int n,
+                                 hipStream_t s) {
+  if (n <= 0 || bytes == 0) return hipSuccess;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) | uintptr_t(bytes);
+  auto go = [&](auto unit) {
+    using U = decltype(unit);
+    const size_t units = bytes / sizeof(U);
+    hipLaunchKernelGGL(gather_experts_kernel<U>, dim3(unsigned((units + 255) / 256), unsigned(n)), dim3(256), 0, s,
+                       reinterpret_cast<const U*>(src), reinterpret_cast<U*>(dst), units, ids);
+  };
+  if (al % 16 == 0) go(uint4{});
+  else if (al % 4 == 0) go(uint32_t{});
+  else if (al % 2 == 0) go(uint16_t{});
+  else go(uint8_t{});
+  return hipGetLastError();
+}
+
+// counts[e] += 1 for every valid index among idx[0, n) (the frequency
+// record from which a caller picks the hot set).
+__global__ __launch_bounds__(256) void expert_counts_kernel(const int32_t* __restrict__ idx, int n, int E,
+                                                            uint32_t* __restrict__ counts) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int e = idx[i];
+  if (e >= 0 && e < E) atomicAdd(&counts[e], 1u);
+}
+
+hipError_t launch_expert_counts(const int32_t* idx, int n, int E, uint32_t* counts, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(expert_counts_kernel, dim3((n + 255) / 256), dim3(256), 0, s, idx, n, E, counts);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -240,6 +240,39 @@ moe_status moe_device_error(const moe_layer* layer, void* stream, int32_t* code)
  * selection's certification).  Host pointer; MOE_E_NULL when it is NULL. */
 moe_status moe_layer_stats(const moe_layer* layer, void* stream, uint64_t* exact_refinements);
 
+/* ---- Hot-expert region.
+ *
+ * The pages keep the most-routed experts in the fastest memory and move the
+ * set as the routed topics shift, using a record of how often each expert
+ * is chosen (pyshine source tour, Understanding the Architecture, the
+ * paragraph on three tiers and one residency table; hexlives dispatch, the
+ * paragraph on the calibration step that decides which experts earn the
+ * space).  Here every expert already sits in HBM, so the region is a
+ * compact copy of chosen experts -- fewer DRAM pages and a footprint the
+ * 256 MB Infinity Cache can hold -- which the few-token path (T <= 25
+ * pairs per call: batch-1 decode and verify windows) reads instead of the
+ * pool; larger calls keep reading the pool.  Results are bitwise the same
+ * with or without a region. */
+
+/* Per-expert choice counts: counts[e] += 1 (uint32, device, caller-owned)
+ * for every idx[i] in [0, E) among the n device int32 indices (for example
+ * the idx of moe_grouped_forward calls).  Enqueues one kernel on `stream`;
+ * graph-capturable.  MOE_E_NULL / MOE_E_ALIGN for missing or misaligned
+ * pointers; n == 0 is a no-op. */
+moe_status moe_expert_counts(const moe_layer* layer, const int32_t* idx, int32_t n, uint32_t* counts,
+                             void* stream);
+
+/* Replace the layer's hot region by copies of the n experts ids[0, n) (host
+ * int32, distinct, in [0, E); slot i holds ids[i]); n == 0 removes it.
+ * Synchronises `stream` (before freeing the old region and after the
+ * copies), allocates n * (bytes of one expert) + 4 E + 4 n bytes of device
+ * memory owned by the layer and freed with it.  The layer's pool must hold
+ * the weights that are copied.  Not concurrent with calls that use the layer;
+ * graphs captured before the change keep reading the old region, so
+ * recapture them.  MOE_E_RANGE for n outside [0, E], an index out of range or
+ * repeated; MOE_E_NULL for ids == NULL with n > 0. */
+moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32_t n, void* stream);
+
 /* ---- Batch-1 decode through a stack of layers, one captured graph per layer.
  *
  * The pages' engine composes each token from one captured graph per layer:
