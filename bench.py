@@ -73,6 +73,9 @@ def parse():
                    help="decode configs: copy the N experts most chosen over a 400-token calibration stream "
                         "into the layer's hot region and time the decode stream with it, with a region that "
                         "catches nothing, and without a region")
+    p.add_argument("--host", type=int, default=0,
+                   help="decode configs: move the N experts least chosen over a calibration stream to the "
+                        "host tier (computed by the host's cores) and time the decode stream")
     p.add_argument("--counters", action="store_true",
                    help="hardware-counter run: launch eagerly (no graphs), run the router alone, then "
                         "a plain copy of known size that calibrates the byte counters; prints a summary")
@@ -747,6 +750,33 @@ def hot_main(args, spec):
         return res
 
     base = run("no region (fused decode kernels)")
+    if args.host > 0:
+        host = [int(e) for e in order[spec.E - args.host:]]
+        for L in layers:
+            L.set_host_experts(host)
+        r = run(f"host tier of the {args.host} least chosen experts")
+        for L in layers:
+            L.set_host_experts([])
+        rows = r["idx"]
+        frac = float(np.isin(rows, host).any(axis=1).mean())
+        diff = (r["outputs"] - base["outputs"]).double()
+        rel = float((diff.norm(dim=1) / base["outputs"].double().norm(dim=1)).max())
+        per_expert = 3 * spec.I * spec.H // 2 + 3 * spec.I * (spec.H // 32) * 2
+        res = {
+            "metric": f"MoE-layer decode us per token with host-tier experts ({spec.name})",
+            "value": r["us_per_token"], "unit": "us per token", "n_gpus": 1, "steps": K, "warmup": W,
+            "higher_is_better": False, "data": "synthetic",
+            "config": {"workload": f"{spec.name}: batch-1 decode, {K} tokens, {n_rep} router copies; the "
+                                   f"{args.host} experts least chosen over {ncal} calibration tokens "
+                                   f"({args.host * per_expert / 1e9:.2f} GB) on the host tier",
+                       "tokens_with_host_pairs": frac,
+                       "host_pairs_per_token": float(np.isin(rows, host).sum(axis=1).mean()),
+                       "us_per_token_no_host_tier": base["us_per_token"],
+                       "max_rel_l2_vs_gpu_only": rel,
+                       "device_errors": layers[0].device_error()},
+        }
+        print(json.dumps(res), flush=True)
+        return
     for L in layers:
         L.set_hot_experts(hot)
     with_region = run(f"region of the top {N}")
@@ -800,7 +830,7 @@ def main():
         return grouped_main(args, spec)
     if args.layers > 1:
         return layers_main(args, spec)
-    if args.hot > 0:
+    if args.hot > 0 or args.host > 0:
         return hot_main(args, spec)
     K, W = args.steps, args.warmup
     screen = args.screen == "on"

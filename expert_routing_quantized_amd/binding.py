@@ -30,6 +30,7 @@ EXPORTS = ["moe_layer_create", "moe_layer_destroy", "moe_workspace_bytes", "moe_
            "moe_router_logits", "moe_router_screen", "moe_layer_stats",
            "moe_decoder_create", "moe_decoder_destroy", "moe_decoder_buffers", "moe_decoder_step",
            "moe_decoder_doorbell", "moe_expert_counts", "moe_layer_set_hot_experts",
+           "moe_layer_set_host_experts", "moe_cpu_experts",
            "moe_status_string", "moe_last_error_message", "moe_abi_version"]
 
 
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_layer_stats.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_uint64)]
     lib.moe_expert_counts.argtypes = [vp, vp, i32, vp, vp]
     lib.moe_layer_set_hot_experts.argtypes = [vp, ctypes.POINTER(i32), i32, vp]
+    lib.moe_layer_set_host_experts.argtypes = [vp, ctypes.POINTER(i32), i32, i32, vp]
+    lib.moe_cpu_experts.argtypes = [ctypes.POINTER(LayerDesc), vp, i32, vp, vp, vp, i32]
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -92,7 +95,8 @@ def load_library(path: str = LIB_PATH):
                  "moe_expert_decode", "moe_grouped_forward", "moe_grouped_forward_noalloc", "moe_device_error",
                  "moe_router_logits", "moe_router_screen", "moe_layer_stats", "moe_abi_version",
                  "moe_decoder_create", "moe_decoder_destroy", "moe_decoder_buffers", "moe_decoder_step",
-                 "moe_decoder_doorbell", "moe_expert_counts", "moe_layer_set_hot_experts"]:
+                 "moe_decoder_doorbell", "moe_expert_counts", "moe_layer_set_hot_experts",
+                 "moe_layer_set_host_experts", "moe_cpu_experts"]:
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -111,6 +115,26 @@ def _ptr(t):
     if isinstance(t, int):
         return t
     return t.data_ptr()
+
+
+def _host_ptr(a):
+    """Address of a C-contiguous numpy array (None -> NULL)."""
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def cpu_experts(hidden, n_experts, top_k, inter, act_dtype, expert_dtype, w_gate, w_up, w_down,
+                x, T, idx, gates, out, s_gate=None, s_up=None, s_down=None, n_threads=1):
+    """moe_cpu_experts on host numpy arrays (the pool's arithmetic, no GPU):
+    out [T][H] float32 is written."""
+    lib = load_library()
+    d = LayerDesc(hidden, n_experts, top_k, inter, max(T, 1), act_dtype, expert_dtype, MOE_ROUTER_EH, 0,
+                  None, None, _host_ptr(w_gate), _host_ptr(w_up), _host_ptr(w_down),
+                  _host_ptr(s_gate), _host_ptr(s_up), _host_ptr(s_down))
+    _check(lib.moe_cpu_experts(ctypes.byref(d), _host_ptr(x), T, _host_ptr(idx), _host_ptr(gates),
+                               _host_ptr(out), n_threads), "moe_cpu_experts")
 
 
 def _stream(stream):
@@ -211,6 +235,14 @@ class Layer:
         arr = (ctypes.c_int32 * max(n, 1))(*[int(e) for e in ids])
         _check(self.lib.moe_layer_set_hot_experts(self.handle, arr if n else None, n, _stream(stream)),
                "moe_layer_set_hot_experts")
+
+    def set_host_experts(self, ids, n_threads=0, stream=None):
+        """Move the listed experts (host sequence of ints) to the host tier;
+        an empty sequence removes it."""
+        n = len(ids)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(e) for e in ids])
+        _check(self.lib.moe_layer_set_host_experts(self.handle, arr if n else None, n, n_threads, _stream(stream)),
+               "moe_layer_set_host_experts")
 
     def device_error(self, stream=None) -> int:
         code = ctypes.c_int32()

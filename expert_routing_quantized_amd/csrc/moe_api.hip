@@ -200,6 +200,9 @@ moe_status grouped_check(const Layer& L, const void* x, int32_t T, const int32_t
   if (flags != MOE_ROUTE_INTERNAL && flags != MOE_ROUTE_GIVEN)
     return fail(MOE_E_RANGE, "flags=0x%x must be MOE_ROUTE_INTERNAL or MOE_ROUTE_GIVEN", flags);
   if (T < 0 || T > L.d.max_tokens) return fail(MOE_E_RANGE, "T=%d outside [0, max_tokens=%d]", T, L.d.max_tokens);
+  if (L.host && T > moe::host_tier_tmax(L.host))
+    return fail(MOE_E_RANGE, "T=%d: a layer with host-tier experts serves calls of at most %d tokens", T,
+                moe::host_tier_tmax(L.host));
   if (T == 0) return MOE_OK;
   if (!x || !out) return fail(MOE_E_NULL, "x and out are required");
   if (flags == MOE_ROUTE_GIVEN && (!idx || !gates))
@@ -216,7 +219,7 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
                         uint32_t flags, float* out, char* w, const Workspace& W, hipStream_t s) {
   int32_t* ri = idx ? idx : reinterpret_cast<int32_t*>(w + W.idx);
   float* rg = gates ? gates : reinterpret_cast<float*>(w + W.gates);
-  if (flags == MOE_ROUTE_INTERNAL && T == 1 && L.screen && L.n_hot == 0) {
+  if (flags == MOE_ROUTE_INTERNAL && T == 1 && L.screen && L.tiers == nullptr) {
     // batch-1 decode on the screen: the int8 first pass (with the list),
     // the selection fused with gate/up, then down + combine
     float* z8 = reinterpret_cast<float*>(w + W.z);
@@ -229,7 +232,7 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return MOE_OK;
   }
-  if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T) && L.n_hot == 0) {
+  if (flags == MOE_ROUTE_INTERNAL && !moe::router_uses_mfma(L, T) && moe::decode_fused_fits(L, T) && L.tiers == nullptr) {
     // batch-1 decode: router, then the selection fused with gate/up, then
     // down + combine
     double* z = reinterpret_cast<double*>(w + W.z);
@@ -246,6 +249,13 @@ moe_status grouped_impl(const Layer& L, const void* x, int32_t T, int32_t* idx, 
     if (moe_status st = route_impl(L, x, T, ri, rg, w, W, s)) return st;
   }
   hipError_t e;
+  if (L.host) {                  // the host tier's part on a second stream, beside the GPU's
+    if ((e = moe::host_tier_fork(L.host, x, T, ri, rg, s)) != hipSuccess) return hip_fail(e, "host tier");
+    e = moe::launch_pair_experts(L, x, T, ri, rg, out, reinterpret_cast<float*>(w + (T == 1 ? W.h : W.hm)), s);
+    if (e != hipSuccess) return hip_fail(e, "expert launch");
+    if ((e = moe::host_tier_join(L.host, T, out, s)) != hipSuccess) return hip_fail(e, "host tier");
+    return MOE_OK;
+  }
   if (T == 1)
     e = moe::launch_pair_experts(L, x, 1, ri, rg, out, reinterpret_cast<float*>(w + W.h), s);
   else if (!moe::grouped_uses_mfma(L, T) && moe::pair_path_fits(L, T))
@@ -358,6 +368,8 @@ static void release_layer(Layer& L) {
   if (L.screen_consts) (void)hipFree(L.screen_consts);
   if (L.q8w) (void)hipFree(L.q8w);
   if (L.hot_buf) (void)hipFree(L.hot_buf);
+  delete L.hot_ids;
+  moe::host_tier_destroy(L.host);
 }
 
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out) {
@@ -531,8 +543,11 @@ moe_status moe_expert_decode(const moe_layer* layer, const void* x, const int32_
   if (moe_status st = check_ws(L, 1, ws, ws_bytes, &W)) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* h = reinterpret_cast<float*>(static_cast<char*>(ws) + W.h);
-  hipError_t e = moe::launch_pair_experts(L, x, 1, idx, gates, out, h, s);
+  hipError_t e;
+  if (L.host && (e = moe::host_tier_fork(L.host, x, 1, idx, gates, s)) != hipSuccess) return hip_fail(e, "host tier");
+  e = moe::launch_pair_experts(L, x, 1, idx, gates, out, h, s);
   if (e != hipSuccess) return hip_fail(e, "expert decode launch");
+  if (L.host && (e = moe::host_tier_join(L.host, 1, out, s)) != hipSuccess) return hip_fail(e, "host tier");
   return ok();
 }
 
@@ -571,29 +586,33 @@ moe_status moe_grouped_forward_noalloc(const moe_layer* layer, const void* x, in
   return ok();
 }
 
-moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32_t n, void* stream) {
-  if (moe_status st = check_layer(layer)) return st;
-  Layer& L = layer->L;
+}  // extern "C"
+
+namespace {
+
+// The tier table from the region's experts (L.hot_ids) and the host tier's:
+// slot i of the region holds hot_ids[i]; with a host tier one more slot of
+// zeros, which every host-tier expert points at (the GPU's part of such an
+// expert is then exactly 0).  Synchronises `s`.
+moe_status rebuild_tiers(Layer& L, hipStream_t s) {
   const int E = L.d.n_experts;
-  if (n < 0 || n > E) return fail(MOE_E_RANGE, "n=%d outside [0, n_experts=%d]", n, E);
-  if (n > 0 && !ids) return fail(MOE_E_NULL, "ids is NULL");
-  std::vector<int32_t> loc(size_t(E), -1);
-  for (int i = 0; i < n; ++i) {
-    const int e = ids[i];
-    if (e < 0 || e >= E) return fail(MOE_E_RANGE, "ids[%d]=%d outside [0, %d)", i, e, E);
-    if (loc[e] >= 0) return fail(MOE_E_RANGE, "ids[%d]=%d repeats ids[%d]", i, e, loc[e]);
-    loc[e] = i;
-  }
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipStreamSynchronize(s);            // earlier calls may still read the old region
+  hipError_t e = hipStreamSynchronize(s);            // earlier calls may still read the old table
   if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
   if (L.hot_buf) (void)hipFree(L.hot_buf);
   L.hot_buf = nullptr;
   L.tiers = nullptr;
   L.n_hot = 0;
-  if (n == 0) return ok();
+  const std::vector<int32_t> none;
+  const std::vector<int32_t>& hot = L.hot_ids ? *L.hot_ids : none;
+  const std::vector<int32_t>& cold = L.host ? moe::host_tier_ids(L.host) : none;
+  const int n = int(hot.size());
+  const int nslots = n + (cold.empty() ? 0 : 1);
+  if (nslots == 0) return MOE_OK;
+  std::vector<int32_t> loc(size_t(E), -1);
+  for (int i = 0; i < n; ++i) loc[hot[i]] = i;
+  for (int c : cold) loc[c] = n;
   // per-expert bytes of each array, in the pool's own layout
-  const size_t H = L.d.hidden, I = L.d.inter, N = size_t(n);
+  const size_t H = L.d.hidden, I = L.d.inter, N = size_t(nslots);
   const bool q4 = L.d.expert_dtype == MOE_Q4B32;
   const size_t elt = L.d.expert_dtype == MOE_F32 ? 4 : 2;
   const size_t gu = q4 ? I * H / 2 : I * H * elt, dn = q4 ? H * I / 2 : H * I * elt;
@@ -618,16 +637,19 @@ moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32
   rec.su = q4 ? reinterpret_cast<const uint16_t*>(buf + o_su) : nullptr;
   rec.sd = q4 ? reinterpret_cast<const uint16_t*>(buf + o_sd) : nullptr;
   const int32_t* dids = reinterpret_cast<const int32_t*>(buf + o_ids);
-  if ((e = hipMemcpyAsync(buf + o_loc, loc.data(), size_t(E) * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
-      (e = hipMemcpyAsync(buf + o_ids, ids, N * 4, hipMemcpyHostToDevice, s)) != hipSuccess ||
-      (e = hipMemcpyAsync(buf + o_rec, &rec, sizeof(rec), hipMemcpyHostToDevice, s)) != hipSuccess ||
-      (e = moe::launch_gather_experts(L.d.w_gate, buf + o_wg, gu, dids, n, s)) != hipSuccess ||
-      (e = moe::launch_gather_experts(L.d.w_up, buf + o_wu, gu, dids, n, s)) != hipSuccess ||
-      (e = moe::launch_gather_experts(L.d.w_down, buf + o_wd, dn, dids, n, s)) != hipSuccess ||
-      (q4 && (e = moe::launch_gather_experts(L.d.s_gate, buf + o_sg, sgu, dids, n, s)) != hipSuccess) ||
-      (q4 && (e = moe::launch_gather_experts(L.d.s_up, buf + o_su, sgu, dids, n, s)) != hipSuccess) ||
-      (q4 && (e = moe::launch_gather_experts(L.d.s_down, buf + o_sd, sdn, dids, n, s)) != hipSuccess) ||
-      (e = hipStreamSynchronize(s)) != hipSuccess) {
+  const size_t sizes[6] = {gu, gu, dn, sgu, sgu, sdn};
+  const size_t offs[6] = {o_wg, o_wu, o_wd, o_sg, o_su, o_sd};
+  const void* srcs[6] = {L.d.w_gate, L.d.w_up, L.d.w_down, L.d.s_gate, L.d.s_up, L.d.s_down};
+  e = hipMemcpyAsync(buf + o_loc, loc.data(), size_t(E) * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess && n > 0) e = hipMemcpyAsync(buf + o_ids, hot.data(), size_t(n) * 4, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(buf + o_rec, &rec, sizeof(rec), hipMemcpyHostToDevice, s);
+  for (int a = 0; a < 6 && e == hipSuccess; ++a) {
+    if (sizes[a] == 0) continue;
+    e = moe::launch_gather_experts(srcs[a], buf + offs[a], sizes[a], dids, n, s);
+    if (e == hipSuccess && nslots > n) e = hipMemsetAsync(buf + offs[a] + size_t(n) * sizes[a], 0, sizes[a], s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
     (void)hipStreamSynchronize(s);
     (void)hipFree(buf);
     return hip_fail(e, "hot region copies");
@@ -635,6 +657,81 @@ moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32
   L.hot_buf = buf;
   L.tiers = reinterpret_cast<const moe::ExpertTiers*>(buf + o_rec);
   L.n_hot = n;
+  return MOE_OK;
+}
+
+// ids distinct, in [0, E) and, when `other` is given, not in it.
+moe_status check_ids(const Layer& L, const int32_t* ids, int n, const std::vector<int32_t>* other,
+                     const char* other_name) {
+  const int E = L.d.n_experts;
+  if (n < 0 || n > E) return fail(MOE_E_RANGE, "n=%d outside [0, n_experts=%d]", n, E);
+  if (n > 0 && !ids) return fail(MOE_E_NULL, "ids is NULL");
+  std::vector<int32_t> seen(size_t(E), -1);
+  if (other)
+    for (int e : *other) seen[e] = -2;
+  for (int i = 0; i < n; ++i) {
+    const int e = ids[i];
+    if (e < 0 || e >= E) return fail(MOE_E_RANGE, "ids[%d]=%d outside [0, %d)", i, e, E);
+    if (seen[e] == -2) return fail(MOE_E_RANGE, "ids[%d]=%d is in the %s", i, e, other_name);
+    if (seen[e] >= 0) return fail(MOE_E_RANGE, "ids[%d]=%d repeats ids[%d]", i, e, seen[e]);
+    seen[e] = i;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32_t n, void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  Layer& L = layer->L;
+  const std::vector<int32_t>* host = L.host ? &moe::host_tier_ids(L.host) : nullptr;
+  if (moe_status st = check_ids(L, ids, n, host, "host tier")) return st;
+  delete L.hot_ids;
+  L.hot_ids = n > 0 ? new std::vector<int32_t>(ids, ids + n) : nullptr;
+  if (moe_status st = rebuild_tiers(L, reinterpret_cast<hipStream_t>(stream))) return st;
+  return ok();
+}
+
+moe_status moe_layer_set_host_experts(moe_layer* layer, const int32_t* ids, int32_t n, int32_t n_threads,
+                                      void* stream) {
+  if (moe_status st = check_layer(layer)) return st;
+  Layer& L = layer->L;
+  if (moe_status st = check_ids(L, ids, n, L.hot_ids, "hot region")) return st;
+  if (n_threads < 0 || n_threads > 1024) return fail(MOE_E_RANGE, "n_threads=%d outside [0, 1024]", n_threads);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  moe::host_tier_destroy(L.host);
+  L.host = nullptr;
+  if (n > 0 && (e = moe::host_tier_create(L, ids, n, n_threads, s, &L.host)) != hipSuccess)
+    return hip_fail(e, "host tier");
+  if (moe_status st = rebuild_tiers(L, s)) return st;
+  return ok();
+}
+
+moe_status moe_cpu_experts(const moe_layer_desc* desc, const void* x, int32_t T, const int32_t* idx,
+                           const float* gates, float* out, int32_t n_threads) {
+  if (!desc) return fail(MOE_E_NULL, "desc is NULL");
+  const moe_layer_desc& d = *desc;
+  if (d.act_dtype != MOE_F32 && d.act_dtype != MOE_BF16)
+    return fail(MOE_E_DTYPE, "act_dtype %d unsupported (MOE_F32 or MOE_BF16)", d.act_dtype);
+  if (d.expert_dtype != MOE_F32 && d.expert_dtype != MOE_BF16 && d.expert_dtype != MOE_Q4B32)
+    return fail(MOE_E_DTYPE, "expert_dtype %d unsupported", d.expert_dtype);
+  const int mult = (d.expert_dtype == MOE_Q4B32) ? 32 : 8;
+  if (d.hidden < 8 || d.hidden > moe::kMaxH || d.hidden % mult || d.inter < 8 || d.inter > moe::kMaxI ||
+      d.inter % mult || d.n_experts < 1 || d.top_k < 1 || d.top_k > moe::kMaxK)
+    return fail(MOE_E_GEOMETRY, "hidden=%d inter=%d n_experts=%d top_k=%d unsupported", d.hidden, d.inter,
+                d.n_experts, d.top_k);
+  if (!d.w_gate || !d.w_up || !d.w_down) return fail(MOE_E_NULL, "w_gate, w_up and w_down are required");
+  const bool q4 = d.expert_dtype == MOE_Q4B32;
+  if (q4 && (!d.s_gate || !d.s_up || !d.s_down)) return fail(MOE_E_NULL, "4-bit experts need s_gate, s_up and s_down");
+  if (T < 0) return fail(MOE_E_RANGE, "T=%d is negative", T);
+  if (T == 0) return ok();
+  if (!x || !idx || !gates || !out) return fail(MOE_E_NULL, "x, idx, gates and out are required");
+  if (n_threads < 0 || n_threads > 1024) return fail(MOE_E_RANGE, "n_threads=%d outside [0, 1024]", n_threads);
+  moe::cpu_experts(d, x, T, idx, gates, out, n_threads == 0 ? 1 : n_threads);
   return ok();
 }
 

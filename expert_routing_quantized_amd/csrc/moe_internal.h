@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/moe.h"
 
 namespace moe {
@@ -86,7 +88,9 @@ struct Layer {
   // the hot-expert region, when n_hot > 0 (the few-token path reads through it)
   int n_hot;
   void* hot_buf;            // owned: loc table, the ExpertTiers record and the copies
-  const ExpertTiers* tiers; // inside hot_buf (null without a region)
+  const ExpertTiers* tiers; // inside hot_buf (null without a region or host tier)
+  std::vector<int32_t>* hot_ids;   // owned: the region's experts (null: none)
+  struct HostTier* host;    // owned: the host tier (host_tier.hip), null without one
 };
 
 // Verify windows of up to this many tokens route through the int8 screen
@@ -481,6 +485,18 @@ hipError_t launch_decode_screen(const Layer& L, const void* x, const float* z8, 
 hipError_t launch_gather_experts(const void* src, void* dst, size_t bytes, const int32_t* ids, int n,
                                  hipStream_t s);
 hipError_t launch_expert_counts(const int32_t* idx, int n, int E, uint32_t* counts, hipStream_t s);
+// host_tier.hip: experts computed on the host's cores (moe_layer_set_host_experts).
+struct HostTier;
+hipError_t host_tier_create(const Layer& L, const int32_t* ids, int n, int n_threads, hipStream_t s,
+                            HostTier** out);
+void host_tier_destroy(HostTier* h);
+const std::vector<int32_t>& host_tier_ids(const HostTier* h);
+int host_tier_tmax(const HostTier* h);
+hipError_t host_tier_fork(HostTier* h, const void* x, int T, const int32_t* idx, const float* gates,
+                          hipStream_t s);
+hipError_t host_tier_join(HostTier* h, int T, float* out, hipStream_t s);
+void cpu_experts(const moe_layer_desc& d, const void* x, int T, const int32_t* idx, const float* gates, float* out,
+                 int n_threads);
 // prep.hip: layer creation helpers.
 hipError_t launch_transpose_router(const Layer& L, void* dst, hipStream_t s);
 hipError_t launch_router_norms(const Layer& L, hipStream_t s);

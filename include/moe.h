@@ -273,6 +273,39 @@ moe_status moe_expert_counts(const moe_layer* layer, const int32_t* idx, int32_t
  * repeated; MOE_E_NULL for ids == NULL with n > 0. */
 moe_status moe_layer_set_hot_experts(moe_layer* layer, const int32_t* ids, int32_t n, void* stream);
 
+/* ---- Host tier: experts computed by the host's cores.
+ *
+ * The pages compute the experts the GPU does not hold on the host's cores,
+ * from 4-bit weights in host RAM with wide vector instructions, while the
+ * GPU computes the rest, and add the parts at the combine (pyshine source
+ * tour, Understanding the Architecture, the paragraphs on three tiers and
+ * one residency table and on the CPU pool behind a doorbell). */
+
+/* Move the n experts ids[0, n) (host int32, distinct, in [0, E), none in the
+ * hot region) to the host tier; n == 0 removes it.  Their weights are copied
+ * from the device pool into pinned host memory; from then on the GPU kernels
+ * read an all-zero expert in their place (so their part of the GPU's sum is
+ * exactly 0) and a pool of n_threads host threads (0: up to 16) computes
+ * them.  In each call, on a second stream: the call's indices, gates and
+ * hidden states to pinned memory, a host node that runs the pool, its
+ * output back to the device; the call's stream waits for it before adding it
+ * to the GPU's output (graph-capturable).  Calls on such a layer take at most
+ * floor(256 / k) tokens, run the few-token kernels and must not overlap one
+ * another.  Synchronises `stream`.  MOE_E_RANGE for bad ids or n_threads
+ * outside [0, 1024]. */
+moe_status moe_layer_set_host_experts(moe_layer* layer, const int32_t* ids, int32_t n, int32_t n_threads,
+                                      void* stream);
+
+/* The host pool's arithmetic on caller host arrays, no GPU: for each token t
+ * of the T hidden states x (act_dtype, [T][H]), out[t] (fp32 [H]) = the sum
+ * over j < k in order of gates[t][j] * y_e(x_t), e = idx[t][j] (host int32
+ * and fp32 [T][k]; an index outside [0, E) adds nothing), with y_e =
+ * D_e (silu(G_e x) * (U_e x)) in binary32 from desc's expert pools, which are
+ * HOST pointers here (the router fields are not read).  n_threads threads
+ * (0 or 1: the calling thread alone). */
+moe_status moe_cpu_experts(const moe_layer_desc* desc, const void* x, int32_t T, const int32_t* idx,
+                           const float* gates, float* out, int32_t n_threads);
+
 /* ---- Batch-1 decode through a stack of layers, one captured graph per layer.
  *
  * The pages' engine composes each token from one captured graph per layer:

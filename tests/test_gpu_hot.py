@@ -1,11 +1,14 @@
-"""The hot-expert region on the GPU.
+"""The hot-expert region and the host tier on the GPU.
 
 moe_expert_counts equals a histogram of the routed indices; with the
 most-routed experts copied into the layer's region, batch-1 decode, verify
 windows and moe_expert_decode give the same outputs as without a region,
 bit for bit, and as the oracle's; and the outputs come from the copies:
 overwriting the pool's weights of the hot experts afterwards changes
-nothing, while the same overwrite changes a layer without a region."""
+nothing, while the same overwrite changes a layer without a region.
+Experts moved to the host tier are computed by the host pool: outputs as
+the oracle's, independent of the device pool's copies, the same bits in
+graph replays."""
 import dataclasses
 
 import numpy as np
@@ -174,5 +177,139 @@ def test_hot_region_fullsize_decode():
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 6000, n)
     G.compare(np.concatenate([u[0] for u in b]), np.concatenate([u[1] for u in b]),
               np.concatenate([u[2] for u in b]), o_idx, o_g, o_out, "hot region full size")
+    assert layer.device_error() == 0
+    del layer, dl
+
+
+# ---------------------------------------------------------------- host tier
+@pytest.mark.parametrize("name", list(SPECS))
+def test_host_tier_against_oracle_and_relocated(name):
+    """Experts moved to the host tier (the most chosen ones among them, so
+    most tokens have host pairs): batch-1 decode, windows and
+    moe_expert_decode as the oracle's; overwriting the device pool's copies
+    of those experts afterwards changes nothing (the GPU reads zeros in
+    their place, the host pool its own copies); with a hot region beside it
+    the results are the same bits."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_ON
+    from expert_routing_quantized_amd.binding import MoeError
+    spec = SPECS[name]
+    G.note("host tier", name)
+    dl = cloned(SD.device_layer(spec))
+    L = G.host_oracle(spec)
+    n1, T, nwin = 20, 4, 3
+    first = 700
+    x = SD.device_tokens(spec, first, n1 + T * nwin)
+    layer = SD.make_layer(dl, max_tokens=8, flags=MOE_LAYER_SCREEN_ON)
+    ws1, wsw = layer.workspace(1), layer.workspace(T)
+    ref, fi = run_all(layer, x, n1, T, nwin, ws1, wsw)
+    hist = np.bincount(ref[0].ravel(), minlength=spec.E)
+    order = np.lexsort((np.arange(spec.E), -hist))
+    host = [int(e) for e in order[0:spec.E // 4:2]]          # every other of the most chosen
+    hot = [int(e) for e in order[1:spec.E // 4:2]]
+    layer.set_host_experts(host, n_threads=4)
+    got, _ = run_all(layer, x, n1, T, nwin, ws1, wsw)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, first, n1 + T * nwin)
+    G.compare(got[0], got[1], got[2], o_idx[:n1], o_g[:n1], o_out[:n1], f"{name} host tier batch 1")
+    G.compare(got[3], got[4], got[5], o_idx[n1:], o_g[n1:], o_out[n1:], f"{name} host tier windows")
+    G.compare(got[0], got[1], got[6], o_idx[:n1], o_g[:n1], o_out[:n1], f"{name} host tier expert_decode")
+    assert np.isin(got[0], host).any(axis=1).mean() > 0.5
+    # the device pool's copies of the host experts are not read any more
+    host_t = torch.tensor(host, dtype=torch.long, device="cuda")
+    for f in ("w_gate", "w_up", "w_down"):
+        t = getattr(dl, f)
+        if t.dtype == torch.uint8:
+            t[host_t] = 0x77
+        else:
+            t[host_t] = t[host_t] * 5
+    torch.cuda.synchronize()
+    got2, _ = run_all(layer, x, n1, T, nwin, ws1, wsw)
+    bitwise_equal(got2, got)
+    # a hot region beside the host tier (disjoint sets; overlap refused)
+    with pytest.raises(MoeError):
+        layer.set_hot_experts(host[:1])
+    layer.set_hot_experts(hot)
+    got3, _ = run_all(layer, x, n1, T, nwin, ws1, wsw)
+    bitwise_equal(got3, got)
+    with pytest.raises(MoeError) as e:                      # calls above floor(256 / k) tokens
+        layer.grouped_forward(x, 256 // spec.k + 1, None, None, 0,
+                              torch.empty((1,), device="cuda"), layer.workspace(8))
+    assert e.value.status == -6
+    layer.set_host_experts([])
+    layer.set_hot_experts([])
+    assert layer.device_error() == 0
+
+
+def test_host_tier_graph_replays():
+    """Batch-1 calls with host-tier experts captured in a graph (a host node
+    on a second stream): every replay, with eager calls in between, gives
+    the eager calls' bits."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_ON
+    spec = SPECS["wide_q4"]
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=1, flags=MOE_LAYER_SCREEN_ON)
+    layer.set_host_experts(list(range(0, spec.E, 3)))
+    n = 6
+    x = SD.device_tokens(spec, 40, n)
+    ws = layer.workspace(1)
+    idx = torch.empty((n, spec.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((n, spec.k), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, spec.H), dtype=torch.float32, device="cuda")
+    for t in range(n):
+        layer.grouped_forward(x[t], 1, idx[t], gates[t], 0, out[t], ws)
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for t in range(n):
+                layer.grouped_forward(x[t], 1, idx[t], gates[t], 0, out[t], ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        with torch.cuda.stream(s):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
+        eager = G.run_grouped(layer, x[rep:rep + 1], ws=ws)
+        assert np.array_equal(eager[2].view(np.uint32), ref[rep:rep + 1].cpu().numpy().view(np.uint32))
+    assert layer.device_error() == 0
+
+
+def test_host_tier_fullsize_decode():
+    """The 4-bit decode layer at full size with 300 experts (among them the
+    100 most chosen over 200 tokens) on the host: 16 tokens as the oracle's."""
+    torch = G.torch_mod()
+    import synth.device as SD
+    spec = synth.CONFIGS["decode_q4"]
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=1)
+    ws = layer.workspace(1)
+    calib = SD.device_tokens(spec, 5000, 200)
+    idx = torch.empty((200, spec.k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((200, spec.k), dtype=torch.float32, device="cuda")
+    out = torch.empty((200, spec.H), dtype=torch.float32, device="cuda")
+    counts = torch.zeros(spec.E, dtype=torch.int32, device="cuda")
+    for t in range(200):
+        layer.grouped_forward(calib[t], 1, idx[t], gates[t], 0, out[t], ws)
+    layer.expert_counts(idx, 200 * spec.k, counts)
+    order = np.lexsort((np.arange(spec.E), -counts.cpu().numpy()))
+    host = [int(e) for e in order[:100]] + [int(e) for e in order[-200:]]
+    layer.set_host_experts(host)
+    n = 16
+    x = SD.device_tokens(spec, 7000, n)
+    b = [G.run_grouped(layer, x[t:t + 1], ws=ws) for t in range(n)]
+    gi = np.concatenate([u[0] for u in b])
+    print(f"full size: {100 * np.isin(gi, host).any(axis=1).mean():.0f} % of tokens have host pairs")
+    G.note("host tier full size: oracle")
+    L = G.host_oracle(spec)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 7000, n)
+    G.compare(gi, np.concatenate([u[1] for u in b]), np.concatenate([u[2] for u in b]), o_idx, o_g, o_out,
+              "host tier full size")
     assert layer.device_error() == 0
     del layer, dl
