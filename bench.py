@@ -619,8 +619,9 @@ def layers_main(args, spec):
 def parity_main(args):
     """Every output of whole workloads against the oracle (float64), on the
     seeded synthetic inputs: indices exactly, gates and outputs within the
-    tolerances of the parity tests; also the exact-refinement counts and, at
-    batch 1 through the screen, how many calls selected from its list."""
+    tolerances of the parity tests; also the exact-refinement counts and,
+    through the screen (batch 1 and verify windows), how many calls selected
+    from its list.""" 
     import numpy as np
     import torch
 
@@ -649,7 +650,9 @@ def parity_main(args):
             layer.grouped_forward(X[a:b], T, idx[a:b], gates[a:b], 0, out[a:b], ws)
         torch.cuda.synchronize()
         nref = layer.exact_refinements() - r0
-        listed = int(ws[12:16].view(torch.int32).item()) if (T == 1 and spec.act == synth.DT_BF16) else None
+        # calls whose selection took the screen's list (windows: token 0's list)
+        screened = T <= 8 and spec.act == synth.DT_BF16 and spec.E >= 4096 and spec.H % 32 == 0
+        listed = int(ws[12:16].view(torch.int32).item()) if screened else None
         errs = layer.device_error()
         gi, gg, go = idx.cpu().numpy(), gates.cpu().numpy(), out.cpu().numpy()
         log(f"{name}: {steps} calls of T={T} on the GPU in {time.time() - t0:.1f} s; oracle ...")
