@@ -15,13 +15,12 @@
 //
 // The int8 router is stored a second time in the operands' lane order (q8w):
 // group G of 16 experts and slab s of 64 hidden positions fill one 1 KB
-// block at (s ngroups + G) 1024, lane L's 16 bytes at 16 L holding expert
+// block at (G NS + s) 1024, lane L's 16 bytes at 16 L holding expert
 // 16 G + (L & 15) at positions 64 s + 16 (L >> 4) + [0, 16) -- the lane and
 // byte to reduction-index map of the operands is the same for both, so only
-// the row/column lanes matter.  One wave streams its group's NS blocks, all
-// in flight at once; slab-major order puts the blocks that all waves ask
-// for at the same moment next to one another (group-major order, every wave
-// starting 32 KB from the next, ran at half the rate).  The wave's block
+// the row/column lanes matter.  A wave streams a contiguous run of its
+// group's blocks (group-major order: 0.2-0.8 us faster than slab-major,
+// where all waves ask for neighbouring blocks at once), and its block
 // builds the digit planes in LDS in the same order while they arrive.
 //
 // After the product, lane L holds the exact sums of planes 4 (L >> 4) + r
@@ -66,9 +65,10 @@ __global__ __launch_bounds__(256) void screen_swizzle_kernel(const int8_t* __res
   const size_t c = size_t(blockIdx.x) * 256 + threadIdx.x;
   if (c >= nchunks) return;
   const int L = int(c & 63);
-  const size_t sg = c >> 6;                          // slab-major: block s ngroups + G
-  const int G = int(sg % size_t(ngroups));
-  const int s = int(sg / size_t(ngroups));
+  const size_t sg = c >> 6;                          // block G NS + s
+  const int NS = int(nchunks / 64 / size_t(ngroups));
+  const int G = int(sg / size_t(NS));
+  const int s = int(sg % size_t(NS));
   const int e = 16 * G + (L & 15);
   const int h0 = 64 * s + 16 * (L >> 4);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kWinWaves * kWinSplit * 64, 4) void screen_window_k
   for (int t = 0; t < kWinMaxT; ++t)
     xr[t] = *reinterpret_cast<const xw_t*>(a.x + size_t(min(t, T - 1)) * H + min(c * EPT, H - EPT));
   constexpr int NB = NBUF < NSP ? NBUF : NSP;      // slabs in flight per wave
-  const i32x4* qsrc = reinterpret_cast<const i32x4*>(a.q8w) + (size_t(part * NSP) * a.ngroups + G) * 64 + lane;
-  const size_t qstride = size_t(a.ngroups) * 64;
+  const i32x4* qsrc = reinterpret_cast<const i32x4*>(a.q8w) + (size_t(G) * NS + part * NSP) * 64 + lane;
+  const size_t qstride = 64;
   i32x4 bq[NB];
 #pragma unroll
   for (int s = 0; s < NB; ++s) bq[s] = __builtin_nontemporal_load(qsrc + s * qstride);
