@@ -107,7 +107,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(GroupArgs a) {
     return q * pitch + (j - q * per);
   };
   if (lds) {
-    for (int j = tid; j < a.E; j += 1024) s_c[spos(j)] = a.counts[j];
+    // every count load issued before the first store (a load-store loop
+    // waited one L2 round trip per count)
+    int ld[kScanLdsPer];
+#pragma unroll
+    for (int i = 0; i < kScanLdsPer; ++i) ld[i] = a.counts[min(tid + 1024 * i, a.E - 1)];
+#pragma unroll
+    for (int i = 0; i < kScanLdsPer; ++i)
+      if (tid + 1024 * i < a.E) s_c[spos(tid + 1024 * i)] = ld[i];
     __syncthreads();
   }
   int c[kScanMaxPer];
