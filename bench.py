@@ -630,13 +630,19 @@ def parity_main(args):
     import synth.device as SD
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    plan = [("tiny_f32", 1, 1000), ("decode_bf16", 1, 1000), ("decode_q4", 1, 1000),
-            ("verify_q4", 5, 1000), ("prefill_bf16", 2048, 1)]
-    for name, T, steps in plan:
+    from expert_routing_quantized_amd import MOE_LAYER_FORCE_EXACT_REFINE
+    # the last three rows force every near-tie logit through the exact
+    # refinement (MOE_LAYER_FORCE_EXACT_REFINE), so that path is checked on
+    # whole streams at T = 1, 5 and 2048 too
+    plan = [("tiny_f32", 1, 1000, 0), ("decode_bf16", 1, 1000, 0), ("decode_q4", 1, 1000, 0),
+            ("verify_q4", 5, 1000, 0), ("prefill_bf16", 2048, 1, 0),
+            ("decode_q4", 1, 200, MOE_LAYER_FORCE_EXACT_REFINE), ("verify_q4", 5, 200, MOE_LAYER_FORCE_EXACT_REFINE),
+            ("prefill_bf16", 2048, 1, MOE_LAYER_FORCE_EXACT_REFINE)]
+    for name, T, steps, lflags in plan:
         spec = synth.CONFIGS[name]
         t0 = time.time()
         dl = SD.device_layer(spec)
-        layer = SD.make_layer(dl, max_tokens=T)
+        layer = SD.make_layer(dl, max_tokens=T, flags=lflags)
         n = T * steps
         X = SD.device_tokens(spec, 0, n)
         ws = layer.workspace(T)
@@ -683,7 +689,7 @@ def parity_main(args):
             log(f"{name}: oracle {c1}/{n} tokens")
         rel = np.linalg.norm(go.astype(np.float64) - o_out, axis=1) / np.maximum(np.linalg.norm(o_out, axis=1), 1e-300)
         print(json.dumps({
-            "workload": name, "T": T, "calls": steps, "tokens": n,
+            "workload": name, "T": T, "calls": steps, "tokens": n, "forced_exact_refinement": bool(lflags),
             "idx_mismatched_tokens": int((gi != o_idx).any(axis=1).sum()),
             "gate_max_abs_err": float(np.abs(gg.astype(np.float64) - o_g).max()),
             "out_rel_l2_max": float(rel.max()), "out_rel_l2_median": float(np.median(rel)),
