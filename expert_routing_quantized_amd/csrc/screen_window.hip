@@ -123,6 +123,7 @@ struct WinScreenArgs {
 // in LDS (exactly) by the first part's waves, which finish the group.
 template <int NS, int CPL, int NBUF>
 __global__ __launch_bounds__(kWinWaves * kWinSplit * 64, 4) void screen_window_kernel(WinScreenArgs a) {
+  kernarg_lines<sizeof(WinScreenArgs)>();
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   constexpr int NT = kWinWaves * kWinSplit * 64;     // threads
   constexpr int NWV = kWinWaves * kWinSplit;         // waves
@@ -411,6 +412,7 @@ hipError_t launch_screen_window(const Layer& L, const void* x, int T, float* z8,
 // ------------------------------------------------------------------ select
 template <int ACT, int CPL>
 __global__ __launch_bounds__(kSelectThreads) void select_screen_window_kernel(ScreenSelectArgs b) {
+  kernarg_lines<sizeof(ScreenSelectArgs)>();
   const int t = blockIdx.x;
   select_screen_block<ACT, CPL>(b, t, b.sel.idx + size_t(t) * b.sel.k, b.sel.gates + size_t(t) * b.sel.k);
 }
