@@ -118,14 +118,20 @@ typedef struct {
 
 typedef struct moe_layer moe_layer;   /* opaque; immutable after creation */
 
-/* Validate `desc` and build a layer.  The only call that allocates device
+/* Validate `desc` and build a layer (the pages' hand-off contract refuses a
+ * wrong expert geometry instead of mis-indexing it: pyshine tour,
+ * Understanding the Architecture, paragraph on the expert hand-off).  The
+ * only call that allocates device
  * memory (an expert-major router copy when router_layout is MOE_ROUTER_HE,
  * the per-expert router row norms used to bound rounding errors, the sticky
  * device-error word, and -- for bf16 activations, H a multiple of 32 and
  * E >= 4096 unless MOE_LAYER_SCREEN_OFF, or with MOE_LAYER_SCREEN_ON -- the
  * router screen: an int8 copy
  * of the router with a per-expert scale and residual norms, E H + 12 E
- * bytes, see moe_router_screen) and the only one that synchronises `stream`.
+ * bytes, see moe_router_screen; for H <= 2048 and max_tokens >= 2, unless
+ * MOE_LAYER_WINDOW_SCREEN_OFF, a second int8 copy in matrix-core operand
+ * order for verify windows, E H bytes) and the only one that synchronises
+ * `stream` (with moe_layer_set_hot_experts / moe_layer_set_host_experts).
  * Returns MOE_E_RANGE when the router weights or the bias are not finite.
  * On error *out is set to NULL. */
 moe_status moe_layer_create(const moe_layer_desc* desc, void* stream, moe_layer** out);
@@ -138,7 +144,10 @@ moe_status moe_layer_destroy(moe_layer* layer);
  * figure serves moe_route, moe_expert_decode and moe_grouped_forward). */
 moe_status moe_workspace_bytes(const moe_layer* layer, int32_t T, size_t* bytes);
 
-/* Router + exact top-k + softmax gates for T tokens.
+/* Router + exact top-k + softmax gates for T tokens: the router names the
+ * ten experts a token runs (pyshine tour, Why You Need This and Understanding
+ * the Architecture, the paragraph on the routing kernel); the order is
+ * decided on exact logits, ties to the lower index.
  *   x      [T][H] act_dtype (16-byte aligned)
  *   idx    int32 [T][k] out;  gates fp32 [T][k] out
  *   ws     device workspace of >= moe_workspace_bytes(T) bytes, 256-byte aligned */
@@ -172,7 +181,9 @@ moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, d
                              void* ws, size_t ws_bytes, void* stream);
 
 /* The router's int8 first pass ("screen"), which moe_route and
- * moe_grouped_forward use for T = 1 on layers that have one.  The pages'
+ * moe_grouped_forward use for T = 1 and for verify windows of 2 to 8 tokens
+ * on layers that have one (windows: on the int8 matrix cores, values
+ * identical to the batch-1 screen's).  The pages'
  * routing kernel scores every expert for each token (pyshine tour,
  * Understanding the Architecture, paragraph on the residency tiers); at
  * batch 1 that pass is bound by the router bytes it reads, so the screen
@@ -190,7 +201,11 @@ moe_status moe_router_logits(const moe_layer* layer, const void* x, int32_t T, d
 moe_status moe_router_screen(const moe_layer* layer, const void* x, int32_t T, float* v, float* bound,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Experts of one token: out[H] = sum_j gates[j] * expert_{idx[j]}(x).
+/* Experts of one token: out[H] = sum_j gates[j] * expert_{idx[j]}(x), the
+ * gates applied once, at the combine (pyshine tour, Understanding the
+ * Architecture, paragraph on the expert hand-off); the single-token expert
+ * GEMVs are bandwidth-bound and run on the vector units (hexlives dispatch,
+ * paragraph on the archived tensor-core benchmark).
  *   x [1][H] act_dtype; idx int32 [k]; gates fp32 [k]; out fp32 [H].
  * idx/gates normally come from moe_route; any values are accepted (the
  * gates are used as given), and bad indices raise the device flag. */
@@ -204,6 +219,10 @@ moe_status moe_expert_decode(const moe_layer* layer, const void* x,
 /* The whole layer for T tokens: route (or take the given routing), group the
  * T*k token-expert pairs by expert, run each active expert once over its
  * tokens, and un-permute with the weighted combine.  out fp32 [T][H].
+ * T = 1 is a decode step, 2 <= T <= 8 a verify window of drafted tokens,
+ * larger T a prefill chunk (pyshine tour, Understanding the Architecture,
+ * the paragraphs on guessing then checking drafts and on reading prompts in
+ * chunks).
  * idx and gates are identical to those of moe_route on the same T tokens;
  * row t of out equals moe_expert_decode of x[t] with that routing within
  * fp32 accumulation error (bit for bit at T = 1, where the selection runs
@@ -227,7 +246,9 @@ moe_status moe_grouped_forward_noalloc(const moe_layer* layer, const void* x, in
                                        int32_t* idx, float* gates, uint32_t flags,
                                        float* out, void* stream);
 
-/* Synchronise `stream`, return the sticky device-fault bits in *code (0 when
+/* Faults only the device sees (the hand-off contract's refusal of bad
+ * geometry, per token: pyshine tour, paragraph on the expert hand-off).
+ * Synchronise `stream`, return the sticky device-fault bits in *code (0 when
  * clean: 1 = expert index out of range, 2 = expert repeated within a token,
  * 4 = non-finite router logit, 8 = internal range check) and clear them.
  * Returns MOE_E_DEVICE_FLAG when *code != 0. */
