@@ -409,7 +409,8 @@ def grouped_main(args, spec):
                 "avg_launch_us": router_s * 1e6, "flops_per_launch": router_flops}
     elif win_screen:
         sbytes = screen_bytes(spec) + (T - 1) * spec.H * act
-        roof = {"bound": "hbm", "kernel": ("window screen (moe::screen_window_kernel<32, 4, 4>: int8 router on "
+        nbuf = 8 if 4 <= T <= 6 else 4
+        roof = {"bound": "hbm", "kernel": (f"window screen (moe::screen_window_kernel<32, 4, {nbuf}>: int8 router on "
                                            "v_mfma_i32_16x16x64_i8, exact integer sums)"),
                 "achieved": sbytes / router_s / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": sbytes / router_s / 1e9 / HBM_PEAK_GBS, "traffic": None,
