@@ -426,7 +426,7 @@ def test_windows_and_batch1_share_a_screened_workspace(name, T):
 
 
 # ---------------------------------------------------------------- windows
-WIN_T = [2, 5, 8]
+WIN_T = [2, 4, 5, 6, 8]   # 4-6: the deeper slab ring at H = 2048
 WIN_COUNTS = slice(20, 52)      # the windows' per-token list counters in the hint
 
 
