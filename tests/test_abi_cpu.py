@@ -125,3 +125,14 @@ def test_binding_raises_typed_errors():
     with pytest.raises(B.MoeError) as ei:
         B._check(-2, "where")
     assert ei.value.status == -2
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The bench runs one GPU's share: --gpus above 1 exits non-zero with a
+    message before touching a device."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode != 0
+    assert "--gpus above 1 is not supported" in (r.stdout + r.stderr)
