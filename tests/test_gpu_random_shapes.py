@@ -18,7 +18,7 @@ DTYPES = [(synth.DT_F32, synth.DT_F32), (synth.DT_BF16, synth.DT_BF16), (synth.D
           (synth.DT_F32, synth.DT_BF16), (synth.DT_F32, synth.DT_Q4)]
 
 
-@settings(max_examples=30, deadline=None, derandomize=True, database=None,
+@settings(max_examples=100, deadline=None, derandomize=True, database=None,
           suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
 @given(data=st.data())
 def test_random_small_layers(data):
