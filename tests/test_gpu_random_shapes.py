@@ -45,3 +45,34 @@ def test_random_small_layers(data):
     o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, T)
     G.compare(fi, fg, fo, o_idx, o_g, o_out, f"random H={H} I={I} E={E} k={k} T={T}")
     assert layer.device_error() == 0
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, database=None,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(data=st.data())
+def test_random_window_layers(data):
+    """Verify windows through the int8 window screen at the hidden sizes it
+    is built for (H = 1024 and 2048, its 16- and 32-slab kernels, every ring
+    depth), 4-bit or bf16 experts, with and without bias."""
+    G.torch_mod()
+    import synth.device as SD
+    from expert_routing_quantized_amd import MOE_LAYER_SCREEN_ON
+    expert = data.draw(st.sampled_from([synth.DT_Q4, synth.DT_BF16]), label="expert")
+    H = data.draw(st.sampled_from([1024, 2048]), label="H")
+    I = 32 * data.draw(st.integers(2, 8), label="I/32")
+    E = data.draw(st.integers(40, 600), label="E")
+    k = data.draw(st.integers(1, 10), label="k")
+    T = data.draw(st.integers(2, 8), label="T")
+    bias = data.draw(st.sampled_from([None, 0.37]), label="bias")
+    seed = data.draw(st.integers(1, 10_000), label="seed")
+    spec = synth.small_spec(H=H, E=E, k=k, I=I, act=synth.DT_BF16, expert=expert, bias_alpha=bias,
+                            weight_seed=seed, token_seed=seed + 1, name="random_window")
+    G.note("random window layer", dict(H=H, I=I, E=E, k=k, T=T, expert=expert, bias=bias, seed=seed))
+    dl = SD.device_layer(spec)
+    layer = SD.make_layer(dl, max_tokens=T, flags=MOE_LAYER_SCREEN_ON)
+    x = SD.device_tokens(spec, 0, T)
+    fi, fg, fo = G.run_grouped(layer, x)
+    L = G.host_oracle(spec)
+    o_idx, o_g, _, o_out = G.oracle_tokens(spec, L, 0, T)
+    G.compare(fi, fg, fo, o_idx, o_g, o_out, f"random window H={H} I={I} E={E} k={k} T={T}")
+    assert layer.device_error() == 0
