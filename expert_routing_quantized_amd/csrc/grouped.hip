@@ -431,9 +431,9 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupArgs a) {
 }
 
 // --------------------------------------------------------------- combine
-// One block per (256 outputs, token): the token's k positions and gates go
+// One block per (1024 outputs, token): the token's k positions and gates go
 // to LDS once (with the bad / repeated index check), then each thread sums
-// its output over the pairs in selection order.
+// its 4 outputs over the pairs in selection order.
 __global__ __launch_bounds__(256) void combine_kernel(GroupArgs a) {
   __shared__ int s_pos[kMaxK];
   __shared__ float s_g[kMaxK];
@@ -459,19 +459,37 @@ __global__ __launch_bounds__(256) void combine_kernel(GroupArgs a) {
     if (lane == 0) s_bad = any_bad ? 1 : 0;
   }
   __syncthreads();
-  const int o = blockIdx.x * blockDim.x + threadIdx.x;
+  const int o = 4 * (blockIdx.x * blockDim.x + threadIdx.x);   // 4 consecutive outputs (H % 8 == 0)
   if (o >= a.H) return;
-  // the k rows' values in flight together (groups of 8), summed in j order
-  float acc = 0.f;
+  // the k rows' 16-byte pieces in flight together (groups of 8), each output
+  // summed in j order
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j0 = 0; j0 < k; j0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = (j0 + u < k) ? a.y[size_t(s_pos[j0 + u]) * a.H + o] : 0.f;
+    float4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (j0 + u < k) acc = fmaf(s_g[j0 + u], v[u], acc);
+      v[u] = (j0 + u < k) ? *reinterpret_cast<const float4*>(a.y + size_t(s_pos[j0 + u]) * a.H + o)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k) {
+        const float g = s_g[j0 + u];
+        acc.x = fmaf(g, v[u].x, acc.x);
+        acc.y = fmaf(g, v[u].y, acc.y);
+        acc.z = fmaf(g, v[u].z, acc.z);
+        acc.w = fmaf(g, v[u].w, acc.w);
+      }
   }
-  a.out[size_t(t) * a.H + o] = s_bad ? NAN : acc;
+  if (s_bad) acc = make_float4(NAN, NAN, NAN, NAN);
+  float* dst = a.out + size_t(t) * a.H + o;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {   // the caller's out need not be 16-byte aligned
+    *reinterpret_cast<float4*>(dst) = acc;
+  } else {
+    dst[0] = acc.x;
+    dst[1] = acc.y;
+    dst[2] = acc.z;
+    dst[3] = acc.w;
+  }
 }
 
 hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const int32_t* idx,
@@ -579,7 +597,7 @@ hipError_t launch_grouped_experts(const Layer& L, const void* x, int T, const in
     err = launch_grouped_mfma(a, s);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(combine_kernel, dim3((a.H + 255) / 256, T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_kernel, dim3((a.H + 1023) / 1024, T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
