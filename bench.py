@@ -762,8 +762,10 @@ def hot_main(args, spec):
     base = run("no region (fused decode kernels)")
     if args.host > 0:
         host = [int(e) for e in order[spec.E - args.host:]]
-        for L in layers:
+        for i, L in enumerate(layers):     # each router copy's layer pins its own host copies
+            t1 = time.time()
             L.set_host_experts(host)
+            log(f"host tier set on layer {i + 1}/{len(layers)} in {time.time() - t1:.1f}s")
         r = run(f"host tier of the {args.host} least chosen experts")
         for L in layers:
             L.set_host_experts([])
